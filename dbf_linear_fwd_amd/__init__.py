@@ -1,0 +1,263 @@
+"""Python binding of libdbf, the MI355X DBF linear-forward library.
+
+Double Binary Factorization stores a weight matrix as
+W = diag(a) A diag(mid) B diag(b) with +/-1 factors A (n x k), B (k x m) and
+fp16 scale vectors ("Addition is almost all you need: Compressing large
+language models with double binary factorization", gist.science technical
+summary, §2.1).  The library evaluates Y = X W^T on the GPU without forming W.
+
+This module only marshals arguments to the C ABI declared in include/dbf.h:
+every step of the forward runs in the library's HIP kernels.  PyTorch is
+used for device memory and the current stream, nothing else.  If the shared
+library has not been built the first call raises a RuntimeError; there is no
+fallback of any kind.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+import numpy as np
+
+__all__ = [
+    "DBF_OK", "DBF_ERR_INVALID_ARG", "DBF_ERR_SHAPE", "DBF_ERR_OOM", "DBF_ERR_HIP", "DBF_ERR_UNSUPPORTED",
+    "DBF_PATH_AUTO", "DBF_PATH_DECODE", "DBF_PATH_PREFILL", "EXPORTED_SYMBOLS",
+    "DbfError", "lib", "library_path",
+    "dbf_pack", "dbf_linear_forward", "dbf_linear_forward_ex", "dbf_free", "dbf_get_info",
+    "dbf_status_string", "dbf_pack_signs", "dbf_layout_signs", "dbf_layout_words",
+    "dbf_timing_enable", "dbf_timing_read", "Layer",
+]
+
+DBF_OK = 0
+DBF_ERR_INVALID_ARG = 1
+DBF_ERR_SHAPE = 2
+DBF_ERR_OOM = 3
+DBF_ERR_HIP = 4
+DBF_ERR_UNSUPPORTED = 5
+
+DBF_PATH_AUTO = 0
+DBF_PATH_DECODE = 1
+DBF_PATH_PREFILL = 2
+
+DECODE_MAX_BATCH = 16
+
+EXPORTED_SYMBOLS = (
+    "dbf_pack", "dbf_linear_forward", "dbf_linear_forward_ex", "dbf_free", "dbf_get_info",
+    "dbf_status_string", "dbf_pack_signs", "dbf_layout_signs", "dbf_layout_words",
+    "dbf_timing_enable", "dbf_timing_read",
+)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libdbf.so")
+_lib: Optional[ctypes.CDLL] = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+class DbfError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {dbf_status_string(status)} (status {status})")
+
+
+class _Info(ctypes.Structure):
+    _fields_ = [
+        ("n", ctypes.c_int32), ("m", ctypes.c_int32), ("k", ctypes.c_int32),
+        ("n_pad", ctypes.c_int32), ("m_pad", ctypes.c_int32), ("k_pad", ctypes.c_int32),
+        ("max_batch", ctypes.c_int32), ("device", ctypes.c_int32),
+        ("packed_bytes", ctypes.c_size_t), ("scale_bytes", ctypes.c_size_t),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class _KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double)]
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdbf.so (once).  Raises RuntimeError if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is missing: build it with `python -m dbf_linear_fwd_amd.build` "
+            "(the DBF forward has no non-HIP implementation)")
+    L = ctypes.CDLL(_LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    L.dbf_pack.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, i32, ctypes.POINTER(vp)]
+    L.dbf_pack.restype = ctypes.c_int
+    L.dbf_linear_forward.argtypes = [vp, vp, vp, i32, vp]
+    L.dbf_linear_forward.restype = ctypes.c_int
+    L.dbf_linear_forward_ex.argtypes = [vp, vp, vp, i32, i32, vp]
+    L.dbf_linear_forward_ex.restype = ctypes.c_int
+    L.dbf_free.argtypes = [vp]
+    L.dbf_free.restype = None
+    L.dbf_get_info.argtypes = [vp, ctypes.POINTER(_Info)]
+    L.dbf_get_info.restype = ctypes.c_int
+    L.dbf_status_string.argtypes = [ctypes.c_int]
+    L.dbf_status_string.restype = ctypes.c_char_p
+    L.dbf_pack_signs.argtypes = [vp, i32, i32, vp, i32]
+    L.dbf_pack_signs.restype = ctypes.c_int
+    L.dbf_layout_signs.argtypes = [vp, i32, i32, vp]
+    L.dbf_layout_signs.restype = ctypes.c_int
+    L.dbf_layout_words.argtypes = [i32, i32]
+    L.dbf_layout_words.restype = sz
+    L.dbf_timing_enable.argtypes = [vp, i32]
+    L.dbf_timing_enable.restype = ctypes.c_int
+    L.dbf_timing_read.argtypes = [vp, ctypes.POINTER(_KernelTime), i32, ctypes.POINTER(i32)]
+    L.dbf_timing_read.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(status: int, where: str) -> None:
+    if status != DBF_OK:
+        raise DbfError(status, where)
+
+
+def _ptr(arr: np.ndarray) -> int:
+    return arr.ctypes.data
+
+
+def dbf_status_string(status: int) -> str:
+    return lib().dbf_status_string(int(status)).decode()
+
+
+def _as_signs(S) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(S), dtype=np.int8)
+
+
+def _as_half_bits(v) -> np.ndarray:
+    v = np.asarray(v)
+    if v.dtype == np.uint16:
+        return np.ascontiguousarray(v)
+    return np.ascontiguousarray(v.astype(np.float16)).view(np.uint16)
+
+
+def dbf_pack(n: int, m: int, k: int, A_signs, B_signs, a, mid, b, max_batch: int) -> int:
+    """Build a layer handle (see dbf_pack in include/dbf.h).  Returns the handle as an int."""
+    A = _as_signs(A_signs)
+    B = _as_signs(B_signs)
+    if A.size != n * k or B.size != k * m:
+        raise ValueError("A must hold n*k and B k*m entries")
+    a16, mid16, b16 = _as_half_bits(a), _as_half_bits(mid), _as_half_bits(b)
+    if a16.size != n or mid16.size != k or b16.size != m:
+        raise ValueError("a, mid, b must have lengths n, k, m")
+    h = ctypes.c_void_p()
+    st = lib().dbf_pack(n, m, k, _ptr(A), _ptr(B), _ptr(a16), _ptr(mid16), _ptr(b16), max_batch,
+                        ctypes.byref(h))
+    _check(st, "dbf_pack")
+    return h.value
+
+
+def dbf_linear_forward(h: int, x_ptr: int, y_ptr: int, batch: int, stream: int = 0) -> None:
+    _check(lib().dbf_linear_forward(h, x_ptr, y_ptr, batch, stream), "dbf_linear_forward")
+
+
+def dbf_linear_forward_ex(h: int, x_ptr: int, y_ptr: int, batch: int, path: int, stream: int = 0) -> None:
+    _check(lib().dbf_linear_forward_ex(h, x_ptr, y_ptr, batch, path, stream), "dbf_linear_forward_ex")
+
+
+def dbf_free(h: Optional[int]) -> None:
+    lib().dbf_free(h)
+
+
+def dbf_get_info(h: int) -> Dict[str, int]:
+    info = _Info()
+    _check(lib().dbf_get_info(h, ctypes.byref(info)), "dbf_get_info")
+    return {name: getattr(info, name) for name, _ in _Info._fields_}
+
+
+def dbf_pack_signs(S, words_per_row: Optional[int] = None) -> np.ndarray:
+    """Pack a +/-1 matrix along its columns (host only)."""
+    S = _as_signs(S)
+    if S.ndim != 2:
+        raise ValueError("S must be 2-D")
+    rows, cols = S.shape
+    wpr = (cols + 31) // 32 if words_per_row is None else int(words_per_row)
+    out = np.zeros((rows, max(wpr, 1)), dtype=np.uint32)
+    _check(lib().dbf_pack_signs(_ptr(S), rows, cols, _ptr(out), wpr), "dbf_pack_signs")
+    return out
+
+
+def dbf_layout_words(rows: int, words: int) -> int:
+    return int(lib().dbf_layout_words(rows, words))
+
+
+def dbf_layout_signs(packed: np.ndarray) -> np.ndarray:
+    """Device tiling of packed signs (host only)."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint32)
+    rows, words = packed.shape
+    out = np.zeros(max(dbf_layout_words(rows, words), 1), dtype=np.uint32)
+    _check(lib().dbf_layout_signs(_ptr(packed), rows, words, _ptr(out)), "dbf_layout_signs")
+    return out
+
+
+def dbf_timing_enable(h: int, enable: bool = True) -> None:
+    _check(lib().dbf_timing_enable(h, 1 if enable else 0), "dbf_timing_enable")
+
+
+def dbf_timing_read(h: int) -> Dict[str, Dict[str, float]]:
+    """Per kernel name: launches and summed event time (ms) since the last read."""
+    cap = 32
+    buf = (_KernelTime * cap)()
+    cnt = ctypes.c_int32()
+    _check(lib().dbf_timing_read(h, buf, cap, ctypes.byref(cnt)), "dbf_timing_read")
+    return {buf[i].name.decode(): {"launches": int(buf[i].launches), "total_ms": float(buf[i].total_ms)}
+            for i in range(min(cnt.value, cap))}
+
+
+class Layer:
+    """A DBF linear layer on the current GPU: ``y = layer(x)``.
+
+    A (n x k) and B (k x m) are +/-1 arrays; a, mid, b are fp16 vectors.
+    ``x`` is a contiguous fp16 CUDA (HIP) tensor of shape (batch, m) with
+    batch <= max_batch; the result is a new fp16 tensor of shape (batch, n)
+    computed on the current stream.
+    """
+
+    def __init__(self, A, B, a, mid, b, max_batch: int = 2048):
+        A = np.asarray(A)
+        B = np.asarray(B)
+        if A.ndim != 2 or B.ndim != 2 or A.shape[1] != B.shape[0]:
+            raise ValueError("A must be n x k and B k x m")
+        self.n, self.k = A.shape
+        self.m = B.shape[1]
+        self.max_batch = int(max_batch)
+        self.handle = dbf_pack(self.n, self.m, self.k, A, B, a, mid, b, self.max_batch)
+
+    def info(self) -> Dict[str, int]:
+        return dbf_get_info(self.handle)
+
+    def forward(self, x, out=None, path: int = DBF_PATH_AUTO):
+        import torch
+        if x.dtype != torch.float16 or not x.is_cuda or x.dim() != 2 or x.shape[1] != self.m:
+            raise ValueError(f"x must be a CUDA float16 tensor of shape (batch, {self.m})")
+        if not x.is_contiguous():
+            raise ValueError("x must be contiguous")
+        batch = x.shape[0]
+        if out is None:
+            out = torch.empty((batch, self.n), dtype=torch.float16, device=x.device)
+        elif out.shape != (batch, self.n) or out.dtype != torch.float16 or not out.is_contiguous():
+            raise ValueError("out must be a contiguous float16 tensor of shape (batch, n)")
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        dbf_linear_forward_ex(self.handle, x.data_ptr(), out.data_ptr(), batch, path, stream)
+        return out
+
+    __call__ = forward
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            dbf_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

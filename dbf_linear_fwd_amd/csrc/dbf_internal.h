@@ -1,0 +1,62 @@
+// Internal declarations shared by the runtime and the kernel files.
+#ifndef DBF_INTERNAL_H_
+#define DBF_INTERNAL_H_
+
+#include <cstddef>
+#include <cstdint>
+
+#include "dbf.h"
+
+#if defined(__HIPCC__)
+#define DBF_HD __host__ __device__
+#else
+#define DBF_HD
+#endif
+
+namespace dbf {
+
+// Largest batch served by the decode (signed-sum) kernels.
+constexpr int kDecodeMaxBatch = 16;
+// Decode chunking: words of 32 signs handled by one workgroup along a
+// reduction dimension (1024 elements); bounds the LDS copy of the activations.
+constexpr int kChunkWords = 32;
+
+uint32_t reorder_word(uint32_t canonical);
+
+// Index of word w of row `row` in the tiled device layout (rows in tiles of
+// 64, words in pairs); `words` is the (even) number of words per row.
+DBF_HD inline size_t tiled_index(int row, int w, int words) {
+    return ((static_cast<size_t>(row >> 6) * (words >> 1) + (w >> 1)) * 64 + (row & 63)) * 2 + (w & 1);
+}
+
+struct DecodePlan {
+    int nchunk_m;   // chunks along m (stage 1)
+    int nchunk_k;   // chunks along k (stage 2)
+};
+
+// ---- kernel launchers (return hipError_t as int to keep HIP types out of here)
+
+// Stage 1 of the decode path: partial t[c][r][j] = sum over chunk c of
+// B[j][l] * x[r][l] * b[l]  for j < k_pad, r < batch.
+int launch_decode_stage1(const uint32_t *B_dev, const void *x, const void *b_dev, float *tpart,
+                         int batch, int m, int m_pad, int k_pad, int nchunk_m, void *stream);
+
+// Stage 2: v = mid * sum_c tpart[c]; partial y[c][r][i] = sum over chunk c of A[i][j] * v[r][j].
+int launch_decode_stage2(const uint32_t *A_dev, const float *tpart, const void *mid_dev, float *ypart,
+                         int batch, int n_pad, int k_pad, int nchunk_m, int nchunk_k, void *stream);
+
+// Final: y[r][i] = rne16(a[i] * sum_c ypart[c][r][i]) for i < n.
+int launch_decode_final(const float *ypart, const void *a_dev, void *y, int batch, int n, int n_pad,
+                        int nchunk_k, void *stream);
+
+// Matrix-core product with a sign matrix:
+//   out[i][c] = rne16( sn[c] * sum_kk P[i][kk] * S[c][kk] * (sk ? sk[kk] : 1) )
+// for i < M, c < n_out.  P is fp16 row-major with leading dimension ldp and
+// K valid columns (columns >= K read as 0); S is the tiled sign matrix with
+// `words` words per row and at least n_rows_pad >= n_out rows.
+int launch_sign_gemm(const void *P, int ldp, int M, int K, const uint32_t *S, int words, int n_rows_pad,
+                     const void *sk, const void *sn, void *out, int ldo, int n_out, void *stream);
+
+}  // namespace dbf
+
+#endif  // DBF_INTERNAL_H_

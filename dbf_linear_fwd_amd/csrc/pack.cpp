@@ -1,0 +1,80 @@
+// Host-side sign packing for the DBF layer.
+//
+// The factors A (n x k) and B (k x m) hold only +1 and -1 ("Addition is almost
+// all you need", gist.science technical summary, §2.1), so one bit per entry
+// suffices.  Signs are packed along each matrix's reduction dimension, 32 per
+// uint32, least significant bit first, bit 1 meaning -1.  The device copy is
+// re-tiled so that a wavefront reading one row per lane reads contiguous
+// memory, and the bits inside a word are reordered so that two neighbouring
+// elements land on the two fp16 sign-bit positions after a single shift.
+
+#include <cstdint>
+#include <cstring>
+
+#include "dbf.h"
+#include "dbf_internal.h"
+
+namespace dbf {
+
+// Device bit position of element e (0..31) of a 32-element block.
+static inline uint32_t device_bit(uint32_t e) { return (e & 1u) ? 16u + (e >> 1) : (e >> 1); }
+
+uint32_t reorder_word(uint32_t canonical) {
+    uint32_t out = 0;
+    for (uint32_t e = 0; e < 32; ++e) {
+        out |= ((canonical >> e) & 1u) << device_bit(e);
+    }
+    return out;
+}
+
+}  // namespace dbf
+
+extern "C" dbf_status_t dbf_pack_signs(const int8_t *S, int32_t rows, int32_t cols, uint32_t *out,
+                                       int32_t words_per_row) {
+    if (!S || !out || rows < 1 || cols < 1) return DBF_ERR_INVALID_ARG;
+    const int64_t need = (static_cast<int64_t>(cols) + 31) / 32;
+    if (words_per_row < need) return DBF_ERR_INVALID_ARG;
+    for (int64_t r = 0; r < rows; ++r) {
+        const int8_t *src = S + r * static_cast<int64_t>(cols);
+        uint32_t *dst = out + r * static_cast<int64_t>(words_per_row);
+        for (int64_t w = 0; w < words_per_row; ++w) {
+            uint32_t word = 0;
+            const int64_t c0 = w * 32;
+            for (int64_t p = 0; p < 32 && c0 + p < cols; ++p) {
+                const int8_t s = src[c0 + p];
+                if (s == -1) {
+                    word |= 1u << p;
+                } else if (s != 1) {
+                    return DBF_ERR_INVALID_ARG;
+                }
+            }
+            dst[w] = word;
+        }
+    }
+    return DBF_OK;
+}
+
+extern "C" size_t dbf_layout_words(int32_t rows, int32_t words) {
+    if (rows < 1 || words < 1) return 0;
+    const size_t tiles = (static_cast<size_t>(rows) + 63) / 64;
+    const size_t wpad = (static_cast<size_t>(words) + 1) & ~static_cast<size_t>(1);
+    return tiles * 64 * wpad;
+}
+
+extern "C" dbf_status_t dbf_layout_signs(const uint32_t *in, int32_t rows, int32_t words, uint32_t *out) {
+    if (!in || !out || rows < 1 || words < 1 || (words & 1)) return DBF_ERR_INVALID_ARG;
+    const int64_t tiles = (static_cast<int64_t>(rows) + 63) / 64;
+    const int64_t pairs = words / 2;
+    for (int64_t t = 0; t < tiles; ++t) {
+        for (int64_t p = 0; p < pairs; ++p) {
+            for (int64_t r = 0; r < 64; ++r) {
+                const int64_t row = t * 64 + r;
+                for (int64_t h = 0; h < 2; ++h) {
+                    const int64_t o = ((t * pairs + p) * 64 + r) * 2 + h;
+                    out[o] = row < rows ? dbf::reorder_word(in[row * words + 2 * p + h]) : 0u;
+                }
+            }
+        }
+    }
+    return DBF_OK;
+}

@@ -1,0 +1,356 @@
+// Host runtime of the DBF layer: handle, upload, kernel choice and launch.
+//
+// The layer is W = diag(a) A diag(mid) B diag(b) with ±1 factors A (n x k),
+// B (k x m) and fp16 scales ("Addition is almost all you need", gist.science
+// technical summary, §2.1; the fp16 formats are from Figure 1's caption on the
+// sciencestack.ai page).  This file owns the device copies of the packed
+// signs and the zero-padded scales, the workspace, and the choice between
+// the decode kernels (batch <= 16) and the matrix-core kernels.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "dbf.h"
+#include "dbf_internal.h"
+
+struct dbf_layer {
+    int32_t n = 0, m = 0, k = 0;
+    int32_t n_pad = 0, m_pad = 0, k_pad = 0;
+    int32_t max_batch = 0;
+    int32_t device = 0;
+    int32_t Wk = 0, Wm = 0;  // words per row of A (along k) and of B (along m)
+    uint32_t *A_dev = nullptr;
+    uint32_t *B_dev = nullptr;
+    uint16_t *a_dev = nullptr, *mid_dev = nullptr, *b_dev = nullptr;
+    // workspace
+    float *tpart = nullptr;   // decode stage-1 partials [nchunk_m][16][k_pad]
+    float *ypart = nullptr;   // decode stage-2 partials [nchunk_k][16][n_pad]
+    uint16_t *T = nullptr;    // prefill intermediate    [max_batch][k_pad] fp16
+    size_t packed_bytes = 0, scale_bytes = 0, workspace_bytes = 0;
+    dbf::DecodePlan plan{};
+    // kernel timing
+    bool timing = false;
+    struct Pending {
+        std::string name;
+        hipEvent_t start, stop;
+    };
+    std::vector<Pending> pending;
+    std::vector<hipEvent_t> event_pool;
+    std::map<std::string, std::pair<int64_t, double>> totals;
+};
+
+namespace {
+
+int g_alloc_calls = 0;  // device allocations made by the current dbf_pack call
+
+// Test hook: DBF_TEST_FAIL_ALLOC=N makes the N-th device allocation (1-based)
+// of each dbf_pack call fail as if the device were out of memory.
+bool injected_alloc_failure() {
+    const char *env = std::getenv("DBF_TEST_FAIL_ALLOC");
+    ++g_alloc_calls;
+    if (!env) return false;
+    return std::atoi(env) == g_alloc_calls;
+}
+
+dbf_status_t dev_alloc(void **p, size_t bytes) {
+    *p = nullptr;
+    if (injected_alloc_failure()) return DBF_ERR_OOM;
+    hipError_t e = hipMalloc(p, bytes);
+    if (e == hipErrorOutOfMemory) return DBF_ERR_OOM;
+    if (e != hipSuccess) {
+        *p = nullptr;
+        return DBF_ERR_HIP;
+    }
+    return DBF_OK;
+}
+
+void release(dbf_layer *h) {
+    if (!h) return;
+    (void)hipFree(h->A_dev);
+    (void)hipFree(h->B_dev);
+    (void)hipFree(h->a_dev);
+    (void)hipFree(h->mid_dev);
+    (void)hipFree(h->b_dev);
+    (void)hipFree(h->tpart);
+    (void)hipFree(h->ypart);
+    (void)hipFree(h->T);
+    for (auto &p : h->pending) {
+        (void)hipEventDestroy(p.start);
+        (void)hipEventDestroy(p.stop);
+    }
+    for (auto e : h->event_pool) (void)hipEventDestroy(e);
+    delete h;
+}
+
+int32_t round_up(int32_t v, int32_t q) { return (v + q - 1) / q * q; }
+
+// Pack a +/-1 matrix (rows x cols) along cols and tile it for the device.
+dbf_status_t pack_tiled(const int8_t *S, int32_t rows, int32_t cols, int32_t words,
+                        std::vector<uint32_t> &tiled) {
+    std::vector<uint32_t> canon;
+    try {
+        canon.assign(static_cast<size_t>(rows) * words, 0u);
+        tiled.assign(dbf_layout_words(rows, words), 0u);
+    } catch (const std::bad_alloc &) {
+        return DBF_ERR_OOM;
+    }
+    dbf_status_t st = dbf_pack_signs(S, rows, cols, canon.data(), words);
+    if (st != DBF_OK) return st;
+    return dbf_layout_signs(canon.data(), rows, words, tiled.data());
+}
+
+dbf_status_t upload(void *dst, const void *src, size_t bytes) {
+    return hipMemcpy(dst, src, bytes, hipMemcpyHostToDevice) == hipSuccess ? DBF_OK : DBF_ERR_HIP;
+}
+
+dbf_status_t upload_scales(uint16_t **dst, const uint16_t *src, int32_t len, int32_t len_pad) {
+    std::vector<uint16_t> buf;
+    try {
+        buf.assign(static_cast<size_t>(len_pad), 0u);  // zero padding: the padded entries are +0.0
+    } catch (const std::bad_alloc &) {
+        return DBF_ERR_OOM;
+    }
+    std::memcpy(buf.data(), src, sizeof(uint16_t) * static_cast<size_t>(len));
+    dbf_status_t st = dev_alloc(reinterpret_cast<void **>(dst), buf.size() * sizeof(uint16_t));
+    if (st != DBF_OK) return st;
+    return upload(*dst, buf.data(), buf.size() * sizeof(uint16_t));
+}
+
+hipEvent_t take_event(dbf_layer *h) {
+    if (!h->event_pool.empty()) {
+        hipEvent_t e = h->event_pool.back();
+        h->event_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Launch one kernel through `fn`, bracketed by events when timing is on.
+template <typename F>
+dbf_status_t timed_launch(dbf_layer *h, const char *name, hipStream_t stream, F fn) {
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (h->timing) {
+        e0 = take_event(h);
+        e1 = take_event(h);
+        if (e0 && e1) (void)hipEventRecord(e0, stream);
+    }
+    const int err = fn();
+    if (e0 && e1) {
+        (void)hipEventRecord(e1, stream);
+        h->pending.push_back({name, e0, e1});
+    } else {
+        if (e0) h->event_pool.push_back(e0);
+        if (e1) h->event_pool.push_back(e1);
+    }
+    return err == 0 ? DBF_OK : DBF_ERR_HIP;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" const char *dbf_status_string(dbf_status_t s) {
+    switch (s) {
+        case DBF_OK: return "success";
+        case DBF_ERR_INVALID_ARG: return "invalid argument";
+        case DBF_ERR_SHAPE: return "unsupported or overflowing shape";
+        case DBF_ERR_OOM: return "out of memory";
+        case DBF_ERR_HIP: return "HIP runtime error";
+        case DBF_ERR_UNSUPPORTED: return "unsupported request";
+    }
+    return "unknown status";
+}
+
+extern "C" dbf_status_t dbf_pack(int32_t n, int32_t m, int32_t k, const int8_t *A_signs, const int8_t *B_signs,
+                                 const uint16_t *a, const uint16_t *mid, const uint16_t *b, int32_t max_batch,
+                                 dbf_handle_t *out) {
+    if (out) *out = nullptr;
+    if (!out || !A_signs || !B_signs || !a || !mid || !b) return DBF_ERR_INVALID_ARG;
+    if (n < 1 || m < 1 || k < 1 || max_batch < 1) return DBF_ERR_INVALID_ARG;
+    // Padded sizes must stay inside int32 element counts for the kernels.
+    const int64_t lim = int64_t(1) << 30;
+    if (n > lim || m > lim || k > lim) return DBF_ERR_SHAPE;
+    const int32_t n_pad = round_up(n, 64), m_pad = round_up(m, 64), k_pad = round_up(k, 64);
+    if (int64_t(n_pad) * k_pad > (int64_t(1) << 40) || int64_t(k_pad) * m_pad > (int64_t(1) << 40) ||
+        int64_t(max_batch) * k_pad > (int64_t(1) << 31) || int64_t(max_batch) * n > (int64_t(1) << 31) ||
+        int64_t(max_batch) * m > (int64_t(1) << 31))
+        return DBF_ERR_SHAPE;
+    // Validate every sign before touching the device.
+    for (int64_t i = 0; i < int64_t(n) * k; ++i)
+        if (A_signs[i] != 1 && A_signs[i] != -1) return DBF_ERR_INVALID_ARG;
+    for (int64_t i = 0; i < int64_t(k) * m; ++i)
+        if (B_signs[i] != 1 && B_signs[i] != -1) return DBF_ERR_INVALID_ARG;
+
+    dbf_layer *h = new (std::nothrow) dbf_layer();
+    if (!h) return DBF_ERR_OOM;
+    g_alloc_calls = 0;
+    h->n = n;
+    h->m = m;
+    h->k = k;
+    h->n_pad = n_pad;
+    h->m_pad = m_pad;
+    h->k_pad = k_pad;
+    h->max_batch = max_batch;
+    h->Wk = k_pad / 32;
+    h->Wm = m_pad / 32;
+    h->plan.nchunk_m = (h->Wm + dbf::kChunkWords - 1) / dbf::kChunkWords;
+    h->plan.nchunk_k = (h->Wk + dbf::kChunkWords - 1) / dbf::kChunkWords;
+
+    dbf_status_t st = DBF_OK;
+    if (hipGetDevice(&h->device) != hipSuccess) st = DBF_ERR_HIP;
+
+    std::vector<uint32_t> tiled;
+    if (st == DBF_OK) st = pack_tiled(A_signs, n, k, h->Wk, tiled);
+    if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->A_dev), tiled.size() * 4);
+    if (st == DBF_OK) st = upload(h->A_dev, tiled.data(), tiled.size() * 4);
+    if (st == DBF_OK) h->packed_bytes += tiled.size() * 4;
+    if (st == DBF_OK) st = pack_tiled(B_signs, k, m, h->Wm, tiled);
+    if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->B_dev), tiled.size() * 4);
+    if (st == DBF_OK) st = upload(h->B_dev, tiled.data(), tiled.size() * 4);
+    if (st == DBF_OK) h->packed_bytes += tiled.size() * 4;
+    std::vector<uint32_t>().swap(tiled);
+    if (st == DBF_OK) st = upload_scales(&h->a_dev, a, n, n_pad);
+    if (st == DBF_OK) st = upload_scales(&h->mid_dev, mid, k, k_pad);
+    if (st == DBF_OK) st = upload_scales(&h->b_dev, b, m, m_pad);
+    if (st == DBF_OK) h->scale_bytes = 2 * size_t(n_pad + k_pad + m_pad);
+
+    const int32_t dec_b = max_batch < dbf::kDecodeMaxBatch ? max_batch : dbf::kDecodeMaxBatch;
+    const size_t tpart_bytes = sizeof(float) * size_t(h->plan.nchunk_m) * dec_b * k_pad;
+    const size_t ypart_bytes = sizeof(float) * size_t(h->plan.nchunk_k) * dec_b * n_pad;
+    const size_t T_bytes = sizeof(uint16_t) * size_t(max_batch) * k_pad;
+    if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->tpart), tpart_bytes);
+    if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->ypart), ypart_bytes);
+    if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->T), T_bytes);
+    if (st == DBF_OK) h->workspace_bytes = tpart_bytes + ypart_bytes + T_bytes;
+
+    if (st != DBF_OK) {
+        release(h);
+        return st;
+    }
+    *out = h;
+    return DBF_OK;
+}
+
+extern "C" void dbf_free(dbf_handle_t h) {
+    if (!h) return;
+    int cur = 0;
+    if (hipGetDevice(&cur) == hipSuccess && cur != h->device) {
+        (void)hipSetDevice(h->device);
+        (void)hipDeviceSynchronize();
+        (void)hipSetDevice(cur);
+    } else {
+        (void)hipDeviceSynchronize();
+    }
+    release(h);
+}
+
+extern "C" dbf_status_t dbf_get_info(dbf_handle_t h, dbf_info_t *info) {
+    if (!h || !info) return DBF_ERR_INVALID_ARG;
+    info->n = h->n;
+    info->m = h->m;
+    info->k = h->k;
+    info->n_pad = h->n_pad;
+    info->m_pad = h->m_pad;
+    info->k_pad = h->k_pad;
+    info->max_batch = h->max_batch;
+    info->device = h->device;
+    info->packed_bytes = h->packed_bytes;
+    info->scale_bytes = h->scale_bytes;
+    info->workspace_bytes = h->workspace_bytes;
+    return DBF_OK;
+}
+
+static dbf_status_t forward_decode(dbf_layer *h, const void *x, void *y, int32_t batch, hipStream_t stream) {
+    dbf_status_t st = timed_launch(h, "decode_stage1", stream, [&] {
+        return dbf::launch_decode_stage1(h->B_dev, x, h->b_dev, h->tpart, batch, h->m, h->m_pad, h->k_pad,
+                                         h->plan.nchunk_m, stream);
+    });
+    if (st != DBF_OK) return st;
+    st = timed_launch(h, "decode_stage2", stream, [&] {
+        return dbf::launch_decode_stage2(h->A_dev, h->tpart, h->mid_dev, h->ypart, batch, h->n_pad, h->k_pad,
+                                         h->plan.nchunk_m, h->plan.nchunk_k, stream);
+    });
+    if (st != DBF_OK) return st;
+    return timed_launch(h, "decode_final", stream, [&] {
+        return dbf::launch_decode_final(h->ypart, h->a_dev, y, batch, h->n, h->n_pad, h->plan.nchunk_k, stream);
+    });
+}
+
+static dbf_status_t forward_prefill(dbf_layer *h, const void *x, void *y, int32_t batch, hipStream_t stream) {
+    // T = rne16(mid ⊙ (X (B ⊙ b)ᵀ)), all k_pad columns (padded ones are 0).
+    dbf_status_t st = timed_launch(h, "prefill_gemm1", stream, [&] {
+        return dbf::launch_sign_gemm(x, h->m, batch, h->m, h->B_dev, h->Wm, h->k_pad, h->b_dev, h->mid_dev, h->T,
+                                     h->k_pad, h->k_pad, stream);
+    });
+    if (st != DBF_OK) return st;
+    // Y = rne16(a ⊙ (T Aᵀ)).
+    return timed_launch(h, "prefill_gemm2", stream, [&] {
+        return dbf::launch_sign_gemm(h->T, h->k_pad, batch, h->k_pad, h->A_dev, h->Wk, h->n_pad, nullptr,
+                                     h->a_dev, y, h->n, h->n, stream);
+    });
+}
+
+extern "C" dbf_status_t dbf_linear_forward_ex(dbf_handle_t h, const void *x, void *y, int32_t batch, int32_t path,
+                                              hipStream_t stream) {
+    if (!h) return DBF_ERR_INVALID_ARG;
+    if (batch < 0 || batch > h->max_batch) return DBF_ERR_INVALID_ARG;
+    if (path != DBF_PATH_AUTO && path != DBF_PATH_DECODE && path != DBF_PATH_PREFILL) return DBF_ERR_INVALID_ARG;
+    if (path == DBF_PATH_DECODE && batch > dbf::kDecodeMaxBatch) return DBF_ERR_INVALID_ARG;
+    if (batch == 0) return DBF_OK;
+    if (!x || !y || !aligned16(x) || !aligned16(y)) return DBF_ERR_INVALID_ARG;
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return DBF_ERR_HIP;
+    if (cur != h->device) return DBF_ERR_INVALID_ARG;
+    const bool decode = path == DBF_PATH_DECODE || (path == DBF_PATH_AUTO && batch <= dbf::kDecodeMaxBatch);
+    return decode ? forward_decode(h, x, y, batch, stream) : forward_prefill(h, x, y, batch, stream);
+}
+
+extern "C" dbf_status_t dbf_linear_forward(dbf_handle_t h, const void *x, void *y, int32_t batch,
+                                           hipStream_t stream) {
+    return dbf_linear_forward_ex(h, x, y, batch, DBF_PATH_AUTO, stream);
+}
+
+extern "C" dbf_status_t dbf_timing_enable(dbf_handle_t h, int32_t enable) {
+    if (!h) return DBF_ERR_INVALID_ARG;
+    h->timing = enable != 0;
+    return DBF_OK;
+}
+
+extern "C" dbf_status_t dbf_timing_read(dbf_handle_t h, dbf_kernel_time_t *out, int32_t cap, int32_t *count) {
+    if (!h || !count || cap < 0 || (cap > 0 && !out)) return DBF_ERR_INVALID_ARG;
+    dbf_status_t st = DBF_OK;
+    for (auto &p : h->pending) {
+        float ms = 0.0f;
+        if (hipEventSynchronize(p.stop) != hipSuccess || hipEventElapsedTime(&ms, p.start, p.stop) != hipSuccess) {
+            st = DBF_ERR_HIP;
+        } else {
+            auto &t = h->totals[p.name];
+            t.first += 1;
+            t.second += ms;
+        }
+        h->event_pool.push_back(p.start);
+        h->event_pool.push_back(p.stop);
+    }
+    h->pending.clear();
+    int32_t i = 0;
+    for (auto &kv : h->totals) {
+        if (i < cap) {
+            std::memset(out[i].name, 0, sizeof(out[i].name));
+            std::strncpy(out[i].name, kv.first.c_str(), sizeof(out[i].name) - 1);
+            out[i].launches = kv.second.first;
+            out[i].total_ms = kv.second.second;
+        }
+        ++i;
+    }
+    *count = i;
+    h->totals.clear();
+    return st;
+}

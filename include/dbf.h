@@ -1,0 +1,189 @@
+/*
+ * dbf.h -- C ABI of the Double Binary Factorization (DBF) linear forward for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes
+ * -------------------------
+ * Source: "Addition is almost all you need: Compressing large language models
+ * with double binary factorization", technical summary on gist.science,
+ * §2.1 (mathematical formulation), and Figure 1's caption on the
+ * sciencestack.ai page of the same paper.
+ *
+ * A weight matrix W (n x m; n outputs, m inputs) is stored as
+ *     W = diag(a) * A * diag(mid) * B * diag(b)
+ * with A an n x k matrix of +1/-1, B a k x m matrix of +1/-1 and fp16 scale
+ * vectors a (n), mid (k) and b (m).  (The pages name the middle vector "m";
+ * it is "mid" here because m is also the input width.)  For an fp16 input X
+ * of shape batch x m the layer returns the fp16 matrix Y = X * W^T of shape
+ * batch x n, evaluated right to left as §2.1 orders it: scale the input
+ * columns by b, take signed sums along m with B, scale by mid, take signed
+ * sums along k with A, scale by a.  The products with A and B are additions
+ * and sign flips; no dense W is formed.
+ *
+ * Numerics: fp16 in and out, fp32 accumulation, one round-to-nearest-even
+ * to fp16 at the end; no flush-to-zero.  For batch > 16 the intermediate
+ * (t * mid, batch x k) is rounded once to fp16 because it is the operand of
+ * the 16-bit matrix-core products.
+ *
+ * Packed sign format (the pages fix none; this is the library's own)
+ * ----------------------------------------------------------------------
+ * Signs are packed along each matrix's reduction dimension: A along k, B
+ * along m.  32 signs per uint32, element 32*w + p of a row in bit p of word w
+ * (least significant bit first); bit value 1 means -1, 0 means +1.  Bits past
+ * the end of a row are 0.  This is the format dbf_pack_signs() writes.  The
+ * device keeps its own tiled copy (see dbf_layout_signs()).
+ *
+ * Conventions
+ * -----------
+ * All functions have C linkage and return a status; no C++ exception crosses
+ * this boundary.  Host pointers are read during the call and not retained
+ * (the caller keeps ownership).  Device pointers stay owned by the caller.
+ * Kernel launches are asynchronous on the given stream; a device fault
+ * surfaces at the caller's next synchronisation, not in the return value.
+ */
+#ifndef DBF_H_
+#define DBF_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* The HIP runtime's stream type (identical to its own declaration). */
+typedef struct ihipStream_t *hipStream_t;
+
+typedef struct dbf_layer *dbf_handle_t;
+
+typedef enum {
+    DBF_OK = 0,
+    DBF_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, sign not +/-1, bad batch */
+    DBF_ERR_SHAPE = 2,       /* sizes whose byte counts overflow, or exceed the kernels' limits */
+    DBF_ERR_OOM = 3,         /* device or host allocation failed; nothing leaks */
+    DBF_ERR_HIP = 4,         /* a HIP runtime call failed (includes: no GPU present) */
+    DBF_ERR_UNSUPPORTED = 5  /* a valid request this build does not implement */
+} dbf_status_t;
+
+/* Kernel-path selection for dbf_linear_forward_ex(). */
+typedef enum {
+    DBF_PATH_AUTO = 0,    /* batch <= 16: decode kernels; batch > 16: matrix-core kernels */
+    DBF_PATH_DECODE = 1,  /* signed-sum decode kernels; batch must be <= 16 */
+    DBF_PATH_PREFILL = 2  /* matrix-core (MFMA) kernels; any batch */
+} dbf_path_t;
+
+typedef struct {
+    int32_t n, m, k;          /* logical sizes */
+    int32_t n_pad, m_pad, k_pad; /* device sizes: each rounded up to a multiple of 64 */
+    int32_t max_batch;
+    int32_t device;           /* HIP device the handle lives on */
+    size_t packed_bytes;      /* device bytes of packed A and B (padding included) */
+    size_t scale_bytes;       /* device bytes of a, mid, b (padding included) */
+    size_t workspace_bytes;   /* device scratch owned by the handle */
+} dbf_info_t;
+
+/*
+ * dbf_pack -- build a layer handle from its factors (§2.1: A, B, a, mid, b).
+ *   n, m, k     >= 1: output width, input width, middle dimension.
+ *   A_signs     host int8, n x k row-major, every entry +1 or -1.
+ *   B_signs     host int8, k x m row-major, every entry +1 or -1.
+ *   a, mid, b   host fp16 bit patterns (uint16), lengths n, k, m.
+ *   max_batch   >= 1: largest batch later passed to dbf_linear_forward.
+ *   out         receives the handle.
+ * Packs the signs on the CPU, uploads them and the scales to the current HIP
+ * device, and allocates the handle's workspace for max_batch.  Arguments are
+ * validated before any HIP call.  On failure *out is set to NULL (when out is
+ * not NULL) and nothing leaks.  Errors: DBF_ERR_INVALID_ARG, DBF_ERR_SHAPE,
+ * DBF_ERR_OOM, DBF_ERR_HIP.
+ */
+dbf_status_t dbf_pack(int32_t n, int32_t m, int32_t k,
+                      const int8_t *A_signs, const int8_t *B_signs,
+                      const uint16_t *a, const uint16_t *mid, const uint16_t *b,
+                      int32_t max_batch, dbf_handle_t *out);
+
+/*
+ * dbf_linear_forward -- Y = X W^T for the layer h (§2.1 evaluation order).
+ *   x      device fp16, batch x m row-major (caller-owned, 16-byte aligned).
+ *   y      device fp16, batch x n row-major (caller-owned, 16-byte aligned,
+ *          must not overlap x).  Fully overwritten.
+ *   batch  0 <= batch <= max_batch; 0 returns DBF_OK without launching.
+ *   stream HIP stream to launch on (NULL = the null stream).
+ * Enqueues the kernels and returns; no host synchronisation.  The current
+ * HIP device must be the handle's.  The handle's workspace is shared by its
+ * calls: calls on one handle must be ordered (e.g. all on one stream).
+ * Errors: DBF_ERR_INVALID_ARG (null handle or pointers, batch out of range,
+ * misaligned pointers, wrong device), DBF_ERR_HIP (launch failure).
+ */
+dbf_status_t dbf_linear_forward(dbf_handle_t h, const void *x, void *y, int32_t batch,
+                                hipStream_t stream);
+
+/*
+ * dbf_linear_forward_ex -- dbf_linear_forward with an explicit kernel path
+ * (dbf_path_t).  DBF_PATH_DECODE with batch > 16 is DBF_ERR_INVALID_ARG.
+ * Both paths compute the same function; they differ in the fp16 rounding of
+ * the intermediate (see "Numerics" above).
+ */
+dbf_status_t dbf_linear_forward_ex(dbf_handle_t h, const void *x, void *y, int32_t batch,
+                                   int32_t path, hipStream_t stream);
+
+/* dbf_free -- release the handle and its device memory.  NULL is a no-op.
+ * Synchronises the handle's device first, so pending work on it finishes. */
+void dbf_free(dbf_handle_t h);
+
+/* dbf_get_info -- sizes of the handle (host-only; no HIP call). */
+dbf_status_t dbf_get_info(dbf_handle_t h, dbf_info_t *info);
+
+/* dbf_status_string -- static English text for a status code. */
+const char *dbf_status_string(dbf_status_t s);
+
+/*
+ * dbf_pack_signs -- host-only packer into the format described above.
+ *   S              host int8, rows x cols row-major, entries +1 or -1.
+ *   out            host uint32, rows x words_per_row, fully written
+ *                  (words past ceil(cols/32) are written as 0).
+ *   words_per_row  >= ceil(cols / 32).
+ * Errors: DBF_ERR_INVALID_ARG (null pointer, rows/cols < 1, a sign not +/-1,
+ * words_per_row too small).  Needs no GPU.
+ */
+dbf_status_t dbf_pack_signs(const int8_t *S, int32_t rows, int32_t cols,
+                            uint32_t *out, int32_t words_per_row);
+
+/*
+ * dbf_layout_signs -- host-only: the device copy's tiling of packed signs.
+ *   in         host uint32, rows x words row-major, in the dbf_pack_signs format.
+ *   rows       >= 1;  words >= 1 and even.
+ *   out        host uint32 of dbf_layout_words(rows, words) entries.
+ * Layout: rows are grouped in tiles of 64 (the last tile zero-filled), words
+ * in pairs; out[((tile * (words/2) + pair) * 64 + r) * 2 + h] holds word
+ * 2*pair + h of row 64*tile + r, so one wavefront reading one row per lane
+ * touches 512 contiguous bytes.  Inside each word the bits are reordered so
+ * that element 2q of the 32-element block is at bit q and element 2q+1 at
+ * bit 16+q (q = 0..15): a pair of neighbouring elements then sits at the two
+ * fp16 sign-bit positions after one shift.  Needs no GPU.
+ */
+dbf_status_t dbf_layout_signs(const uint32_t *in, int32_t rows, int32_t words, uint32_t *out);
+size_t dbf_layout_words(int32_t rows, int32_t words);
+
+/*
+ * Kernel timing (measurement support).  When enabled on a handle, every
+ * kernel the handle launches is bracketed by a pair of HIP events recorded on
+ * the same stream; dbf_timing_read() synchronises those events and returns,
+ * per kernel name, the number of launches and the summed elapsed time since
+ * the last read.  Disabled by default; enabling adds two event records per
+ * launch.  dbf_timing_read fills at most `cap` entries and sets *count to the
+ * number of distinct kernels seen.
+ */
+typedef struct {
+    char name[48];
+    int64_t launches;
+    double total_ms;
+} dbf_kernel_time_t;
+
+dbf_status_t dbf_timing_enable(dbf_handle_t h, int32_t enable);
+dbf_status_t dbf_timing_read(dbf_handle_t h, dbf_kernel_time_t *out, int32_t cap, int32_t *count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DBF_H_ */

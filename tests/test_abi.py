@@ -1,0 +1,129 @@
+"""The C-ABI library: it loads, exports everything include/dbf.h declares, and
+validates arguments on the host before any HIP call.  No GPU is needed (and
+no compute is attempted): on a host without a GPU a well-formed dbf_pack
+returns DBF_ERR_HIP."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import dbf_linear_fwd_amd as dbf
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dbf.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dbf_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("dbf_pack", "dbf_linear_forward", "dbf_free"):
+        assert required in names
+    assert set(names) == set(dbf.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = dbf.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", dbf.library_path()], capture_output=True, text=True)
+    exported = set(re.findall(r"\sT\s(dbf_[a-z_]+)$", out.stdout, flags=re.M))
+    assert set(declared_functions()) <= exported
+
+
+def test_header_compiles_as_c():
+    """The header is plain C: it compiles in a C translation unit without HIP headers."""
+    src = '#include "dbf.h"\nint main(void){ dbf_info_t i; (void)i; return (int)DBF_OK; }\n'
+    tmp = os.path.join(ROOT, "_work", "hdr_check")
+    os.makedirs(tmp, exist_ok=True)
+    c = os.path.join(tmp, "t.c")
+    open(c, "w").write(src)
+    res = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                          "-c", c, "-o", os.path.join(tmp, "t.o")], capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+
+
+def test_status_strings():
+    for code in range(6):
+        assert dbf.dbf_status_string(code)
+    assert dbf.dbf_status_string(0) == "success"
+    assert dbf.dbf_status_string(99) == "unknown status"
+
+
+def _small():
+    rng = np.random.default_rng(0)
+    n, m, k = 8, 12, 4
+    A = (1 - 2 * rng.integers(0, 2, size=(n, k))).astype(np.int8)
+    B = (1 - 2 * rng.integers(0, 2, size=(k, m))).astype(np.int8)
+    a = np.ones(n, np.float16).view(np.uint16)
+    mid = np.ones(k, np.float16).view(np.uint16)
+    b = np.ones(m, np.float16).view(np.uint16)
+    return n, m, k, A, B, a, mid, b
+
+
+def _raw_pack(n, m, k, A, B, a, mid, b, max_batch, out=True):
+    L = dbf.lib()
+    h = ctypes.c_void_p()
+    p = lambda arr: None if arr is None else arr.ctypes.data
+    return L.dbf_pack(n, m, k, p(A), p(B), p(a), p(mid), p(b), max_batch, ctypes.byref(h) if out else None), h
+
+
+def test_pack_argument_validation_before_any_hip_call():
+    n, m, k, A, B, a, mid, b = _small()
+    E = dbf.DBF_ERR_INVALID_ARG
+    assert _raw_pack(n, m, k, A, B, a, mid, b, 4, out=False)[0] == E
+    assert _raw_pack(n, m, k, None, B, a, mid, b, 4)[0] == E
+    assert _raw_pack(n, m, k, A, None, a, mid, b, 4)[0] == E
+    assert _raw_pack(n, m, k, A, B, None, mid, b, 4)[0] == E
+    assert _raw_pack(n, m, k, A, B, a, None, b, 4)[0] == E
+    assert _raw_pack(n, m, k, A, B, a, mid, None, 4)[0] == E
+    for bad in ((0, m, k), (n, 0, k), (n, m, 0), (-1, m, k)):
+        assert _raw_pack(*bad, A, B, a, mid, b, 4)[0] == E
+    assert _raw_pack(n, m, k, A, B, a, mid, b, 0)[0] == E
+    A0 = A.copy()
+    A0[3, 2] = 0
+    st, h = _raw_pack(n, m, k, A0, B, a, mid, b, 4)
+    assert st == E and h.value is None
+    B0 = B.copy()
+    B0[1, 5] = 3
+    assert _raw_pack(n, m, k, A, B0, a, mid, b, 4)[0] == E
+    # sizes whose byte counts overflow are a shape error
+    big = 1 << 30
+    assert _raw_pack(big + 1, m, k, A, B, a, mid, b, 4)[0] == dbf.DBF_ERR_SHAPE
+
+
+def test_forward_and_info_validation():
+    L = dbf.lib()
+    assert L.dbf_linear_forward(None, None, None, 1, None) == dbf.DBF_ERR_INVALID_ARG
+    assert L.dbf_linear_forward_ex(None, None, None, 1, 0, None) == dbf.DBF_ERR_INVALID_ARG
+    assert L.dbf_get_info(None, None) == dbf.DBF_ERR_INVALID_ARG
+    assert L.dbf_timing_enable(None, 1) == dbf.DBF_ERR_INVALID_ARG
+    cnt = ctypes.c_int32()
+    assert L.dbf_timing_read(None, None, 0, ctypes.byref(cnt)) == dbf.DBF_ERR_INVALID_ARG
+    L.dbf_free(None)  # no-op
+
+
+def _have_gpu():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_have_gpu(), reason="checks the no-GPU error path")
+def test_pack_without_gpu_reports_hip_error():
+    n, m, k, A, B, a, mid, b = _small()
+    st, h = _raw_pack(n, m, k, A, B, a, mid, b, 4)
+    assert st == dbf.DBF_ERR_HIP and h.value is None
+    with pytest.raises(dbf.DbfError) as e:
+        dbf.dbf_pack(n, m, k, A, B, a, mid, b, 4)
+    assert e.value.status == dbf.DBF_ERR_HIP

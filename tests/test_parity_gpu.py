@@ -1,0 +1,346 @@
+"""GPU parity: the HIP path against the fp64 CPU oracle on the same seeded inputs.
+
+What is compared (the layer is W = diag(a) A diag(mid) B diag(b) with +/-1
+factors and Y = X W^T, "Addition is almost all you need", gist.science
+technical summary, §2.1):
+
+* tolerance suites: per batch row, max_i |y_i - ŷ_i| / max_i |ŷ_i| <= 2e-3
+  against the unrounded fp64 oracle (fp16 output, fp32 accumulation);
+* integer sub-suite: activations in {-1, 0, 1} and scales in {1, 2} (or
+  powers of two), where every partial sum is an exact integer on both sides;
+  the fp16 bits must equal the oracle's single rounding, +0 and -0 equal;
+* both kernel paths (decode for batch <= 16, matrix cores for any batch) on
+  shapes that span several tiles and ragged tails, on the five workloads at
+  full size (large batches on sampled rows), and on edge cases;
+* determinism, batch-row independence, output guard regions, error paths.
+
+Every case prints its name before it touches the GPU.
+"""
+
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import dbf_linear_fwd_amd as dbf
+from oracle import dbf_oracle as O
+from tests import inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def run(layer, X, path=dbf.DBF_PATH_AUTO, max_batch=None):
+    """Forward X (numpy fp16, batch x m) through a fresh handle; returns numpy fp16."""
+    torch = _torch()
+    mb = max_batch or max(1, X.shape[0])
+    L = dbf.Layer(layer.A, layer.B, layer.a, layer.mid, layer.b, max_batch=mb)
+    try:
+        x = torch.from_numpy(np.ascontiguousarray(X)).cuda()
+        y = L.forward(x, path=path)
+        torch.cuda.synchronize()
+        return y.cpu().numpy()
+    finally:
+        L.close()
+
+
+def rel_rows(y16, ref64):
+    y = y16.astype(np.float64)
+    den = np.maximum(np.abs(ref64).max(axis=1), 1e-300)
+    return (np.abs(y - ref64).max(axis=1) / den)
+
+
+def assert_tol(y16, ref64, what):
+    assert np.all(np.isfinite(y16.astype(np.float64))), f"{what}: non-finite output"
+    r = rel_rows(y16, ref64)
+    assert r.max() <= TOL, f"{what}: worst row rel err {r.max():.3e} (row {int(r.argmax())})"
+    return float(r.max())
+
+
+def assert_bits(y16, ref64, what):
+    want = O.rne_fp16(ref64)
+    got_bits = y16.view(np.uint16).copy()
+    want_bits = want.view(np.uint16).copy()
+    # +0 and -0 compare equal
+    got_bits[(got_bits & 0x7FFF) == 0] = 0
+    want_bits[(want_bits & 0x7FFF) == 0] = 0
+    bad = np.argwhere(got_bits != want_bits)
+    assert bad.size == 0, (f"{what}: {len(bad)} mismatches, first at {tuple(bad[0])}: "
+                           f"got {y16[tuple(bad[0])]} want {want[tuple(bad[0])]}")
+
+
+def integer_preconditions(layer, X, prefill: bool):
+    """The realized data keep every partial sum an exact integer in fp32 and
+    (for the matrix-core path) the fp16 intermediate exact."""
+    u, t, v, s, y = O.factored_intermediate(X, layer.A, layer.B, layer.a, layer.mid, layer.b)
+    m, k = layer.m, layer.k
+    assert np.all(np.abs(u) <= 4) and np.abs(t).max() + np.abs(u).sum(axis=1).max() < 2 ** 24
+    assert np.abs(v).sum(axis=1).max() < 2 ** 24
+    if prefill:
+        assert np.abs(v).max() <= 2048, "intermediate would not be exact in fp16"
+    assert np.abs(y).max() <= 65504
+
+
+# --------------------------------------------------------------------------- small and ragged shapes
+
+SHAPES = [
+    # n, m, k
+    (1, 1, 1),
+    (3, 5, 7),
+    (64, 64, 64),
+    (65, 97, 33),
+    (130, 200, 190),
+    (256, 256, 128),
+    (100, 1100, 70),   # m spans two decode chunks and a ragged tail
+    (70, 300, 1500),   # k spans two decode chunks
+]
+
+
+@pytest.mark.parametrize("n,m,k", SHAPES)
+@pytest.mark.parametrize("batch", [1, 3, 16])
+def test_decode_small_shapes(gpu, n, m, k, batch):
+    _say(f"decode n={n} m={m} k={k} batch={batch}")
+    X, A, B, a, mid, b = inputs.tiny_case(1000 + n + m + k + batch, n, m, k, batch, signed_scales=True)
+    L = inputs.Layer("s", n, m, k, A, B, a, mid, b, {})
+    y = run(L, X, dbf.DBF_PATH_DECODE)
+    assert y.shape == (batch, n)
+    assert_tol(y, O.dense_forward(X, A, B, a, mid, b), f"decode {n}x{m}x{k} b{batch}")
+
+
+@pytest.mark.parametrize("n,m,k", SHAPES)
+@pytest.mark.parametrize("batch", [1, 17, 100])
+def test_prefill_small_shapes(gpu, n, m, k, batch):
+    _say(f"prefill n={n} m={m} k={k} batch={batch}")
+    X, A, B, a, mid, b = inputs.tiny_case(2000 + n + m + k + batch, n, m, k, batch, signed_scales=True)
+    L = inputs.Layer("s", n, m, k, A, B, a, mid, b, {})
+    y = run(L, X, dbf.DBF_PATH_PREFILL)
+    assert y.shape == (batch, n)
+    assert_tol(y, O.dense_forward(X, A, B, a, mid, b), f"prefill {n}x{m}x{k} b{batch}")
+
+
+# --------------------------------------------------------------------------- integer sub-suite (bit-exact)
+
+INT_SHAPES = [
+    (1, 1, 1, 1),
+    (65, 97, 33, 5),
+    (256, 256, 128, 16),
+    (300, 1100, 200, 9),
+]
+
+
+@pytest.mark.parametrize("n,m,k,batch", INT_SHAPES)
+@pytest.mark.parametrize("path", [dbf.DBF_PATH_DECODE, dbf.DBF_PATH_PREFILL])
+def test_integer_bit_exact_small(gpu, n, m, k, batch, path):
+    _say(f"integer n={n} m={m} k={k} batch={batch} path={path}")
+    L = inputs.integer_layer("i", n, m, k, 77 + n, (batch,), a_vals=(0.5, 1.0), mid_vals=(1.0, 2.0),
+                             b_vals=(1.0, 2.0))
+    X = L.X[batch]
+    integer_preconditions(L, X, prefill=path == dbf.DBF_PATH_PREFILL)
+    y = run(L, X, path)
+    assert_bits(y, O.factored_forward(X, L.A, L.B, L.a, L.mid, L.b), f"integer {n}x{m}x{k}")
+
+
+# Full-size shapes of the five workloads with small-integer values.  Where
+# b, mid in {1, 2} could overflow fp16 at the output (the 14336-wide layers),
+# b = mid = 1.
+INT_FULL = [
+    ("c1", 256, 256, 128, (1.0, 2.0)),
+    ("c2", 4096, 4096, 2048, (1.0, 2.0)),
+    ("c3", 4096, 4096, 4096, (1.0, 2.0)),
+    ("c4-up", 14336, 4096, 4800, (1.0,)),
+    ("c4-down", 4096, 14336, 4800, (1.0,)),
+]
+
+
+@pytest.mark.parametrize("name,n,m,k,vals", INT_FULL, ids=[c[0] for c in INT_FULL])
+@pytest.mark.parametrize("batch,path", [(1, dbf.DBF_PATH_DECODE), (16, dbf.DBF_PATH_DECODE),
+                                        (16, dbf.DBF_PATH_PREFILL), (2048, dbf.DBF_PATH_PREFILL)])
+def test_integer_bit_exact_full_size(gpu, name, n, m, k, vals, batch, path):
+    _say(f"integer full {name} batch={batch} path={path}")
+    L = inputs.integer_layer(name, n, m, k, 5000 + n + k, (batch,), a_vals=(1.0,), mid_vals=vals, b_vals=vals)
+    X = L.X[batch]
+    rows = np.arange(batch) if batch <= 16 else np.random.default_rng(1).choice(batch, 12, replace=False)
+    ref = O.sampled_forward(X, L.A, L.B, L.a, L.mid, L.b, rows, np.arange(n))
+    assert np.abs(ref).max() <= 65504
+    if path == dbf.DBF_PATH_PREFILL:
+        u, t, v, s, y = O.factored_intermediate(X[rows], L.A, L.B, L.a, L.mid, L.b)
+        assert np.abs(v).max() <= 2048
+    y = run(L, X, path)
+    assert_bits(y[rows], ref, f"integer full {name} b{batch}")
+
+
+# --------------------------------------------------------------------------- the five workloads
+
+def _workload_cases():
+    cases = []
+    for cid in inputs.CONFIG_IDS:
+        for bt in {1: (1,), 2: (1, 16), 3: (1, 16, 2048), 4: (1, 2048), 5: (1, 2048)}[cid]:
+            cases.append((cid, bt))
+    return cases
+
+
+@pytest.mark.parametrize("cid,batch", _workload_cases(), ids=[f"c{c}-b{b}" for c, b in _workload_cases()])
+def test_workload_tolerance(gpu, cid, batch):
+    cfg = inputs.config(cid)
+    for L in cfg.layers:
+        _say(f"workload c{cid} layer={L.name} batch={batch}")
+        X = L.X[batch]
+        rows = np.arange(batch) if batch <= 16 else np.random.default_rng(cid).choice(batch, 12, replace=False)
+        ref = O.sampled_forward(X, L.A, L.B, L.a, L.mid, L.b, rows, np.arange(L.n))
+        y = run(L, X)
+        err = assert_tol(y[rows], ref, f"c{cid} {L.name} b{batch}")
+        _say(f"  worst row rel err {err:.3e}")
+
+
+# --------------------------------------------------------------------------- invariants and edge cases
+
+def test_determinism_and_batch_independence(gpu):
+    torch = _torch()
+    L = inputs.random_layer("d", 1000, 1300, 600, 9, 0.05, 1.0, 0.05, (16, 40))
+    for path, bt in ((dbf.DBF_PATH_DECODE, 16), (dbf.DBF_PATH_PREFILL, 40)):
+        _say(f"determinism path={path} batch={bt}")
+        X = L.X[bt]
+        H = dbf.Layer(L.A, L.B, L.a, L.mid, L.b, max_batch=bt)
+        try:
+            x = torch.from_numpy(X).cuda()
+            y1 = H.forward(x, path=path).cpu().numpy()
+            y2 = H.forward(x, path=path).cpu().numpy()
+            assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
+            for r in (0, 5, bt - 1):
+                yr = H.forward(x[r:r + 1].clone(), path=path).cpu().numpy()
+                assert np.array_equal(yr[0].view(np.uint16), y1[r].view(np.uint16)), f"row {r}"
+        finally:
+            H.close()
+
+
+def test_output_guard_regions(gpu):
+    """No write outside y: the output slice sits between two guard regions."""
+    torch = _torch()
+    L = inputs.random_layer("g", 333, 257, 129, 4, 0.05, 1.0, 0.05, (7, 33))
+    H = dbf.Layer(L.A, L.B, L.a, L.mid, L.b, max_batch=64)
+    try:
+        for bt, path in ((7, dbf.DBF_PATH_DECODE), (33, dbf.DBF_PATH_PREFILL)):
+            _say(f"guard batch={bt} path={path}")
+            guard = 4096
+            buf = torch.full((guard * 2 + bt * L.n,), 12345.0, dtype=torch.float16, device="cuda")
+            out = buf[guard:guard + bt * L.n].view(bt, L.n)
+            x = torch.from_numpy(L.X[bt]).cuda()
+            H.forward(x, out=out, path=path)
+            torch.cuda.synchronize()
+            b = buf.cpu().numpy()
+            assert np.all(b[:guard] == np.float16(12345.0)) and np.all(b[-guard:] == np.float16(12345.0))
+            assert_tol(out.cpu().numpy(), O.dense_forward(L.X[bt], L.A, L.B, L.a, L.mid, L.b), "guard")
+    finally:
+        H.close()
+
+
+def test_sign_flip_symmetry_on_gpu(gpu):
+    """Negating row i of A together with a_i leaves the output unchanged."""
+    L = inputs.random_layer("f", 200, 300, 100, 6, 0.05, 1.0, 0.05, (4,))
+    A2, a2 = L.A.copy(), L.a.copy()
+    A2[[3, 50, 199]] *= -1
+    a2[[3, 50, 199]] = -a2[[3, 50, 199]]
+    L2 = inputs.Layer("f2", L.n, L.m, L.k, A2, L.B, a2, L.mid, L.b, L.X)
+    for path in (dbf.DBF_PATH_DECODE, dbf.DBF_PATH_PREFILL):
+        _say(f"sign flip path={path}")
+        y1 = run(L, L.X[4], path)
+        y2 = run(L2, L.X[4], path)
+        assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
+
+
+def test_zero_input_and_zero_batch(gpu):
+    torch = _torch()
+    L = inputs.random_layer("z", 64, 96, 32, 2, 0.05, 1.0, 0.05, (3,))
+    _say("zero input")
+    for path in (dbf.DBF_PATH_DECODE, dbf.DBF_PATH_PREFILL):
+        y = run(L, np.zeros((3, 96), np.float16), path)
+        assert np.all(y.astype(np.float64) == 0)
+    _say("zero batch")
+    H = dbf.Layer(L.A, L.B, L.a, L.mid, L.b, max_batch=4)
+    try:
+        x = torch.zeros((0, 96), dtype=torch.float16, device="cuda")
+        y = H.forward(x)
+        assert y.shape == (0, 64)
+        dbf.dbf_linear_forward(H.handle, 0, 0, 0, 0)   # batch 0 with null pointers: no launch
+    finally:
+        H.close()
+
+
+def test_error_paths_on_gpu(gpu):
+    torch = _torch()
+    L = inputs.random_layer("e", 64, 96, 32, 3, 0.05, 1.0, 0.05, (20,))
+    H = dbf.Layer(L.A, L.B, L.a, L.mid, L.b, max_batch=20)
+    try:
+        _say("error paths")
+        x = torch.from_numpy(L.X[20]).cuda()
+        y = torch.empty((20, 64), dtype=torch.float16, device="cuda")
+        with pytest.raises(dbf.DbfError) as e:
+            dbf.dbf_linear_forward(H.handle, x.data_ptr(), y.data_ptr(), 21, 0)
+        assert e.value.status == dbf.DBF_ERR_INVALID_ARG
+        with pytest.raises(dbf.DbfError):
+            dbf.dbf_linear_forward(H.handle, x.data_ptr(), y.data_ptr(), -1, 0)
+        with pytest.raises(dbf.DbfError):
+            dbf.dbf_linear_forward_ex(H.handle, x.data_ptr(), y.data_ptr(), 20, dbf.DBF_PATH_DECODE, 0)
+        with pytest.raises(dbf.DbfError):
+            dbf.dbf_linear_forward_ex(H.handle, x.data_ptr(), y.data_ptr(), 4, 7, 0)
+        with pytest.raises(dbf.DbfError):   # misaligned output pointer
+            dbf.dbf_linear_forward(H.handle, x.data_ptr(), y.data_ptr() + 2, 4, 0)
+        info = H.info()
+        assert (info["n"], info["m"], info["k"], info["max_batch"]) == (64, 96, 32, 20)
+        assert info["k_pad"] == 64 and info["m_pad"] == 128 and info["n_pad"] == 64
+    finally:
+        H.close()
+
+
+def test_injected_allocation_failure_leaks_nothing(gpu):
+    torch = _torch()
+    L = inputs.random_layer("o", 512, 512, 256, 3, 0.05, 1.0, 0.05, (1,))
+    torch.cuda.synchronize()
+    free0 = torch.cuda.mem_get_info()[0]
+    try:
+        for nth in range(1, 9):
+            _say(f"inject allocation failure #{nth}")
+            os.environ["DBF_TEST_FAIL_ALLOC"] = str(nth)
+            with pytest.raises(dbf.DbfError) as e:
+                dbf.dbf_pack(L.n, L.m, L.k, L.A, L.B, L.a, L.mid, L.b, 64)
+            assert e.value.status == dbf.DBF_ERR_OOM
+        os.environ["DBF_TEST_FAIL_ALLOC"] = "100"
+        h = dbf.dbf_pack(L.n, L.m, L.k, L.A, L.B, L.a, L.mid, L.b, 64)   # the 9th+ allocation never happens
+        dbf.dbf_free(h)
+    finally:
+        os.environ.pop("DBF_TEST_FAIL_ALLOC", None)
+    torch.cuda.synchronize()
+    free1 = torch.cuda.mem_get_info()[0]
+    assert abs(free1 - free0) < (8 << 20), (free0, free1)
+
+
+def test_timing_facility(gpu):
+    torch = _torch()
+    L = inputs.random_layer("t", 256, 256, 128, 3, 0.05, 1.0, 0.05, (1, 32))
+    H = dbf.Layer(L.A, L.B, L.a, L.mid, L.b, max_batch=32)
+    try:
+        _say("timing")
+        dbf.dbf_timing_enable(H.handle, True)
+        for bt in (1, 32):
+            x = torch.from_numpy(L.X[bt]).cuda()
+            for _ in range(3):
+                H.forward(x)
+        t = dbf.dbf_timing_read(H.handle)
+        assert sum(v["launches"] for v in t.values()) >= 6
+        assert all(v["total_ms"] > 0 for v in t.values())
+        dbf.dbf_timing_enable(H.handle, False)
+        assert dbf.dbf_timing_read(H.handle) == {}
+    finally:
+        H.close()
