@@ -1,0 +1,297 @@
+"""Benchmark of the DBF linear forward on one MI355X.
+
+Workload (default): the 4096x4096 projection at about 1 bit per weight
+(n = m = 4096, k = 2048), signs uniform +/-1, a, b ~ |N(0,1)|*0.02,
+mid ~ |N(0,1)|, x ~ N(0,1) in fp16, batch 1.  One step is one full forward
+(input scaling, both signed sums, middle and output scaling) of one layer.
+The step rotates over R distinct copies of the layer's packed weights,
+R * bytes >= 512 MB, so that the 256 MB Infinity Cache cannot hold them and
+every step streams its weights from HBM.  x is resident in HBM before the
+timed region starts.
+
+Metric: packed-weight GB/s = (n*k + k*m)/8 + 2*(n + k + m) bytes per step,
+divided by the wall time of the timed steps (events around K steps, after W
+warm-up steps).  A secondary measurement covers the batch-2048 half of the
+metric (TFLOP/s-equivalent = 2*batch*k*(n+m) per forward) on the 4096x4096
+projection at about 2 bits per weight (k = 4096).
+
+Also reported: the roofline of the dominant kernel, from per-launch HIP
+events recorded by the library on the launch stream over a second pass of
+the same steps, and the CPU oracle (fp64, dense reconstruction) timed on the
+host on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix-core peak
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=4860)
+    p.add_argument("--warmup", type=int, default=486)
+    p.add_argument("--rotate-mb", type=int, default=512)
+    p.add_argument("--mode", choices=("graph", "eager"), default="graph",
+                   help="graph: the timed steps replay a captured HIP graph of forwards")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-secondary", action="store_true", help="skip the batch-2048 measurement")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--copy-probe-mb", type=int, default=0,
+                   help="only run a plain device copy of this size (counter scaling) and exit")
+    p.add_argument("--only", choices=("decode", "prefill"), default=None,
+                   help="run one leg only (for profiling)")
+    return p.parse_args()
+
+
+def layer_copies(layer, count):
+    import dbf_linear_fwd_amd as dbf
+    return [dbf.Layer(layer.A, layer.B, layer.a, layer.mid, layer.b, max_batch=max(layer.X)) for _ in range(count)]
+
+
+def time_steps(fwd, steps, warmup, mode):
+    """Run `fwd(i)` for warm-up then timed steps; returns elapsed seconds of the timed steps."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        fwd(i)
+    torch.cuda.synchronize()
+    if mode == "graph":
+        # capture one pass over the rotation, replay it for the timed steps
+        period = getattr(fwd, "period", 1)
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(stream)
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for i in range(period):
+                    fwd(i)
+        stream.wait_stream(s)
+        reps = max(1, steps // period)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3, reps * period
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        fwd(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1e3, steps
+
+
+def kernel_times(layers, fwd, steps):
+    """Per-kernel average event time (ms) over `steps` eager steps."""
+    import dbf_linear_fwd_amd as dbf
+    import torch
+    for L in layers:
+        dbf.dbf_timing_enable(L.handle, True)
+        dbf.dbf_timing_read(L.handle)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        fwd(i)
+    torch.cuda.synchronize()
+    tot = {}
+    for L in layers:
+        for name, v in dbf.dbf_timing_read(L.handle).items():
+            t = tot.setdefault(name, [0, 0.0])
+            t[0] += v["launches"]
+            t[1] += v["total_ms"]
+        dbf.dbf_timing_enable(L.handle, False)
+    return {k: {"launches": v[0], "avg_us": 1e3 * v[1] / max(v[0], 1)} for k, v in tot.items()}
+
+
+def decode_kernel_bytes(layer, batch):
+    """Algorithmic bytes each decode kernel must move (signs + scales + activations)."""
+    n, m, k = layer.n, layer.m, layer.k
+    return {
+        "decode_stage1": k * m // 8 + 2 * m + 2 * batch * m,
+        "decode_stage2": n * k // 8 + 2 * k + 2 * n + 2 * batch * n,
+    }
+
+
+def prefill_kernel_flops(layer, batch):
+    n, m, k = layer.n, layer.m, layer.k
+    return {"prefill_gemm1": 2 * batch * k * m, "prefill_gemm2": 2 * batch * k * n}
+
+
+def cpu_baseline(layer, seconds):
+    """The fp64 oracle (dense reconstruction + X W^T, one batch-1 forward per
+    call) on the host, repeated for about `seconds`; GB/s of packed weights."""
+    from oracle import dbf_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    X = layer.X[1]
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        O.dense_forward(X, layer.A, layer.B, layer.a, layer.mid, layer.b)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    gbs = (layer.sign_bytes + layer.scale_bytes) * calls / el / 1e9
+    return {"value": gbs, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{calls} batch-1 forwards of the 4096x4096 k=2048 layer through the fp64 dense oracle "
+                      f"(W rebuilt each call) in {el:.1f} s"}
+
+
+def copy_probe(mb):
+    import torch
+    n = mb * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "launches": 3}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import dbf_linear_fwd_amd as dbf
+    from tests import inputs
+
+    torch.cuda.set_device(0)
+    if args.copy_probe_mb:
+        copy_probe(args.copy_probe_mb)
+        return
+
+    result = {}
+    # ---------------------------------------------------------------- decode, batch 1 (headline)
+    if args.only in (None, "decode"):
+        cfg = inputs.config(2)
+        layer = cfg.layers[0]
+        bytes_step = layer.sign_bytes + layer.scale_bytes
+        R = max(1, -(-args.rotate_mb * (1 << 20) // bytes_step))
+        print(f"[bench] decode: {layer.n}x{layer.m} k={layer.k}, {R} weight copies "
+              f"({R * bytes_step / 2**20:.0f} MiB), {args.steps} steps, mode={args.mode}", file=sys.stderr, flush=True)
+        copies = layer_copies(layer, R)
+        x = torch.from_numpy(layer.X[1]).cuda()
+        y = torch.empty((1, layer.n), dtype=torch.float16, device="cuda")
+
+        def fwd(i):
+            copies[i % R].forward(x, out=y)
+        fwd.period = R
+
+        el, done = time_steps(fwd, args.steps, args.warmup, args.mode)
+        gbs = bytes_step * done / el / 1e9
+        print(f"[bench] decode: {done} steps in {el * 1e3:.2f} ms -> {gbs:.1f} GB/s", file=sys.stderr, flush=True)
+        el_e, done_e = time_steps(fwd, min(args.steps, 2 * R), min(args.warmup, R), "eager")
+        kt = kernel_times(copies, fwd, min(args.steps, 2 * R))
+        print(f"[bench] kernel event times: {kt}", file=sys.stderr, flush=True)
+        kb = decode_kernel_bytes(layer, 1)
+        dom = max(kb, key=lambda kname: kt.get(kname, {"avg_us": 0})["avg_us"])
+        ach = kb[dom] / (kt[dom]["avg_us"] * 1e-6) / 1e9
+        result["decode"] = {
+            "value": gbs, "ms_per_step": el * 1e3 / done, "steps": done,
+            "eager_gbs": bytes_step * done_e / el_e / 1e9,
+            "kernels": kt, "dominant": dom,
+            "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": ach / HBM_PEAK_GBS, "traffic": None, "kernel": dom,
+                         "algorithmic_bytes_per_launch": kb[dom]},
+            "layer": layer, "copies": copies,
+        }
+        for c in copies:
+            c.close()
+        del copies
+        torch.cuda.synchronize()
+
+    # ---------------------------------------------------------------- prefill, batch 2048 (secondary)
+    if args.only in (None, "prefill") and not args.no_secondary:
+        layer = inputs.config(3).layers[0]
+        bt = 2048
+        print(f"[bench] prefill: {layer.n}x{layer.m} k={layer.k} batch {bt}", file=sys.stderr, flush=True)
+        L = dbf.Layer(layer.A, layer.B, layer.a, layer.mid, layer.b, max_batch=bt)
+        x = torch.from_numpy(layer.X[bt]).cuda()
+        y = torch.empty((bt, layer.n), dtype=torch.float16, device="cuda")
+
+        def pf(i):
+            L.forward(x, out=y)
+        reps = 50
+        el, done = time_steps(pf, reps, 10, "eager")
+        flops = 2 * bt * layer.k * (layer.n + layer.m)
+        tfs = flops * done / el / 1e12
+        kt = kernel_times([L], pf, 20)
+        kf = prefill_kernel_flops(layer, bt)
+        dom = max(kf, key=lambda kname: kt.get(kname, {"avg_us": 0})["avg_us"])
+        ach = kf[dom] / (kt[dom]["avg_us"] * 1e-6) / 1e12
+        print(f"[bench] prefill: {tfs:.1f} TFLOP/s-eq; kernels {kt}", file=sys.stderr, flush=True)
+        result["prefill"] = {
+            "value": tfs, "unit": "TFLOP/s-eq", "ms_per_forward": el * 1e3 / done,
+            "frac_of_mfma_peak": tfs / MFMA_F16_PEAK_TFLOPS, "kernels": kt,
+            "roofline": {"bound": "mfma", "achieved": ach, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": ach / MFMA_F16_PEAK_TFLOPS, "traffic": None, "kernel": dom,
+                         "algorithmic_flops_per_launch": kf[dom]},
+            "workload": "4096x4096 projection, k=4096 (~2 bits/weight), batch 2048",
+        }
+        L.close()
+
+    if args.only is not None:
+        print(json.dumps({k: {kk: vv for kk, vv in v.items() if kk not in ("layer", "copies")}
+                          for k, v in result.items()}, default=str))
+        return
+
+    d = result["decode"]
+    cpu = None
+    if not args.no_cpu:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(d["layer"], args.cpu_seconds)
+    line = {
+        "metric": "DBF linear packed-weight GB/s (% HBM peak) at batch 1; TFLOP/s-eq at batch 2048",
+        "value": round(d["value"], 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": d["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": d["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "DBF linear 4096x4096, k=2048 (~1 bit/weight), batch 1, fp16 I/O, "
+                               f"{d['layer'].n}x{d['layer'].m}; weights rotated over >=512 MB; {args.mode}",
+                   "n": d["layer"].n, "m": d["layer"].m, "k": d["layer"].k, "batch": 1,
+                   "mode": args.mode},
+        "frac_of_hbm_peak": d["value"] / HBM_PEAK_GBS,
+        "roofline": d["roofline"],
+        "cpu_baseline": cpu,
+        "decode_kernels_us": d["kernels"],
+        "eager_gbs": d["eager_gbs"],
+    }
+    if "prefill" in result:
+        line["prefill_batch2048"] = result["prefill"]
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()
