@@ -54,6 +54,8 @@ def parse():
                    help="only run a plain device copy of this size (counter scaling) and exit")
     p.add_argument("--only", choices=("decode", "prefill"), default=None,
                    help="run one leg only (for profiling)")
+    p.add_argument("--decode-path", choices=("mfma", "table"), default="mfma",
+                   help="decode kernels: matrix cores (default) or vector-ALU lookup tables")
     return p.parse_args()
 
 
@@ -198,8 +200,10 @@ def main():
         x = torch.from_numpy(layer.X[1]).cuda()
         y = torch.empty((1, layer.n), dtype=torch.float16, device="cuda")
 
+        dpath = dbf.DBF_PATH_DECODE if args.decode_path == "mfma" else dbf.DBF_PATH_DECODE_TABLE
+
         def fwd(i):
-            copies[i % R].forward(x, out=y)
+            copies[i % R].forward(x, out=y, path=dpath)
         fwd.period = R
 
         el, done = time_steps(fwd, args.steps, args.warmup, args.mode)
@@ -209,6 +213,8 @@ def main():
         kt = kernel_times(copies, fwd, min(args.steps, 2 * R))
         print(f"[bench] kernel event times: {kt}", file=sys.stderr, flush=True)
         kb = decode_kernel_bytes(layer, 1)
+        if args.decode_path == "table":
+            kb = {"table_" + kname.split("_", 1)[1]: v for kname, v in kb.items()}
         dom = max(kb, key=lambda kname: kt.get(kname, {"avg_us": 0})["avg_us"])
         ach = kb[dom] / (kt[dom]["avg_us"] * 1e-6) / 1e9
         result["decode"] = {

@@ -23,7 +23,7 @@ import numpy as np
 
 __all__ = [
     "DBF_OK", "DBF_ERR_INVALID_ARG", "DBF_ERR_SHAPE", "DBF_ERR_OOM", "DBF_ERR_HIP", "DBF_ERR_UNSUPPORTED",
-    "DBF_PATH_AUTO", "DBF_PATH_DECODE", "DBF_PATH_PREFILL", "EXPORTED_SYMBOLS",
+    "DBF_PATH_AUTO", "DBF_PATH_DECODE", "DBF_PATH_PREFILL", "DBF_PATH_DECODE_TABLE", "EXPORTED_SYMBOLS",
     "DbfError", "lib", "library_path",
     "dbf_pack", "dbf_linear_forward", "dbf_linear_forward_ex", "dbf_free", "dbf_get_info",
     "dbf_status_string", "dbf_pack_signs", "dbf_layout_signs", "dbf_layout_words",
@@ -40,6 +40,7 @@ DBF_ERR_UNSUPPORTED = 5
 DBF_PATH_AUTO = 0
 DBF_PATH_DECODE = 1
 DBF_PATH_PREFILL = 2
+DBF_PATH_DECODE_TABLE = 3
 
 DECODE_MAX_BATCH = 16
 

@@ -29,10 +29,48 @@ DBF_HD inline size_t tiled_index(int row, int w, int words) {
     return ((static_cast<size_t>(row >> 6) * (words >> 1) + (w >> 1)) * 64 + (row & 63)) * 2 + (w & 1);
 }
 
+// Largest batch served by the lookup-table decode kernels.
+constexpr int kLutMaxBatch = 4;
+// Upper bound on the words of one lookup-table chunk (register budget).
+constexpr int kMaxLutChunkWords = 124;
+
 struct DecodePlan {
     int nchunk_m;   // chunks along m (stage 1)
     int nchunk_k;   // chunks along k (stage 2)
 };
+
+// Arguments of the decode kernels for one forward.
+struct DecodeArgs {
+    const uint32_t *A_dev, *B_dev;
+    const void *a_dev, *mid_dev, *b_dev;
+    const void *x;
+    void *y;
+    float *tpart, *ypart;
+    unsigned *tickets;   // one per 64-row tile of A, zero between calls
+    int batch, n, m, n_pad, m_pad, k_pad;
+    int cw_m, nchunk_m;  // stage-1 chunk (words of B per workgroup) and chunk count
+    int cw_k, nchunk_k;  // stage-2 chunk (words of A per workgroup) and chunk count
+};
+
+// Arguments of the matrix-core decode kernels (batch 1..16).
+struct MfmaDecodeArgs {
+    const uint32_t *A_dev, *B_dev;
+    const void *a_dev, *mid_dev, *b_dev;
+    const void *x;
+    void *y;
+    uint16_t *v16;       // [2][batch][k_pad] fp16: v_hi then v_lo planes
+    int batch, n, m, n_pad, m_pad, k_pad;
+};
+
+// which = 1: stage 1 (writes v16); which = 2: stage 2 (writes y).
+int launch_mfma_decode(const MfmaDecodeArgs &d, void *stream, int which);
+
+// Words per lookup-table chunk allowed by the LDS budget for `nb` batch rows.
+int lut_max_chunk_words(int nb);
+// Lookup-table decode (batch 1..4): stage 1 writes chunk partials of t;
+// stage 2 builds the table of mid * t, sums along k and finishes y.
+int launch_lut_stage1(const DecodeArgs &d, void *stream);
+int launch_lut_stage2(const DecodeArgs &d, void *stream);
 
 // ---- kernel launchers (return hipError_t as int to keep HIP types out of here)
 

@@ -1,0 +1,411 @@
+// Decode path (batch 1..16) of the DBF linear forward on the CDNA4 matrix cores.
+//
+// §2.1 of the gist.science technical summary of "Addition is almost all you
+// need" evaluates X W^T as ((((X ⊙ bᵀ) Bᵀ) ⊙ midᵀ) Aᵀ) ⊙ aᵀ.  Both signed sums
+// run here as 16x16x32 f16 MFMA products: the sign matrix is the A operand,
+// expanded from its bits to ±1.0 in registers, and the activations are the B
+// operand with the batch as the (at most 16 wide) N dimension.
+//   stage 1: u = x ⊙ b is formed in fp32 (exact: a product of two fp16) and
+//            split into u_hi = rne16(u) and u_lo = rne16(u - u_hi), which
+//            carry about 22 significant bits; t = B u_hi + B u_lo in fp32;
+//            the epilogue forms v = t * mid and stores it the same way, as
+//            fp16 planes v_hi, v_lo.
+//   stage 2: s = A v_hi + A v_lo in fp32; y = rne16(s * a).
+// For batch <= 8 the hi and lo parts ride in columns r and r + 8 of one
+// MFMA; for batch 9..16 they take two MFMAs.
+//
+// Work split.  A workgroup of 8 waves owns 16*RT rows of the sign matrix and
+// its whole reduction dimension, taken in rounds that fit LDS (one round for
+// the layer shapes of interest at batch <= 4).  Per round it first issues
+// every global load it needs -- its block of sign words as coalesced 16-byte
+// loads (the rows of one pair are contiguous in the tiled layout), and the
+// activations of the round -- then writes them to LDS: the signs as they
+// are, the activations as the hi/lo planes above.  Word pair p belongs to
+// wave p mod 8, which accumulates in MFMA registers in increasing p; the
+// waves reduce through LDS in a fixed order, so every output is summed in
+// the same order whatever the batch size.  No partial sums leave the
+// workgroup: a forward is two kernel launches.
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+
+#include <algorithm>
+
+#include "dbf_internal.h"
+
+namespace dbf {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kNW = 8;                      // waves per workgroup
+constexpr int kThreads = kNW * 64;
+constexpr int kMaxItems = 8;                // 16-byte sign loads per thread in flight per batch
+constexpr size_t kLdsBudget = 144 * 1024;   // LDS of one workgroup (of 160 KiB per CU)
+constexpr uint32_t kSignPair = 0x80008000u;
+constexpr uint32_t kOnePair = 0x3C003C00u;  // two fp16 +1.0
+
+// Halves 8g..8g+7 of a 32-element sign word as ±1.0 MFMA operand.  Element
+// 2q sits at bit q and element 2q+1 at bit 16+q, so after one shift by 12-4g
+// the pair (8g+2p, 8g+2p+1) is at bits (12+p, 28+p) and a further shift by
+// 3-p puts it on the two fp16 sign bits.
+__device__ __forceinline__ f16x8 expand_pm1(uint32_t word, int g) {
+    const uint32_t sh = word << (12 - 4 * g);
+    u32x4 r;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) r[p] = ((sh << (3 - p)) & kSignPair) | kOnePair;
+    return __builtin_bit_cast(f16x8, r);
+}
+
+__device__ __forceinline__ f16x8 zero8() { return __builtin_bit_cast(f16x8, u32x4{0u, 0u, 0u, 0u}); }
+
+template <int NB>
+struct Acc {
+    static constexpr bool kShared = NB <= 8;  // hi and lo in one MFMA (columns r and r + 8)
+    static constexpr int N = kShared ? 1 : 2;
+};
+
+// LDS layout of one round of PR pairs:
+//   signs  [PR][16*RT rows][2 words]           PR * 128 * RT bytes
+//   planes [2][NB][64*PR] fp16 (hi, lo)         PR * 256 * NB bytes
+//   reduce [Acc::N][kNW][RT][64 lanes][4] fp32  Acc::N * kNW * RT * 1 KiB
+template <int NB, int RT>
+__host__ __device__ constexpr size_t lds_bytes(int PR) {
+    return static_cast<size_t>(PR) * (128 * RT + 256 * NB) + sizeof(float) * Acc<NB>::N * kNW * RT * 256;
+}
+
+// Pairs per round that fit the LDS budget.
+template <int NB, int RT>
+int round_pairs() {
+    const size_t fixed = sizeof(float) * Acc<NB>::N * kNW * RT * 256;
+    return static_cast<int>((kLdsBudget - fixed) / (128 * RT + 256 * NB));
+}
+
+// Issue the loads of this thread's 16-byte sign items of the round, items
+// it = item0 + threadIdx.x + kThreads * q (q < kMaxItems) of the block [pairs][rows].
+template <int RT>
+__device__ __forceinline__ void load_sign_items(u32x4 (&v)[kMaxItems], const uint32_t *__restrict__ S, int words,
+                                                int r0, int pr0, int nitems, int item0) {
+    const int tile = r0 >> 6, roff = r0 & 63;
+#pragma unroll
+    for (int q = 0; q < kMaxItems; ++q) {
+        const int it = item0 + threadIdx.x + kThreads * q;
+        if (it < nitems) {
+            const int p = pr0 + it / (8 * RT);
+            const int off = (it % (8 * RT)) * 4;  // in words
+            v[q] = *reinterpret_cast<const u32x4 *>(
+                S + ((static_cast<size_t>(tile) * (words >> 1) + p) * 64 + roff) * 2 + off);
+        }
+    }
+}
+
+__device__ __forceinline__ void store_sign_items(const u32x4 (&v)[kMaxItems], uint32_t *sgn, int nitems, int item0) {
+#pragma unroll
+    for (int q = 0; q < kMaxItems; ++q) {
+        const int it = item0 + threadIdx.x + kThreads * q;
+        if (it < nitems) *reinterpret_cast<u32x4 *>(sgn + 4 * it) = v[q];
+    }
+}
+
+// One round: pairs [pr0, pr1) of rows r0..r0+16RT-1 from the LDS copies.
+template <int NB, int RT>
+__device__ __forceinline__ void round_mma(f32x4 (&acc)[Acc<NB>::N][RT], const uint32_t *sgn, const _Float16 *act,
+                                          int KR, int pr0, int pr1, int wave, int li, int g) {
+    constexpr bool kShared = Acc<NB>::kShared;
+    const _Float16 *arow0 = nullptr, *arow1 = nullptr;  // nullptr: a zero column
+    if (kShared) {
+        if (li < NB) arow0 = act + li * KR;
+        else if (li >= 8 && li < 8 + NB) arow0 = act + (NB + li - 8) * KR;
+    } else if (li < NB) {
+        arow0 = act + li * KR;
+        arow1 = act + (NB + li) * KR;
+    }
+    for (int p = pr0 + wave; p < pr1; p += kNW) {
+        const int pl = p - pr0;
+        uint2 w[RT];
+#pragma unroll
+        for (int t = 0; t < RT; ++t) w[t] = *reinterpret_cast<const uint2 *>(sgn + (pl * 16 * RT + 16 * t + li) * 2);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int e = 64 * pl + 32 * h + 8 * g;
+            const f16x8 v0 = arow0 ? *reinterpret_cast<const f16x8 *>(arow0 + e) : zero8();
+            f16x8 v1 = zero8();
+            if (!kShared) v1 = arow1 ? *reinterpret_cast<const f16x8 *>(arow1 + e) : zero8();
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+                const f16x8 s = expand_pm1(h ? w[t].y : w[t].x, g);
+                acc[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(s, v0, acc[0][t], 0, 0, 0);
+                if (!kShared)
+                    acc[Acc<NB>::N - 1][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(s, v1, acc[Acc<NB>::N - 1][t], 0, 0, 0);
+            }
+        }
+    }
+}
+
+// Sum the waves' accumulators through LDS in a fixed wave order; wave 0's
+// slots then hold the workgroup totals.
+template <int NB, int RT>
+__device__ __forceinline__ void reduce_waves(const f32x4 (&acc)[Acc<NB>::N][RT], float *red, int wave, int lane) {
+    constexpr int N = Acc<NB>::N;
+#pragma unroll
+    for (int c = 0; c < N; ++c)
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+            *reinterpret_cast<f32x4 *>(&red[((c * kNW + wave) * RT + t) * 256 + lane * 4]) = acc[c][t];
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < N * RT * 256; idx += kThreads) {
+        const int c = idx / (RT * 256);
+        const int rest = idx - c * RT * 256;
+        float s = red[(c * kNW) * RT * 256 + rest];
+#pragma unroll
+        for (int w = 1; w < kNW; ++w) s += red[((c * kNW + w) * RT) * 256 + rest];
+        red[(c * kNW) * RT * 256 + rest] = s;
+    }
+    __syncthreads();
+}
+
+// hi + lo total for (row tile t, this lane's 4 rows, batch column li).
+template <int NB, int RT>
+__device__ __forceinline__ f32x4 total(const float *red, int t, int lane) {
+    const f32x4 dh = *reinterpret_cast<const f32x4 *>(&red[t * 256 + lane * 4]);
+    const f32x4 dl = Acc<NB>::kShared ? *reinterpret_cast<const f32x4 *>(&red[t * 256 + (lane + 8) * 4])
+                                      : *reinterpret_cast<const f32x4 *>(&red[(kNW * RT + t) * 256 + lane * 4]);
+    return dh + dl;
+}
+
+// Stage 1: v = mid * (B (x ⊙ b)), stored as fp16 hi/lo planes [2][NB][k_pad].
+template <int NB, int RT>
+__global__ __launch_bounds__(kThreads) void mfma_stage1_kernel(const uint32_t *__restrict__ Bt, int Wm,
+                                                               const __half *__restrict__ x, int m,
+                                                               const __half *__restrict__ b,
+                                                               const __half *__restrict__ mid,
+                                                               __half *__restrict__ v16, int k_pad, int PR) {
+    extern __shared__ float lds[];
+    const int KR = 64 * PR;
+    char *base = reinterpret_cast<char *>(lds);
+    uint32_t *sgn = reinterpret_cast<uint32_t *>(base);
+    _Float16 *act = reinterpret_cast<_Float16 *>(base + static_cast<size_t>(PR) * 128 * RT);
+    float *red = reinterpret_cast<float *>(base + static_cast<size_t>(PR) * (128 * RT + 256 * NB));
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4;
+    const int li = lane & 15;
+    const int j0 = blockIdx.x * 16 * RT;
+
+    float mid_pre[RT][4];  // epilogue scales, fetched early
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) mid_pre[t][v] = __half2float(mid[j0 + 16 * t + 4 * g + v]);
+
+    f32x4 acc[Acc<NB>::N][RT];
+#pragma unroll
+    for (int c = 0; c < Acc<NB>::N; ++c)
+#pragma unroll
+        for (int t = 0; t < RT; ++t) acc[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int npairs = Wm >> 1;
+    for (int pr0 = 0; pr0 < npairs; pr0 += PR) {
+        const int pr1 = min(pr0 + PR, npairs);
+        const int nitems = (pr1 - pr0) * 8 * RT;
+        if (pr0 > 0) __syncthreads();  // the previous round is done with LDS
+        for (int item0 = 0; item0 < nitems; item0 += kThreads * kMaxItems) {
+            u32x4 v[kMaxItems];
+            load_sign_items<RT>(v, Bt, Wm, j0, pr0, nitems, item0);
+            if (item0 == 0) {
+                // activations of the round: u = x ⊙ b as hi/lo planes, 8 elements per item
+                const int k0 = 64 * pr0, len = 64 * (pr1 - pr0);
+                for (int it = threadIdx.x; it < NB * (len >> 3); it += kThreads) {
+                    const int r = it / (len >> 3);
+                    const int e = (it - r * (len >> 3)) * 8;
+                    const int l = k0 + e;
+                    f16x8 xv = zero8();
+                    if ((m & 7) == 0 && l + 8 <= m) {
+                        xv = *reinterpret_cast<const f16x8 *>(x + static_cast<size_t>(r) * m + l);
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 8; ++q)
+                            if (l + q < m) xv[q] = static_cast<_Float16>(__half2float(x[static_cast<size_t>(r) * m + l + q]));
+                    }
+                    const f16x8 bv = *reinterpret_cast<const f16x8 *>(b + l);  // b is zero-padded to m_pad
+                    f16x8 hi, lo;
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        const float u = static_cast<float>(xv[q]) * static_cast<float>(bv[q]);
+                        hi[q] = static_cast<_Float16>(u);
+                        lo[q] = static_cast<_Float16>(u - static_cast<float>(hi[q]));
+                    }
+                    *reinterpret_cast<f16x8 *>(act + r * KR + e) = hi;
+                    *reinterpret_cast<f16x8 *>(act + (NB + r) * KR + e) = lo;
+                }
+            }
+            store_sign_items(v, sgn, nitems, item0);
+        }
+        __syncthreads();
+        round_mma<NB, RT>(acc, sgn, act, KR, pr0, pr1, wave, li, g);
+    }
+
+    reduce_waves<NB, RT>(acc, red, wave, lane);
+    // epilogue (wave 0): D[row 4g+v][col li] of row tile t is t[li][j0 + 16t + 4g + v]
+    if (wave == 0 && li < NB) {
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+            const int row0 = j0 + 16 * t + 4 * g;
+            const f32x4 d = total<NB, RT>(red, t, lane);
+            f16x4 hi, lo;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const float val = d[v] * mid_pre[t][v];
+                hi[v] = static_cast<_Float16>(val);
+                lo[v] = static_cast<_Float16>(val - static_cast<float>(hi[v]));
+            }
+            *reinterpret_cast<f16x4 *>(v16 + static_cast<size_t>(li) * k_pad + row0) = hi;
+            *reinterpret_cast<f16x4 *>(v16 + static_cast<size_t>(NB + li) * k_pad + row0) = lo;
+        }
+    }
+}
+
+// Stage 2: y = rne16(a ⊙ (A (v_hi + v_lo))).
+template <int NB, int RT>
+__global__ __launch_bounds__(kThreads) void mfma_stage2_kernel(const uint32_t *__restrict__ At, int Wk,
+                                                               const __half *__restrict__ v16, int k_pad,
+                                                               const __half *__restrict__ a,
+                                                               __half *__restrict__ y, int n, int PR) {
+    extern __shared__ float lds[];
+    const int KR = 64 * PR;
+    char *base = reinterpret_cast<char *>(lds);
+    uint32_t *sgn = reinterpret_cast<uint32_t *>(base);
+    _Float16 *act = reinterpret_cast<_Float16 *>(base + static_cast<size_t>(PR) * 128 * RT);
+    float *red = reinterpret_cast<float *>(base + static_cast<size_t>(PR) * (128 * RT + 256 * NB));
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4;
+    const int li = lane & 15;
+    const int i0 = blockIdx.x * 16 * RT;
+
+    float a_pre[RT][4];  // epilogue scales, fetched early
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int row = i0 + 16 * t + 4 * g + v;
+            a_pre[t][v] = row < n ? __half2float(a[row]) : 0.0f;
+        }
+
+    f32x4 acc[Acc<NB>::N][RT];
+#pragma unroll
+    for (int c = 0; c < Acc<NB>::N; ++c)
+#pragma unroll
+        for (int t = 0; t < RT; ++t) acc[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int npairs = Wk >> 1;
+    for (int pr0 = 0; pr0 < npairs; pr0 += PR) {
+        const int pr1 = min(pr0 + PR, npairs);
+        const int nitems = (pr1 - pr0) * 8 * RT;
+        if (pr0 > 0) __syncthreads();
+        for (int item0 = 0; item0 < nitems; item0 += kThreads * kMaxItems) {
+            u32x4 v[kMaxItems];
+            load_sign_items<RT>(v, At, Wk, i0, pr0, nitems, item0);
+            if (item0 == 0) {
+                // the round of the v_hi / v_lo planes, 16 bytes per item
+                const int k0 = 64 * pr0, len = 64 * (pr1 - pr0);
+                for (int it = threadIdx.x; it < 2 * NB * (len >> 3); it += kThreads) {
+                    const int r = it / (len >> 3);  // plane row: hi rows then lo rows
+                    const int e = (it - r * (len >> 3)) * 8;
+                    *reinterpret_cast<f16x8 *>(act + r * KR + e) =
+                        *reinterpret_cast<const f16x8 *>(v16 + static_cast<size_t>(r) * k_pad + k0 + e);
+                }
+            }
+            store_sign_items(v, sgn, nitems, item0);
+        }
+        __syncthreads();
+        round_mma<NB, RT>(acc, sgn, act, KR, pr0, pr1, wave, li, g);
+    }
+
+    reduce_waves<NB, RT>(acc, red, wave, lane);
+    if (wave == 0 && li < NB) {
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+            const int row0 = i0 + 16 * t + 4 * g;
+            const f32x4 d = total<NB, RT>(red, t, lane);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int row = row0 + v;
+                if (row < n) y[static_cast<size_t>(li) * n + row] = __float2half_rn(d[v] * a_pre[t][v]);
+            }
+        }
+    }
+}
+
+template <typename K>
+void allow_lds(K kernel, size_t bytes) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              static_cast<int>(bytes));
+}
+
+template <int NB, int RT>
+int launch_rt(const MfmaDecodeArgs &d, hipStream_t s, int which) {
+    if (which == 1) {
+        static const bool once = (allow_lds(mfma_stage1_kernel<NB, RT>, kLdsBudget), true);
+        (void)once;
+        const int PR = std::min(d.m_pad / 64, round_pairs<NB, RT>());
+        const size_t lds = lds_bytes<NB, RT>(PR);
+        hipLaunchKernelGGL((mfma_stage1_kernel<NB, RT>), dim3(d.k_pad / (16 * RT)), dim3(kThreads), lds, s, d.B_dev,
+                           d.m_pad / 32, static_cast<const __half *>(d.x), d.m, static_cast<const __half *>(d.b_dev),
+                           static_cast<const __half *>(d.mid_dev), reinterpret_cast<__half *>(d.v16), d.k_pad, PR);
+    } else {
+        static const bool once = (allow_lds(mfma_stage2_kernel<NB, RT>, kLdsBudget), true);
+        (void)once;
+        const int PR = std::min(d.k_pad / 64, round_pairs<NB, RT>());
+        const size_t lds = lds_bytes<NB, RT>(PR);
+        hipLaunchKernelGGL((mfma_stage2_kernel<NB, RT>), dim3(d.n_pad / (16 * RT)), dim3(kThreads), lds, s, d.A_dev,
+                           d.k_pad / 32, reinterpret_cast<const __half *>(d.v16), d.k_pad,
+                           static_cast<const __half *>(d.a_dev), static_cast<__half *>(d.y), d.n, PR);
+    }
+    return static_cast<int>(hipGetLastError());
+}
+
+// Rows per workgroup: 16, 32 or 64, the smallest that keeps the grid within
+// one workgroup per CU of the 256-CU MI355X (batch <= 4; larger use 16).
+template <int NB>
+int launch_nb(const MfmaDecodeArgs &d, hipStream_t s, int which) {
+    const int rows = which == 1 ? d.k_pad : d.n_pad;
+    constexpr int kOneRound = 256;
+    if constexpr (NB <= 4) {
+        if (rows / 16 <= kOneRound) return launch_rt<NB, 1>(d, s, which);
+        if (rows / 32 <= kOneRound) return launch_rt<NB, 2>(d, s, which);
+        return launch_rt<NB, 4>(d, s, which);
+    } else {
+        return launch_rt<NB, 1>(d, s, which);
+    }
+}
+
+}  // namespace
+
+int launch_mfma_decode(const MfmaDecodeArgs &d, void *stream, int which) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    switch (d.batch) {
+        case 1: return launch_nb<1>(d, s, which);
+        case 2: return launch_nb<2>(d, s, which);
+        case 3: return launch_nb<3>(d, s, which);
+        case 4: return launch_nb<4>(d, s, which);
+        case 5: return launch_nb<5>(d, s, which);
+        case 6: return launch_nb<6>(d, s, which);
+        case 7: return launch_nb<7>(d, s, which);
+        case 8: return launch_nb<8>(d, s, which);
+        case 9: return launch_nb<9>(d, s, which);
+        case 10: return launch_nb<10>(d, s, which);
+        case 11: return launch_nb<11>(d, s, which);
+        case 12: return launch_nb<12>(d, s, which);
+        case 13: return launch_nb<13>(d, s, which);
+        case 14: return launch_nb<14>(d, s, which);
+        case 15: return launch_nb<15>(d, s, which);
+        case 16: return launch_nb<16>(d, s, which);
+        default: return static_cast<int>(hipErrorInvalidValue);
+    }
+}
+
+}  // namespace dbf

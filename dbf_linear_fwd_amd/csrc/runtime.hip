@@ -9,6 +9,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 #include <map>
@@ -32,8 +33,13 @@ struct dbf_layer {
     float *tpart = nullptr;   // decode stage-1 partials [nchunk_m][16][k_pad]
     float *ypart = nullptr;   // decode stage-2 partials [nchunk_k][16][n_pad]
     uint16_t *T = nullptr;    // prefill intermediate    [max_batch][k_pad] fp16
+    unsigned *tickets = nullptr;  // per 64-row tile of A; zero between calls
+    uint16_t *v16 = nullptr;      // matrix-core decode intermediate [2][16][k_pad] fp16
     size_t packed_bytes = 0, scale_bytes = 0, workspace_bytes = 0;
-    dbf::DecodePlan plan{};
+    dbf::DecodePlan plan{};   // one-add-per-sign decode kernels (batch 5..16)
+    struct LutPlan {
+        int cw_m, nchunk_m, cw_k, nchunk_k;
+    } lut[dbf::kLutMaxBatch + 1]{};
     // kernel timing
     bool timing = false;
     struct Pending {
@@ -80,6 +86,8 @@ void release(dbf_layer *h) {
     (void)hipFree(h->tpart);
     (void)hipFree(h->ypart);
     (void)hipFree(h->T);
+    (void)hipFree(h->tickets);
+    (void)hipFree(h->v16);
     for (auto &p : h->pending) {
         (void)hipEventDestroy(p.start);
         (void)hipEventDestroy(p.stop);
@@ -89,6 +97,22 @@ void release(dbf_layer *h) {
 }
 
 int32_t round_up(int32_t v, int32_t q) { return (v + q - 1) / q * q; }
+
+// Workgroups a decode stage aims for: one per CU of the 256-CU MI355X.
+constexpr int kDecodeTargetGroups = 256;
+
+// Split `words` (even) words of each row among chunks so that tiles x chunks
+// is near the target, each chunk an even number of words <= max_cw.
+void choose_chunks(int tiles, int words, int max_cw, int &cw, int &nchunk) {
+    int nc = (kDecodeTargetGroups + tiles / 2) / tiles;
+    if (nc < 1) nc = 1;
+    if (nc > words / 2) nc = words / 2;
+    const int need = (words + max_cw - 1) / max_cw;
+    if (nc < need) nc = need;
+    cw = (((words + nc - 1) / nc) + 1) & ~1;
+    if (cw > max_cw) cw = max_cw;
+    nchunk = (words + cw - 1) / cw;
+}
 
 // Pack a +/-1 matrix (rows x cols) along cols and tile it for the device.
 dbf_status_t pack_tiled(const int8_t *S, int32_t rows, int32_t cols, int32_t words,
@@ -223,13 +247,29 @@ extern "C" dbf_status_t dbf_pack(int32_t n, int32_t m, int32_t k, const int8_t *
     if (st == DBF_OK) h->scale_bytes = 2 * size_t(n_pad + k_pad + m_pad);
 
     const int32_t dec_b = max_batch < dbf::kDecodeMaxBatch ? max_batch : dbf::kDecodeMaxBatch;
-    const size_t tpart_bytes = sizeof(float) * size_t(h->plan.nchunk_m) * dec_b * k_pad;
-    const size_t ypart_bytes = sizeof(float) * size_t(h->plan.nchunk_k) * dec_b * n_pad;
+    size_t tpart_elems = size_t(h->plan.nchunk_m) * dec_b * k_pad;
+    size_t ypart_elems = size_t(h->plan.nchunk_k) * dec_b * n_pad;
+    for (int nb = 1; nb <= dbf::kLutMaxBatch && nb <= max_batch; ++nb) {
+        auto &lp = h->lut[nb];
+        const int maxcw = dbf::lut_max_chunk_words(nb);
+        choose_chunks(k_pad / 64, h->Wm, maxcw, lp.cw_m, lp.nchunk_m);
+        choose_chunks(n_pad / 64, h->Wk, maxcw, lp.cw_k, lp.nchunk_k);
+        tpart_elems = std::max(tpart_elems, size_t(lp.nchunk_m) * nb * k_pad);
+        ypart_elems = std::max(ypart_elems, size_t(lp.nchunk_k) * nb * n_pad);
+    }
+    const size_t tpart_bytes = sizeof(float) * tpart_elems;
+    const size_t ypart_bytes = sizeof(float) * ypart_elems;
+    const size_t ticket_bytes = sizeof(unsigned) * size_t(n_pad / 64);
     const size_t T_bytes = sizeof(uint16_t) * size_t(max_batch) * k_pad;
     if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->tpart), tpart_bytes);
     if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->ypart), ypart_bytes);
     if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->T), T_bytes);
-    if (st == DBF_OK) h->workspace_bytes = tpart_bytes + ypart_bytes + T_bytes;
+    if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->tickets), ticket_bytes);
+    if (st == DBF_OK && hipMemset(h->tickets, 0, ticket_bytes) != hipSuccess) st = DBF_ERR_HIP;
+    if (st == DBF_OK && hipDeviceSynchronize() != hipSuccess) st = DBF_ERR_HIP;
+    const size_t v16_bytes = sizeof(uint16_t) * 2 * size_t(dec_b) * k_pad;
+    if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->v16), v16_bytes);
+    if (st == DBF_OK) h->workspace_bytes = tpart_bytes + ypart_bytes + T_bytes + ticket_bytes + v16_bytes;
 
     if (st != DBF_OK) {
         release(h);
@@ -268,18 +308,67 @@ extern "C" dbf_status_t dbf_get_info(dbf_handle_t h, dbf_info_t *info) {
     return DBF_OK;
 }
 
+static dbf_status_t forward_decode_mfma(dbf_layer *h, const void *x, void *y, int32_t batch,
+                                        hipStream_t stream) {
+    dbf::MfmaDecodeArgs d{};
+    d.A_dev = h->A_dev;
+    d.B_dev = h->B_dev;
+    d.a_dev = h->a_dev;
+    d.mid_dev = h->mid_dev;
+    d.b_dev = h->b_dev;
+    d.x = x;
+    d.y = y;
+    d.v16 = h->v16;
+    d.batch = batch;
+    d.n = h->n;
+    d.m = h->m;
+    d.n_pad = h->n_pad;
+    d.m_pad = h->m_pad;
+    d.k_pad = h->k_pad;
+    dbf_status_t st = timed_launch(h, "decode_stage1", stream, [&] { return dbf::launch_mfma_decode(d, stream, 1); });
+    if (st != DBF_OK) return st;
+    return timed_launch(h, "decode_stage2", stream, [&] { return dbf::launch_mfma_decode(d, stream, 2); });
+}
+
 static dbf_status_t forward_decode(dbf_layer *h, const void *x, void *y, int32_t batch, hipStream_t stream) {
-    dbf_status_t st = timed_launch(h, "decode_stage1", stream, [&] {
+    if (batch <= dbf::kLutMaxBatch) {
+        const auto &lp = h->lut[batch];
+        dbf::DecodeArgs d{};
+        d.A_dev = h->A_dev;
+        d.B_dev = h->B_dev;
+        d.a_dev = h->a_dev;
+        d.mid_dev = h->mid_dev;
+        d.b_dev = h->b_dev;
+        d.x = x;
+        d.y = y;
+        d.tpart = h->tpart;
+        d.ypart = h->ypart;
+        d.tickets = h->tickets;
+        d.batch = batch;
+        d.n = h->n;
+        d.m = h->m;
+        d.n_pad = h->n_pad;
+        d.m_pad = h->m_pad;
+        d.k_pad = h->k_pad;
+        d.cw_m = lp.cw_m;
+        d.nchunk_m = lp.nchunk_m;
+        d.cw_k = lp.cw_k;
+        d.nchunk_k = lp.nchunk_k;
+        dbf_status_t st = timed_launch(h, "table_stage1", stream, [&] { return dbf::launch_lut_stage1(d, stream); });
+        if (st != DBF_OK) return st;
+        return timed_launch(h, "table_stage2", stream, [&] { return dbf::launch_lut_stage2(d, stream); });
+    }
+    dbf_status_t st = timed_launch(h, "decode_add_stage1", stream, [&] {
         return dbf::launch_decode_stage1(h->B_dev, x, h->b_dev, h->tpart, batch, h->m, h->m_pad, h->k_pad,
                                          h->plan.nchunk_m, stream);
     });
     if (st != DBF_OK) return st;
-    st = timed_launch(h, "decode_stage2", stream, [&] {
+    st = timed_launch(h, "decode_add_stage2", stream, [&] {
         return dbf::launch_decode_stage2(h->A_dev, h->tpart, h->mid_dev, h->ypart, batch, h->n_pad, h->k_pad,
                                          h->plan.nchunk_m, h->plan.nchunk_k, stream);
     });
     if (st != DBF_OK) return st;
-    return timed_launch(h, "decode_final", stream, [&] {
+    return timed_launch(h, "decode_add_final", stream, [&] {
         return dbf::launch_decode_final(h->ypart, h->a_dev, y, batch, h->n, h->n_pad, h->plan.nchunk_k, stream);
     });
 }
@@ -302,15 +391,19 @@ extern "C" dbf_status_t dbf_linear_forward_ex(dbf_handle_t h, const void *x, voi
                                               hipStream_t stream) {
     if (!h) return DBF_ERR_INVALID_ARG;
     if (batch < 0 || batch > h->max_batch) return DBF_ERR_INVALID_ARG;
-    if (path != DBF_PATH_AUTO && path != DBF_PATH_DECODE && path != DBF_PATH_PREFILL) return DBF_ERR_INVALID_ARG;
+    if (path != DBF_PATH_AUTO && path != DBF_PATH_DECODE && path != DBF_PATH_PREFILL &&
+        path != DBF_PATH_DECODE_TABLE)
+        return DBF_ERR_INVALID_ARG;
     if (path == DBF_PATH_DECODE && batch > dbf::kDecodeMaxBatch) return DBF_ERR_INVALID_ARG;
+    if (path == DBF_PATH_DECODE_TABLE && batch > dbf::kDecodeMaxBatch) return DBF_ERR_INVALID_ARG;
     if (batch == 0) return DBF_OK;
     if (!x || !y || !aligned16(x) || !aligned16(y)) return DBF_ERR_INVALID_ARG;
     int cur = -1;
     if (hipGetDevice(&cur) != hipSuccess) return DBF_ERR_HIP;
     if (cur != h->device) return DBF_ERR_INVALID_ARG;
+    if (path == DBF_PATH_DECODE_TABLE) return forward_decode(h, x, y, batch, stream);
     const bool decode = path == DBF_PATH_DECODE || (path == DBF_PATH_AUTO && batch <= dbf::kDecodeMaxBatch);
-    return decode ? forward_decode(h, x, y, batch, stream) : forward_prefill(h, x, y, batch, stream);
+    return decode ? forward_decode_mfma(h, x, y, batch, stream) : forward_prefill(h, x, y, batch, stream);
 }
 
 extern "C" dbf_status_t dbf_linear_forward(dbf_handle_t h, const void *x, void *y, int32_t batch,

@@ -21,9 +21,11 @@
  * and sign flips; no dense W is formed.
  *
  * Numerics: fp16 in and out, fp32 accumulation, one round-to-nearest-even
- * to fp16 at the end; no flush-to-zero.  For batch > 16 the intermediate
- * (t * mid, batch x k) is rounded once to fp16 because it is the operand of
- * the 16-bit matrix-core products.
+ * to fp16 at the end; no flush-to-zero.  The intermediate v = t * mid
+ * (batch x k) is an operand of 16-bit matrix-core products: on the decode
+ * path it is kept as the sum of two fp16 numbers (about 22 significant bits),
+ * on the prefill path it is rounded once to fp16.  On both it must stay
+ * inside the fp16 range (|v| < 65520); the table path keeps it in fp32.
  *
  * Packed sign format (the pages fix none; this is the library's own)
  * ----------------------------------------------------------------------
@@ -67,9 +69,12 @@ typedef enum {
 
 /* Kernel-path selection for dbf_linear_forward_ex(). */
 typedef enum {
-    DBF_PATH_AUTO = 0,    /* batch <= 16: decode kernels; batch > 16: matrix-core kernels */
-    DBF_PATH_DECODE = 1,  /* signed-sum decode kernels; batch must be <= 16 */
-    DBF_PATH_PREFILL = 2  /* matrix-core (MFMA) kernels; any batch */
+    DBF_PATH_AUTO = 0,         /* batch <= 16: DBF_PATH_DECODE; batch > 16: DBF_PATH_PREFILL */
+    DBF_PATH_DECODE = 1,       /* small-batch kernels: batch as the MFMA N dimension, intermediate
+                                  kept as an fp16 hi+lo pair; batch must be <= 16 */
+    DBF_PATH_PREFILL = 2,      /* tiled MFMA products, intermediate rounded once to fp16; any batch */
+    DBF_PATH_DECODE_TABLE = 3  /* vector-ALU signed sums (4-sign lookup tables for batch <= 4, one
+                                  add per sign above), intermediate in fp32; batch must be <= 16 */
 } dbf_path_t;
 
 typedef struct {

@@ -108,13 +108,17 @@ SHAPES = [
 ]
 
 
+DECODE_PATHS = [dbf.DBF_PATH_DECODE, dbf.DBF_PATH_DECODE_TABLE]
+
+
 @pytest.mark.parametrize("n,m,k", SHAPES)
-@pytest.mark.parametrize("batch", [1, 3, 16])
-def test_decode_small_shapes(gpu, n, m, k, batch):
-    _say(f"decode n={n} m={m} k={k} batch={batch}")
+@pytest.mark.parametrize("batch", [1, 3, 9, 16])
+@pytest.mark.parametrize("path", DECODE_PATHS, ids=["mfma", "table"])
+def test_decode_small_shapes(gpu, n, m, k, batch, path):
+    _say(f"decode path={path} n={n} m={m} k={k} batch={batch}")
     X, A, B, a, mid, b = inputs.tiny_case(1000 + n + m + k + batch, n, m, k, batch, signed_scales=True)
     L = inputs.Layer("s", n, m, k, A, B, a, mid, b, {})
-    y = run(L, X, dbf.DBF_PATH_DECODE)
+    y = run(L, X, path)
     assert y.shape == (batch, n)
     assert_tol(y, O.dense_forward(X, A, B, a, mid, b), f"decode {n}x{m}x{k} b{batch}")
 
@@ -141,7 +145,7 @@ INT_SHAPES = [
 
 
 @pytest.mark.parametrize("n,m,k,batch", INT_SHAPES)
-@pytest.mark.parametrize("path", [dbf.DBF_PATH_DECODE, dbf.DBF_PATH_PREFILL])
+@pytest.mark.parametrize("path", [dbf.DBF_PATH_DECODE, dbf.DBF_PATH_DECODE_TABLE, dbf.DBF_PATH_PREFILL])
 def test_integer_bit_exact_small(gpu, n, m, k, batch, path):
     _say(f"integer n={n} m={m} k={k} batch={batch} path={path}")
     L = inputs.integer_layer("i", n, m, k, 77 + n, (batch,), a_vals=(0.5, 1.0), mid_vals=(1.0, 2.0),
@@ -166,7 +170,8 @@ INT_FULL = [
 
 @pytest.mark.parametrize("name,n,m,k,vals", INT_FULL, ids=[c[0] for c in INT_FULL])
 @pytest.mark.parametrize("batch,path", [(1, dbf.DBF_PATH_DECODE), (16, dbf.DBF_PATH_DECODE),
-                                        (16, dbf.DBF_PATH_PREFILL), (2048, dbf.DBF_PATH_PREFILL)])
+                                        (1, dbf.DBF_PATH_DECODE_TABLE), (16, dbf.DBF_PATH_PREFILL),
+                                        (2048, dbf.DBF_PATH_PREFILL)])
 def test_integer_bit_exact_full_size(gpu, name, n, m, k, vals, batch, path):
     _say(f"integer full {name} batch={batch} path={path}")
     L = inputs.integer_layer(name, n, m, k, 5000 + n + k, (batch,), a_vals=(1.0,), mid_vals=vals, b_vals=vals)
@@ -202,6 +207,10 @@ def test_workload_tolerance(gpu, cid, batch):
         y = run(L, X)
         err = assert_tol(y[rows], ref, f"c{cid} {L.name} b{batch}")
         _say(f"  worst row rel err {err:.3e}")
+        if batch == 1:
+            yt = run(L, X, dbf.DBF_PATH_DECODE_TABLE)
+            err = assert_tol(yt[rows], ref, f"c{cid} {L.name} b{batch} table")
+            _say(f"  table path: worst row rel err {err:.3e}")
 
 
 # --------------------------------------------------------------------------- invariants and edge cases
@@ -209,7 +218,7 @@ def test_workload_tolerance(gpu, cid, batch):
 def test_determinism_and_batch_independence(gpu):
     torch = _torch()
     L = inputs.random_layer("d", 1000, 1300, 600, 9, 0.05, 1.0, 0.05, (16, 40))
-    for path, bt in ((dbf.DBF_PATH_DECODE, 16), (dbf.DBF_PATH_PREFILL, 40)):
+    for path, bt in ((dbf.DBF_PATH_DECODE, 16), (dbf.DBF_PATH_DECODE_TABLE, 16), (dbf.DBF_PATH_PREFILL, 40)):
         _say(f"determinism path={path} batch={bt}")
         X = L.X[bt]
         H = dbf.Layer(L.A, L.B, L.a, L.mid, L.b, max_batch=bt)
@@ -220,7 +229,16 @@ def test_determinism_and_batch_independence(gpu):
             assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
             for r in (0, 5, bt - 1):
                 yr = H.forward(x[r:r + 1].clone(), path=path).cpu().numpy()
-                assert np.array_equal(yr[0].view(np.uint16), y1[r].view(np.uint16)), f"row {r}"
+                if path != dbf.DBF_PATH_DECODE_TABLE:
+                    # the same kernel code serves both batch sizes and every
+                    # output column is summed in the same order: identical bits
+                    assert np.array_equal(yr[0].view(np.uint16), y1[r].view(np.uint16)), f"row {r}"
+                else:
+                    # batch 1 and batch 16 run different table-path kernels
+                    # (lookups vs one add per sign): fp32 sums in another order,
+                    # so the fp16 results may differ by one rounding step
+                    d = np.abs(yr[0].astype(np.float64) - y1[r].astype(np.float64)).max()
+                    assert d <= 2.0 ** -10 * np.abs(y1[r].astype(np.float64)).max(), f"row {r}"
         finally:
             H.close()
 
@@ -253,7 +271,7 @@ def test_sign_flip_symmetry_on_gpu(gpu):
     A2[[3, 50, 199]] *= -1
     a2[[3, 50, 199]] = -a2[[3, 50, 199]]
     L2 = inputs.Layer("f2", L.n, L.m, L.k, A2, L.B, a2, L.mid, L.b, L.X)
-    for path in (dbf.DBF_PATH_DECODE, dbf.DBF_PATH_PREFILL):
+    for path in (dbf.DBF_PATH_DECODE, dbf.DBF_PATH_DECODE_TABLE, dbf.DBF_PATH_PREFILL):
         _say(f"sign flip path={path}")
         y1 = run(L, L.X[4], path)
         y2 = run(L2, L.X[4], path)
@@ -264,7 +282,7 @@ def test_zero_input_and_zero_batch(gpu):
     torch = _torch()
     L = inputs.random_layer("z", 64, 96, 32, 2, 0.05, 1.0, 0.05, (3,))
     _say("zero input")
-    for path in (dbf.DBF_PATH_DECODE, dbf.DBF_PATH_PREFILL):
+    for path in (dbf.DBF_PATH_DECODE, dbf.DBF_PATH_DECODE_TABLE, dbf.DBF_PATH_PREFILL):
         y = run(L, np.zeros((3, 96), np.float16), path)
         assert np.all(y.astype(np.float64) == 0)
     _say("zero batch")
@@ -294,6 +312,8 @@ def test_error_paths_on_gpu(gpu):
         with pytest.raises(dbf.DbfError):
             dbf.dbf_linear_forward_ex(H.handle, x.data_ptr(), y.data_ptr(), 20, dbf.DBF_PATH_DECODE, 0)
         with pytest.raises(dbf.DbfError):
+            dbf.dbf_linear_forward_ex(H.handle, x.data_ptr(), y.data_ptr(), 20, dbf.DBF_PATH_DECODE_TABLE, 0)
+        with pytest.raises(dbf.DbfError):
             dbf.dbf_linear_forward_ex(H.handle, x.data_ptr(), y.data_ptr(), 4, 7, 0)
         with pytest.raises(dbf.DbfError):   # misaligned output pointer
             dbf.dbf_linear_forward(H.handle, x.data_ptr(), y.data_ptr() + 2, 4, 0)
@@ -310,14 +330,14 @@ def test_injected_allocation_failure_leaks_nothing(gpu):
     torch.cuda.synchronize()
     free0 = torch.cuda.mem_get_info()[0]
     try:
-        for nth in range(1, 9):
+        for nth in range(1, 11):
             _say(f"inject allocation failure #{nth}")
             os.environ["DBF_TEST_FAIL_ALLOC"] = str(nth)
             with pytest.raises(dbf.DbfError) as e:
                 dbf.dbf_pack(L.n, L.m, L.k, L.A, L.B, L.a, L.mid, L.b, 64)
             assert e.value.status == dbf.DBF_ERR_OOM
         os.environ["DBF_TEST_FAIL_ALLOC"] = "100"
-        h = dbf.dbf_pack(L.n, L.m, L.k, L.A, L.B, L.a, L.mid, L.b, 64)   # the 9th+ allocation never happens
+        h = dbf.dbf_pack(L.n, L.m, L.k, L.A, L.B, L.a, L.mid, L.b, 64)   # a pack makes 10 allocations
         dbf.dbf_free(h)
     finally:
         os.environ.pop("DBF_TEST_FAIL_ALLOC", None)
