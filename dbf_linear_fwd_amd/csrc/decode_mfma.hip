@@ -44,20 +44,45 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kNW = 8;                      // waves per workgroup
 constexpr int kThreads = kNW * 64;
 constexpr int kMaxItems = 8;                // 16-byte sign loads per thread in flight per batch
-constexpr size_t kLdsBudget = 144 * 1024;   // LDS of one workgroup (of 160 KiB per CU)
+constexpr int kMaxAct = 4;                  // activation items (8 elements) per thread per batch
+#ifndef DBF_DECODE_LDS_KB
+#define DBF_DECODE_LDS_KB 144
+#endif
+#ifndef DBF_DECODE_ONE_ROUND
+#define DBF_DECODE_ONE_ROUND 256
+#endif
+constexpr size_t kLdsBudget = DBF_DECODE_LDS_KB * 1024;   // LDS of one workgroup (of 160 KiB per CU)
 constexpr uint32_t kSignPair = 0x80008000u;
 constexpr uint32_t kOnePair = 0x3C003C00u;  // two fp16 +1.0
 
 // Halves 8g..8g+7 of a 32-element sign word as ±1.0 MFMA operand.  Element
 // 2q sits at bit q and element 2q+1 at bit 16+q, so after one shift by 12-4g
 // the pair (8g+2p, 8g+2p+1) is at bits (12+p, 28+p) and a further shift by
-// 3-p puts it on the two fp16 sign bits.
-__device__ __forceinline__ f16x8 expand_pm1(uint32_t word, int g) {
+// 3-p puts it on the two fp16 sign bits.  `mask` (the two sign bits) and
+// `one` (two fp16 +1.0) are passed in registers so that each register of the
+// operand is one v_and_or_b32: this ISA's VOP3 form cannot carry two literal
+// constants, and with literals the compiler splits it into an and plus an or.
+__device__ __forceinline__ f16x8 expand_pm1(uint32_t word, int g, uint32_t mask, uint32_t one) {
     const uint32_t sh = word << (12 - 4 * g);
     u32x4 r;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) r[p] = ((sh << (3 - p)) & kSignPair) | kOnePair;
+    for (int p = 0; p < 4; ++p) r[p] = ((sh << (3 - p)) & mask) | one;
     return __builtin_bit_cast(f16x8, r);
+}
+
+// The two constants of expand_pm1 as register values the compiler cannot
+// fold back into literals: the sign mask in a scalar register, +1.0 pair in
+// a vector register.  Called once at kernel entry, before any MFMA has been
+// issued, so the vector move cannot collide with an MFMA still reading its
+// operands (the hazard recognizer does not see inside inline asm).
+struct ExpandConsts {
+    uint32_t mask, one;
+};
+__device__ __forceinline__ ExpandConsts expand_consts() {
+    ExpandConsts c;
+    asm volatile("s_mov_b32 %0, 0x80008000" : "=s"(c.mask));
+    asm volatile("v_mov_b32 %0, 0x3c003c00" : "=v"(c.one));
+    return c;
 }
 
 __device__ __forceinline__ f16x8 zero8() { return __builtin_bit_cast(f16x8, u32x4{0u, 0u, 0u, 0u}); }
@@ -85,20 +110,20 @@ int round_pairs() {
 }
 
 // Issue the loads of this thread's 16-byte sign items of the round, items
-// it = item0 + threadIdx.x + kThreads * q (q < kMaxItems) of the block [pairs][rows].
+// it = item0 + threadIdx.x + kThreads * q (q < kMaxItems) of the block
+// [pairs][rows].  Items past the end load a valid item instead (the index is
+// clamped) and are not stored: the loads are straight-line code, so they are
+// all in flight together instead of waiting on one another at branch joins.
 template <int RT>
 __device__ __forceinline__ void load_sign_items(u32x4 (&v)[kMaxItems], const uint32_t *__restrict__ S, int words,
                                                 int r0, int pr0, int nitems, int item0) {
     const int tile = r0 >> 6, roff = r0 & 63;
 #pragma unroll
     for (int q = 0; q < kMaxItems; ++q) {
-        const int it = item0 + threadIdx.x + kThreads * q;
-        if (it < nitems) {
-            const int p = pr0 + it / (8 * RT);
-            const int off = (it % (8 * RT)) * 4;  // in words
-            v[q] = *reinterpret_cast<const u32x4 *>(
-                S + ((static_cast<size_t>(tile) * (words >> 1) + p) * 64 + roff) * 2 + off);
-        }
+        const int it = min(item0 + static_cast<int>(threadIdx.x) + kThreads * q, nitems - 1);
+        const int p = pr0 + it / (8 * RT);
+        const int off = (it % (8 * RT)) * 4;  // in words
+        v[q] = *reinterpret_cast<const u32x4 *>(S + ((static_cast<size_t>(tile) * (words >> 1) + p) * 64 + roff) * 2 + off);
     }
 }
 
@@ -113,16 +138,14 @@ __device__ __forceinline__ void store_sign_items(const u32x4 (&v)[kMaxItems], ui
 // One round: pairs [pr0, pr1) of rows r0..r0+16RT-1 from the LDS copies.
 template <int NB, int RT>
 __device__ __forceinline__ void round_mma(f32x4 (&acc)[Acc<NB>::N][RT], const uint32_t *sgn, const _Float16 *act,
-                                          int KR, int pr0, int pr1, int wave, int li, int g) {
+                                          int KR, int pr0, int pr1, int wave, int li, int g, ExpandConsts ec) {
     constexpr bool kShared = Acc<NB>::kShared;
-    const _Float16 *arow0 = nullptr, *arow1 = nullptr;  // nullptr: a zero column
-    if (kShared) {
-        if (li < NB) arow0 = act + li * KR;
-        else if (li >= 8 && li < 8 + NB) arow0 = act + (NB + li - 8) * KR;
-    } else if (li < NB) {
-        arow0 = act + li * KR;
-        arow1 = act + (NB + li) * KR;
-    }
+    // Activation rows this lane feeds.  Column c of the B operand only
+    // reaches output column c, so lanes of unused columns simply repeat a
+    // valid row (no branches, no zeroing); those outputs are never read.
+    const int r = (li & 7) < NB ? (li & 7) : NB - 1;
+    const _Float16 *arow0 = kShared ? act + ((li < 8 ? 0 : NB) + r) * KR : act + (li < NB ? li : NB - 1) * KR;
+    const _Float16 *arow1 = kShared ? arow0 : act + (NB + (li < NB ? li : NB - 1)) * KR;
     for (int p = pr0 + wave; p < pr1; p += kNW) {
         const int pl = p - pr0;
         uint2 w[RT];
@@ -131,15 +154,15 @@ __device__ __forceinline__ void round_mma(f32x4 (&acc)[Acc<NB>::N][RT], const ui
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int e = 64 * pl + 32 * h + 8 * g;
-            const f16x8 v0 = arow0 ? *reinterpret_cast<const f16x8 *>(arow0 + e) : zero8();
-            f16x8 v1 = zero8();
-            if (!kShared) v1 = arow1 ? *reinterpret_cast<const f16x8 *>(arow1 + e) : zero8();
+            const f16x8 v0 = *reinterpret_cast<const f16x8 *>(arow0 + e);
+            f16x8 v1 = v0;
+            if (!kShared) v1 = *reinterpret_cast<const f16x8 *>(arow1 + e);
 #pragma unroll
             for (int t = 0; t < RT; ++t) {
-                const f16x8 s = expand_pm1(h ? w[t].y : w[t].x, g);
-                acc[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(s, v0, acc[0][t], 0, 0, 0);
+                const f16x8 sv = expand_pm1(h ? w[t].y : w[t].x, g, ec.mask, ec.one);
+                acc[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sv, v0, acc[0][t], 0, 0, 0);
                 if (!kShared)
-                    acc[Acc<NB>::N - 1][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(s, v1, acc[Acc<NB>::N - 1][t], 0, 0, 0);
+                    acc[Acc<NB>::N - 1][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sv, v1, acc[Acc<NB>::N - 1][t], 0, 0, 0);
             }
         }
     }
@@ -194,6 +217,7 @@ __global__ __launch_bounds__(kThreads) void mfma_stage1_kernel(const uint32_t *_
     const int g = lane >> 4;
     const int li = lane & 15;
     const int j0 = blockIdx.x * 16 * RT;
+    const ExpandConsts ec = expand_consts();
 
     float mid_pre[RT][4];  // epilogue scales, fetched early
 #pragma unroll
@@ -212,40 +236,64 @@ __global__ __launch_bounds__(kThreads) void mfma_stage1_kernel(const uint32_t *_
         const int pr1 = min(pr0 + PR, npairs);
         const int nitems = (pr1 - pr0) * 8 * RT;
         if (pr0 > 0) __syncthreads();  // the previous round is done with LDS
-        for (int item0 = 0; item0 < nitems; item0 += kThreads * kMaxItems) {
+        // Every load of a batch (sign items, x and b fragments) is issued
+        // before any of it is used; one batch covers the layer shapes of
+        // interest, so the workgroup waits for memory once per round.
+        const int k0 = 64 * pr0, len = 64 * (pr1 - pr0);
+        const int nact = NB * (len >> 3);  // 8-element activation items
+        const bool xvec = (m & 7) == 0;
+        for (int item0 = 0, act0 = 0; item0 < nitems || act0 < nact;
+             item0 += kThreads * kMaxItems, act0 += kThreads * kMaxAct) {
             u32x4 v[kMaxItems];
             load_sign_items<RT>(v, Bt, Wm, j0, pr0, nitems, item0);
-            if (item0 == 0) {
-                // activations of the round: u = x ⊙ b as hi/lo planes, 8 elements per item
-                const int k0 = 64 * pr0, len = 64 * (pr1 - pr0);
-                for (int it = threadIdx.x; it < NB * (len >> 3); it += kThreads) {
-                    const int r = it / (len >> 3);
-                    const int e = (it - r * (len >> 3)) * 8;
-                    const int l = k0 + e;
-                    f16x8 xv = zero8();
-                    if ((m & 7) == 0 && l + 8 <= m) {
-                        xv = *reinterpret_cast<const f16x8 *>(x + static_cast<size_t>(r) * m + l);
-                    } else {
+            f16x8 xv[kMaxAct], bv[kMaxAct];
+            const int per_row = len >> 3;
+            if (xvec) {
+                // rows of x are 16-byte aligned: clamped, unconditional vector loads
 #pragma unroll
-                        for (int q = 0; q < 8; ++q)
-                            if (l + q < m) xv[q] = static_cast<_Float16>(__half2float(x[static_cast<size_t>(r) * m + l + q]));
-                    }
-                    const f16x8 bv = *reinterpret_cast<const f16x8 *>(b + l);  // b is zero-padded to m_pad
+                for (int q = 0; q < kMaxAct; ++q) {
+                    const int it = min(act0 + static_cast<int>(threadIdx.x) + kThreads * q, nact - 1);
+                    const int r = NB == 1 ? 0 : it / per_row;
+                    const int l = k0 + (it - r * per_row) * 8;
+                    // columns past m (zero-padded b) read some valid x instead
+                    xv[q] = *reinterpret_cast<const f16x8 *>(x + static_cast<size_t>(r) * m + min(l, m - 8));
+                    bv[q] = *reinterpret_cast<const f16x8 *>(b + l);  // b is zero-padded to m_pad
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < kMaxAct; ++q) {
+                    const int it = min(act0 + static_cast<int>(threadIdx.x) + kThreads * q, nact - 1);
+                    const int r = NB == 1 ? 0 : it / per_row;
+                    const int l = k0 + (it - r * per_row) * 8;
+                    xv[q] = zero8();
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (l + e < m) xv[q][e] = static_cast<_Float16>(__half2float(x[static_cast<size_t>(r) * m + l + e]));
+                    bv[q] = *reinterpret_cast<const f16x8 *>(b + l);
+                }
+            }
+            store_sign_items(v, sgn, nitems, item0);
+            // u = x ⊙ b (exact in fp32) as hi/lo planes
+#pragma unroll
+            for (int q = 0; q < kMaxAct; ++q) {
+                const int it = act0 + threadIdx.x + kThreads * q;
+                if (it < nact) {
+                    const int r = NB == 1 ? 0 : it / per_row;
+                    const int e = (it - r * per_row) * 8;
                     f16x8 hi, lo;
 #pragma unroll
-                    for (int q = 0; q < 8; ++q) {
-                        const float u = static_cast<float>(xv[q]) * static_cast<float>(bv[q]);
-                        hi[q] = static_cast<_Float16>(u);
-                        lo[q] = static_cast<_Float16>(u - static_cast<float>(hi[q]));
+                    for (int c = 0; c < 8; ++c) {
+                        const float u = static_cast<float>(xv[q][c]) * static_cast<float>(bv[q][c]);
+                        hi[c] = static_cast<_Float16>(u);
+                        lo[c] = static_cast<_Float16>(u - static_cast<float>(hi[c]));
                     }
                     *reinterpret_cast<f16x8 *>(act + r * KR + e) = hi;
                     *reinterpret_cast<f16x8 *>(act + (NB + r) * KR + e) = lo;
                 }
             }
-            store_sign_items(v, sgn, nitems, item0);
         }
         __syncthreads();
-        round_mma<NB, RT>(acc, sgn, act, KR, pr0, pr1, wave, li, g);
+        round_mma<NB, RT>(acc, sgn, act, KR, pr0, pr1, wave, li, g, ec);
     }
 
     reduce_waves<NB, RT>(acc, red, wave, lane);
@@ -285,6 +333,7 @@ __global__ __launch_bounds__(kThreads) void mfma_stage2_kernel(const uint32_t *_
     const int g = lane >> 4;
     const int li = lane & 15;
     const int i0 = blockIdx.x * 16 * RT;
+    const ExpandConsts ec = expand_consts();
 
     float a_pre[RT][4];  // epilogue scales, fetched early
 #pragma unroll
@@ -306,23 +355,35 @@ __global__ __launch_bounds__(kThreads) void mfma_stage2_kernel(const uint32_t *_
         const int pr1 = min(pr0 + PR, npairs);
         const int nitems = (pr1 - pr0) * 8 * RT;
         if (pr0 > 0) __syncthreads();
-        for (int item0 = 0; item0 < nitems; item0 += kThreads * kMaxItems) {
+        // all loads of a batch (sign items, v_hi / v_lo items) are issued first
+        const int k0 = 64 * pr0, len = 64 * (pr1 - pr0);
+        const int nact = 2 * NB * (len >> 3);  // 16-byte plane items: hi rows then lo rows
+        for (int item0 = 0, act0 = 0; item0 < nitems || act0 < nact;
+             item0 += kThreads * kMaxItems, act0 += kThreads * kMaxAct) {
             u32x4 v[kMaxItems];
             load_sign_items<RT>(v, At, Wk, i0, pr0, nitems, item0);
-            if (item0 == 0) {
-                // the round of the v_hi / v_lo planes, 16 bytes per item
-                const int k0 = 64 * pr0, len = 64 * (pr1 - pr0);
-                for (int it = threadIdx.x; it < 2 * NB * (len >> 3); it += kThreads) {
-                    const int r = it / (len >> 3);  // plane row: hi rows then lo rows
-                    const int e = (it - r * (len >> 3)) * 8;
-                    *reinterpret_cast<f16x8 *>(act + r * KR + e) =
-                        *reinterpret_cast<const f16x8 *>(v16 + static_cast<size_t>(r) * k_pad + k0 + e);
-                }
+            f16x8 av[kMaxAct];
+            const int per_row = len >> 3;
+#pragma unroll
+            for (int q = 0; q < kMaxAct; ++q) {
+                const int it = min(act0 + static_cast<int>(threadIdx.x) + kThreads * q, nact - 1);
+                const int r = it / per_row;
+                const int e = (it - r * per_row) * 8;
+                av[q] = *reinterpret_cast<const f16x8 *>(v16 + static_cast<size_t>(r) * k_pad + k0 + e);
             }
             store_sign_items(v, sgn, nitems, item0);
+#pragma unroll
+            for (int q = 0; q < kMaxAct; ++q) {
+                const int it = act0 + threadIdx.x + kThreads * q;
+                if (it < nact) {
+                    const int r = it / per_row;
+                    const int e = (it - r * per_row) * 8;
+                    *reinterpret_cast<f16x8 *>(act + r * KR + e) = av[q];
+                }
+            }
         }
         __syncthreads();
-        round_mma<NB, RT>(acc, sgn, act, KR, pr0, pr1, wave, li, g);
+        round_mma<NB, RT>(acc, sgn, act, KR, pr0, pr1, wave, li, g, ec);
     }
 
     reduce_waves<NB, RT>(acc, red, wave, lane);
@@ -373,7 +434,7 @@ int launch_rt(const MfmaDecodeArgs &d, hipStream_t s, int which) {
 template <int NB>
 int launch_nb(const MfmaDecodeArgs &d, hipStream_t s, int which) {
     const int rows = which == 1 ? d.k_pad : d.n_pad;
-    constexpr int kOneRound = 256;
+    constexpr int kOneRound = DBF_DECODE_ONE_ROUND;
     if constexpr (NB <= 4) {
         if (rows / 16 <= kOneRound) return launch_rt<NB, 1>(d, s, which);
         if (rows / 32 <= kOneRound) return launch_rt<NB, 2>(d, s, which);

@@ -123,6 +123,27 @@ def test_decode_small_shapes(gpu, n, m, k, batch, path):
     assert_tol(y, O.dense_forward(X, A, B, a, mid, b), f"decode {n}x{m}x{k} b{batch}")
 
 
+# Shapes whose row counts (k for stage 1, n for stage 2) exceed 4096 / 8192,
+# so the decode kernels take their 32- and 64-row workgroup variants.
+ROW_TILE_SHAPES = [
+    # n, m, k
+    (64, 96, 4160),     # stage 1: 32-row workgroups
+    (4160, 96, 64),     # stage 2: 32-row workgroups
+    (70, 100, 8256),    # stage 1: 64-row workgroups
+    (8256, 130, 200),   # stage 2: 64-row workgroups, ragged n
+]
+
+
+@pytest.mark.parametrize("n,m,k", ROW_TILE_SHAPES)
+@pytest.mark.parametrize("batch", [1, 4])
+def test_decode_row_tile_variants(gpu, n, m, k, batch):
+    _say(f"decode row tiles n={n} m={m} k={k} batch={batch}")
+    X, A, B, a, mid, b = inputs.tiny_case(3000 + n + m + k + batch, n, m, k, batch, signed_scales=True)
+    L = inputs.Layer("s", n, m, k, A, B, a, mid, b, {})
+    y = run(L, X, dbf.DBF_PATH_DECODE)
+    assert_tol(y, O.dense_forward(X, A, B, a, mid, b), f"decode row tiles {n}x{m}x{k} b{batch}")
+
+
 @pytest.mark.parametrize("n,m,k", SHAPES)
 @pytest.mark.parametrize("batch", [1, 17, 100])
 def test_prefill_small_shapes(gpu, n, m, k, batch):
