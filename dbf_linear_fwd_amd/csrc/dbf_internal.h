@@ -8,6 +8,8 @@
 #include "dbf.h"
 
 #if defined(__HIPCC__)
+#include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #define DBF_HD __host__ __device__
 #else
 #define DBF_HD
@@ -86,6 +88,27 @@ int launch_decode_stage2(const uint32_t *A_dev, const float *tpart, const void *
 // Final: y[r][i] = rne16(a[i] * sum_c ypart[c][r][i]) for i < n.
 int launch_decode_final(const float *ypart, const void *a_dev, void *y, int batch, int n, int n_pad,
                         int nchunk_k, void *stream);
+
+// Events that bracket the next kernel launch when the runtime times kernels
+// (null otherwise).  They are handed to the launch itself, so the elapsed time
+// between them is the kernel's own execution, without queueing around it.
+struct LaunchEvents {
+    void *start = nullptr, *stop = nullptr;
+};
+LaunchEvents &launch_events();
+
+#if defined(__HIPCC__)
+// Launch through hipExtLaunchKernel when launch events are set, plainly otherwise.
+template <typename K, typename... Args>
+inline void launch_kernel(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, Args... args) {
+    const LaunchEvents &e = launch_events();
+    if (e.start && e.stop)
+        hipExtLaunchKernelGGL(kernel, grid, block, static_cast<uint32_t>(lds), s, static_cast<hipEvent_t>(e.start),
+                              static_cast<hipEvent_t>(e.stop), 0u, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+}
+#endif
 
 // Matrix-core product with a sign matrix:
 //   out[i][c] = rne16( sn[c] * sum_kk P[i][kk] * S[c][kk] * (sk ? sk[kk] : 1) )

@@ -391,7 +391,7 @@ size_t lut_lds_bytes(int CW) {
 
 template <int NB>
 int lut_stage1(const DecodeArgs &d, hipStream_t s) {
-    hipLaunchKernelGGL(lut_stage1_kernel<NB>, dim3(d.k_pad / 64, d.nchunk_m), dim3(kThreads),
+    launch_kernel(lut_stage1_kernel<NB>, dim3(d.k_pad / 64, d.nchunk_m), dim3(kThreads),
                        lut_lds_bytes<NB>(d.cw_m), s, d.B_dev, static_cast<const __half *>(d.x),
                        static_cast<const __half *>(d.b_dev), d.tpart, d.m, d.m_pad / 32, d.k_pad, d.cw_m);
     return static_cast<int>(hipGetLastError());
@@ -399,7 +399,7 @@ int lut_stage1(const DecodeArgs &d, hipStream_t s) {
 
 template <int NB>
 int lut_stage2(const DecodeArgs &d, hipStream_t s) {
-    hipLaunchKernelGGL(lut_stage2_kernel<NB>, dim3(d.n_pad / 64, d.nchunk_k), dim3(kThreads),
+    launch_kernel(lut_stage2_kernel<NB>, dim3(d.n_pad / 64, d.nchunk_k), dim3(kThreads),
                        lut_lds_bytes<NB>(d.cw_k), s, d.A_dev, d.tpart, static_cast<const __half *>(d.mid_dev),
                        static_cast<const __half *>(d.a_dev), d.ypart, d.tickets, static_cast<__half *>(d.y), d.n,
                        d.k_pad / 32, d.n_pad, d.k_pad, d.nchunk_m, d.nchunk_k, d.cw_k);
@@ -440,7 +440,7 @@ int launch_lut_stage2(const DecodeArgs &d, void *stream) {
 int launch_decode_stage1(const uint32_t *B_dev, const void *x, const void *b_dev, float *tpart, int batch,
                          int m, int m_pad, int k_pad, int nchunk_m, void *stream) {
     dim3 grid(k_pad / 64, nchunk_m);
-    hipLaunchKernelGGL(decode_stage1_kernel, grid, dim3(64), 0, static_cast<hipStream_t>(stream), B_dev,
+    launch_kernel(decode_stage1_kernel, grid, dim3(64), 0, static_cast<hipStream_t>(stream), B_dev,
                        static_cast<const __half *>(x), static_cast<const __half *>(b_dev), tpart, batch, m,
                        m_pad / 32, k_pad);
     return static_cast<int>(hipGetLastError());
@@ -449,7 +449,7 @@ int launch_decode_stage1(const uint32_t *B_dev, const void *x, const void *b_dev
 int launch_decode_stage2(const uint32_t *A_dev, const float *tpart, const void *mid_dev, float *ypart,
                          int batch, int n_pad, int k_pad, int nchunk_m, int nchunk_k, void *stream) {
     dim3 grid(n_pad / 64, nchunk_k);
-    hipLaunchKernelGGL(decode_stage2_kernel, grid, dim3(64), 0, static_cast<hipStream_t>(stream), A_dev,
+    launch_kernel(decode_stage2_kernel, grid, dim3(64), 0, static_cast<hipStream_t>(stream), A_dev,
                        tpart, static_cast<const __half *>(mid_dev), ypart, batch, k_pad / 32, n_pad, k_pad,
                        nchunk_m);
     return static_cast<int>(hipGetLastError());
@@ -459,7 +459,7 @@ int launch_decode_final(const float *ypart, const void *a_dev, void *y, int batc
                         int nchunk_k, void *stream) {
     const int total = batch * n;
     dim3 grid((total + 255) / 256);
-    hipLaunchKernelGGL(decode_final_kernel, grid, dim3(256), 0, static_cast<hipStream_t>(stream), ypart,
+    launch_kernel(decode_final_kernel, grid, dim3(256), 0, static_cast<hipStream_t>(stream), ypart,
                        static_cast<const __half *>(a_dev), static_cast<__half *>(y), batch, n, n_pad,
                        nchunk_k);
     return static_cast<int>(hipGetLastError());

@@ -414,7 +414,7 @@ int launch_rt(const MfmaDecodeArgs &d, hipStream_t s, int which) {
         (void)once;
         const int PR = std::min(d.m_pad / 64, round_pairs<NB, RT>());
         const size_t lds = lds_bytes<NB, RT>(PR);
-        hipLaunchKernelGGL((mfma_stage1_kernel<NB, RT>), dim3(d.k_pad / (16 * RT)), dim3(kThreads), lds, s, d.B_dev,
+        launch_kernel((mfma_stage1_kernel<NB, RT>), dim3(d.k_pad / (16 * RT)), dim3(kThreads), lds, s, d.B_dev,
                            d.m_pad / 32, static_cast<const __half *>(d.x), d.m, static_cast<const __half *>(d.b_dev),
                            static_cast<const __half *>(d.mid_dev), reinterpret_cast<__half *>(d.v16), d.k_pad, PR);
     } else {
@@ -422,7 +422,7 @@ int launch_rt(const MfmaDecodeArgs &d, hipStream_t s, int which) {
         (void)once;
         const int PR = std::min(d.k_pad / 64, round_pairs<NB, RT>());
         const size_t lds = lds_bytes<NB, RT>(PR);
-        hipLaunchKernelGGL((mfma_stage2_kernel<NB, RT>), dim3(d.n_pad / (16 * RT)), dim3(kThreads), lds, s, d.A_dev,
+        launch_kernel((mfma_stage2_kernel<NB, RT>), dim3(d.n_pad / (16 * RT)), dim3(kThreads), lds, s, d.A_dev,
                            d.k_pad / 32, reinterpret_cast<const __half *>(d.v16), d.k_pad,
                            static_cast<const __half *>(d.a_dev), static_cast<__half *>(d.y), d.n, PR);
     }

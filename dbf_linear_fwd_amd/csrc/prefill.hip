@@ -213,7 +213,7 @@ void launch(const void *P, int ldp, int M, int K, const uint32_t *S, int words, 
             const void *sn, void *out, int ldo, int n_out, hipStream_t s) {
     const int nbm = (M + BM - 1) / BM;
     const int nbn = (n_out + BN - 1) / BN;
-    hipLaunchKernelGGL((sign_gemm_kernel<HAS_SK, PVEC>), dim3(nbm * nbn), dim3(kThreads), 0, s,
+    launch_kernel((sign_gemm_kernel<HAS_SK, PVEC>), dim3(nbm * nbn), dim3(kThreads), 0, s,
                        static_cast<const __half *>(P), ldp, M, K, S, words, n_rows_pad,
                        static_cast<const __half *>(sk), static_cast<const __half *>(sn), static_cast<__half *>(out),
                        ldo, n_out, nbm, nbn);

@@ -146,6 +146,17 @@ dbf_status_t upload_scales(uint16_t **dst, const uint16_t *src, int32_t len, int
     return upload(*dst, buf.data(), buf.size() * sizeof(uint16_t));
 }
 
+}  // namespace
+
+namespace dbf {
+LaunchEvents &launch_events() {
+    static thread_local LaunchEvents ev;
+    return ev;
+}
+}  // namespace dbf
+
+namespace {
+
 hipEvent_t take_event(dbf_layer *h) {
     if (!h->event_pool.empty()) {
         hipEvent_t e = h->event_pool.back();
@@ -157,18 +168,20 @@ hipEvent_t take_event(dbf_layer *h) {
     return e;
 }
 
-// Launch one kernel through `fn`, bracketed by events when timing is on.
+// Launch one kernel through `fn`; with timing on, a pair of events rides on
+// the launch itself (see launch_kernel) and is kept for dbf_timing_read.
 template <typename F>
 dbf_status_t timed_launch(dbf_layer *h, const char *name, hipStream_t stream, F fn) {
+    (void)stream;
     hipEvent_t e0 = nullptr, e1 = nullptr;
     if (h->timing) {
         e0 = take_event(h);
         e1 = take_event(h);
-        if (e0 && e1) (void)hipEventRecord(e0, stream);
+        if (e0 && e1) dbf::launch_events() = {e0, e1};
     }
     const int err = fn();
+    dbf::launch_events() = {};
     if (e0 && e1) {
-        (void)hipEventRecord(e1, stream);
         h->pending.push_back({name, e0, e1});
     } else {
         if (e0) h->event_pool.push_back(e0);

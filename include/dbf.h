@@ -171,12 +171,12 @@ size_t dbf_layout_words(int32_t rows, int32_t words);
 
 /*
  * Kernel timing (measurement support).  When enabled on a handle, every
- * kernel the handle launches is bracketed by a pair of HIP events recorded on
- * the same stream; dbf_timing_read() synchronises those events and returns,
- * per kernel name, the number of launches and the summed elapsed time since
- * the last read.  Disabled by default; enabling adds two event records per
- * launch.  dbf_timing_read fills at most `cap` entries and sets *count to the
- * number of distinct kernels seen.
+ * kernel the handle launches carries a pair of HIP events on the launch itself
+ * (hipExtLaunchKernel), so their elapsed time is that kernel's execution on
+ * its stream.  dbf_timing_read() synchronises those events and returns, per
+ * kernel name, the number of launches and the summed elapsed time since the
+ * last read.  Disabled by default.  dbf_timing_read fills at most `cap`
+ * entries and sets *count to the number of distinct kernels seen.
  */
 typedef struct {
     char name[48];
