@@ -131,6 +131,26 @@ def decode_kernel_bytes(layer, batch):
     }
 
 
+def recorded_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    record (FETCH_SIZE and WRITE_SIZE scaled by a plain copy's reading), or
+    None when the kernel's source has changed since it was recorded."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+    try:
+        text = open(path).read()
+        rec = json.loads(re.search(r"```json\n(.*?)```", text, re.S).group(1))
+        k = rec["kernels"][kernel]
+        src = open(os.path.join(ROOT, k["source"]), "rb").read()
+    except (OSError, KeyError, AttributeError, ValueError):
+        return None
+    if hashlib.sha256(src).hexdigest() != k["sha256"]:
+        return None
+    sc = rec["scale"]
+    return 1024.0 * (k["FETCH_SIZE"] * sc["FETCH_SIZE"] + k["WRITE_SIZE"] * sc["WRITE_SIZE"])
+
+
 def prefill_kernel_flops(layer, batch):
     n, m, k = layer.n, layer.m, layer.k
     return {"prefill_gemm1": 2 * batch * k * m, "prefill_gemm2": 2 * batch * k * n}
@@ -222,7 +242,7 @@ def main():
             "eager_gbs": bytes_step * done_e / el_e / 1e9,
             "kernels": kt, "dominant": dom,
             "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": ach / HBM_PEAK_GBS, "traffic": None, "kernel": dom,
+                         "frac": ach / HBM_PEAK_GBS, "traffic": recorded_traffic(dom), "kernel": dom,
                          "algorithmic_bytes_per_launch": kb[dom]},
             "layer": layer, "copies": copies,
         }
@@ -255,7 +275,7 @@ def main():
             "value": tfs, "unit": "TFLOP/s-eq", "ms_per_forward": el * 1e3 / done,
             "frac_of_mfma_peak": tfs / MFMA_F16_PEAK_TFLOPS, "kernels": kt,
             "roofline": {"bound": "mfma", "achieved": ach, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": ach / MFMA_F16_PEAK_TFLOPS, "traffic": None, "kernel": dom,
+                         "frac": ach / MFMA_F16_PEAK_TFLOPS, "traffic": recorded_traffic(dom), "kernel": dom,
                          "algorithmic_flops_per_launch": kf[dom]},
             "workload": "4096x4096 projection, k=4096 (~2 bits/weight), batch 2048",
         }
