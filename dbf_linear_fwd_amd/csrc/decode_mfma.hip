@@ -96,17 +96,29 @@ struct Acc {
 // LDS layout of one round of PR pairs:
 //   signs  [PR][16*RT rows][2 words]           PR * 128 * RT bytes
 //   planes [2][NB][64*PR] fp16 (hi, lo)         PR * 256 * NB bytes
+// and, after the last round, over the same bytes:
 //   reduce [Acc::N][kNW][RT][64 lanes][4] fp32  Acc::N * kNW * RT * 1 KiB
+// followed by kLdsTail bytes for workgroup-wide scalars.
+constexpr size_t kLdsTail = 64;
+template <int NB, int RT>
+__host__ __device__ constexpr size_t lds_round_bytes(int PR) {
+    return static_cast<size_t>(PR) * (128 * RT + 256 * NB);
+}
+template <int NB, int RT>
+__host__ __device__ constexpr size_t lds_reduce_bytes() {
+    return sizeof(float) * Acc<NB>::N * kNW * RT * 256;
+}
 template <int NB, int RT>
 __host__ __device__ constexpr size_t lds_bytes(int PR) {
-    return static_cast<size_t>(PR) * (128 * RT + 256 * NB) + sizeof(float) * Acc<NB>::N * kNW * RT * 256;
+    return (lds_round_bytes<NB, RT>(PR) > lds_reduce_bytes<NB, RT>() ? lds_round_bytes<NB, RT>(PR)
+                                                                       : lds_reduce_bytes<NB, RT>()) +
+           kLdsTail;
 }
 
 // Pairs per round that fit the LDS budget.
 template <int NB, int RT>
 int round_pairs() {
-    const size_t fixed = sizeof(float) * Acc<NB>::N * kNW * RT * 256;
-    return static_cast<int>((kLdsBudget - fixed) / (128 * RT + 256 * NB));
+    return static_cast<int>((kLdsBudget - kLdsTail) / (128 * RT + 256 * NB));
 }
 
 // Issue the loads of this thread's 16-byte sign items of the round, items
@@ -173,6 +185,7 @@ __device__ __forceinline__ void round_mma(f32x4 (&acc)[Acc<NB>::N][RT], const ui
 template <int NB, int RT>
 __device__ __forceinline__ void reduce_waves(const f32x4 (&acc)[Acc<NB>::N][RT], float *red, int wave, int lane) {
     constexpr int N = Acc<NB>::N;
+    __syncthreads();  // every wave is done reading the round buffers that `red` overlays
 #pragma unroll
     for (int c = 0; c < N; ++c)
 #pragma unroll
@@ -199,24 +212,22 @@ __device__ __forceinline__ f32x4 total(const float *red, int t, int lane) {
     return dh + dl;
 }
 
-// Stage 1: v = mid * (B (x ⊙ b)), stored as fp16 hi/lo planes [2][NB][k_pad].
+// Stage 1 for row block `blk` (rows 16*RT*blk ..): v = mid * (B (x ⊙ b)),
+// stored as fp16 hi/lo planes [2][NB][k_pad].
 template <int NB, int RT>
-__global__ __launch_bounds__(kThreads) void mfma_stage1_kernel(const uint32_t *__restrict__ Bt, int Wm,
-                                                               const __half *__restrict__ x, int m,
-                                                               const __half *__restrict__ b,
-                                                               const __half *__restrict__ mid,
-                                                               __half *__restrict__ v16, int k_pad, int PR) {
-    extern __shared__ float lds[];
+__device__ __forceinline__ void stage1_body(int blk, char *base, const uint32_t *__restrict__ Bt, int Wm,
+                                            const __half *__restrict__ x, int m, const __half *__restrict__ b,
+                                            const __half *__restrict__ mid, __half *__restrict__ v16, int k_pad,
+                                            int PR) {
     const int KR = 64 * PR;
-    char *base = reinterpret_cast<char *>(lds);
     uint32_t *sgn = reinterpret_cast<uint32_t *>(base);
     _Float16 *act = reinterpret_cast<_Float16 *>(base + static_cast<size_t>(PR) * 128 * RT);
-    float *red = reinterpret_cast<float *>(base + static_cast<size_t>(PR) * (128 * RT + 256 * NB));
+    float *red = reinterpret_cast<float *>(base);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4;
     const int li = lane & 15;
-    const int j0 = blockIdx.x * 16 * RT;
+    const int j0 = blk * 16 * RT;
     const ExpandConsts ec = expand_consts();
 
     float mid_pre[RT][4];  // epilogue scales, fetched early
@@ -316,23 +327,20 @@ __global__ __launch_bounds__(kThreads) void mfma_stage1_kernel(const uint32_t *_
     }
 }
 
-// Stage 2: y = rne16(a ⊙ (A (v_hi + v_lo))).
+// Stage 2 for row block `blk`: y = rne16(a ⊙ (A (v_hi + v_lo))).
 template <int NB, int RT>
-__global__ __launch_bounds__(kThreads) void mfma_stage2_kernel(const uint32_t *__restrict__ At, int Wk,
-                                                               const __half *__restrict__ v16, int k_pad,
-                                                               const __half *__restrict__ a,
-                                                               __half *__restrict__ y, int n, int PR) {
-    extern __shared__ float lds[];
+__device__ __forceinline__ void stage2_body(int blk, char *base, const uint32_t *__restrict__ At, int Wk,
+                                            const __half *__restrict__ v16, int k_pad, const __half *__restrict__ a,
+                                            __half *__restrict__ y, int n, int PR) {
     const int KR = 64 * PR;
-    char *base = reinterpret_cast<char *>(lds);
     uint32_t *sgn = reinterpret_cast<uint32_t *>(base);
     _Float16 *act = reinterpret_cast<_Float16 *>(base + static_cast<size_t>(PR) * 128 * RT);
-    float *red = reinterpret_cast<float *>(base + static_cast<size_t>(PR) * (128 * RT + 256 * NB));
+    float *red = reinterpret_cast<float *>(base);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4;
     const int li = lane & 15;
-    const int i0 = blockIdx.x * 16 * RT;
+    const int i0 = blk * 16 * RT;
     const ExpandConsts ec = expand_consts();
 
     float a_pre[RT][4];  // epilogue scales, fetched early
@@ -355,15 +363,15 @@ __global__ __launch_bounds__(kThreads) void mfma_stage2_kernel(const uint32_t *_
         const int pr1 = min(pr0 + PR, npairs);
         const int nitems = (pr1 - pr0) * 8 * RT;
         if (pr0 > 0) __syncthreads();
-        // all loads of a batch (sign items, v_hi / v_lo items) are issued first
         const int k0 = 64 * pr0, len = 64 * (pr1 - pr0);
         const int nact = 2 * NB * (len >> 3);  // 16-byte plane items: hi rows then lo rows
+        const int per_row = len >> 3;
+        // all loads of a batch (sign items, v_hi / v_lo items) are issued first
         for (int item0 = 0, act0 = 0; item0 < nitems || act0 < nact;
              item0 += kThreads * kMaxItems, act0 += kThreads * kMaxAct) {
             u32x4 v[kMaxItems];
             load_sign_items<RT>(v, At, Wk, i0, pr0, nitems, item0);
             f16x8 av[kMaxAct];
-            const int per_row = len >> 3;
 #pragma unroll
             for (int q = 0; q < kMaxAct; ++q) {
                 const int it = min(act0 + static_cast<int>(threadIdx.x) + kThreads * q, nact - 1);
@@ -401,6 +409,25 @@ __global__ __launch_bounds__(kThreads) void mfma_stage2_kernel(const uint32_t *_
     }
 }
 
+template <int NB, int RT>
+__global__ __launch_bounds__(kThreads) void mfma_stage1_kernel(const uint32_t *__restrict__ Bt, int Wm,
+                                                               const __half *__restrict__ x, int m,
+                                                               const __half *__restrict__ b,
+                                                               const __half *__restrict__ mid,
+                                                               __half *__restrict__ v16, int k_pad, int PR) {
+    extern __shared__ float lds[];
+    stage1_body<NB, RT>(blockIdx.x, reinterpret_cast<char *>(lds), Bt, Wm, x, m, b, mid, v16, k_pad, PR);
+}
+
+template <int NB, int RT>
+__global__ __launch_bounds__(kThreads) void mfma_stage2_kernel(const uint32_t *__restrict__ At, int Wk,
+                                                               const __half *__restrict__ v16, int k_pad,
+                                                               const __half *__restrict__ a,
+                                                               __half *__restrict__ y, int n, int PR) {
+    extern __shared__ float lds[];
+    stage2_body<NB, RT>(blockIdx.x, reinterpret_cast<char *>(lds), At, Wk, v16, k_pad, a, y, n, PR);
+}
+
 template <typename K>
 void allow_lds(K kernel, size_t bytes) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -415,16 +442,16 @@ int launch_rt(const MfmaDecodeArgs &d, hipStream_t s, int which) {
         const int PR = std::min(d.m_pad / 64, round_pairs<NB, RT>());
         const size_t lds = lds_bytes<NB, RT>(PR);
         launch_kernel((mfma_stage1_kernel<NB, RT>), dim3(d.k_pad / (16 * RT)), dim3(kThreads), lds, s, d.B_dev,
-                           d.m_pad / 32, static_cast<const __half *>(d.x), d.m, static_cast<const __half *>(d.b_dev),
-                           static_cast<const __half *>(d.mid_dev), reinterpret_cast<__half *>(d.v16), d.k_pad, PR);
+                      d.m_pad / 32, static_cast<const __half *>(d.x), d.m, static_cast<const __half *>(d.b_dev),
+                      static_cast<const __half *>(d.mid_dev), reinterpret_cast<__half *>(d.v16), d.k_pad, PR);
     } else {
         static const bool once = (allow_lds(mfma_stage2_kernel<NB, RT>, kLdsBudget), true);
         (void)once;
         const int PR = std::min(d.k_pad / 64, round_pairs<NB, RT>());
         const size_t lds = lds_bytes<NB, RT>(PR);
         launch_kernel((mfma_stage2_kernel<NB, RT>), dim3(d.n_pad / (16 * RT)), dim3(kThreads), lds, s, d.A_dev,
-                           d.k_pad / 32, reinterpret_cast<const __half *>(d.v16), d.k_pad,
-                           static_cast<const __half *>(d.a_dev), static_cast<__half *>(d.y), d.n, PR);
+                      d.k_pad / 32, reinterpret_cast<const __half *>(d.v16), d.k_pad,
+                      static_cast<const __half *>(d.a_dev), static_cast<__half *>(d.y), d.n, PR);
     }
     return static_cast<int>(hipGetLastError());
 }
@@ -432,16 +459,24 @@ int launch_rt(const MfmaDecodeArgs &d, hipStream_t s, int which) {
 // Rows per workgroup: 16, 32 or 64, the smallest that keeps the grid within
 // one workgroup per CU of the 256-CU MI355X (batch <= 4; larger use 16).
 template <int NB>
-int launch_nb(const MfmaDecodeArgs &d, hipStream_t s, int which) {
-    const int rows = which == 1 ? d.k_pad : d.n_pad;
-    constexpr int kOneRound = DBF_DECODE_ONE_ROUND;
+int split_rt(int rows) {
     if constexpr (NB <= 4) {
-        if (rows / 16 <= kOneRound) return launch_rt<NB, 1>(d, s, which);
-        if (rows / 32 <= kOneRound) return launch_rt<NB, 2>(d, s, which);
-        return launch_rt<NB, 4>(d, s, which);
+        if (rows / 16 <= DBF_DECODE_ONE_ROUND) return 1;
+        if (rows / 32 <= DBF_DECODE_ONE_ROUND) return 2;
+        return 4;
     } else {
-        return launch_rt<NB, 1>(d, s, which);
+        return 1;
     }
+}
+
+template <int NB>
+int launch_nb(const MfmaDecodeArgs &d, hipStream_t s, int which) {
+    const int rt = split_rt<NB>(which == 1 ? d.k_pad : d.n_pad);
+    if constexpr (NB <= 4) {
+        if (rt == 2) return launch_rt<NB, 2>(d, s, which);
+        if (rt == 4) return launch_rt<NB, 4>(d, s, which);
+    }
+    return launch_rt<NB, 1>(d, s, which);
 }
 
 }  // namespace

@@ -8,16 +8,22 @@
 //   Y = rne16( a ⊙ (T Aᵀ) )                 batch x n
 // The fp16 rounding of T is the one extra rounding of this path.
 //
-// Both are instances of one kernel, C[M x N] = P[M x K] · S'ᵀ with S' the
-// sign rows expanded to ±1 (or ±sk[k]) and a per-column epilogue scale.
-// Block tile 128 (M) x 256 (N) x 64 (K), four waves of 64 x 128 each, as
-// 2 x 4 tiles of the 32x32x16 f16 MFMA.  The P tile goes through LDS, double
-// buffered: the global loads of the next K step are in flight while the
-// current one is multiplied.  The signs of a K step are one 8-byte word pair
-// per sign row (1 bit per element), loaded straight into registers one step
-// ahead and expanded there; each expanded fragment feeds two MFMAs.  Blocks
-// are ordered so that the blocks resident on one XCD (blockIdx mod 8) share
-// rows of P, which then come from that XCD's L2.
+// Both are instances of one product, C[M x N] = P[M x K] · S'ᵀ with S' the
+// sign rows expanded to ±1 (or ±sk[k]) and a per-column epilogue scale, on
+// the 32x32x16 f16 MFMA.  The signs of a K step of 64 are one 8-byte word
+// pair per sign row (1 bit per element), expanded in registers right before
+// their MFMAs; each expanded fragment feeds every M fragment of its wave.
+// Blocks are ordered so that the blocks resident on one XCD (blockIdx mod 8)
+// share rows of P, which then come from that XCD's L2.
+//
+// sign_gemm_dma_kernel (K % 64 == 0, 16-byte aligned rows; the usual case):
+// block 128 x 256, eight waves of 64 x 64 (two per SIMD).  The operands of a
+// step go from global memory straight into a ring of LDS stages
+// (global_load_lds), several steps ahead of the MFMAs.
+//
+// sign_gemm_kernel (any K, any alignment): block 128 x 256, four waves of
+// 64 x 128, P tile staged through registers into a double-buffered LDS tile,
+// signs loaded into registers one step ahead.
 
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
@@ -31,7 +37,21 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 128, BN = 256, BK = 64;
+#ifndef DBF_PREFILL_NF
+#define DBF_PREFILL_NF 4
+#endif
+#ifndef DBF_PREFILL_MF
+#define DBF_PREFILL_MF 2
+#endif
+#ifndef DBF_PREFILL_OCC
+#define DBF_PREFILL_OCC 1
+#endif
+constexpr int MF = DBF_PREFILL_MF;   // 32-row M fragments per wave
+constexpr int NF = DBF_PREFILL_NF;   // 32-wide N fragments per wave
+constexpr int BM = 128, BK = 64;
+constexpr int WGM = BM / (32 * MF);  // waves along M
+constexpr int WGN = 4 / WGM;         // waves along N
+constexpr int BN = 32 * NF * WGN;
 constexpr int LDP = BK + 8;          // LDS row stride of the P tile (halves), padded against bank conflicts
 constexpr int kThreads = 256;
 constexpr int kXcds = 8;             // MI355X: blocks are dispatched round-robin over 8 XCDs
@@ -69,9 +89,10 @@ __device__ __forceinline__ f16x8 expand(uint32_t word, int g, const u32x4 &sc, E
 // (zero beyond).  S: tiled sign rows, `words` per row, n_rows_pad rows.
 // sk: fp16 scale per K (zero-padded to words*32) or unused.  sn: fp16 scale
 // per output column.  out: fp16 [M][ldo], columns < n_out written.
-// PVEC: rows of P are 16-byte aligned (ldp % 8 == 0).
-template <bool HAS_SK, bool PVEC>
-__global__ __launch_bounds__(kThreads) void sign_gemm_kernel(const __half *__restrict__ P, int ldp, int M, int K,
+// PVEC: rows of P are 16-byte aligned (ldp % 8 == 0).  KFULL: also K % 64
+// == 0, so every K step loads whole 16-byte items with no bounds test.
+template <bool HAS_SK, bool PVEC, bool KFULL>
+__global__ __launch_bounds__(kThreads, DBF_PREFILL_OCC) void sign_gemm_kernel(const __half *__restrict__ P, int ldp, int M, int K,
                                                              const uint32_t *__restrict__ S, int words,
                                                              int n_rows_pad, const __half *__restrict__ sk,
                                                              const __half *__restrict__ sn,
@@ -91,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void sign_gemm_kernel(const __half *__res
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WGN, wn = wave % WGN;
     const int l32 = lane & 31, kg = lane >> 5;
 
     const uint2 *S2 = reinterpret_cast<const uint2 *>(S);
@@ -99,12 +120,12 @@ __global__ __launch_bounds__(kThreads) void sign_gemm_kernel(const __half *__res
 
     // sign rows of this lane's four N fragments (clamped: rows past the end
     // are loaded but never written out)
-    int srow[4];
+    int srow[NF];
 #pragma unroll
-    for (int f = 0; f < 4; ++f) srow[f] = min(n0 + wn * 128 + f * 32 + l32, n_rows_pad - 1);
-    auto load_signs = [&](int kt, uint2 (&w)[4]) {
+    for (int f = 0; f < NF; ++f) srow[f] = min(n0 + wn * 32 * NF + f * 32 + l32, n_rows_pad - 1);
+    auto load_signs = [&](int kt, uint2 (&w)[NF]) {
 #pragma unroll
-        for (int f = 0; f < 4; ++f)
+        for (int f = 0; f < NF; ++f)
             w[f] = S2[(static_cast<size_t>(srow[f] >> 6) * (words >> 1) + kt) * 64 + (srow[f] & 63)];
     };
 
@@ -113,7 +134,7 @@ __global__ __launch_bounds__(kThreads) void sign_gemm_kernel(const __half *__res
     u32x4 skv = {0u, 0u, 0u, 0u};
     auto load_p = [&](int kt) {
         const int k0 = kt * BK;
-        const bool full = PVEC && (k0 + BK <= K);
+        const bool full = KFULL || (PVEC && (k0 + BK <= K));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int it = tid + kThreads * i;
@@ -141,22 +162,22 @@ __global__ __launch_bounds__(kThreads) void sign_gemm_kernel(const __half *__res
         if (HAS_SK && tid < BK / 8) *reinterpret_cast<u32x4 *>(&Ss[buf][tid * 4]) = skv;
     };
 
-    f32x16 acc[2][4];
+    f32x16 acc[MF][NF];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MF; ++i)
 #pragma unroll
-        for (int f = 0; f < 4; ++f)
+        for (int f = 0; f < NF; ++f)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][f][v] = 0.0f;
 
-    float snv[4];  // epilogue column scales, fetched early
+    float snv[NF];  // epilogue column scales, fetched early
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-        const int col = n0 + wn * 128 + f * 32 + l32;
+    for (int f = 0; f < NF; ++f) {
+        const int col = n0 + wn * 32 * NF + f * 32 + l32;
         snv[f] = col < n_out ? __half2float(sn[col]) : 0.0f;
     }
 
-    uint2 wcur[4], wnxt[4];
+    uint2 wcur[NF], wnxt[NF];
     load_signs(0, wcur);
     load_p(0);
     store_p(0);
@@ -168,25 +189,27 @@ __global__ __launch_bounds__(kThreads) void sign_gemm_kernel(const __half *__res
             load_signs(kt + 1, wnxt);
             load_p(kt + 1);
         }
-        const _Float16 *pa = &Ps[buf][(wm * 64 + l32) * LDP + 8 * kg];
+        const _Float16 *pa = &Ps[buf][(wm * 32 * MF + l32) * LDP + 8 * kg];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {  // K sub-steps of 16
-            f16x8 a0 = *reinterpret_cast<const f16x8 *>(pa + s * 16);
-            f16x8 a1 = *reinterpret_cast<const f16x8 *>(pa + 32 * LDP + s * 16);
+            f16x8 af[MF];
+#pragma unroll
+            for (int i = 0; i < MF; ++i) af[i] = *reinterpret_cast<const f16x8 *>(pa + i * 32 * LDP + s * 16);
             u32x4 sc = {0u, 0u, 0u, 0u};
             if (HAS_SK) sc = *reinterpret_cast<const u32x4 *>(&Ss[buf][s * 8 + 4 * kg]);
             const int g = 2 * (s & 1) + kg;  // which 8 elements of the 32-element word
 #pragma unroll
-            for (int f = 0; f < 4; ++f) {
+            for (int f = 0; f < NF; ++f) {
                 const f16x8 bf = expand<HAS_SK>(s < 2 ? wcur[f].x : wcur[f].y, g, sc, ec);
-                acc[0][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, bf, acc[0][f], 0, 0, 0);
-                acc[1][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, bf, acc[1][f], 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < MF; ++i)
+                    acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf, acc[i][f], 0, 0, 0);
             }
         }
         if (kt + 1 < nk) {
             store_p(buf ^ 1);
 #pragma unroll
-            for (int f = 0; f < 4; ++f) wcur[f] = wnxt[f];
+            for (int f = 0; f < NF; ++f) wcur[f] = wnxt[f];
         }
         __syncthreads();
     }
@@ -194,29 +217,249 @@ __global__ __launch_bounds__(kThreads) void sign_gemm_kernel(const __half *__res
     // epilogue: 32x32 MFMA result register v of a lane holds row
     // 8*(v/4) + 4*(lane/32) + v%4 and column lane%32 of its tile
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < MF; ++i) {
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
-            const int col = n0 + wn * 128 + f * 32 + l32;
+        for (int f = 0; f < NF; ++f) {
+            const int col = n0 + wn * 32 * NF + f * 32 + l32;
             if (col >= n_out) continue;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int row = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * kg + (v & 3);
+                const int row = m0 + wm * 32 * MF + i * 32 + 8 * (v >> 2) + 4 * kg + (v & 3);
                 if (row < M) out[static_cast<size_t>(row) * ldo + col] = __float2half_rn(acc[i][f][v] * snv[f]);
             }
         }
     }
 }
 
-template <bool HAS_SK, bool PVEC>
+template <bool HAS_SK, bool PVEC, bool KFULL>
 void launch(const void *P, int ldp, int M, int K, const uint32_t *S, int words, int n_rows_pad, const void *sk,
             const void *sn, void *out, int ldo, int n_out, hipStream_t s) {
     const int nbm = (M + BM - 1) / BM;
     const int nbn = (n_out + BN - 1) / BN;
-    launch_kernel((sign_gemm_kernel<HAS_SK, PVEC>), dim3(nbm * nbn), dim3(kThreads), 0, s,
+    launch_kernel((sign_gemm_kernel<HAS_SK, PVEC, KFULL>), dim3(nbm * nbn), dim3(kThreads), 0, s,
                        static_cast<const __half *>(P), ldp, M, K, S, words, n_rows_pad,
                        static_cast<const __half *>(sk), static_cast<const __half *>(sn), static_cast<__half *>(out),
                        ldo, n_out, nbm, nbn);
+}
+
+
+// ---------------------------------------------------------------------------
+// Deep-pipelined form for K % 64 == 0 and 16-byte aligned rows of P.
+//
+// The operands of a K step go from global memory straight into LDS
+// (global_load_lds_dwordx4 / _dword, no register staging) into a ring of
+// kStages buffers, so kStages - 1 steps are in flight while one is
+// multiplied: the loads have several microseconds of MFMA work to arrive
+// instead of one step's.  Per step and wave the loads are uniform (P: 4
+// 16-byte loads, signs: 2 dword loads, sk: 1 dword load), so the wait for a
+// step is a fixed `s_waitcnt vmcnt`.  The waves meet at one barrier per step;
+// the compiler's own barrier would also wait for the younger steps' loads,
+// hence the raw s_barrier with explicit counts.
+//
+// P tile in LDS: 128 rows of 64 halves (8 chunks of 16 bytes), chunk c of row
+// r stored at position c ^ (r & 7): the eight rows that one MFMA operand read
+// touches then cover all 32 banks once.
+#ifndef DBF_PREFILL_DMA_MF
+#define DBF_PREFILL_DMA_MF 2
+#endif
+#ifndef DBF_PREFILL_DMA_NF
+#define DBF_PREFILL_DMA_NF 2
+#endif
+#ifndef DBF_PREFILL_STAGES
+#define DBF_PREFILL_STAGES 4
+#endif
+#ifndef DBF_PREFILL_DMA_WAVES
+#define DBF_PREFILL_DMA_WAVES 8
+#endif
+constexpr int kDWaves = DBF_PREFILL_DMA_WAVES;
+constexpr int kDThreads = 64 * kDWaves;
+constexpr int DMF = DBF_PREFILL_DMA_MF;
+constexpr int DNF = DBF_PREFILL_DMA_NF;
+constexpr int DWGM = BM / (32 * DMF);
+constexpr int DWGN = kDWaves / DWGM;
+constexpr int DBN = 32 * DNF * DWGN;
+constexpr int kStages = DBF_PREFILL_STAGES;
+constexpr int kPBytes = BM * BK * 2;          // 16 KiB
+constexpr int kSBytes = DBN * 8;              // one word pair per sign row
+constexpr int kKBytes = BK * 2;               // sk of the step
+constexpr int kStageBytes = kPBytes + kSBytes + kKBytes;
+constexpr size_t kDmaLds = static_cast<size_t>(kStages) * kStageBytes;
+constexpr int kPI = BM * BK * 2 / 1024 / kDWaves;   // 1 KiB P loads per wave and step
+constexpr int kSI = DBN / 64 * 2 / kDWaves;          // 256-byte sign loads per wave and step
+static_assert(kPI * kDWaves * 1024 == kPBytes && kSI * kDWaves * 256 == kSBytes && kSI >= 1,
+              "loads of a step divide evenly over the waves");
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void dma16(const void *g, char *l) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void *)(l), 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void *g, char *l) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void *)(l), 4, 0, 0);
+}
+
+// Wait until at most n of this wave's loads are outstanding (n constant).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // s_waitcnt: vmcnt bits [3:0] and [15:14]; expcnt [6:4] and lgkmcnt [11:8] left at "no wait"
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Wait until this wave's loads of a step have landed while the loads of its
+// `y` younger steps (0 <= y <= Y) may still be in flight; D loads per step.
+template <int D, int Y>
+__device__ __forceinline__ void wait_step(int y) {
+    if constexpr (Y == 0) {
+        wait_vm<0>();
+    } else {
+        if (y >= Y) wait_vm<Y * D>();
+        else wait_step<D, Y - 1>(y);
+    }
+}
+
+// One K step of sign_gemm_dma_kernel: start the loads of step `nxt` into
+// stage `dst` (if `go`), then multiply the operands in stage `src`.  The two
+// stage pointers are restrict-qualified: they never overlap, and the compiler
+// then does not hold the LDS reads of `src` back until the loads into `dst`
+// have landed (the kernel orders them itself with vmcnt and the barrier).
+template <bool HAS_SK, typename Issue>
+__device__ __forceinline__ void dma_step(bool go, int nxt, char *__restrict__ dst, const char *__restrict__ src,
+                                         Issue &issue, f32x16 (&acc)[DMF][DNF], int wm, int wn, int l32, int kg,
+                                         ExpandConsts ec) {
+    if (go) issue(nxt, dst);
+    const uint2 *sg = reinterpret_cast<const uint2 *>(src + kPBytes);
+    uint2 w[DNF];
+#pragma unroll
+    for (int f = 0; f < DNF; ++f) w[f] = sg[wn * 32 * DNF + f * 32 + l32];
+    const char *prow = src + (wm * 32 * DMF + l32) * (BK * 2);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {  // K sub-steps of 16
+        const int pc = ((2 * s + kg) ^ (l32 & 7)) * 16;
+        f16x8 af[DMF];
+#pragma unroll
+        for (int i = 0; i < DMF; ++i) af[i] = *reinterpret_cast<const f16x8 *>(prow + i * 32 * (BK * 2) + pc);
+        u32x4 sc = {0u, 0u, 0u, 0u};
+        if (HAS_SK) sc = *reinterpret_cast<const u32x4 *>(src + kPBytes + kSBytes + (s * 8 + 4 * kg) * 4);
+        const int g = 2 * (s & 1) + kg;
+#pragma unroll
+        for (int f = 0; f < DNF; ++f) {
+            const f16x8 bf = expand<HAS_SK>(s < 2 ? w[f].x : w[f].y, g, sc, ec);
+#pragma unroll
+            for (int i = 0; i < DMF; ++i)
+                acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf, acc[i][f], 0, 0, 0);
+        }
+    }
+}
+
+template <bool HAS_SK>
+__global__ __launch_bounds__(kDThreads) void sign_gemm_dma_kernel(const __half *__restrict__ P, int ldp, int M,
+                                                                 const uint32_t *__restrict__ S, int words,
+                                                                 int n_rows_pad, const __half *__restrict__ sk,
+                                                                 const __half *__restrict__ sn,
+                                                                 __half *__restrict__ out, int ldo, int n_out,
+                                                                 int nbm, int nbn) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    constexpr int D = kPI + kSI + (HAS_SK ? 1 : 0);  // loads per step and wave
+
+    const ExpandConsts ec = expand_consts();
+    const int G = nbm * nbn;
+    const int b = blockIdx.x;
+    const int xcd = b % kXcds, slot = b / kXcds, q = G / kXcds, rem = G % kXcds;
+    const int tile = xcd * q + min(xcd, rem) + slot;
+    const int bm = tile / nbn, bn = tile - (tile / nbn) * nbn;
+    const int m0 = bm * BM, n0 = bn * DBN;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int wm = wave / DWGN, wn = wave % DWGN;
+    const int l32 = lane & 31, kg = lane >> 5;
+    const int nk = words >> 1;
+
+    // per-lane source offsets of the step loads (the step adds 64 halves / one word pair)
+    const __half *psrc[kPI];
+#pragma unroll
+    for (int qq = 0; qq < kPI; ++qq) {
+        const int c = (wave * kPI + qq) * 64 + lane;  // 16-byte chunk of the tile
+        const int r = c >> 3, pc = c & 7;
+        const int lc = pc ^ (r & 7);
+        psrc[qq] = P + static_cast<size_t>(min(m0 + r, M - 1)) * ldp + lc * 8;
+    }
+    const uint32_t *ssrc[kSI];
+#pragma unroll
+    for (int h = 0; h < kSI; ++h) {
+        const int ii = wave * kSI + h;                    // loads of 256 bytes: row tiles x 2 halves
+        const int t = min((n0 >> 6) + (ii >> 1), n_rows_pad / 64 - 1);  // tiles past the end: loaded, unused
+        ssrc[h] = S + static_cast<size_t>(t) * (words >> 1) * 128 + (ii & 1) * 64 + lane;
+    }
+    auto issue = [&](int kt, char *st) {
+#pragma unroll
+        for (int qq = 0; qq < kPI; ++qq) dma16(psrc[qq] + kt * BK, st + (wave * kPI + qq) * 1024);
+#pragma unroll
+        for (int h = 0; h < kSI; ++h) dma4(ssrc[h] + kt * 128, st + kPBytes + (wave * kSI + h) * 256);
+        if (HAS_SK) {
+            if (lane < 32) dma4(sk + kt * BK + 2 * lane, st + kPBytes + kSBytes);  // every wave: same 128 bytes
+        }
+    };
+
+    f32x16 acc[DMF][DNF];
+#pragma unroll
+    for (int i = 0; i < DMF; ++i)
+#pragma unroll
+        for (int f = 0; f < DNF; ++f)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][f][v] = 0.0f;
+
+    float snv[DNF];
+#pragma unroll
+    for (int f = 0; f < DNF; ++f) {
+        const int col = n0 + wn * 32 * DNF + f * 32 + l32;
+        snv[f] = col < n_out ? __half2float(sn[col]) : 0.0f;
+    }
+
+#pragma unroll
+    for (int s0 = 0; s0 < kStages - 1; ++s0)
+        if (s0 < nk) issue(s0, lds + s0 * kStageBytes);
+
+    for (int kt = 0; kt < nk; ++kt) {
+        // this wave's loads of step kt have landed; younger steps may be in flight
+        wait_step<D, kStages - 2>(min(kStages - 2, nk - 1 - kt));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();  // ... and every other wave's; step kt - 1's buffer is free
+        asm volatile("" ::: "memory");
+        const int nxt = kt + kStages - 1;
+        dma_step<HAS_SK>(nxt < nk, nxt, lds + (nxt % kStages) * kStageBytes, lds + (kt % kStages) * kStageBytes, issue,
+                         acc, wm, wn, l32, kg, ec);
+    }
+
+#pragma unroll
+    for (int i = 0; i < DMF; ++i) {
+#pragma unroll
+        for (int f = 0; f < DNF; ++f) {
+            const int col = n0 + wn * 32 * DNF + f * 32 + l32;
+            if (col >= n_out) continue;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = m0 + wm * 32 * DMF + i * 32 + 8 * (v >> 2) + 4 * kg + (v & 3);
+                if (row < M) out[static_cast<size_t>(row) * ldo + col] = __float2half_rn(acc[i][f][v] * snv[f]);
+            }
+        }
+    }
+}
+
+template <bool HAS_SK>
+void launch_dma(const void *P, int ldp, int M, const uint32_t *S, int words, int n_rows_pad, const void *sk,
+                const void *sn, void *out, int ldo, int n_out, hipStream_t s) {
+    static const bool once = ((void)hipFuncSetAttribute(reinterpret_cast<const void *>(sign_gemm_dma_kernel<HAS_SK>),
+                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                        static_cast<int>(kDmaLds)),
+                              true);
+    (void)once;
+    const int nbm = (M + BM - 1) / BM;
+    const int nbn = (n_out + DBN - 1) / DBN;
+    launch_kernel((sign_gemm_dma_kernel<HAS_SK>), dim3(nbm * nbn), dim3(kDThreads), kDmaLds, s,
+                  static_cast<const __half *>(P), ldp, M, S, words, n_rows_pad, static_cast<const __half *>(sk),
+                  static_cast<const __half *>(sn), static_cast<__half *>(out), ldo, n_out, nbm, nbn);
 }
 
 }  // namespace
@@ -225,12 +468,23 @@ int launch_sign_gemm(const void *P, int ldp, int M, int K, const uint32_t *S, in
                      const void *sk, const void *sn, void *out, int ldo, int n_out, void *stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool pvec = (ldp & 7) == 0;
+    const bool kfull = pvec && (K % BK) == 0;
+#ifndef DBF_PREFILL_NO_DMA
+    if (kfull && (reinterpret_cast<uintptr_t>(P) & 15) == 0 && K == words * 32) {
+        if (sk) launch_dma<true>(P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, s);
+        else launch_dma<false>(P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, s);
+        return static_cast<int>(hipGetLastError());
+    }
+#endif
     if (sk) {
-        if (pvec) launch<true, true>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, s);
-        else launch<true, false>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, s);
+        if (kfull) launch<true, true, true>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, s);
+        else if (pvec) launch<true, true, false>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, s);
+        else launch<true, false, false>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, s);
     } else {
-        if (pvec) launch<false, true>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, s);
-        else launch<false, false>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, s);
+        // the second product's K is k_pad, a multiple of 64
+        if (kfull) launch<false, true, true>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, s);
+        else if (pvec) launch<false, true, false>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, s);
+        else launch<false, false, false>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, s);
     }
     return static_cast<int>(hipGetLastError());
 }
