@@ -279,15 +279,29 @@ constexpr int DWGM = BM / (32 * DMF);
 constexpr int DWGN = kDWaves / DWGM;
 constexpr int DBN = 32 * DNF * DWGN;
 constexpr int kStages = DBF_PREFILL_STAGES;
-constexpr int kPBytes = BM * BK * 2;          // 16 KiB
-constexpr int kSBytes = DBN * 8;              // one word pair per sign row
-constexpr int kKBytes = BK * 2;               // sk of the step
-constexpr int kStageBytes = kPBytes + kSBytes + kKBytes;
-constexpr size_t kDmaLds = static_cast<size_t>(kStages) * kStageBytes;
-constexpr int kPI = BM * BK * 2 / 1024 / kDWaves;   // 1 KiB P loads per wave and step
-constexpr int kSI = DBN / 64 * 2 / kDWaves;          // 256-byte sign loads per wave and step
-static_assert(kPI * kDWaves * 1024 == kPBytes && kSI * kDWaves * 256 == kSBytes && kSI >= 1,
-              "loads of a step divide evenly over the waves");
+
+// Sizes of one pipeline step of KP word pairs (K = 64 * KP).
+template <int KP>
+struct DmaStep {
+    static constexpr int K = 64 * KP;
+    static constexpr int PBytes = BM * K * 2;             // P tile
+    static constexpr int SBytes = DBN * 8 * KP;           // KP word pairs per sign row
+    static constexpr int KBytes = K * 2;                  // sk of the step
+    static constexpr int StageBytes = PBytes + SBytes + KBytes;
+    static constexpr size_t Lds = static_cast<size_t>(kStages) * StageBytes;
+    static constexpr int Chunks = K / 8;                  // 16-byte chunks per P row
+    static constexpr int PI = PBytes / 1024 / kDWaves;    // 1 KiB P loads per wave
+    static constexpr int SIP = DBN / 64 * 2;              // 256-byte sign loads per word pair
+    static constexpr int SI = SIP * KP / kDWaves;         // 256-byte sign loads per wave
+    static_assert(PI * kDWaves * 1024 == PBytes && SI * kDWaves * 256 == SBytes && SI >= 1,
+                  "loads of a step divide evenly over the waves");
+    static_assert(Lds <= 160 * 1024, "LDS of a CU");
+};
+
+#ifndef DBF_PREFILL_PAIRS
+#define DBF_PREFILL_PAIRS 2
+#endif
+constexpr int kDmaPairs = DBF_PREFILL_PAIRS;  // word pairs per pipeline step where K allows
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -323,36 +337,43 @@ __device__ __forceinline__ void wait_step(int y) {
 // stage pointers are restrict-qualified: they never overlap, and the compiler
 // then does not hold the LDS reads of `src` back until the loads into `dst`
 // have landed (the kernel orders them itself with vmcnt and the barrier).
-template <bool HAS_SK, typename Issue>
+template <bool HAS_SK, int KP, int D, typename IssueOne>
 __device__ __forceinline__ void dma_step(bool go, int nxt, char *__restrict__ dst, const char *__restrict__ src,
-                                         Issue &issue, f32x16 (&acc)[DMF][DNF], int wm, int wn, int l32, int kg,
-                                         ExpandConsts ec) {
-    if (go) issue(nxt, dst);
-    const uint2 *sg = reinterpret_cast<const uint2 *>(src + kPBytes);
-    uint2 w[DNF];
+                                         IssueOne &issue_one, f32x16 (&acc)[DMF][DNF], int wm, int wn, int l32,
+                                         int kg, ExpandConsts ec) {
+    using C = DmaStep<KP>;
+    static_assert(D <= 4 * KP, "one load per sub-step");
+    const uint2 *sg = reinterpret_cast<const uint2 *>(src + C::PBytes);
+    const char *prow = src + (wm * 32 * DMF + l32) * (C::K * 2);
 #pragma unroll
-    for (int f = 0; f < DNF; ++f) w[f] = sg[wn * 32 * DNF + f * 32 + l32];
-    const char *prow = src + (wm * 32 * DMF + l32) * (BK * 2);
+    for (int j = 0; j < KP; ++j) {  // word pairs
+        uint2 w[DNF];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {  // K sub-steps of 16
+        for (int f = 0; f < DNF; ++f) w[f] = sg[j * DBN + wn * 32 * DNF + f * 32 + l32];
+#pragma unroll
+        for (int s = 4 * j; s < 4 * j + 4; ++s) {  // K sub-steps of 16
+        // the loads of step nxt go out one per sub-step, between the MFMAs,
+        // so that the memory pipeline works while the matrix cores do
+        if (go && s < D) issue_one(nxt, dst, s);
         const int pc = ((2 * s + kg) ^ (l32 & 7)) * 16;
         f16x8 af[DMF];
 #pragma unroll
-        for (int i = 0; i < DMF; ++i) af[i] = *reinterpret_cast<const f16x8 *>(prow + i * 32 * (BK * 2) + pc);
+        for (int i = 0; i < DMF; ++i) af[i] = *reinterpret_cast<const f16x8 *>(prow + i * 32 * (C::K * 2) + pc);
         u32x4 sc = {0u, 0u, 0u, 0u};
-        if (HAS_SK) sc = *reinterpret_cast<const u32x4 *>(src + kPBytes + kSBytes + (s * 8 + 4 * kg) * 4);
+        if (HAS_SK) sc = *reinterpret_cast<const u32x4 *>(src + C::PBytes + C::SBytes + (s * 8 + 4 * kg) * 4);
         const int g = 2 * (s & 1) + kg;
 #pragma unroll
         for (int f = 0; f < DNF; ++f) {
-            const f16x8 bf = expand<HAS_SK>(s < 2 ? w[f].x : w[f].y, g, sc, ec);
+            const f16x8 bf = expand<HAS_SK>((s & 3) < 2 ? w[f].x : w[f].y, g, sc, ec);
 #pragma unroll
             for (int i = 0; i < DMF; ++i)
                 acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf, acc[i][f], 0, 0, 0);
         }
+        }
     }
 }
 
-template <bool HAS_SK>
+template <bool HAS_SK, int KP>
 __global__ __launch_bounds__(kDThreads) void sign_gemm_dma_kernel(const __half *__restrict__ P, int ldp, int M,
                                                                  const uint32_t *__restrict__ S, int words,
                                                                  int n_rows_pad, const __half *__restrict__ sk,
@@ -360,7 +381,8 @@ __global__ __launch_bounds__(kDThreads) void sign_gemm_dma_kernel(const __half *
                                                                  __half *__restrict__ out, int ldo, int n_out,
                                                                  int nbm, int nbn) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    constexpr int D = kPI + kSI + (HAS_SK ? 1 : 0);  // loads per step and wave
+    using C = DmaStep<KP>;
+    constexpr int D = C::PI + C::SI + (HAS_SK ? 1 : 0);  // loads per step and wave
 
     const ExpandConsts ec = expand_consts();
     const int G = nbm * nbn;
@@ -374,32 +396,40 @@ __global__ __launch_bounds__(kDThreads) void sign_gemm_dma_kernel(const __half *
     const int wave = tid >> 6, lane = tid & 63;
     const int wm = wave / DWGN, wn = wave % DWGN;
     const int l32 = lane & 31, kg = lane >> 5;
-    const int nk = words >> 1;
+    const int nk = words / (2 * KP);
 
-    // per-lane source offsets of the step loads (the step adds 64 halves / one word pair)
-    const __half *psrc[kPI];
+    // per-lane source offsets of the step loads (a step adds K halves / KP word pairs)
+    const __half *psrc[C::PI];
 #pragma unroll
-    for (int qq = 0; qq < kPI; ++qq) {
-        const int c = (wave * kPI + qq) * 64 + lane;  // 16-byte chunk of the tile
-        const int r = c >> 3, pc = c & 7;
+    for (int qq = 0; qq < C::PI; ++qq) {
+        const int c = (wave * C::PI + qq) * 64 + lane;  // 16-byte chunk of the tile
+        const int r = c / C::Chunks, pc = c % C::Chunks;
         const int lc = pc ^ (r & 7);
         psrc[qq] = P + static_cast<size_t>(min(m0 + r, M - 1)) * ldp + lc * 8;
     }
-    const uint32_t *ssrc[kSI];
+    const uint32_t *ssrc[C::SI];
 #pragma unroll
-    for (int h = 0; h < kSI; ++h) {
-        const int ii = wave * kSI + h;                    // loads of 256 bytes: row tiles x 2 halves
-        const int t = min((n0 >> 6) + (ii >> 1), n_rows_pad / 64 - 1);  // tiles past the end: loaded, unused
-        ssrc[h] = S + static_cast<size_t>(t) * (words >> 1) * 128 + (ii & 1) * 64 + lane;
+    for (int h = 0; h < C::SI; ++h) {
+        const int ii = wave * C::SI + h;  // loads of 256 bytes: word pair x row tile x half
+        const int j = ii / C::SIP, rem = ii % C::SIP;
+        const int t = min((n0 >> 6) + (rem >> 1), n_rows_pad / 64 - 1);  // tiles past the end: loaded, unused
+        ssrc[h] = S + (static_cast<size_t>(t) * (words >> 1) + j) * 128 + (rem & 1) * 64 + lane;
     }
+    // load q (0 <= q < D) of this wave for step kt into stage st
+    auto issue_one = [&](int kt, char *st, int q) {
+        if (q < C::PI) {
+            dma16(psrc[q] + kt * C::K, st + (wave * C::PI + q) * 1024);
+        } else if (q < C::PI + C::SI) {
+            const int h = q - C::PI;
+            dma4(ssrc[h] + kt * KP * 128, st + C::PBytes + (wave * C::SI + h) * 256);
+        } else if (HAS_SK) {
+            // every wave: the same K * 2 bytes
+            if (lane < C::K / 2) dma4(sk + kt * C::K + 2 * lane, st + C::PBytes + C::SBytes);
+        }
+    };
     auto issue = [&](int kt, char *st) {
 #pragma unroll
-        for (int qq = 0; qq < kPI; ++qq) dma16(psrc[qq] + kt * BK, st + (wave * kPI + qq) * 1024);
-#pragma unroll
-        for (int h = 0; h < kSI; ++h) dma4(ssrc[h] + kt * 128, st + kPBytes + (wave * kSI + h) * 256);
-        if (HAS_SK) {
-            if (lane < 32) dma4(sk + kt * BK + 2 * lane, st + kPBytes + kSBytes);  // every wave: same 128 bytes
-        }
+        for (int q = 0; q < D; ++q) issue_one(kt, st, q);
     };
 
     f32x16 acc[DMF][DNF];
@@ -419,7 +449,7 @@ __global__ __launch_bounds__(kDThreads) void sign_gemm_dma_kernel(const __half *
 
 #pragma unroll
     for (int s0 = 0; s0 < kStages - 1; ++s0)
-        if (s0 < nk) issue(s0, lds + s0 * kStageBytes);
+        if (s0 < nk) issue(s0, lds + s0 * C::StageBytes);
 
     for (int kt = 0; kt < nk; ++kt) {
         // this wave's loads of step kt have landed; younger steps may be in flight
@@ -428,8 +458,8 @@ __global__ __launch_bounds__(kDThreads) void sign_gemm_dma_kernel(const __half *
         __builtin_amdgcn_s_barrier();  // ... and every other wave's; step kt - 1's buffer is free
         asm volatile("" ::: "memory");
         const int nxt = kt + kStages - 1;
-        dma_step<HAS_SK>(nxt < nk, nxt, lds + (nxt % kStages) * kStageBytes, lds + (kt % kStages) * kStageBytes, issue,
-                         acc, wm, wn, l32, kg, ec);
+        dma_step<HAS_SK, KP, D>(nxt < nk, nxt, lds + (nxt % kStages) * C::StageBytes,
+                                lds + (kt % kStages) * C::StageBytes, issue_one, acc, wm, wn, l32, kg, ec);
     }
 
 #pragma unroll
@@ -447,17 +477,18 @@ __global__ __launch_bounds__(kDThreads) void sign_gemm_dma_kernel(const __half *
     }
 }
 
-template <bool HAS_SK>
+template <bool HAS_SK, int KP>
 void launch_dma(const void *P, int ldp, int M, const uint32_t *S, int words, int n_rows_pad, const void *sk,
                 const void *sn, void *out, int ldo, int n_out, hipStream_t s) {
-    static const bool once = ((void)hipFuncSetAttribute(reinterpret_cast<const void *>(sign_gemm_dma_kernel<HAS_SK>),
-                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                        static_cast<int>(kDmaLds)),
-                              true);
+    using C = DmaStep<KP>;
+    static const bool once =
+        ((void)hipFuncSetAttribute(reinterpret_cast<const void *>(sign_gemm_dma_kernel<HAS_SK, KP>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(C::Lds)),
+         true);
     (void)once;
     const int nbm = (M + BM - 1) / BM;
     const int nbn = (n_out + DBN - 1) / DBN;
-    launch_kernel((sign_gemm_dma_kernel<HAS_SK>), dim3(nbm * nbn), dim3(kDThreads), kDmaLds, s,
+    launch_kernel((sign_gemm_dma_kernel<HAS_SK, KP>), dim3(nbm * nbn), dim3(kDThreads), C::Lds, s,
                   static_cast<const __half *>(P), ldp, M, S, words, n_rows_pad, static_cast<const __half *>(sk),
                   static_cast<const __half *>(sn), static_cast<__half *>(out), ldo, n_out, nbm, nbn);
 }
@@ -471,8 +502,22 @@ int launch_sign_gemm(const void *P, int ldp, int M, int K, const uint32_t *S, in
     const bool kfull = pvec && (K % BK) == 0;
 #ifndef DBF_PREFILL_NO_DMA
     if (kfull && (reinterpret_cast<uintptr_t>(P) & 15) == 0 && K == words * 32) {
-        if (sk) launch_dma<true>(P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, s);
-        else launch_dma<false>(P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, s);
+        // K steps of 128 where K allows and the tiles fit one wave of
+        // workgroups over the 256 CUs; else steps of 64, whose 74 KiB of LDS
+        // lets two workgroups share a CU (a partial last wave of tiles then
+        // runs beside the first instead of after it)
+        if constexpr (kDmaPairs == 2) {
+            const int tiles = ((M + BM - 1) / BM) * ((n_out + DBN - 1) / DBN);
+            if (words % 4 == 0 && tiles <= 256) {
+                if (sk) launch_dma<true, 2>(P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, s);
+                else launch_dma<false, 2>(P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, s);
+                return static_cast<int>(hipGetLastError());
+            }
+        }
+        {
+            if (sk) launch_dma<true, 1>(P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, s);
+            else launch_dma<false, 1>(P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, s);
+        }
         return static_cast<int>(hipGetLastError());
     }
 #endif
