@@ -52,7 +52,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--copy-probe-mb", type=int, default=0,
                    help="only run a plain device copy of this size (counter scaling) and exit")
-    p.add_argument("--only", choices=("decode", "prefill"), default=None,
+    p.add_argument("--no-block", action="store_true", help="skip the decoder-block measurement")
+    p.add_argument("--only", choices=("decode", "prefill", "block"), default=None,
                    help="run one leg only (for profiling)")
     p.add_argument("--decode-path", choices=("mfma", "table"), default="mfma",
                    help="decode kernels: matrix cores (default) or vector-ALU lookup tables")
@@ -180,6 +181,60 @@ def cpu_baseline(layer, seconds):
                       f"(W rebuilt each call) in {el:.1f} s"}
 
 
+def block_leg(args):
+    """The seven linears of a Llama-3-8B-shaped decoder block (q, k, v, o,
+    gate, up, down; per-layer k) at batch 1, one after another on one stream,
+    over enough copies of the block to stream from HBM: each layer on its own,
+    and with the layers that share an input (q, k, v; gate, up) grouped into
+    one pair of launches."""
+    import torch
+
+    import dbf_linear_fwd_amd as dbf
+    from tests import inputs
+
+    layers = inputs.config(5).layers
+    by = {L.name: L for L in layers}
+    block_bytes = sum(L.sign_bytes + L.scale_bytes for L in layers)
+    R = max(1, -(-args.rotate_mb * (1 << 20) // block_bytes))
+    print(f"[bench] block: 7 layers, {block_bytes / 2**20:.1f} MiB per block, {R} copies", file=sys.stderr, flush=True)
+    copies = [{L.name: dbf.Layer(L.A, L.B, L.a, L.mid, L.b, max_batch=1) for L in layers} for _ in range(R)]
+    xs = {L.name: torch.from_numpy(L.X[1]).cuda() for L in layers}
+    ys = {L.name: torch.empty((1, L.n), dtype=torch.float16, device="cuda") for L in layers}
+    order = ["q", "k", "v", "o", "gate", "up", "down"]
+    groups = [["q", "k", "v"], ["o"], ["gate", "up"], ["down"]]
+
+    def per_layer(i):
+        c = copies[i % R]
+        for name in order:
+            c[name].forward(xs[name], out=ys[name])
+    per_layer.period = R
+
+    def grouped(i):
+        c = copies[i % R]
+        for gr in groups:
+            if len(gr) == 1:
+                c[gr[0]].forward(xs[gr[0]], out=ys[gr[0]])
+            else:
+                dbf.forward_group([c[name] for name in gr], xs[gr[0]], [ys[name] for name in gr])
+    grouped.period = R
+
+    steps = max(R, min(args.steps // 7, 20 * R))
+    res = {"workload": "Llama-3-8B-shaped decoder block of 7 DBF linears (q 4096x4096, k/v 1024x4096, o 4096x4096, "
+                       "gate/up 14336x4096, down 4096x14336), k per layer from 1.0-2.3 bits/weight, batch 1",
+           "block_bytes": block_bytes, "copies": R}
+    for name, fn in (("per_layer", per_layer), ("grouped", grouped)):
+        el, done = time_steps(fn, steps, min(args.warmup, 2 * R), args.mode)
+        res[name] = {"us_per_block": el * 1e6 / done, "gbs": block_bytes * done / el / 1e9,
+                     "launches_per_block": 14 if name == "per_layer" else 8}
+        print(f"[bench] block {name}: {res[name]['us_per_block']:.1f} us per block, {res[name]['gbs']:.1f} GB/s",
+              file=sys.stderr, flush=True)
+    for c in copies:
+        for H in c.values():
+            H.close()
+    torch.cuda.synchronize()
+    return res
+
+
 def copy_probe(mb):
     import torch
     n = mb * (1 << 20) // 4
@@ -281,6 +336,10 @@ def main():
         }
         L.close()
 
+    # ---------------------------------------------------------------- decoder block, batch 1 (secondary)
+    if args.only in (None, "block") and not args.no_block:
+        result["block"] = block_leg(args)
+
     if args.only is not None:
         print(json.dumps({k: {kk: vv for kk, vv in v.items() if kk not in ("layer", "copies")}
                           for k, v in result.items()}, default=str))
@@ -316,6 +375,8 @@ def main():
     }
     if "prefill" in result:
         line["prefill_batch2048"] = result["prefill"]
+    if "block" in result:
+        line["decode_block_b1"] = result["block"]
     print(json.dumps(line))
 
 

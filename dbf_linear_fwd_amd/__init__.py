@@ -27,7 +27,7 @@ __all__ = [
     "DbfError", "lib", "library_path",
     "dbf_pack", "dbf_linear_forward", "dbf_linear_forward_ex", "dbf_free", "dbf_get_info",
     "dbf_status_string", "dbf_pack_signs", "dbf_layout_signs", "dbf_layout_words",
-    "dbf_timing_enable", "dbf_timing_read", "Layer",
+    "dbf_timing_enable", "dbf_timing_read", "Layer", "dbf_linear_forward_group", "forward_group",
 ]
 
 DBF_OK = 0
@@ -45,8 +45,8 @@ DBF_PATH_DECODE_TABLE = 3
 DECODE_MAX_BATCH = 16
 
 EXPORTED_SYMBOLS = (
-    "dbf_pack", "dbf_linear_forward", "dbf_linear_forward_ex", "dbf_free", "dbf_get_info",
-    "dbf_status_string", "dbf_pack_signs", "dbf_layout_signs", "dbf_layout_words",
+    "dbf_pack", "dbf_linear_forward", "dbf_linear_forward_ex", "dbf_linear_forward_group", "dbf_free",
+    "dbf_get_info", "dbf_status_string", "dbf_pack_signs", "dbf_layout_signs", "dbf_layout_words",
     "dbf_timing_enable", "dbf_timing_read",
 )
 
@@ -96,6 +96,8 @@ def lib() -> ctypes.CDLL:
     L.dbf_linear_forward.restype = ctypes.c_int
     L.dbf_linear_forward_ex.argtypes = [vp, vp, vp, i32, i32, vp]
     L.dbf_linear_forward_ex.restype = ctypes.c_int
+    L.dbf_linear_forward_group.argtypes = [ctypes.POINTER(vp), i32, vp, ctypes.POINTER(vp), i32, vp]
+    L.dbf_linear_forward_group.restype = ctypes.c_int
     L.dbf_free.argtypes = [vp]
     L.dbf_free.restype = None
     L.dbf_get_info.argtypes = [vp, ctypes.POINTER(_Info)]
@@ -162,6 +164,34 @@ def dbf_linear_forward(h: int, x_ptr: int, y_ptr: int, batch: int, stream: int =
 
 def dbf_linear_forward_ex(h: int, x_ptr: int, y_ptr: int, batch: int, path: int, stream: int = 0) -> None:
     _check(lib().dbf_linear_forward_ex(h, x_ptr, y_ptr, batch, path, stream), "dbf_linear_forward_ex")
+
+
+def dbf_linear_forward_group(hs, x_ptr: int, y_ptrs, batch: int, stream: int = 0) -> None:
+    """Forwards of several layers that share the input x (device pointers)."""
+    hs = list(hs)
+    y_ptrs = list(y_ptrs)
+    if len(hs) != len(y_ptrs):
+        raise ValueError("one output per handle")
+    harr = (ctypes.c_void_p * max(len(hs), 1))(*hs)
+    yarr = (ctypes.c_void_p * max(len(y_ptrs), 1))(*y_ptrs)
+    _check(lib().dbf_linear_forward_group(harr, len(hs), x_ptr, yarr, batch, stream), "dbf_linear_forward_group")
+
+
+def forward_group(layers, x, outs=None):
+    """ys[i] = layers[i](x) for Layer objects sharing the input width; one
+    pair of launches for all of them at decode batch sizes."""
+    import torch
+    if x.dtype != torch.float16 or not x.is_cuda or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 2-D float16 CUDA tensor")
+    if outs is None:
+        outs = [torch.empty((x.shape[0], L.n), dtype=torch.float16, device=x.device) for L in layers]
+    for L, y in zip(layers, outs):
+        if y.dtype != torch.float16 or not y.is_cuda or tuple(y.shape) != (x.shape[0], L.n) or not y.is_contiguous():
+            raise ValueError("outs[i] must be a contiguous float16 CUDA tensor of shape (batch, n_i)")
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    dbf_linear_forward_group([L.handle for L in layers], x.data_ptr(), [y.data_ptr() for y in outs], x.shape[0],
+                             stream)
+    return outs
 
 
 def dbf_free(h: Optional[int]) -> None:

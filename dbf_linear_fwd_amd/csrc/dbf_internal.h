@@ -67,6 +67,24 @@ struct MfmaDecodeArgs {
 // which = 1: stage 1 (writes v16); which = 2: stage 2 (writes y).
 int launch_mfma_decode(const MfmaDecodeArgs &d, void *stream, int which);
 
+// Layers that read the same input, decoded together: one launch per stage
+// for all of them (workgroups map to (layer, row block)).
+constexpr int kMaxGroup = 8;
+struct MfmaGroupLayer {
+    const uint32_t *A_dev, *B_dev;
+    const void *a_dev, *mid_dev, *b_dev;
+    void *y;
+    uint16_t *v16;
+    int n, n_pad, k_pad;
+};
+struct MfmaGroupArgs {
+    MfmaGroupLayer L[kMaxGroup];
+    int count;
+    const void *x;
+    int batch, m, m_pad;
+};
+int launch_mfma_decode_group(const MfmaGroupArgs &g, void *stream, int which);
+
 // Words per lookup-table chunk allowed by the LDS budget for `nb` batch rows.
 int lut_max_chunk_words(int nb);
 // Lookup-table decode (batch 1..4): stage 1 writes chunk partials of t;

@@ -428,6 +428,57 @@ __global__ __launch_bounds__(kThreads) void mfma_stage2_kernel(const uint32_t *_
     stage2_body<NB, RT>(blockIdx.x, reinterpret_cast<char *>(lds), At, Wk, v16, k_pad, a, y, n, PR);
 }
 
+// Grouped form: one launch runs a stage for several layers that share the
+// input.  Workgroup b belongs to the last layer whose first block blk0 <= b.
+struct GroupStage1Layer {
+    const uint32_t *Bt;
+    const __half *b, *mid;
+    __half *v16;
+    int k_pad, blk0;
+};
+struct GroupStage1Args {
+    GroupStage1Layer L[kMaxGroup];
+    int count;
+    const __half *x;
+    int m, Wm, PR;
+};
+struct GroupStage2Layer {
+    const uint32_t *At;
+    const __half *v16, *a;
+    __half *y;
+    int Wk, k_pad, n, PR, blk0;
+};
+struct GroupStage2Args {
+    GroupStage2Layer L[kMaxGroup];
+    int count;
+};
+
+template <typename A>
+__device__ __forceinline__ int group_layer(const A &g) {
+    int l = 0;
+    for (int i = 1; i < g.count; ++i)
+        if (static_cast<int>(blockIdx.x) >= g.L[i].blk0) l = i;
+    return l;
+}
+
+template <int NB, int RT>
+__global__ __launch_bounds__(kThreads) void mfma_group_stage1_kernel(const GroupStage1Args g) {
+    extern __shared__ float lds[];
+    const int l = group_layer(g);
+    const GroupStage1Layer &L = g.L[l];
+    stage1_body<NB, RT>(blockIdx.x - L.blk0, reinterpret_cast<char *>(lds), L.Bt, g.Wm, g.x, g.m, L.b, L.mid, L.v16,
+                        L.k_pad, g.PR);
+}
+
+template <int NB, int RT>
+__global__ __launch_bounds__(kThreads) void mfma_group_stage2_kernel(const GroupStage2Args g) {
+    extern __shared__ float lds[];
+    const int l = group_layer(g);
+    const GroupStage2Layer &L = g.L[l];
+    stage2_body<NB, RT>(blockIdx.x - L.blk0, reinterpret_cast<char *>(lds), L.At, L.Wk, L.v16, L.k_pad, L.a, L.y, L.n,
+                        L.PR);
+}
+
 template <typename K>
 void allow_lds(K kernel, size_t bytes) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -479,6 +530,57 @@ int launch_nb(const MfmaDecodeArgs &d, hipStream_t s, int which) {
     return launch_rt<NB, 1>(d, s, which);
 }
 
+template <int NB, int RT>
+int launch_group_rt(const MfmaGroupArgs &g, hipStream_t s, int which) {
+    if (which == 1) {
+        static const bool once = (allow_lds(mfma_group_stage1_kernel<NB, RT>, kLdsBudget), true);
+        (void)once;
+        GroupStage1Args a{};
+        a.count = g.count;
+        a.x = static_cast<const __half *>(g.x);
+        a.m = g.m;
+        a.Wm = g.m_pad / 32;
+        a.PR = std::min(g.m_pad / 64, round_pairs<NB, RT>());
+        int blocks = 0;
+        for (int i = 0; i < g.count; ++i) {
+            const MfmaGroupLayer &L = g.L[i];
+            a.L[i] = {L.B_dev, static_cast<const __half *>(L.b_dev), static_cast<const __half *>(L.mid_dev),
+                      reinterpret_cast<__half *>(L.v16), L.k_pad, blocks};
+            blocks += L.k_pad / (16 * RT);
+        }
+        launch_kernel((mfma_group_stage1_kernel<NB, RT>), dim3(blocks), dim3(kThreads), lds_bytes<NB, RT>(a.PR), s, a);
+    } else {
+        static const bool once = (allow_lds(mfma_group_stage2_kernel<NB, RT>, kLdsBudget), true);
+        (void)once;
+        GroupStage2Args a{};
+        a.count = g.count;
+        int blocks = 0;
+        size_t lds = 0;
+        for (int i = 0; i < g.count; ++i) {
+            const MfmaGroupLayer &L = g.L[i];
+            const int PR = std::min(L.k_pad / 64, round_pairs<NB, RT>());
+            a.L[i] = {L.A_dev, reinterpret_cast<const __half *>(L.v16), static_cast<const __half *>(L.a_dev),
+                      static_cast<__half *>(L.y), L.k_pad / 32, L.k_pad, L.n, PR, blocks};
+            blocks += L.n_pad / (16 * RT);
+            lds = std::max(lds, lds_bytes<NB, RT>(PR));
+        }
+        launch_kernel((mfma_group_stage2_kernel<NB, RT>), dim3(blocks), dim3(kThreads), lds, s, a);
+    }
+    return static_cast<int>(hipGetLastError());
+}
+
+template <int NB>
+int launch_group_nb(const MfmaGroupArgs &g, hipStream_t s, int which) {
+    int rows = 0;
+    for (int i = 0; i < g.count; ++i) rows += which == 1 ? g.L[i].k_pad : g.L[i].n_pad;
+    const int rt = split_rt<NB>(rows);
+    if constexpr (NB <= 4) {
+        if (rt == 2) return launch_group_rt<NB, 2>(g, s, which);
+        if (rt == 4) return launch_group_rt<NB, 4>(g, s, which);
+    }
+    return launch_group_rt<NB, 1>(g, s, which);
+}
+
 }  // namespace
 
 int launch_mfma_decode(const MfmaDecodeArgs &d, void *stream, int which) {
@@ -500,6 +602,30 @@ int launch_mfma_decode(const MfmaDecodeArgs &d, void *stream, int which) {
         case 14: return launch_nb<14>(d, s, which);
         case 15: return launch_nb<15>(d, s, which);
         case 16: return launch_nb<16>(d, s, which);
+        default: return static_cast<int>(hipErrorInvalidValue);
+    }
+}
+
+int launch_mfma_decode_group(const MfmaGroupArgs &g, void *stream, int which) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (g.count < 1 || g.count > kMaxGroup) return static_cast<int>(hipErrorInvalidValue);
+    switch (g.batch) {
+        case 1: return launch_group_nb<1>(g, s, which);
+        case 2: return launch_group_nb<2>(g, s, which);
+        case 3: return launch_group_nb<3>(g, s, which);
+        case 4: return launch_group_nb<4>(g, s, which);
+        case 5: return launch_group_nb<5>(g, s, which);
+        case 6: return launch_group_nb<6>(g, s, which);
+        case 7: return launch_group_nb<7>(g, s, which);
+        case 8: return launch_group_nb<8>(g, s, which);
+        case 9: return launch_group_nb<9>(g, s, which);
+        case 10: return launch_group_nb<10>(g, s, which);
+        case 11: return launch_group_nb<11>(g, s, which);
+        case 12: return launch_group_nb<12>(g, s, which);
+        case 13: return launch_group_nb<13>(g, s, which);
+        case 14: return launch_group_nb<14>(g, s, which);
+        case 15: return launch_group_nb<15>(g, s, which);
+        case 16: return launch_group_nb<16>(g, s, which);
         default: return static_cast<int>(hipErrorInvalidValue);
     }
 }

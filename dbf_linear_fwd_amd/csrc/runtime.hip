@@ -419,6 +419,45 @@ extern "C" dbf_status_t dbf_linear_forward_ex(dbf_handle_t h, const void *x, voi
     return decode ? forward_decode_mfma(h, x, y, batch, stream) : forward_prefill(h, x, y, batch, stream);
 }
 
+extern "C" dbf_status_t dbf_linear_forward_group(const dbf_handle_t *hs, int32_t count, const void *x, void *const *ys,
+                                                 int32_t batch, hipStream_t stream) {
+    if (!hs || !ys || count < 1 || count > dbf::kMaxGroup || batch < 0) return DBF_ERR_INVALID_ARG;
+    for (int i = 0; i < count; ++i) {
+        if (!hs[i]) return DBF_ERR_INVALID_ARG;
+        if (hs[i]->m != hs[0]->m || hs[i]->device != hs[0]->device || batch > hs[i]->max_batch)
+            return DBF_ERR_INVALID_ARG;
+    }
+    if (batch == 0) return DBF_OK;
+    if (!x || !aligned16(x)) return DBF_ERR_INVALID_ARG;
+    for (int i = 0; i < count; ++i)
+        if (!ys[i] || !aligned16(ys[i])) return DBF_ERR_INVALID_ARG;
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return DBF_ERR_HIP;
+    if (cur != hs[0]->device) return DBF_ERR_INVALID_ARG;
+    if (batch > dbf::kDecodeMaxBatch) {
+        for (int i = 0; i < count; ++i) {
+            const dbf_status_t st = forward_prefill(hs[i], x, ys[i], batch, stream);
+            if (st != DBF_OK) return st;
+        }
+        return DBF_OK;
+    }
+    dbf::MfmaGroupArgs g{};
+    g.count = count;
+    g.x = x;
+    g.batch = batch;
+    g.m = hs[0]->m;
+    g.m_pad = hs[0]->m_pad;
+    for (int i = 0; i < count; ++i) {
+        const dbf_layer *h = hs[i];
+        g.L[i] = {h->A_dev, h->B_dev, h->a_dev, h->mid_dev, h->b_dev, ys[i], h->v16, h->n, h->n_pad, h->k_pad};
+    }
+    dbf_layer *t = hs[0];  // kernel timing follows the first handle
+    dbf_status_t st =
+        timed_launch(t, "decode_group_stage1", stream, [&] { return dbf::launch_mfma_decode_group(g, stream, 1); });
+    if (st != DBF_OK) return st;
+    return timed_launch(t, "decode_group_stage2", stream, [&] { return dbf::launch_mfma_decode_group(g, stream, 2); });
+}
+
 extern "C" dbf_status_t dbf_linear_forward(dbf_handle_t h, const void *x, void *y, int32_t batch,
                                            hipStream_t stream) {
     return dbf_linear_forward_ex(h, x, y, batch, DBF_PATH_AUTO, stream);

@@ -131,6 +131,29 @@ dbf_status_t dbf_linear_forward(dbf_handle_t h, const void *x, void *y, int32_t 
 dbf_status_t dbf_linear_forward_ex(dbf_handle_t h, const void *x, void *y, int32_t batch,
                                    int32_t path, hipStream_t stream);
 
+/*
+ * dbf_linear_forward_group -- the forwards of several layers that read the
+ * same input (for example the q, k and v projections of an attention block,
+ * or the gate and up projections of an MLP, gist.science technical summary
+ * §4 runs DBF on every linear layer of such blocks): ys[i] = x W_i^T for
+ * i < count, each exactly as dbf_linear_forward(hs[i], x, ys[i], batch, ...)
+ * computes it (the same kernels' arithmetic, identical bits).
+ *   hs     count handles (1 <= count <= 8), all with the same input width m,
+ *          all on the current device.
+ *   x      device fp16, batch x m (shared by all layers, 16-byte aligned).
+ *   ys     count device fp16 outputs, ys[i] batch x n_i, 16-byte aligned,
+ *          overlapping neither x nor each other.
+ *   batch  0 <= batch <= every handle's max_batch; 0 returns DBF_OK.
+ * For batch <= 16 all layers share one launch per stage (2 launches in all
+ * instead of 2 per layer); larger batches run each layer's forward in turn.
+ * The handles' workspaces are used: calls involving one handle must be
+ * ordered.  Errors: DBF_ERR_INVALID_ARG (count out of range, null pointers,
+ * differing m, batch out of range, misaligned pointers, wrong device),
+ * DBF_ERR_HIP (launch failure).
+ */
+dbf_status_t dbf_linear_forward_group(const dbf_handle_t *hs, int32_t count, const void *x, void *const *ys,
+                                      int32_t batch, hipStream_t stream);
+
 /* dbf_free -- release the handle and its device memory.  NULL is a no-op.
  * Synchronises the handle's device first, so pending work on it finishes. */
 void dbf_free(dbf_handle_t h);

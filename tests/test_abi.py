@@ -127,3 +127,17 @@ def test_pack_without_gpu_reports_hip_error():
     with pytest.raises(dbf.DbfError) as e:
         dbf.dbf_pack(n, m, k, A, B, a, mid, b, 4)
     assert e.value.status == dbf.DBF_ERR_HIP
+
+
+def test_group_entry_validates_before_any_device_call():
+    """Argument errors of dbf_linear_forward_group are reported without a GPU."""
+    import ctypes
+    L = dbf.lib()
+    vp = ctypes.c_void_p
+    null_hs = ctypes.POINTER(vp)()
+    assert L.dbf_linear_forward_group(null_hs, 1, None, null_hs, 1, None) == dbf.DBF_ERR_INVALID_ARG
+    hs = (vp * 1)(None)
+    ys = (vp * 1)(None)
+    assert L.dbf_linear_forward_group(hs, 0, None, ys, 1, None) == dbf.DBF_ERR_INVALID_ARG   # count 0
+    assert L.dbf_linear_forward_group(hs, 9, None, ys, 1, None) == dbf.DBF_ERR_INVALID_ARG   # count > 8
+    assert L.dbf_linear_forward_group(hs, 1, None, ys, 1, None) == dbf.DBF_ERR_INVALID_ARG   # null handle

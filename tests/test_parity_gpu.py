@@ -385,3 +385,93 @@ def test_timing_facility(gpu):
         assert dbf.dbf_timing_read(H.handle) == {}
     finally:
         H.close()
+
+
+# --------------------------------------------------------------------------- layers sharing one input
+
+GROUPS = [
+    # (m, [(n, k), ...])
+    (300, [(64, 64), (130, 190), (70, 33)]),
+    (1100, [(257, 100), (64, 1500)]),
+    (96, [(64, 64)]),
+    (4096, [(4096, 2688), (1024, 1216), (1024, 1536)]),   # attention q/k/v shapes
+]
+
+
+@pytest.mark.parametrize("gi", range(len(GROUPS)))
+@pytest.mark.parametrize("batch", [1, 3, 9, 16, 40])
+def test_group_forward_equals_single_layers(gpu, gi, batch):
+    """One launch per stage for layers sharing x gives each layer's own
+    forward bit for bit (same kernel arithmetic), and the oracle's values."""
+    torch = _torch()
+    m, dims = GROUPS[gi]
+    if m >= 4096 and batch not in (1, 9, 40):
+        pytest.skip("large group: batches 1, 9 and 40 only")
+    _say(f"group m={m} layers={dims} batch={batch}")
+    rng = np.random.default_rng(100 + gi)
+    big = m >= 4096
+    # the attention-shaped group takes the block workload's value ranges
+    X = (rng.standard_normal((batch, m)) if big else rng.uniform(-4, 4, size=(batch, m))).astype(np.float16)
+    layers, hs = [], []
+    try:
+        for j, (n, k) in enumerate(dims):
+            if big:
+                Lr = inputs.random_layer("g", n, m, k, 7000 + 10 * gi + j, 0.02, 1.0, 0.02, ())
+                A, B, a, mid, b = Lr.A, Lr.B, Lr.a, Lr.mid, Lr.b
+            else:
+                _, A, B, a, mid, b = inputs.tiny_case(7000 + 10 * gi + j, n, m, k, 1, signed_scales=True)
+            layers.append((A, B, a, mid, b))
+            hs.append(dbf.Layer(A, B, a, mid, b, max_batch=batch))
+        x = torch.from_numpy(X).cuda()
+        ys = dbf.forward_group(hs, x)
+        torch.cuda.synchronize()
+        for j, (H, y) in enumerate(zip(hs, ys)):
+            single = H.forward(x).cpu().numpy()
+            got = y.cpu().numpy()
+            assert np.array_equal(got.view(np.uint16), single.view(np.uint16)), f"layer {j}"
+            A, B, a, mid, b = layers[j]
+            if A.shape[0] * m * A.shape[1] <= 1 << 26:
+                assert_tol(got, O.dense_forward(X, A, B, a, mid, b), f"group layer {j}")
+            else:
+                rows = np.arange(min(batch, 3))
+                ref = O.sampled_forward(X, A, B, a, mid, b, rows, np.arange(A.shape[0]))
+                assert_tol(got[rows], ref, f"group layer {j} (sampled rows)")
+    finally:
+        for H in hs:
+            H.close()
+
+
+def test_group_forward_errors(gpu):
+    torch = _torch()
+    L1 = inputs.random_layer("g1", 64, 96, 32, 3, 0.05, 1.0, 0.05, (4,))
+    L2 = inputs.random_layer("g2", 80, 96, 64, 4, 0.05, 1.0, 0.05, (4,))
+    L3 = inputs.random_layer("g3", 64, 128, 32, 5, 0.05, 1.0, 0.05, (4,))
+    H1 = dbf.Layer(L1.A, L1.B, L1.a, L1.mid, L1.b, max_batch=4)
+    H2 = dbf.Layer(L2.A, L2.B, L2.a, L2.mid, L2.b, max_batch=2)
+    H3 = dbf.Layer(L3.A, L3.B, L3.a, L3.mid, L3.b, max_batch=4)
+    try:
+        _say("group errors")
+        x = torch.from_numpy(L1.X[4]).cuda()
+        y1 = torch.empty((4, 64), dtype=torch.float16, device="cuda")
+        y2 = torch.empty((4, 80), dtype=torch.float16, device="cuda")
+        with pytest.raises(dbf.DbfError):   # differing input widths
+            dbf.dbf_linear_forward_group([H1.handle, H3.handle], x.data_ptr(), [y1.data_ptr(), y2.data_ptr()], 4)
+        with pytest.raises(dbf.DbfError):   # batch above one handle's max_batch
+            dbf.dbf_linear_forward_group([H1.handle, H2.handle], x.data_ptr(), [y1.data_ptr(), y2.data_ptr()], 4)
+        with pytest.raises(dbf.DbfError):   # empty group
+            dbf.dbf_linear_forward_group([], x.data_ptr(), [], 4)
+        with pytest.raises(dbf.DbfError):   # more than 8 layers
+            dbf.dbf_linear_forward_group([H1.handle] * 9, x.data_ptr(), [y1.data_ptr()] * 9, 4)
+        with pytest.raises(dbf.DbfError):   # misaligned output
+            dbf.dbf_linear_forward_group([H1.handle], x.data_ptr(), [y1.data_ptr() + 2], 4)
+        with pytest.raises(dbf.DbfError):   # null output
+            dbf.dbf_linear_forward_group([H1.handle], x.data_ptr(), [0], 4)
+        dbf.dbf_linear_forward_group([H1.handle, H2.handle], 0, [0, 0], 0)   # batch 0: no launch
+        # batch 2 is within both max_batch values
+        dbf.dbf_linear_forward_group([H1.handle, H2.handle], x.data_ptr(), [y1.data_ptr(), y2.data_ptr()], 2)
+        torch.cuda.synchronize()
+        assert_tol(y1[:2].cpu().numpy(), O.dense_forward(L1.X[4][:2], L1.A, L1.B, L1.a, L1.mid, L1.b), "group b2")
+    finally:
+        H1.close()
+        H2.close()
+        H3.close()
