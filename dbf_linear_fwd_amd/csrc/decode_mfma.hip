@@ -52,6 +52,13 @@ constexpr int kMaxAct = 4;                  // activation items (8 elements) per
 #define DBF_DECODE_ONE_ROUND 256
 #endif
 constexpr size_t kLdsBudget = DBF_DECODE_LDS_KB * 1024;   // LDS of one workgroup (of 160 KiB per CU)
+#ifndef DBF_DECODE_READAHEAD
+#define DBF_DECODE_READAHEAD 1
+#endif
+constexpr bool kReadahead = DBF_DECODE_READAHEAD != 0;
+constexpr int kCUs = 256;                   // MI355X
+constexpr int kReadaheadBatch = 8;          // read-ahead loads in flight per thread
+constexpr int kReadaheadMax = 16;           // read-ahead only if it needs at most this many loads per thread
 constexpr uint32_t kSignPair = 0x80008000u;
 constexpr uint32_t kOnePair = 0x3C003C00u;  // two fp16 +1.0
 
@@ -409,13 +416,63 @@ __device__ __forceinline__ void stage2_body(int blk, char *base, const uint32_t 
     }
 }
 
+// Read-ahead of the stage-2 sign words.  Stage 1 of a layer at decode sizes
+// leaves CUs idle (k / 16 row blocks); extra workgroups of the stage-1
+// launch read the words stage 2 will read, so that stage 2 finds them in a
+// cache instead of HBM.  Workgroups are dispatched round-robin over the 8
+// XCDs, so read-ahead workgroup number g (XCD g mod 8) reads the rows of the
+// stage-2 workgroups on that same XCD, whose L2 then holds them; the
+// Infinity Cache, shared by all XCDs, holds them too.
+struct Stage2Readahead {
+    const uint4 *A;    // tiled sign words of A, as 16-byte items
+    int pairs;         // word pairs per row
+    int rows_per_wg;   // rows of one stage-2 workgroup (16 * RT)
+    int groups;        // stage-2 workgroups
+    int per_xcd;       // read-ahead workgroups per XCD
+};
+
+__device__ __forceinline__ void readahead_stage2(const Stage2Readahead &ra, int g /* launch-wide block index */,
+                                                 int q /* index among this XCD's read-ahead blocks */) {
+    const int xcd = g & 7;
+    const int half = ra.rows_per_wg >> 1;  // 16-byte items per word pair of one workgroup
+    const int per_wg = ra.pairs * half;
+    const int nwg = (ra.groups - xcd + 7) >> 3;  // stage-2 workgroups b with b mod 8 == xcd
+    const int total = nwg * per_wg;
+    if (total == 0) return;
+    const int stride = ra.per_xcd * kThreads;
+    uint32_t acc = 0;
+    // batches of kReadaheadBatch loads in flight; indexes past the end are
+    // clamped to the last item (straight-line code, no waits between loads)
+    for (int i0 = q * kThreads + static_cast<int>(threadIdx.x); i0 < total; i0 += kReadaheadBatch * stride) {
+        uint4 v[kReadaheadBatch];
+#pragma unroll
+        for (int u = 0; u < kReadaheadBatch; ++u) {
+            const int i = min(i0 + u * stride, total - 1);
+            const int j = i / per_wg, rem = i - j * per_wg;
+            const int row0 = (xcd + 8 * j) * ra.rows_per_wg;
+            const int pr = rem / half, e = rem - pr * half;
+            v[u] = ra.A[((static_cast<size_t>(row0 >> 6) * ra.pairs + pr) * 64 + (row0 & 63)) / 2 + e];
+        }
+#pragma unroll
+        for (int u = 0; u < kReadaheadBatch; ++u) acc ^= v[u].x ^ v[u].w;
+    }
+    asm volatile("" ::"v"(acc));  // the loads are the point: keep them
+}
+
+// Stage 1; workgroups past the k / (16 RT) row blocks read ahead for stage 2.
 template <int NB, int RT>
 __global__ __launch_bounds__(kThreads) void mfma_stage1_kernel(const uint32_t *__restrict__ Bt, int Wm,
                                                                const __half *__restrict__ x, int m,
                                                                const __half *__restrict__ b,
                                                                const __half *__restrict__ mid,
-                                                               __half *__restrict__ v16, int k_pad, int PR) {
+                                                               __half *__restrict__ v16, int k_pad, int PR,
+                                                               const Stage2Readahead ra) {
     extern __shared__ float lds[];
+    const int G1 = k_pad / (16 * RT);
+    if (static_cast<int>(blockIdx.x) >= G1) {
+        readahead_stage2(ra, blockIdx.x, (blockIdx.x - G1) >> 3);
+        return;
+    }
     stage1_body<NB, RT>(blockIdx.x, reinterpret_cast<char *>(lds), Bt, Wm, x, m, b, mid, v16, k_pad, PR);
 }
 
@@ -485,28 +542,6 @@ void allow_lds(K kernel, size_t bytes) {
                               static_cast<int>(bytes));
 }
 
-template <int NB, int RT>
-int launch_rt(const MfmaDecodeArgs &d, hipStream_t s, int which) {
-    if (which == 1) {
-        static const bool once = (allow_lds(mfma_stage1_kernel<NB, RT>, kLdsBudget), true);
-        (void)once;
-        const int PR = std::min(d.m_pad / 64, round_pairs<NB, RT>());
-        const size_t lds = lds_bytes<NB, RT>(PR);
-        launch_kernel((mfma_stage1_kernel<NB, RT>), dim3(d.k_pad / (16 * RT)), dim3(kThreads), lds, s, d.B_dev,
-                      d.m_pad / 32, static_cast<const __half *>(d.x), d.m, static_cast<const __half *>(d.b_dev),
-                      static_cast<const __half *>(d.mid_dev), reinterpret_cast<__half *>(d.v16), d.k_pad, PR);
-    } else {
-        static const bool once = (allow_lds(mfma_stage2_kernel<NB, RT>, kLdsBudget), true);
-        (void)once;
-        const int PR = std::min(d.k_pad / 64, round_pairs<NB, RT>());
-        const size_t lds = lds_bytes<NB, RT>(PR);
-        launch_kernel((mfma_stage2_kernel<NB, RT>), dim3(d.n_pad / (16 * RT)), dim3(kThreads), lds, s, d.A_dev,
-                      d.k_pad / 32, reinterpret_cast<const __half *>(d.v16), d.k_pad,
-                      static_cast<const __half *>(d.a_dev), static_cast<__half *>(d.y), d.n, PR);
-    }
-    return static_cast<int>(hipGetLastError());
-}
-
 // Rows per workgroup: 16, 32 or 64, the smallest that keeps the grid within
 // one workgroup per CU of the 256-CU MI355X (batch <= 4; larger use 16).
 template <int NB>
@@ -518,6 +553,43 @@ int split_rt(int rows) {
     } else {
         return 1;
     }
+}
+
+template <int NB, int RT>
+int launch_rt(const MfmaDecodeArgs &d, hipStream_t s, int which) {
+    if (which == 1) {
+        static const bool once = (allow_lds(mfma_stage1_kernel<NB, RT>, kLdsBudget), true);
+        (void)once;
+        const int PR = std::min(d.m_pad / 64, round_pairs<NB, RT>());
+        const size_t lds = lds_bytes<NB, RT>(PR);
+        const int G1 = d.k_pad / (16 * RT);
+        Stage2Readahead ra{};
+        ra.A = reinterpret_cast<const uint4 *>(d.A_dev);
+        ra.pairs = d.k_pad / 64;
+        const int rt2 = split_rt<NB>(d.n_pad);
+        ra.rows_per_wg = 16 * rt2;
+        ra.groups = d.n_pad / (16 * rt2);
+        // the read-ahead blocks take the CUs stage 1 leaves free, if there are
+        // enough of them to read stage 2's words in a few batches
+        ra.per_xcd = kReadahead ? (kCUs - G1) / 8 : 0;
+        if (ra.per_xcd > 0) {
+            const size_t items = static_cast<size_t>(d.n_pad) * (d.k_pad / 32) / 4;
+            if (items > static_cast<size_t>(kReadaheadMax) * 8 * ra.per_xcd * kThreads) ra.per_xcd = 0;
+        }
+        // the read-ahead blocks start on XCD G1 mod 8; 8 * per_xcd of them cover every XCD equally
+        launch_kernel((mfma_stage1_kernel<NB, RT>), dim3(G1 + 8 * ra.per_xcd), dim3(kThreads), lds, s, d.B_dev,
+                      d.m_pad / 32, static_cast<const __half *>(d.x), d.m, static_cast<const __half *>(d.b_dev),
+                      static_cast<const __half *>(d.mid_dev), reinterpret_cast<__half *>(d.v16), d.k_pad, PR, ra);
+    } else {
+        static const bool once = (allow_lds(mfma_stage2_kernel<NB, RT>, kLdsBudget), true);
+        (void)once;
+        const int PR = std::min(d.k_pad / 64, round_pairs<NB, RT>());
+        const size_t lds = lds_bytes<NB, RT>(PR);
+        launch_kernel((mfma_stage2_kernel<NB, RT>), dim3(d.n_pad / (16 * RT)), dim3(kThreads), lds, s, d.A_dev,
+                      d.k_pad / 32, reinterpret_cast<const __half *>(d.v16), d.k_pad,
+                      static_cast<const __half *>(d.a_dev), static_cast<__half *>(d.y), d.n, PR);
+    }
+    return static_cast<int>(hipGetLastError());
 }
 
 template <int NB>
