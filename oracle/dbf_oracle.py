@@ -27,6 +27,11 @@ page of the same paper.
   columns of X by b, multiply by B^T, scale by mid, multiply by A^T, scale
   by a.  Every product with a sign matrix is a signed sum.
 
+Gradients (``backward``, ``brute_force_backward``): the derivatives of the
+same function with respect to X, a, mid and b, for fine-tuning the factors
+(gist.science technical summary, §4 and §5), written as the plain
+definition; pinned in tests/test_oracle_backward.py.
+
 Readings where the pages are silent:
 * The output is fp16, obtained by one round-to-nearest-even from the exact
   (here: fp64) value.  The pages state fp16 only for X and the scales.
@@ -65,6 +70,8 @@ __all__ = [
     "factored_intermediate",
     "sampled_forward",
     "brute_force",
+    "backward",
+    "brute_force_backward",
 ]
 
 
@@ -212,3 +219,71 @@ def brute_force(X, A, B, a, mid, b):
         xr = [Fraction(float(v)) for v in Xf[r]]
         out.append([sum((xr[l] * W[i][l] for l in range(m)), Fraction(0)) for i in range(n)])
     return out
+
+
+def backward(X, dY, A, B, a, mid, b):
+    """Gradients of the layer for an upstream gradient dY = dL/dY, in fp64.
+
+    The pages fine-tune the factors after factorization (gist.science
+    technical summary, §4: tuning of the discrete parameters improves
+    accuracy; §5: the memory cost of fine-tuning binary factors is open).
+    For the fp16 parameters of Y = X Wᵀ with W = diag(a) A diag(mid) B
+    diag(b), i.e. Y[r,i] = a_i Σ_j A_ij mid_j Σ_l B_jl b_l X[r,l]:
+
+      dX[r,l]  = Σ_i dY[r,i] W[i,l]                    dX = dY W
+      da[i]    = Σ_r dY[r,i] s[r,i]                    s = ((X ⊙ bᵀ) Bᵀ ⊙ midᵀ) Aᵀ
+      dmid[j]  = Σ_r g[r,j] t[r,j]                     t = (X ⊙ bᵀ) Bᵀ,  g = (dY ⊙ aᵀ) A
+      db[l]    = Σ_r h[r,l] X[r,l]                     h = (g ⊙ midᵀ) B
+
+    (each line is the derivative of the sum above with respect to one
+    factor, the others held fixed).  Returns (dX, da, dmid, db), unrounded.
+    """
+    X64, A64, B64, a64, mid64, b64 = _shapes(X, A, B, a, mid, b)
+    dY64 = widen(dY)
+    if dY64.shape != (X64.shape[0], A64.shape[0]):
+        raise ValueError(f"dY must be batch x n = {(X64.shape[0], A64.shape[0])}, got {dY64.shape}")
+    W = dense_weight(A64, B64, a64, mid64, b64)
+    dX = dY64 @ W
+    t = (X64 * b64[None, :]) @ B64.T
+    s = (t * mid64[None, :]) @ A64.T
+    g = (dY64 * a64[None, :]) @ A64
+    h = (g * mid64[None, :]) @ B64
+    da = (dY64 * s).sum(axis=0)
+    dmid = (g * t).sum(axis=0)
+    db = (h * X64).sum(axis=0)
+    return dX, da, dmid, db
+
+
+def brute_force_backward(X, dY, A, B, a, mid, b):
+    """Exact rational gradients straight from Y[r,i] = Σ_j Σ_l a_i A_ij mid_j
+    B_jl b_l X[r,l]: each gradient entry is the sum, over the terms of the
+    loss Σ_r Σ_i dY[r,i] Y[r,i], of the term's factor other than the
+    parameter.  Tiny shapes only.  Returns lists of Fractions (dX as a list of
+    rows)."""
+    A = np.asarray(A)
+    B = np.asarray(B)
+    n, k = A.shape
+    m = B.shape[1]
+    bt = np.asarray(X).shape[0]
+    if bt * n * k * m > 20000:
+        raise ValueError("brute_force_backward is for tiny shapes only")
+    F = lambda v: [Fraction(float(x)) for x in np.asarray(v, dtype=np.float64).ravel()]
+    fa, fmid, fb = F(a), F(mid), F(b)
+    Xf = [F(row) for row in np.asarray(X, dtype=np.float64)]
+    Gf = [F(row) for row in np.asarray(dY, dtype=np.float64)]
+    dX = [[Fraction(0)] * m for _ in range(bt)]
+    da = [Fraction(0)] * n
+    dmid = [Fraction(0)] * k
+    db = [Fraction(0)] * m
+    for r in range(bt):
+        for i in range(n):
+            for j in range(k):
+                for l in range(m):
+                    sign = int(A[i, j]) * int(B[j, l])
+                    w = Gf[r][i] * sign          # dL/dY[r,i] times the signs of the term
+                    dX[r][l] += w * fa[i] * fmid[j] * fb[l]
+                    da[i] += w * fmid[j] * fb[l] * Xf[r][l]
+                    dmid[j] += w * fa[i] * fb[l] * Xf[r][l]
+                    db[l] += w * fa[i] * fmid[j] * Xf[r][l]
+    return dX, da, dmid, db
+
