@@ -53,7 +53,8 @@ def parse():
     p.add_argument("--copy-probe-mb", type=int, default=0,
                    help="only run a plain device copy of this size (counter scaling) and exit")
     p.add_argument("--no-block", action="store_true", help="skip the decoder-block measurement")
-    p.add_argument("--only", choices=("decode", "prefill", "block"), default=None,
+    p.add_argument("--no-backward", action="store_true", help="skip the gradient measurement")
+    p.add_argument("--only", choices=("decode", "prefill", "block", "backward"), default=None,
                    help="run one leg only (for profiling)")
     p.add_argument("--decode-path", choices=("mfma", "table"), default="mfma",
                    help="decode kernels: matrix cores (default) or vector-ALU lookup tables")
@@ -235,6 +236,35 @@ def block_leg(args):
     return res
 
 
+def backward_leg():
+    """Gradients (dX, da, dmid, db) of the 4096x4096, k = 4096 projection at
+    batch 2048: four sign products of 2*batch*k*(n or m) flops each (t, s, g,
+    h) plus the batch reductions; TFLOP/s-equivalent = 4*batch*k*(n+m) per
+    call over the call's time."""
+    import torch
+
+    import dbf_linear_fwd_amd as dbf
+    from tests import inputs
+
+    layer = inputs.config(3).layers[0]
+    bt = 2048
+    H = dbf.Layer(layer.A, layer.B, layer.a, layer.mid, layer.b, max_batch=bt, backward=True)
+    rng = np.random.default_rng(11)
+    x = torch.from_numpy(layer.X[bt]).cuda()
+    dy = torch.from_numpy(rng.standard_normal((bt, layer.n)).astype(np.float16)).cuda()
+
+    def step(i):
+        H.backward(x, dy)
+    el, done = time_steps(step, 30, 5, "eager")
+    flops = 4 * bt * layer.k * (layer.n + layer.m)
+    kt = kernel_times([H], step, 10)
+    print(f"[bench] backward: {flops * done / el / 1e12:.1f} TFLOP/s-eq; kernels {kt}", file=sys.stderr, flush=True)
+    H.close()
+    return {"value": flops * done / el / 1e12, "unit": "TFLOP/s-eq", "ms_per_call": el * 1e3 / done,
+            "kernels": kt, "workload": "gradients of the 4096x4096 projection, k=4096, batch 2048 "
+                                       "(dX, da, dmid, db)"}
+
+
 def copy_probe(mb):
     import torch
     n = mb * (1 << 20) // 4
@@ -336,6 +366,10 @@ def main():
         }
         L.close()
 
+    # ---------------------------------------------------------------- gradients, batch 2048 (secondary)
+    if args.only in (None, "backward") and not args.no_backward:
+        result["backward"] = backward_leg()
+
     # ---------------------------------------------------------------- decoder block, batch 1 (secondary)
     if args.only in (None, "block") and not args.no_block:
         result["block"] = block_leg(args)
@@ -377,6 +411,8 @@ def main():
         line["prefill_batch2048"] = result["prefill"]
     if "block" in result:
         line["decode_block_b1"] = result["block"]
+    if "backward" in result:
+        line["backward_batch2048"] = result["backward"]
     print(json.dumps(line))
 
 

@@ -28,6 +28,7 @@ __all__ = [
     "dbf_pack", "dbf_linear_forward", "dbf_linear_forward_ex", "dbf_free", "dbf_get_info",
     "dbf_status_string", "dbf_pack_signs", "dbf_layout_signs", "dbf_layout_words",
     "dbf_timing_enable", "dbf_timing_read", "Layer", "dbf_linear_forward_group", "forward_group",
+    "dbf_pack_ex", "dbf_linear_backward_data", "dbf_linear_backward", "DBF_PACK_BACKWARD",
 ]
 
 DBF_OK = 0
@@ -42,12 +43,14 @@ DBF_PATH_DECODE = 1
 DBF_PATH_PREFILL = 2
 DBF_PATH_DECODE_TABLE = 3
 
+DBF_PACK_BACKWARD = 1
+
 DECODE_MAX_BATCH = 16
 
 EXPORTED_SYMBOLS = (
-    "dbf_pack", "dbf_linear_forward", "dbf_linear_forward_ex", "dbf_linear_forward_group", "dbf_free",
-    "dbf_get_info", "dbf_status_string", "dbf_pack_signs", "dbf_layout_signs", "dbf_layout_words",
-    "dbf_timing_enable", "dbf_timing_read",
+    "dbf_pack", "dbf_pack_ex", "dbf_linear_forward", "dbf_linear_forward_ex", "dbf_linear_forward_group",
+    "dbf_linear_backward_data", "dbf_linear_backward", "dbf_free", "dbf_get_info", "dbf_status_string",
+    "dbf_pack_signs", "dbf_layout_signs", "dbf_layout_words", "dbf_timing_enable", "dbf_timing_read",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -96,6 +99,12 @@ def lib() -> ctypes.CDLL:
     L.dbf_linear_forward.restype = ctypes.c_int
     L.dbf_linear_forward_ex.argtypes = [vp, vp, vp, i32, i32, vp]
     L.dbf_linear_forward_ex.restype = ctypes.c_int
+    L.dbf_pack_ex.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, i32, i32, ctypes.POINTER(vp)]
+    L.dbf_pack_ex.restype = ctypes.c_int
+    L.dbf_linear_backward_data.argtypes = [vp, vp, vp, i32, vp]
+    L.dbf_linear_backward_data.restype = ctypes.c_int
+    L.dbf_linear_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp]
+    L.dbf_linear_backward.restype = ctypes.c_int
     L.dbf_linear_forward_group.argtypes = [ctypes.POINTER(vp), i32, vp, ctypes.POINTER(vp), i32, vp]
     L.dbf_linear_forward_group.restype = ctypes.c_int
     L.dbf_free.argtypes = [vp]
@@ -142,8 +151,8 @@ def _as_half_bits(v) -> np.ndarray:
     return np.ascontiguousarray(v.astype(np.float16)).view(np.uint16)
 
 
-def dbf_pack(n: int, m: int, k: int, A_signs, B_signs, a, mid, b, max_batch: int) -> int:
-    """Build a layer handle (see dbf_pack in include/dbf.h).  Returns the handle as an int."""
+def dbf_pack(n: int, m: int, k: int, A_signs, B_signs, a, mid, b, max_batch: int, flags: int = 0) -> int:
+    """Build a layer handle (see dbf_pack / dbf_pack_ex in include/dbf.h).  Returns the handle as an int."""
     A = _as_signs(A_signs)
     B = _as_signs(B_signs)
     if A.size != n * k or B.size != k * m:
@@ -152,8 +161,12 @@ def dbf_pack(n: int, m: int, k: int, A_signs, B_signs, a, mid, b, max_batch: int
     if a16.size != n or mid16.size != k or b16.size != m:
         raise ValueError("a, mid, b must have lengths n, k, m")
     h = ctypes.c_void_p()
-    st = lib().dbf_pack(n, m, k, _ptr(A), _ptr(B), _ptr(a16), _ptr(mid16), _ptr(b16), max_batch,
-                        ctypes.byref(h))
+    if flags:
+        st = lib().dbf_pack_ex(n, m, k, _ptr(A), _ptr(B), _ptr(a16), _ptr(mid16), _ptr(b16), max_batch, flags,
+                               ctypes.byref(h))
+    else:
+        st = lib().dbf_pack(n, m, k, _ptr(A), _ptr(B), _ptr(a16), _ptr(mid16), _ptr(b16), max_batch,
+                            ctypes.byref(h))
     _check(st, "dbf_pack")
     return h.value
 
@@ -192,6 +205,16 @@ def forward_group(layers, x, outs=None):
     dbf_linear_forward_group([L.handle for L in layers], x.data_ptr(), [y.data_ptr() for y in outs], x.shape[0],
                              stream)
     return outs
+
+
+def dbf_linear_backward_data(h: int, dy_ptr: int, dx_ptr: int, batch: int, stream: int = 0) -> None:
+    _check(lib().dbf_linear_backward_data(h, dy_ptr, dx_ptr, batch, stream), "dbf_linear_backward_data")
+
+
+def dbf_linear_backward(h: int, x_ptr: int, dy_ptr: int, dx_ptr: int, da_ptr: int, dmid_ptr: int, db_ptr: int,
+                        batch: int, stream: int = 0) -> None:
+    _check(lib().dbf_linear_backward(h, x_ptr, dy_ptr, dx_ptr, da_ptr, dmid_ptr, db_ptr, batch, stream),
+           "dbf_linear_backward")
 
 
 def dbf_free(h: Optional[int]) -> None:
@@ -252,7 +275,7 @@ class Layer:
     computed on the current stream.
     """
 
-    def __init__(self, A, B, a, mid, b, max_batch: int = 2048):
+    def __init__(self, A, B, a, mid, b, max_batch: int = 2048, backward: bool = False):
         A = np.asarray(A)
         B = np.asarray(B)
         if A.ndim != 2 or B.ndim != 2 or A.shape[1] != B.shape[0]:
@@ -260,7 +283,8 @@ class Layer:
         self.n, self.k = A.shape
         self.m = B.shape[1]
         self.max_batch = int(max_batch)
-        self.handle = dbf_pack(self.n, self.m, self.k, A, B, a, mid, b, self.max_batch)
+        self.handle = dbf_pack(self.n, self.m, self.k, A, B, a, mid, b, self.max_batch,
+                               DBF_PACK_BACKWARD if backward else 0)
 
     def info(self) -> Dict[str, int]:
         return dbf_get_info(self.handle)
@@ -281,6 +305,40 @@ class Layer:
         return out
 
     __call__ = forward
+
+    @staticmethod
+    def _check_act(t, width, what):
+        import torch
+        if t.dtype != torch.float16 or not t.is_cuda or t.dim() != 2 or t.shape[1] != width or not t.is_contiguous():
+            raise ValueError(f"{what} must be a contiguous CUDA float16 tensor of shape (batch, {width})")
+
+    def backward_data(self, dy, out=None):
+        """dX = dY W for dY of shape (batch, n); needs backward=True."""
+        import torch
+        self._check_act(dy, self.n, "dy")
+        if out is None:
+            out = torch.empty((dy.shape[0], self.m), dtype=torch.float16, device=dy.device)
+        self._check_act(out, self.m, "out")
+        stream = torch.cuda.current_stream(dy.device).cuda_stream
+        dbf_linear_backward_data(self.handle, dy.data_ptr(), out.data_ptr(), dy.shape[0], stream)
+        return out
+
+    def backward(self, x, dy):
+        """(dX fp16, da, dmid, db fp32) at input x for upstream gradient dy; needs backward=True."""
+        import torch
+        self._check_act(x, self.m, "x")
+        self._check_act(dy, self.n, "dy")
+        if x.shape[0] != dy.shape[0]:
+            raise ValueError("x and dy must have the same batch")
+        dev = x.device
+        dx = torch.empty((x.shape[0], self.m), dtype=torch.float16, device=dev)
+        da = torch.empty(self.n, dtype=torch.float32, device=dev)
+        dmid = torch.empty(self.k, dtype=torch.float32, device=dev)
+        db = torch.empty(self.m, dtype=torch.float32, device=dev)
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        dbf_linear_backward(self.handle, x.data_ptr(), dy.data_ptr(), dx.data_ptr(), da.data_ptr(), dmid.data_ptr(),
+                            db.data_ptr(), x.shape[0], stream)
+        return dx, da, dmid, db
 
     def close(self) -> None:
         if getattr(self, "handle", None):

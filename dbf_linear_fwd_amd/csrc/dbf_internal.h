@@ -133,8 +133,21 @@ inline void launch_kernel(K kernel, dim3 grid, dim3 block, size_t lds, hipStream
 // for i < M, c < n_out.  P is fp16 row-major with leading dimension ldp and
 // K valid columns (columns >= K read as 0); S is the tiled sign matrix with
 // `words` words per row and at least n_rows_pad >= n_out rows.
+//   out (fp16, may be null): rne16(sn[c] * sum); out32 (fp32, may be null):
+//   the unscaled sum, out32[i * ldo32 + c].
 int launch_sign_gemm(const void *P, int ldp, int M, int K, const uint32_t *S, int words, int n_rows_pad,
-                     const void *sk, const void *sn, void *out, int ldo, int n_out, void *stream);
+                     const void *sk, const void *sn, void *out, int ldo, int n_out, float *out32, int ldo32,
+                     void *stream);
+
+// Deterministic column sums of a product of two row-major matrices:
+// out[c] = sum over r < rows of P[r][c] * Q[r][c] for c < cols, summed in row
+// order within chunks of kColChunk rows (launch_colsum_chunks, into partial)
+// and then over the chunks in order (launch_colsum_finish).  P, Q are fp16
+// (flag 0) or fp32 (flag 1); partial holds ceil(rows / kColChunk) * cols floats.
+constexpr int kColChunk = 64;
+int launch_colsum_chunks(const void *P, int p_f32, int ldp, const void *Q, int q_f32, int ldq, int rows, int cols,
+                         float *partial, void *stream);
+int launch_colsum_finish(const float *partial, int rows, int cols, float *out, void *stream);
 
 }  // namespace dbf
 

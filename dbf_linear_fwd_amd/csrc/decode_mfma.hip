@@ -571,7 +571,7 @@ int launch_rt(const MfmaDecodeArgs &d, hipStream_t s, int which) {
         ra.groups = d.n_pad / (16 * rt2);
         // the read-ahead blocks take the CUs stage 1 leaves free, if there are
         // enough of them to read stage 2's words in a few batches
-        ra.per_xcd = kReadahead ? (kCUs - G1) / 8 : 0;
+        ra.per_xcd = kReadahead ? std::max(0, (kCUs - G1) / 8) : 0;  // none when stage 1 fills the CUs
         if (ra.per_xcd > 0) {
             const size_t items = static_cast<size_t>(d.n_pad) * (d.k_pad / 32) / 4;
             if (items > static_cast<size_t>(kReadaheadMax) * 8 * ra.per_xcd * kThreads) ra.per_xcd = 0;

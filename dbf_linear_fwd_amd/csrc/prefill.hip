@@ -96,7 +96,8 @@ __global__ __launch_bounds__(kThreads, DBF_PREFILL_OCC) void sign_gemm_kernel(co
                                                              const uint32_t *__restrict__ S, int words,
                                                              int n_rows_pad, const __half *__restrict__ sk,
                                                              const __half *__restrict__ sn,
-                                                             __half *__restrict__ out, int ldo, int n_out, int nbm,
+                                                             __half *__restrict__ out, int ldo, int n_out,
+                                                             float *__restrict__ out32, int ldo32, int nbm,
                                                              int nbn) {
     __shared__ _Float16 Ps[2][BM * LDP];
     __shared__ uint32_t Ss[2][BK / 2];  // sk of the K step, as half pairs
@@ -174,7 +175,7 @@ __global__ __launch_bounds__(kThreads, DBF_PREFILL_OCC) void sign_gemm_kernel(co
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
         const int col = n0 + wn * 32 * NF + f * 32 + l32;
-        snv[f] = col < n_out ? __half2float(sn[col]) : 0.0f;
+        snv[f] = sn && col < n_out ? __half2float(sn[col]) : 0.0f;
     }
 
     uint2 wcur[NF], wnxt[NF];
@@ -225,7 +226,10 @@ __global__ __launch_bounds__(kThreads, DBF_PREFILL_OCC) void sign_gemm_kernel(co
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int row = m0 + wm * 32 * MF + i * 32 + 8 * (v >> 2) + 4 * kg + (v & 3);
-                if (row < M) out[static_cast<size_t>(row) * ldo + col] = __float2half_rn(acc[i][f][v] * snv[f]);
+                if (row < M) {
+                    if (out) out[static_cast<size_t>(row) * ldo + col] = __float2half_rn(acc[i][f][v] * snv[f]);
+                    if (out32) out32[static_cast<size_t>(row) * ldo32 + col] = acc[i][f][v];
+                }
             }
         }
     }
@@ -233,13 +237,13 @@ __global__ __launch_bounds__(kThreads, DBF_PREFILL_OCC) void sign_gemm_kernel(co
 
 template <bool HAS_SK, bool PVEC, bool KFULL>
 void launch(const void *P, int ldp, int M, int K, const uint32_t *S, int words, int n_rows_pad, const void *sk,
-            const void *sn, void *out, int ldo, int n_out, hipStream_t s) {
+            const void *sn, void *out, int ldo, int n_out, float *out32, int ldo32, hipStream_t s) {
     const int nbm = (M + BM - 1) / BM;
     const int nbn = (n_out + BN - 1) / BN;
     launch_kernel((sign_gemm_kernel<HAS_SK, PVEC, KFULL>), dim3(nbm * nbn), dim3(kThreads), 0, s,
                        static_cast<const __half *>(P), ldp, M, K, S, words, n_rows_pad,
                        static_cast<const __half *>(sk), static_cast<const __half *>(sn), static_cast<__half *>(out),
-                       ldo, n_out, nbm, nbn);
+                       ldo, n_out, out32, ldo32, nbm, nbn);
 }
 
 
@@ -379,6 +383,7 @@ __global__ __launch_bounds__(kDThreads) void sign_gemm_dma_kernel(const __half *
                                                                  int n_rows_pad, const __half *__restrict__ sk,
                                                                  const __half *__restrict__ sn,
                                                                  __half *__restrict__ out, int ldo, int n_out,
+                                                                 float *__restrict__ out32, int ldo32,
                                                                  int nbm, int nbn) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     using C = DmaStep<KP>;
@@ -444,7 +449,7 @@ __global__ __launch_bounds__(kDThreads) void sign_gemm_dma_kernel(const __half *
 #pragma unroll
     for (int f = 0; f < DNF; ++f) {
         const int col = n0 + wn * 32 * DNF + f * 32 + l32;
-        snv[f] = col < n_out ? __half2float(sn[col]) : 0.0f;
+        snv[f] = sn && col < n_out ? __half2float(sn[col]) : 0.0f;
     }
 
 #pragma unroll
@@ -471,7 +476,10 @@ __global__ __launch_bounds__(kDThreads) void sign_gemm_dma_kernel(const __half *
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int row = m0 + wm * 32 * DMF + i * 32 + 8 * (v >> 2) + 4 * kg + (v & 3);
-                if (row < M) out[static_cast<size_t>(row) * ldo + col] = __float2half_rn(acc[i][f][v] * snv[f]);
+                if (row < M) {
+                    if (out) out[static_cast<size_t>(row) * ldo + col] = __float2half_rn(acc[i][f][v] * snv[f]);
+                    if (out32) out32[static_cast<size_t>(row) * ldo32 + col] = acc[i][f][v];
+                }
             }
         }
     }
@@ -479,7 +487,7 @@ __global__ __launch_bounds__(kDThreads) void sign_gemm_dma_kernel(const __half *
 
 template <bool HAS_SK, int KP>
 void launch_dma(const void *P, int ldp, int M, const uint32_t *S, int words, int n_rows_pad, const void *sk,
-                const void *sn, void *out, int ldo, int n_out, hipStream_t s) {
+                const void *sn, void *out, int ldo, int n_out, float *out32, int ldo32, hipStream_t s) {
     using C = DmaStep<KP>;
     static const bool once =
         ((void)hipFuncSetAttribute(reinterpret_cast<const void *>(sign_gemm_dma_kernel<HAS_SK, KP>),
@@ -490,13 +498,14 @@ void launch_dma(const void *P, int ldp, int M, const uint32_t *S, int words, int
     const int nbn = (n_out + DBN - 1) / DBN;
     launch_kernel((sign_gemm_dma_kernel<HAS_SK, KP>), dim3(nbm * nbn), dim3(kDThreads), C::Lds, s,
                   static_cast<const __half *>(P), ldp, M, S, words, n_rows_pad, static_cast<const __half *>(sk),
-                  static_cast<const __half *>(sn), static_cast<__half *>(out), ldo, n_out, nbm, nbn);
+                  static_cast<const __half *>(sn), static_cast<__half *>(out), ldo, n_out, out32, ldo32, nbm, nbn);
 }
 
 }  // namespace
 
 int launch_sign_gemm(const void *P, int ldp, int M, int K, const uint32_t *S, int words, int n_rows_pad,
-                     const void *sk, const void *sn, void *out, int ldo, int n_out, void *stream) {
+                     const void *sk, const void *sn, void *out, int ldo, int n_out, float *out32, int ldo32,
+                     void *stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool pvec = (ldp & 7) == 0;
     const bool kfull = pvec && (K % BK) == 0;
@@ -509,27 +518,27 @@ int launch_sign_gemm(const void *P, int ldp, int M, int K, const uint32_t *S, in
         if constexpr (kDmaPairs == 2) {
             const int tiles = ((M + BM - 1) / BM) * ((n_out + DBN - 1) / DBN);
             if (words % 4 == 0 && tiles <= 256) {
-                if (sk) launch_dma<true, 2>(P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, s);
-                else launch_dma<false, 2>(P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, s);
+                if (sk) launch_dma<true, 2>(P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, s);
+                else launch_dma<false, 2>(P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, s);
                 return static_cast<int>(hipGetLastError());
             }
         }
         {
-            if (sk) launch_dma<true, 1>(P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, s);
-            else launch_dma<false, 1>(P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, s);
+            if (sk) launch_dma<true, 1>(P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, s);
+            else launch_dma<false, 1>(P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, s);
         }
         return static_cast<int>(hipGetLastError());
     }
 #endif
     if (sk) {
-        if (kfull) launch<true, true, true>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, s);
-        else if (pvec) launch<true, true, false>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, s);
-        else launch<true, false, false>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, s);
+        if (kfull) launch<true, true, true>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, s);
+        else if (pvec) launch<true, true, false>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, s);
+        else launch<true, false, false>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, s);
     } else {
         // the second product's K is k_pad, a multiple of 64
-        if (kfull) launch<false, true, true>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, s);
-        else if (pvec) launch<false, true, false>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, s);
-        else launch<false, false, false>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, s);
+        if (kfull) launch<false, true, true>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, s);
+        else if (pvec) launch<false, true, false>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, s);
+        else launch<false, false, false>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, s);
     }
     return static_cast<int>(hipGetLastError());
 }

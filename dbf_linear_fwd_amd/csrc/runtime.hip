@@ -36,6 +36,15 @@ struct dbf_layer {
     unsigned *tickets = nullptr;  // per 64-row tile of A; zero between calls
     uint16_t *v16 = nullptr;      // matrix-core decode intermediate [2][16][k_pad] fp16
     size_t packed_bytes = 0, scale_bytes = 0, workspace_bytes = 0;
+    // backward (dbf_pack_ex with DBF_PACK_BACKWARD): the transposed layer
+    // Wᵀ = diag(b) Bᵀ diag(mid) Aᵀ diag(a), and fp32 intermediates of the
+    // scale gradients, [max_batch][width] each
+    dbf_layer *bwd = nullptr;
+    float *t32 = nullptr;     // (X ⊙ b) Bᵀ                 width k_pad
+    float *s32 = nullptr;     // T Aᵀ (before a)            width n
+    float *g32 = nullptr;     // (dY ⊙ a) A (before mid)    width k_pad
+    float *h32 = nullptr;     // G B (before b)             width m
+    float *red = nullptr;     // column-sum partials [ceil(max_batch / 64)][max(n, k_pad, m)]
     dbf::DecodePlan plan{};   // one-add-per-sign decode kernels (batch 5..16)
     struct LutPlan {
         int cw_m, nchunk_m, cw_k, nchunk_k;
@@ -78,6 +87,7 @@ dbf_status_t dev_alloc(void **p, size_t bytes) {
 
 void release(dbf_layer *h) {
     if (!h) return;
+    // (the transposed layer of a backward-capable handle is released with it)
     (void)hipFree(h->A_dev);
     (void)hipFree(h->B_dev);
     (void)hipFree(h->a_dev);
@@ -88,6 +98,12 @@ void release(dbf_layer *h) {
     (void)hipFree(h->T);
     (void)hipFree(h->tickets);
     (void)hipFree(h->v16);
+    (void)hipFree(h->t32);
+    (void)hipFree(h->s32);
+    (void)hipFree(h->g32);
+    (void)hipFree(h->h32);
+    (void)hipFree(h->red);
+    release(h->bwd);
     for (auto &p : h->pending) {
         (void)hipEventDestroy(p.start);
         (void)hipEventDestroy(p.stop);
@@ -206,9 +222,10 @@ extern "C" const char *dbf_status_string(dbf_status_t s) {
     return "unknown status";
 }
 
-extern "C" dbf_status_t dbf_pack(int32_t n, int32_t m, int32_t k, const int8_t *A_signs, const int8_t *B_signs,
-                                 const uint16_t *a, const uint16_t *mid, const uint16_t *b, int32_t max_batch,
-                                 dbf_handle_t *out) {
+// The layer handle for (A, B, a, mid, b); arguments are validated first.
+static dbf_status_t pack_layer(int32_t n, int32_t m, int32_t k, const int8_t *A_signs, const int8_t *B_signs,
+                               const uint16_t *a, const uint16_t *mid, const uint16_t *b, int32_t max_batch,
+                               dbf_handle_t *out) {
     if (out) *out = nullptr;
     if (!out || !A_signs || !B_signs || !a || !mid || !b) return DBF_ERR_INVALID_ARG;
     if (n < 1 || m < 1 || k < 1 || max_batch < 1) return DBF_ERR_INVALID_ARG;
@@ -228,7 +245,6 @@ extern "C" dbf_status_t dbf_pack(int32_t n, int32_t m, int32_t k, const int8_t *
 
     dbf_layer *h = new (std::nothrow) dbf_layer();
     if (!h) return DBF_ERR_OOM;
-    g_alloc_calls = 0;
     h->n = n;
     h->m = m;
     h->k = k;
@@ -288,6 +304,58 @@ extern "C" dbf_status_t dbf_pack(int32_t n, int32_t m, int32_t k, const int8_t *
         release(h);
         return st;
     }
+    *out = h;
+    return DBF_OK;
+}
+
+extern "C" dbf_status_t dbf_pack(int32_t n, int32_t m, int32_t k, const int8_t *A_signs, const int8_t *B_signs,
+                                 const uint16_t *a, const uint16_t *mid, const uint16_t *b, int32_t max_batch,
+                                 dbf_handle_t *out) {
+    return dbf_pack_ex(n, m, k, A_signs, B_signs, a, mid, b, max_batch, 0, out);
+}
+
+extern "C" dbf_status_t dbf_pack_ex(int32_t n, int32_t m, int32_t k, const int8_t *A_signs, const int8_t *B_signs,
+                                    const uint16_t *a, const uint16_t *mid, const uint16_t *b, int32_t max_batch,
+                                    int32_t flags, dbf_handle_t *out) {
+    if (out) *out = nullptr;
+    if (!out || (flags & ~DBF_PACK_BACKWARD) != 0) return DBF_ERR_INVALID_ARG;
+    g_alloc_calls = 0;
+    dbf_layer *h = nullptr;
+    dbf_status_t st = pack_layer(n, m, k, A_signs, B_signs, a, mid, b, max_batch, &h);
+    if (st != DBF_OK || !(flags & DBF_PACK_BACKWARD)) {
+        *out = h;
+        return st;
+    }
+    // transposed signs on the host: Aᵀ (k x n) and Bᵀ (m x k)
+    std::vector<int8_t> At, Bt;
+    try {
+        At.resize(static_cast<size_t>(k) * n);
+        Bt.resize(static_cast<size_t>(m) * k);
+    } catch (const std::bad_alloc &) {
+        release(h);
+        return DBF_ERR_OOM;
+    }
+    for (int64_t i = 0; i < n; ++i)
+        for (int64_t j = 0; j < k; ++j) At[j * n + i] = A_signs[i * k + j];
+    for (int64_t j = 0; j < k; ++j)
+        for (int64_t l = 0; l < m; ++l) Bt[l * k + j] = B_signs[j * m + l];
+    st = pack_layer(m, n, k, Bt.data(), At.data(), b, mid, a, max_batch, &h->bwd);
+    std::vector<int8_t>().swap(At);
+    std::vector<int8_t>().swap(Bt);
+    const size_t mb = static_cast<size_t>(max_batch);
+    const size_t wmax = static_cast<size_t>(std::max({h->n, h->k_pad, h->m}));
+    const size_t nchunk = (mb + dbf::kColChunk - 1) / dbf::kColChunk;
+    if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->t32), 4 * mb * h->k_pad);
+    if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->s32), 4 * mb * h->n);
+    if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->g32), 4 * mb * h->k_pad);
+    if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->h32), 4 * mb * h->m);
+    if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->red), 4 * nchunk * wmax);
+    if (st != DBF_OK) {
+        release(h);
+        return st;
+    }
+    h->workspace_bytes += 4 * mb * (2 * size_t(h->k_pad) + h->n + h->m) + 4 * nchunk * wmax;
+    h->packed_bytes += h->bwd->packed_bytes;
     *out = h;
     return DBF_OK;
 }
@@ -390,13 +458,13 @@ static dbf_status_t forward_prefill(dbf_layer *h, const void *x, void *y, int32_
     // T = rne16(mid ⊙ (X (B ⊙ b)ᵀ)), all k_pad columns (padded ones are 0).
     dbf_status_t st = timed_launch(h, "prefill_gemm1", stream, [&] {
         return dbf::launch_sign_gemm(x, h->m, batch, h->m, h->B_dev, h->Wm, h->k_pad, h->b_dev, h->mid_dev, h->T,
-                                     h->k_pad, h->k_pad, stream);
+                                     h->k_pad, h->k_pad, nullptr, 0, stream);
     });
     if (st != DBF_OK) return st;
     // Y = rne16(a ⊙ (T Aᵀ)).
     return timed_launch(h, "prefill_gemm2", stream, [&] {
         return dbf::launch_sign_gemm(h->T, h->k_pad, batch, h->k_pad, h->A_dev, h->Wk, h->n_pad, nullptr,
-                                     h->a_dev, y, h->n, h->n, stream);
+                                     h->a_dev, y, h->n, h->n, nullptr, 0, stream);
     });
 }
 
@@ -458,6 +526,74 @@ extern "C" dbf_status_t dbf_linear_forward_group(const dbf_handle_t *hs, int32_t
     return timed_launch(t, "decode_group_stage2", stream, [&] { return dbf::launch_mfma_decode_group(g, stream, 2); });
 }
 
+extern "C" dbf_status_t dbf_linear_backward_data(dbf_handle_t h, const void *dy, void *dx, int32_t batch,
+                                                 hipStream_t stream) {
+    if (!h) return DBF_ERR_INVALID_ARG;
+    if (!h->bwd) return DBF_ERR_UNSUPPORTED;
+    return dbf_linear_forward_ex(h->bwd, dy, dx, batch, DBF_PATH_AUTO, stream);
+}
+
+extern "C" dbf_status_t dbf_linear_backward(dbf_handle_t h, const void *x, const void *dy, void *dx, float *da,
+                                            float *dmid, float *db, int32_t batch, hipStream_t stream) {
+    if (!h) return DBF_ERR_INVALID_ARG;
+    if (!h->bwd) return DBF_ERR_UNSUPPORTED;
+    if (batch < 0 || batch > h->max_batch) return DBF_ERR_INVALID_ARG;
+    if (batch == 0) return DBF_OK;
+    if (!x || !dy || !aligned16(x) || !aligned16(dy) || (dx && !aligned16(dx))) return DBF_ERR_INVALID_ARG;
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return DBF_ERR_HIP;
+    if (cur != h->device) return DBF_ERR_INVALID_ARG;
+    dbf_layer *t = h->bwd;
+    dbf_status_t st = DBF_OK;
+    auto colsum = [&](const char *name, const void *P, int pf, int ldp, const void *Q, int qf, int ldq, int cols,
+                      float *out) {
+        st = timed_launch(h, name, stream, [&] {
+            return dbf::launch_colsum_chunks(P, pf, ldp, Q, qf, ldq, batch, cols, h->red, stream);
+        });
+        if (st == DBF_OK)
+            st = timed_launch(h, "grad_colsum_finish", stream,
+                              [&] { return dbf::launch_colsum_finish(h->red, batch, cols, out, stream); });
+    };
+    if (da || dmid) {
+        // t = (X ⊙ b) Bᵀ in fp32 (for dmid) and T = rne16(t ⊙ mid) (for s), one product
+        st = timed_launch(h, "grad_t", stream, [&] {
+            return dbf::launch_sign_gemm(x, h->m, batch, h->m, h->B_dev, h->Wm, h->k_pad, h->b_dev, h->mid_dev, h->T,
+                                         h->k_pad, h->k_pad, dmid ? h->t32 : nullptr, h->k_pad, stream);
+        });
+        if (st != DBF_OK) return st;
+    }
+    if (da) {
+        // s = T Aᵀ (fp32, before a); da = Σ_r dY ⊙ s
+        st = timed_launch(h, "grad_s", stream, [&] {
+            return dbf::launch_sign_gemm(h->T, h->k_pad, batch, h->k_pad, h->A_dev, h->Wk, h->n_pad, nullptr, nullptr,
+                                         nullptr, 0, h->n, h->s32, h->n, stream);
+        });
+        if (st == DBF_OK) colsum("grad_colsum_a", dy, 0, h->n, h->s32, 1, h->n, h->n, da);
+        if (st != DBF_OK) return st;
+    }
+    if (dmid || db || dx) {
+        // g = (dY ⊙ a) A in fp32 (for dmid) and G = rne16(g ⊙ mid); the transposed layer holds Aᵀ packed along n
+        // and a as its input scale
+        st = timed_launch(h, "grad_g", stream, [&] {
+            return dbf::launch_sign_gemm(dy, h->n, batch, h->n, t->B_dev, t->Wm, t->k_pad, t->b_dev, t->mid_dev, t->T,
+                                         t->k_pad, t->k_pad, dmid ? h->g32 : nullptr, h->k_pad, stream);
+        });
+        if (st != DBF_OK) return st;
+        if (dmid) colsum("grad_colsum_mid", h->g32, 1, h->k_pad, h->t32, 1, h->k_pad, h->k, dmid);
+        if (st != DBF_OK) return st;
+    }
+    if (db || dx) {
+        // h = G B in fp32 (for db; Bᵀ packed along k in the transposed layer), dX = rne16(h ⊙ b)
+        st = timed_launch(h, "grad_h", stream, [&] {
+            return dbf::launch_sign_gemm(t->T, t->k_pad, batch, t->k_pad, t->A_dev, t->Wk, t->n_pad, nullptr,
+                                         t->a_dev, dx, h->m, h->m, db ? h->h32 : nullptr, h->m, stream);
+        });
+        if (st != DBF_OK) return st;
+        if (db) colsum("grad_colsum_b", h->h32, 1, h->m, x, 0, h->m, h->m, db);
+    }
+    return st;
+}
+
 extern "C" dbf_status_t dbf_linear_forward(dbf_handle_t h, const void *x, void *y, int32_t batch,
                                            hipStream_t stream) {
     return dbf_linear_forward_ex(h, x, y, batch, DBF_PATH_AUTO, stream);
@@ -466,12 +602,21 @@ extern "C" dbf_status_t dbf_linear_forward(dbf_handle_t h, const void *x, void *
 extern "C" dbf_status_t dbf_timing_enable(dbf_handle_t h, int32_t enable) {
     if (!h) return DBF_ERR_INVALID_ARG;
     h->timing = enable != 0;
+    if (h->bwd) h->bwd->timing = h->timing;
     return DBF_OK;
 }
 
 extern "C" dbf_status_t dbf_timing_read(dbf_handle_t h, dbf_kernel_time_t *out, int32_t cap, int32_t *count) {
     if (!h || !count || cap < 0 || (cap > 0 && !out)) return DBF_ERR_INVALID_ARG;
     dbf_status_t st = DBF_OK;
+    if (h->bwd) {
+        // launches of the transposed layer (dbf_linear_backward_data) count as "bwd_<kernel>"
+        for (auto &p : h->bwd->pending) {
+            p.name = "bwd_" + p.name;
+            h->pending.push_back(p);
+        }
+        h->bwd->pending.clear();
+    }
     for (auto &p : h->pending) {
         float ms = 0.0f;
         if (hipEventSynchronize(p.stop) != hipSuccess || hipEventElapsedTime(&ms, p.start, p.stop) != hipSuccess) {

@@ -82,7 +82,8 @@ typedef struct {
     int32_t n_pad, m_pad, k_pad; /* device sizes: each rounded up to a multiple of 64 */
     int32_t max_batch;
     int32_t device;           /* HIP device the handle lives on */
-    size_t packed_bytes;      /* device bytes of packed A and B (padding included) */
+    size_t packed_bytes;      /* device bytes of packed A and B (padding included; with DBF_PACK_BACKWARD
+                                 the transposed copies too) */
     size_t scale_bytes;       /* device bytes of a, mid, b (padding included) */
     size_t workspace_bytes;   /* device scratch owned by the handle */
 } dbf_info_t;
@@ -153,6 +154,51 @@ dbf_status_t dbf_linear_forward_ex(dbf_handle_t h, const void *x, void *y, int32
  */
 dbf_status_t dbf_linear_forward_group(const dbf_handle_t *hs, int32_t count, const void *x, void *const *ys,
                                       int32_t batch, hipStream_t stream);
+
+/*
+ * dbf_pack_ex -- dbf_pack with flags.  DBF_PACK_BACKWARD also packs the
+ * transposed factors (Aᵀ along n, Bᵀ along k; the transpose of a DBF matrix
+ * is the DBF matrix diag(b) Bᵀ diag(mid) Aᵀ diag(a)) and allocates the fp32
+ * workspace of the gradients (4 * max_batch * (2 k_pad + n + m) bytes and
+ * the reduction partials), for dbf_linear_backward_data and
+ * dbf_linear_backward.  Unknown flags are DBF_ERR_INVALID_ARG.
+ */
+#define DBF_PACK_BACKWARD 1
+dbf_status_t dbf_pack_ex(int32_t n, int32_t m, int32_t k,
+                         const int8_t *A_signs, const int8_t *B_signs,
+                         const uint16_t *a, const uint16_t *mid, const uint16_t *b,
+                         int32_t max_batch, int32_t flags, dbf_handle_t *out);
+
+/*
+ * dbf_linear_backward_data -- dX = dY W (batch x m, fp16) for an upstream
+ * gradient dY (batch x n, fp16): the forward of the transposed layer, with
+ * the same kernels and numerics as dbf_linear_forward.  Fine-tuning of the
+ * factors is part of the method (gist.science technical summary, §4: tuning
+ * of the binary factors; §5: its memory cost as open work).  Needs a handle
+ * packed with DBF_PACK_BACKWARD (else DBF_ERR_UNSUPPORTED).  Pointer and
+ * batch rules as dbf_linear_forward.
+ */
+dbf_status_t dbf_linear_backward_data(dbf_handle_t h, const void *dy, void *dx, int32_t batch,
+                                      hipStream_t stream);
+
+/*
+ * dbf_linear_backward -- gradients of the layer at input x (batch x m, fp16)
+ * for the upstream gradient dy (batch x n, fp16):
+ *   dx[r,l]  = Σ_i dy[r,i] W[i,l]                        fp16, batch x m
+ *   da[i]    = Σ_r dy[r,i] s[r,i],   s = ((x ⊙ b) Bᵀ ⊙ mid) Aᵀ      fp32, n
+ *   dmid[j]  = Σ_r g[r,j] t[r,j],    t = (x ⊙ b) Bᵀ, g = (dy ⊙ a) A  fp32, k
+ *   db[l]    = Σ_r h[r,l] x[r,l],    h = (g ⊙ mid) B                fp32, m
+ * All four products run on the matrix cores (the prefill kernels) with fp32
+ * accumulation; t ⊙ mid and g ⊙ mid are rounded once to fp16 as operands of
+ * the second products (as on the prefill forward).  Sums over the batch are
+ * taken in a fixed order: repeated calls give identical bits.  Any of dx,
+ * da, dmid, db may be NULL (not computed).  Device pointers, caller-owned;
+ * x, dy, dx 16-byte aligned.  0 <= batch <= max_batch.  Needs
+ * DBF_PACK_BACKWARD (else DBF_ERR_UNSUPPORTED).  Calls on one handle must be
+ * ordered (the workspace is shared).
+ */
+dbf_status_t dbf_linear_backward(dbf_handle_t h, const void *x, const void *dy, void *dx, float *da,
+                                 float *dmid, float *db, int32_t batch, hipStream_t stream);
 
 /* dbf_free -- release the handle and its device memory.  NULL is a no-op.
  * Synchronises the handle's device first, so pending work on it finishes. */

@@ -141,3 +141,23 @@ def test_group_entry_validates_before_any_device_call():
     assert L.dbf_linear_forward_group(hs, 0, None, ys, 1, None) == dbf.DBF_ERR_INVALID_ARG   # count 0
     assert L.dbf_linear_forward_group(hs, 9, None, ys, 1, None) == dbf.DBF_ERR_INVALID_ARG   # count > 8
     assert L.dbf_linear_forward_group(hs, 1, None, ys, 1, None) == dbf.DBF_ERR_INVALID_ARG   # null handle
+
+
+def test_backward_entries_validate_before_any_device_call():
+    import ctypes
+    L = dbf.lib()
+    A = np.ones((4, 3), np.int8)
+    B = np.ones((3, 5), np.int8)
+    a = np.ones(4, np.float16).view(np.uint16)
+    mid = np.ones(3, np.float16).view(np.uint16)
+    b = np.ones(5, np.float16).view(np.uint16)
+    h = ctypes.c_void_p()
+    p = lambda arr: arr.ctypes.data_as(ctypes.c_void_p)
+    # unknown flag bits
+    assert L.dbf_pack_ex(4, 5, 3, p(A), p(B), p(a), p(mid), p(b), 2, 6, ctypes.byref(h)) == dbf.DBF_ERR_INVALID_ARG
+    assert h.value is None
+    # null output pointer
+    assert L.dbf_pack_ex(4, 5, 3, p(A), p(B), p(a), p(mid), p(b), 2, 1, None) == dbf.DBF_ERR_INVALID_ARG
+    # null handles
+    assert L.dbf_linear_backward_data(None, None, None, 1, None) == dbf.DBF_ERR_INVALID_ARG
+    assert L.dbf_linear_backward(None, None, None, None, None, None, None, 1, None) == dbf.DBF_ERR_INVALID_ARG

@@ -135,7 +135,7 @@ ROW_TILE_SHAPES = [
 
 
 @pytest.mark.parametrize("n,m,k", ROW_TILE_SHAPES)
-@pytest.mark.parametrize("batch", [1, 4])
+@pytest.mark.parametrize("batch", [1, 4, 9])   # 9: 16-row blocks, more stage-1 blocks than CUs (k >= 4160)
 def test_decode_row_tile_variants(gpu, n, m, k, batch):
     _say(f"decode row tiles n={n} m={m} k={k} batch={batch}")
     X, A, B, a, mid, b = inputs.tiny_case(3000 + n + m + k + batch, n, m, k, batch, signed_scales=True)
@@ -475,3 +475,130 @@ def test_group_forward_errors(gpu):
         H1.close()
         H2.close()
         H3.close()
+
+
+# --------------------------------------------------------------------------- gradients (fine-tuning of the factors)
+
+def _vec_rel(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-300))
+
+
+BWD_SHAPES = [
+    # n, m, k
+    (1, 1, 1),
+    (3, 5, 7),
+    (64, 64, 64),
+    (130, 200, 190),
+    (257, 96, 130),
+    (100, 1100, 70),
+]
+
+
+@pytest.mark.parametrize("n,m,k", BWD_SHAPES)
+@pytest.mark.parametrize("batch", [1, 3, 17, 100])
+def test_backward_data_matches_oracle_and_transposed_forward(gpu, n, m, k, batch):
+    """dX = dY W: the oracle's value, and the same bits as the forward of a
+    layer packed directly from the transposed factors (Bᵀ, Aᵀ, b, mid, a)."""
+    torch = _torch()
+    _say(f"backward data n={n} m={m} k={k} batch={batch}")
+    _, A, B, a, mid, b = inputs.tiny_case(8000 + n + m + k, n, m, k, 1, signed_scales=True)
+    dY = np.random.default_rng(batch + n).uniform(-4, 4, (batch, n)).astype(np.float16)
+    H = dbf.Layer(A, B, a, mid, b, max_batch=batch, backward=True)
+    Ht = dbf.Layer(np.ascontiguousarray(B.T), np.ascontiguousarray(A.T), b, mid, a, max_batch=batch)
+    try:
+        dy = torch.from_numpy(dY).cuda()
+        dx = H.backward_data(dy).cpu().numpy()
+        direct = Ht.forward(dy).cpu().numpy()
+        assert np.array_equal(dx.view(np.uint16), direct.view(np.uint16))
+        X0 = np.zeros((batch, m), np.float16)
+        ref = O.backward(X0, dY, A, B, a, mid, b)[0]
+        assert_tol(dx, ref, f"dX {n}x{m}x{k}")
+    finally:
+        H.close()
+        Ht.close()
+
+
+@pytest.mark.parametrize("n,m,k", BWD_SHAPES)
+@pytest.mark.parametrize("batch", [1, 5, 70, 300])
+def test_backward_gradients_match_oracle(gpu, n, m, k, batch):
+    torch = _torch()
+    _say(f"backward n={n} m={m} k={k} batch={batch}")
+    X, A, B, a, mid, b = inputs.tiny_case(9000 + n + m + k + batch, n, m, k, batch, signed_scales=True)
+    dY = np.random.default_rng(7 * batch + n).uniform(-4, 4, (batch, n)).astype(np.float16)
+    H = dbf.Layer(A, B, a, mid, b, max_batch=batch, backward=True)
+    try:
+        x = torch.from_numpy(X).cuda()
+        dy = torch.from_numpy(dY).cuda()
+        dx, da, dmid, db = (t.cpu().numpy() for t in H.backward(x, dy))
+        rdx, rda, rdmid, rdb = O.backward(X, dY, A, B, a, mid, b)
+        assert_tol(dx, rdx, "dX")
+        for name, got, ref in (("da", da, rda), ("dmid", dmid, rdmid), ("db", db, rdb)):
+            err = _vec_rel(got, ref)
+            assert err <= TOL, f"{name}: rel err {err:.3e}"
+        # deterministic: a second call gives the same bits
+        again = [t.cpu().numpy() for t in H.backward(x, dy)]
+        for g1, g2 in zip((dx, da, dmid, db), again):
+            assert np.array_equal(g1.view(np.uint8), g2.view(np.uint8))
+    finally:
+        H.close()
+
+
+def test_backward_partial_outputs_and_errors(gpu):
+    """Any of dx, da, dmid, db may be skipped; the rest are unchanged.  A
+    handle packed without backward support refuses."""
+    torch = _torch()
+    n, m, k, bt = 130, 200, 190, 33
+    X, A, B, a, mid, b = inputs.tiny_case(4242, n, m, k, bt, signed_scales=True)
+    dY = np.random.default_rng(5).uniform(-4, 4, (bt, n)).astype(np.float16)
+    H = dbf.Layer(A, B, a, mid, b, max_batch=bt, backward=True)
+    H0 = dbf.Layer(A, B, a, mid, b, max_batch=bt)
+    try:
+        _say("backward partial outputs")
+        x = torch.from_numpy(X).cuda()
+        dy = torch.from_numpy(dY).cuda()
+        full = [t.cpu().numpy() for t in H.backward(x, dy)]
+        for keep in range(4):
+            outs = [torch.full((bt, m), 7.0, dtype=torch.float16, device="cuda"),
+                    torch.full((n,), 7.0, device="cuda"), torch.full((k,), 7.0, device="cuda"),
+                    torch.full((m,), 7.0, device="cuda")]
+            ptrs = [o.data_ptr() if i == keep else 0 for i, o in enumerate(outs)]
+            dbf.dbf_linear_backward(H.handle, x.data_ptr(), dy.data_ptr(), *ptrs, bt,
+                                    torch.cuda.current_stream().cuda_stream)
+            got = outs[keep].cpu().numpy()
+            assert np.array_equal(got.view(np.uint8), full[keep].view(np.uint8)), keep
+        with pytest.raises(dbf.DbfError) as e:
+            dbf.dbf_linear_backward_data(H0.handle, dy.data_ptr(), x.data_ptr(), bt)
+        assert e.value.status == dbf.DBF_ERR_UNSUPPORTED
+        with pytest.raises(ValueError):   # batch of dy differs from x (the binding's check)
+            H.backward(x, torch.cat([dy, dy]))
+        with pytest.raises(dbf.DbfError) as e:
+            dbf.dbf_linear_backward(H.handle, x.data_ptr(), dy.data_ptr(), 0, 0, 0, 0, bt + 1, 0)
+        assert e.value.status == dbf.DBF_ERR_INVALID_ARG
+    finally:
+        H.close()
+        H0.close()
+
+
+def test_backward_full_size_projection(gpu):
+    """The 4096 x 4096, k = 2048 projection at batch 256 with its workload's
+    value ranges and a unit-scale upstream gradient."""
+    torch = _torch()
+    L = inputs.config(2).layers[0]
+    bt = 256
+    rng = np.random.default_rng(3)
+    X = rng.standard_normal((bt, L.m)).astype(np.float16)
+    dY = rng.standard_normal((bt, L.n)).astype(np.float16)
+    _say("backward full size 4096x4096 k2048 batch 256")
+    H = dbf.Layer(L.A, L.B, L.a, L.mid, L.b, max_batch=bt, backward=True)
+    try:
+        dx, da, dmid, db = (t.cpu().numpy() for t in H.backward(torch.from_numpy(X).cuda(), torch.from_numpy(dY).cuda()))
+        rdx, rda, rdmid, rdb = O.backward(X, dY, L.A, L.B, L.a, L.mid, L.b)
+        assert_tol(dx, rdx, "dX full")
+        for name, got, ref in (("da", da, rda), ("dmid", dmid, rdmid), ("db", db, rdb)):
+            err = _vec_rel(got, ref)
+            _say(f"  {name} rel err {err:.3e}")
+            assert err <= TOL, f"{name}: rel err {err:.3e}"
+    finally:
+        H.close()
