@@ -134,20 +134,19 @@ inline void launch_kernel(K kernel, dim3 grid, dim3 block, size_t lds, hipStream
 // K valid columns (columns >= K read as 0); S is the tiled sign matrix with
 // `words` words per row and at least n_rows_pad >= n_out rows.
 //   out (fp16, may be null): rne16(sn[c] * sum); out32 (fp32, may be null):
-//   the unscaled sum, out32[i * ldo32 + c].
+//   the unscaled sum, out32[i * ldo32 + c]; dpart (may be null): batch sums
+//   of sum * Q[i][c] over each group of 64 rows i (Q fp16 or fp32 as dq_f32,
+//   leading dimension lddq), dpart[(i / 64) * n_out + c], to be finished by
+//   launch_colsum_finish(dpart, M, n_out, ...).
 int launch_sign_gemm(const void *P, int ldp, int M, int K, const uint32_t *S, int words, int n_rows_pad,
                      const void *sk, const void *sn, void *out, int ldo, int n_out, float *out32, int ldo32,
-                     void *stream);
+                     const void *dq, int dq_f32, int lddq, float *dpart, void *stream);
 
-// Deterministic column sums of a product of two row-major matrices:
-// out[c] = sum over r < rows of P[r][c] * Q[r][c] for c < cols, summed in row
-// order within chunks of kColChunk rows (launch_colsum_chunks, into partial)
-// and then over the chunks in order (launch_colsum_finish).  P, Q are fp16
-// (flag 0) or fp32 (flag 1); partial holds ceil(rows / kColChunk) * cols floats.
+// Batch sums of the gradients: out[c] = sum over g < ceil(rows / 64) of
+// partial[g * ld + c] for c < cols, added in g order (the partials are
+// 64-row sums written by launch_sign_gemm's dpart epilogue).
 constexpr int kColChunk = 64;
-int launch_colsum_chunks(const void *P, int p_f32, int ldp, const void *Q, int q_f32, int ldq, int rows, int cols,
-                         float *partial, void *stream);
-int launch_colsum_finish(const float *partial, int rows, int cols, float *out, void *stream);
+int launch_colsum_finish(const float *partial, int ld, int rows, int cols, float *out, void *stream);
 
 }  // namespace dbf
 

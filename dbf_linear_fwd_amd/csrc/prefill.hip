@@ -85,6 +85,64 @@ __device__ __forceinline__ f16x8 expand(uint32_t word, int g, const u32x4 &sc, E
     return __builtin_bit_cast(f16x8, r);
 }
 
+// Batch-sum epilogue (gradients): for every output column c, the sum over
+// the wave's 64 rows of C[r][c] * Q[r][c], written to part[(r0 / 64) * n_out
+// + c]; summing the parts in order gives Σ_r C[r][c] Q[r][c] (grad.hip).
+struct DotArgs {
+    const void *q;  // fp16 or fp32 (q_f32), row-major, leading dimension ldq
+    int q_f32, ldq;
+    float *part;    // null: no batch sums
+};
+
+// The epilogue of both product kernels.  32x32 MFMA result register v of a
+// lane holds row 8*(v/4) + 4*(lane/32) + v%4 and column lane%32 of its tile;
+// row0 / col0 are the wave's first row and column.
+template <int MF_, int NF_>
+__device__ __forceinline__ void epilogue(const f32x16 (&acc)[MF_][NF_], const float (&snv)[NF_], int M, int n_out,
+                                         int row0, int col0, int l32, int kg, __half *__restrict__ out, int ldo,
+                                         float *__restrict__ out32, int ldo32, const DotArgs &dot) {
+    static_assert(32 * MF_ == 64, "batch-sum groups are the waves' 64 rows");
+#pragma unroll
+    for (int i = 0; i < MF_; ++i) {
+#pragma unroll
+        for (int f = 0; f < NF_; ++f) {
+            const int col = col0 + f * 32 + l32;
+            if (col >= n_out) continue;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = row0 + i * 32 + 8 * (v >> 2) + 4 * kg + (v & 3);
+                if (row < M) {
+                    if (out) out[static_cast<size_t>(row) * ldo + col] = __float2half_rn(acc[i][f][v] * snv[f]);
+                    if (out32) out32[static_cast<size_t>(row) * ldo32 + col] = acc[i][f][v];
+                }
+            }
+        }
+    }
+    if (dot.part) {
+#pragma unroll
+        for (int f = 0; f < NF_; ++f) {
+            const int col = col0 + f * 32 + l32;
+            float sum = 0.0f;
+            if (col < n_out) {
+#pragma unroll
+                for (int i = 0; i < MF_; ++i)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int row = row0 + i * 32 + 8 * (v >> 2) + 4 * kg + (v & 3);
+                        if (row < M) {
+                            const size_t qi = static_cast<size_t>(row) * dot.ldq + col;
+                            const float qv = dot.q_f32 ? static_cast<const float *>(dot.q)[qi]
+                                                       : __half2float(static_cast<const __half *>(dot.q)[qi]);
+                            sum += acc[i][f][v] * qv;
+                        }
+                    }
+            }
+            sum += __shfl_xor(sum, 32);  // the two halves of the wave hold alternate row quads of the column
+            if (kg == 0 && col < n_out && row0 < M) dot.part[static_cast<size_t>(row0 / 64) * n_out + col] = sum;
+        }
+    }
+}
+
 // C = P S'ᵀ (see the file comment).  P: fp16 [M][ldp], K valid columns
 // (zero beyond).  S: tiled sign rows, `words` per row, n_rows_pad rows.
 // sk: fp16 scale per K (zero-padded to words*32) or unused.  sn: fp16 scale
@@ -97,7 +155,8 @@ __global__ __launch_bounds__(kThreads, DBF_PREFILL_OCC) void sign_gemm_kernel(co
                                                              int n_rows_pad, const __half *__restrict__ sk,
                                                              const __half *__restrict__ sn,
                                                              __half *__restrict__ out, int ldo, int n_out,
-                                                             float *__restrict__ out32, int ldo32, int nbm,
+                                                             float *__restrict__ out32, int ldo32, const DotArgs dot,
+                                                             int nbm,
                                                              int nbn) {
     __shared__ _Float16 Ps[2][BM * LDP];
     __shared__ uint32_t Ss[2][BK / 2];  // sk of the K step, as half pairs
@@ -215,35 +274,19 @@ __global__ __launch_bounds__(kThreads, DBF_PREFILL_OCC) void sign_gemm_kernel(co
         __syncthreads();
     }
 
-    // epilogue: 32x32 MFMA result register v of a lane holds row
-    // 8*(v/4) + 4*(lane/32) + v%4 and column lane%32 of its tile
-#pragma unroll
-    for (int i = 0; i < MF; ++i) {
-#pragma unroll
-        for (int f = 0; f < NF; ++f) {
-            const int col = n0 + wn * 32 * NF + f * 32 + l32;
-            if (col >= n_out) continue;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int row = m0 + wm * 32 * MF + i * 32 + 8 * (v >> 2) + 4 * kg + (v & 3);
-                if (row < M) {
-                    if (out) out[static_cast<size_t>(row) * ldo + col] = __float2half_rn(acc[i][f][v] * snv[f]);
-                    if (out32) out32[static_cast<size_t>(row) * ldo32 + col] = acc[i][f][v];
-                }
-            }
-        }
-    }
+    epilogue<MF, NF>(acc, snv, M, n_out, m0 + wm * 32 * MF, n0 + wn * 32 * NF, l32, kg, out, ldo, out32, ldo32, dot);
 }
 
 template <bool HAS_SK, bool PVEC, bool KFULL>
 void launch(const void *P, int ldp, int M, int K, const uint32_t *S, int words, int n_rows_pad, const void *sk,
-            const void *sn, void *out, int ldo, int n_out, float *out32, int ldo32, hipStream_t s) {
+            const void *sn, void *out, int ldo, int n_out, float *out32, int ldo32, const DotArgs &dot,
+            hipStream_t s) {
     const int nbm = (M + BM - 1) / BM;
     const int nbn = (n_out + BN - 1) / BN;
     launch_kernel((sign_gemm_kernel<HAS_SK, PVEC, KFULL>), dim3(nbm * nbn), dim3(kThreads), 0, s,
                        static_cast<const __half *>(P), ldp, M, K, S, words, n_rows_pad,
                        static_cast<const __half *>(sk), static_cast<const __half *>(sn), static_cast<__half *>(out),
-                       ldo, n_out, out32, ldo32, nbm, nbn);
+                       ldo, n_out, out32, ldo32, dot, nbm, nbn);
 }
 
 
@@ -383,7 +426,7 @@ __global__ __launch_bounds__(kDThreads) void sign_gemm_dma_kernel(const __half *
                                                                  int n_rows_pad, const __half *__restrict__ sk,
                                                                  const __half *__restrict__ sn,
                                                                  __half *__restrict__ out, int ldo, int n_out,
-                                                                 float *__restrict__ out32, int ldo32,
+                                                                 float *__restrict__ out32, int ldo32, const DotArgs dot,
                                                                  int nbm, int nbn) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     using C = DmaStep<KP>;
@@ -467,27 +510,14 @@ __global__ __launch_bounds__(kDThreads) void sign_gemm_dma_kernel(const __half *
                                 lds + (kt % kStages) * C::StageBytes, issue_one, acc, wm, wn, l32, kg, ec);
     }
 
-#pragma unroll
-    for (int i = 0; i < DMF; ++i) {
-#pragma unroll
-        for (int f = 0; f < DNF; ++f) {
-            const int col = n0 + wn * 32 * DNF + f * 32 + l32;
-            if (col >= n_out) continue;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int row = m0 + wm * 32 * DMF + i * 32 + 8 * (v >> 2) + 4 * kg + (v & 3);
-                if (row < M) {
-                    if (out) out[static_cast<size_t>(row) * ldo + col] = __float2half_rn(acc[i][f][v] * snv[f]);
-                    if (out32) out32[static_cast<size_t>(row) * ldo32 + col] = acc[i][f][v];
-                }
-            }
-        }
-    }
+    epilogue<DMF, DNF>(acc, snv, M, n_out, m0 + wm * 32 * DMF, n0 + wn * 32 * DNF, l32, kg, out, ldo, out32, ldo32,
+                       dot);
 }
 
 template <bool HAS_SK, int KP>
 void launch_dma(const void *P, int ldp, int M, const uint32_t *S, int words, int n_rows_pad, const void *sk,
-                const void *sn, void *out, int ldo, int n_out, float *out32, int ldo32, hipStream_t s) {
+                const void *sn, void *out, int ldo, int n_out, float *out32, int ldo32, const DotArgs &dot,
+            hipStream_t s) {
     using C = DmaStep<KP>;
     static const bool once =
         ((void)hipFuncSetAttribute(reinterpret_cast<const void *>(sign_gemm_dma_kernel<HAS_SK, KP>),
@@ -498,14 +528,15 @@ void launch_dma(const void *P, int ldp, int M, const uint32_t *S, int words, int
     const int nbn = (n_out + DBN - 1) / DBN;
     launch_kernel((sign_gemm_dma_kernel<HAS_SK, KP>), dim3(nbm * nbn), dim3(kDThreads), C::Lds, s,
                   static_cast<const __half *>(P), ldp, M, S, words, n_rows_pad, static_cast<const __half *>(sk),
-                  static_cast<const __half *>(sn), static_cast<__half *>(out), ldo, n_out, out32, ldo32, nbm, nbn);
+                  static_cast<const __half *>(sn), static_cast<__half *>(out), ldo, n_out, out32, ldo32, dot, nbm, nbn);
 }
 
 }  // namespace
 
 int launch_sign_gemm(const void *P, int ldp, int M, int K, const uint32_t *S, int words, int n_rows_pad,
                      const void *sk, const void *sn, void *out, int ldo, int n_out, float *out32, int ldo32,
-                     void *stream) {
+                     const void *dq, int dq_f32, int lddq, float *dpart, void *stream) {
+    const DotArgs dot{dq, dq_f32, lddq, dpart};
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool pvec = (ldp & 7) == 0;
     const bool kfull = pvec && (K % BK) == 0;
@@ -518,27 +549,27 @@ int launch_sign_gemm(const void *P, int ldp, int M, int K, const uint32_t *S, in
         if constexpr (kDmaPairs == 2) {
             const int tiles = ((M + BM - 1) / BM) * ((n_out + DBN - 1) / DBN);
             if (words % 4 == 0 && tiles <= 256) {
-                if (sk) launch_dma<true, 2>(P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, s);
-                else launch_dma<false, 2>(P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, s);
+                if (sk) launch_dma<true, 2>(P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, dot, s);
+                else launch_dma<false, 2>(P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, dot, s);
                 return static_cast<int>(hipGetLastError());
             }
         }
         {
-            if (sk) launch_dma<true, 1>(P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, s);
-            else launch_dma<false, 1>(P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, s);
+            if (sk) launch_dma<true, 1>(P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, dot, s);
+            else launch_dma<false, 1>(P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, dot, s);
         }
         return static_cast<int>(hipGetLastError());
     }
 #endif
     if (sk) {
-        if (kfull) launch<true, true, true>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, s);
-        else if (pvec) launch<true, true, false>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, s);
-        else launch<true, false, false>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, s);
+        if (kfull) launch<true, true, true>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, dot, s);
+        else if (pvec) launch<true, true, false>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, dot, s);
+        else launch<true, false, false>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, dot, s);
     } else {
         // the second product's K is k_pad, a multiple of 64
-        if (kfull) launch<false, true, true>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, s);
-        else if (pvec) launch<false, true, false>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, s);
-        else launch<false, false, false>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, s);
+        if (kfull) launch<false, true, true>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, dot, s);
+        else if (pvec) launch<false, true, false>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, dot, s);
+        else launch<false, false, false>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, dot, s);
     }
     return static_cast<int>(hipGetLastError());
 }

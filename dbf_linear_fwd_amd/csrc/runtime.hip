@@ -40,11 +40,8 @@ struct dbf_layer {
     // Wᵀ = diag(b) Bᵀ diag(mid) Aᵀ diag(a), and fp32 intermediates of the
     // scale gradients, [max_batch][width] each
     dbf_layer *bwd = nullptr;
-    float *t32 = nullptr;     // (X ⊙ b) Bᵀ                 width k_pad
-    float *s32 = nullptr;     // T Aᵀ (before a)            width n
-    float *g32 = nullptr;     // (dY ⊙ a) A (before mid)    width k_pad
-    float *h32 = nullptr;     // G B (before b)             width m
-    float *red = nullptr;     // column-sum partials [ceil(max_batch / 64)][max(n, k_pad, m)]
+    float *t32 = nullptr;     // (X ⊙ b) Bᵀ in fp32          [max_batch][k_pad]
+    float *red = nullptr;     // batch-sum partials [ceil(max_batch / 64)][max(n, k_pad, m)]
     dbf::DecodePlan plan{};   // one-add-per-sign decode kernels (batch 5..16)
     struct LutPlan {
         int cw_m, nchunk_m, cw_k, nchunk_k;
@@ -99,9 +96,6 @@ void release(dbf_layer *h) {
     (void)hipFree(h->tickets);
     (void)hipFree(h->v16);
     (void)hipFree(h->t32);
-    (void)hipFree(h->s32);
-    (void)hipFree(h->g32);
-    (void)hipFree(h->h32);
     (void)hipFree(h->red);
     release(h->bwd);
     for (auto &p : h->pending) {
@@ -346,15 +340,12 @@ extern "C" dbf_status_t dbf_pack_ex(int32_t n, int32_t m, int32_t k, const int8_
     const size_t wmax = static_cast<size_t>(std::max({h->n, h->k_pad, h->m}));
     const size_t nchunk = (mb + dbf::kColChunk - 1) / dbf::kColChunk;
     if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->t32), 4 * mb * h->k_pad);
-    if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->s32), 4 * mb * h->n);
-    if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->g32), 4 * mb * h->k_pad);
-    if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->h32), 4 * mb * h->m);
     if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->red), 4 * nchunk * wmax);
     if (st != DBF_OK) {
         release(h);
         return st;
     }
-    h->workspace_bytes += 4 * mb * (2 * size_t(h->k_pad) + h->n + h->m) + 4 * nchunk * wmax;
+    h->workspace_bytes += 4 * mb * size_t(h->k_pad) + 4 * nchunk * wmax;
     h->packed_bytes += h->bwd->packed_bytes;
     *out = h;
     return DBF_OK;
@@ -458,13 +449,13 @@ static dbf_status_t forward_prefill(dbf_layer *h, const void *x, void *y, int32_
     // T = rne16(mid ⊙ (X (B ⊙ b)ᵀ)), all k_pad columns (padded ones are 0).
     dbf_status_t st = timed_launch(h, "prefill_gemm1", stream, [&] {
         return dbf::launch_sign_gemm(x, h->m, batch, h->m, h->B_dev, h->Wm, h->k_pad, h->b_dev, h->mid_dev, h->T,
-                                     h->k_pad, h->k_pad, nullptr, 0, stream);
+                                     h->k_pad, h->k_pad, nullptr, 0, nullptr, 0, 0, nullptr, stream);
     });
     if (st != DBF_OK) return st;
     // Y = rne16(a ⊙ (T Aᵀ)).
     return timed_launch(h, "prefill_gemm2", stream, [&] {
         return dbf::launch_sign_gemm(h->T, h->k_pad, batch, h->k_pad, h->A_dev, h->Wk, h->n_pad, nullptr,
-                                     h->a_dev, y, h->n, h->n, nullptr, 0, stream);
+                                     h->a_dev, y, h->n, h->n, nullptr, 0, nullptr, 0, 0, nullptr, stream);
     });
 }
 
@@ -545,51 +536,47 @@ extern "C" dbf_status_t dbf_linear_backward(dbf_handle_t h, const void *x, const
     if (cur != h->device) return DBF_ERR_INVALID_ARG;
     dbf_layer *t = h->bwd;
     dbf_status_t st = DBF_OK;
-    auto colsum = [&](const char *name, const void *P, int pf, int ldp, const void *Q, int qf, int ldq, int cols,
-                      float *out) {
-        st = timed_launch(h, name, stream, [&] {
-            return dbf::launch_colsum_chunks(P, pf, ldp, Q, qf, ldq, batch, cols, h->red, stream);
-        });
-        if (st == DBF_OK)
-            st = timed_launch(h, "grad_colsum_finish", stream,
-                              [&] { return dbf::launch_colsum_finish(h->red, batch, cols, out, stream); });
+    auto finish = [&](int ld, int cols, float *out) {
+        return timed_launch(h, "grad_sum_finish", stream,
+                            [&] { return dbf::launch_colsum_finish(h->red, ld, batch, cols, out, stream); });
     };
     if (da || dmid) {
         // t = (X ⊙ b) Bᵀ in fp32 (for dmid) and T = rne16(t ⊙ mid) (for s), one product
         st = timed_launch(h, "grad_t", stream, [&] {
             return dbf::launch_sign_gemm(x, h->m, batch, h->m, h->B_dev, h->Wm, h->k_pad, h->b_dev, h->mid_dev, h->T,
-                                         h->k_pad, h->k_pad, dmid ? h->t32 : nullptr, h->k_pad, stream);
+                                         h->k_pad, h->k_pad, dmid ? h->t32 : nullptr, h->k_pad, nullptr, 0, 0,
+                                         nullptr, stream);
         });
         if (st != DBF_OK) return st;
     }
     if (da) {
-        // s = T Aᵀ (fp32, before a); da = Σ_r dY ⊙ s
+        // s = T Aᵀ (before a), summed against dY over the batch in the epilogue: da = Σ_r dY ⊙ s
         st = timed_launch(h, "grad_s", stream, [&] {
             return dbf::launch_sign_gemm(h->T, h->k_pad, batch, h->k_pad, h->A_dev, h->Wk, h->n_pad, nullptr, nullptr,
-                                         nullptr, 0, h->n, h->s32, h->n, stream);
+                                         nullptr, 0, h->n, nullptr, 0, dy, 0, h->n, h->red, stream);
         });
-        if (st == DBF_OK) colsum("grad_colsum_a", dy, 0, h->n, h->s32, 1, h->n, h->n, da);
+        if (st == DBF_OK) st = finish(h->n, h->n, da);
         if (st != DBF_OK) return st;
     }
     if (dmid || db || dx) {
-        // g = (dY ⊙ a) A in fp32 (for dmid) and G = rne16(g ⊙ mid); the transposed layer holds Aᵀ packed along n
-        // and a as its input scale
+        // g = (dY ⊙ a) A (the transposed layer holds Aᵀ packed along n and a as its input scale),
+        // G = rne16(g ⊙ mid); dmid = Σ_r g ⊙ t in the epilogue
         st = timed_launch(h, "grad_g", stream, [&] {
             return dbf::launch_sign_gemm(dy, h->n, batch, h->n, t->B_dev, t->Wm, t->k_pad, t->b_dev, t->mid_dev, t->T,
-                                         t->k_pad, t->k_pad, dmid ? h->g32 : nullptr, h->k_pad, stream);
+                                         t->k_pad, t->k_pad, nullptr, 0, h->t32, 1, h->k_pad,
+                                         dmid ? h->red : nullptr, stream);
         });
-        if (st != DBF_OK) return st;
-        if (dmid) colsum("grad_colsum_mid", h->g32, 1, h->k_pad, h->t32, 1, h->k_pad, h->k, dmid);
+        if (st == DBF_OK && dmid) st = finish(t->k_pad, h->k, dmid);  // the first k of the k_pad columns
         if (st != DBF_OK) return st;
     }
     if (db || dx) {
-        // h = G B in fp32 (for db; Bᵀ packed along k in the transposed layer), dX = rne16(h ⊙ b)
+        // h = G B (Bᵀ packed along k in the transposed layer), dX = rne16(h ⊙ b), db = Σ_r h ⊙ X in the epilogue
         st = timed_launch(h, "grad_h", stream, [&] {
             return dbf::launch_sign_gemm(t->T, t->k_pad, batch, t->k_pad, t->A_dev, t->Wk, t->n_pad, nullptr,
-                                         t->a_dev, dx, h->m, h->m, db ? h->h32 : nullptr, h->m, stream);
+                                         t->a_dev, dx, h->m, h->m, nullptr, 0, x, 0, h->m, db ? h->red : nullptr,
+                                         stream);
         });
-        if (st != DBF_OK) return st;
-        if (db) colsum("grad_colsum_b", h->h32, 1, h->m, x, 0, h->m, h->m, db);
+        if (st == DBF_OK && db) st = finish(h->m, h->m, db);
     }
     return st;
 }
