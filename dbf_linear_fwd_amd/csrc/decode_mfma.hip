@@ -165,25 +165,49 @@ __device__ __forceinline__ void round_mma(f32x4 (&acc)[Acc<NB>::N][RT], const ui
     const int r = (li & 7) < NB ? (li & 7) : NB - 1;
     const _Float16 *arow0 = kShared ? act + ((li < 8 ? 0 : NB) + r) * KR : act + (li < NB ? li : NB - 1) * KR;
     const _Float16 *arow1 = kShared ? arow0 : act + (NB + (li < NB ? li : NB - 1)) * KR;
-    for (int p = pr0 + wave; p < pr1; p += kNW) {
-        const int pl = p - pr0;
+    // operands of one word pair from LDS
+    struct PairOps {
         uint2 w[RT];
+        f16x8 v0[2], v1[2];
+    };
+    auto load_pair = [&](int p, PairOps &o) {
+        const int pl = p - pr0;
 #pragma unroll
-        for (int t = 0; t < RT; ++t) w[t] = *reinterpret_cast<const uint2 *>(sgn + (pl * 16 * RT + 16 * t + li) * 2);
+        for (int t = 0; t < RT; ++t) o.w[t] = *reinterpret_cast<const uint2 *>(sgn + (pl * 16 * RT + 16 * t + li) * 2);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int e = 64 * pl + 32 * h + 8 * g;
-            const f16x8 v0 = *reinterpret_cast<const f16x8 *>(arow0 + e);
-            f16x8 v1 = v0;
-            if (!kShared) v1 = *reinterpret_cast<const f16x8 *>(arow1 + e);
+            o.v0[h] = *reinterpret_cast<const f16x8 *>(arow0 + e);
+            o.v1[h] = kShared ? o.v0[h] : *reinterpret_cast<const f16x8 *>(arow1 + e);
+        }
+    };
+    auto mma_pair = [&](const PairOps &o) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int t = 0; t < RT; ++t) {
-                const f16x8 sv = expand_pm1(h ? w[t].y : w[t].x, g, ec.mask, ec.one);
-                acc[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sv, v0, acc[0][t], 0, 0, 0);
+                const f16x8 sv = expand_pm1(h ? o.w[t].y : o.w[t].x, g, ec.mask, ec.one);
+                acc[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sv, o.v0[h], acc[0][t], 0, 0, 0);
                 if (!kShared)
-                    acc[Acc<NB>::N - 1][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sv, v1, acc[Acc<NB>::N - 1][t], 0, 0, 0);
+                    acc[Acc<NB>::N - 1][t] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_f16(sv, o.v1[h], acc[Acc<NB>::N - 1][t], 0, 0, 0);
             }
-        }
+    };
+    // two pairs per iteration: the LDS reads of both are issued before
+    // either's MFMAs, so their latencies overlap (the pairs are still summed
+    // in increasing order)
+    int p = pr0 + wave;
+    for (; p + kNW < pr1; p += 2 * kNW) {
+        PairOps o0, o1;
+        load_pair(p, o0);
+        load_pair(p + kNW, o1);
+        mma_pair(o0);
+        mma_pair(o1);
+    }
+    if (p < pr1) {
+        PairOps o0;
+        load_pair(p, o0);
+        mma_pair(o0);
     }
 }
 
