@@ -345,10 +345,24 @@ def test_error_paths_on_gpu(gpu):
         H.close()
 
 
+def _warm_library(L, flags=0):
+    """One pack, forward and free, so that the runtime's one-time set-up on
+    the library's first allocation and launch (code objects, heaps) is not
+    counted as a leak by a test that compares free device memory."""
+    torch = _torch()
+    h = dbf.Layer(L.A, L.B, L.a, L.mid, L.b, max_batch=64, backward=bool(flags))
+    x = torch.zeros((64, L.m), dtype=torch.float16, device="cuda")
+    h.forward(x[:1])
+    h.forward(x)
+    torch.cuda.synchronize()
+    h.close()
+    torch.cuda.synchronize()
+
+
 def test_injected_allocation_failure_leaks_nothing(gpu):
     torch = _torch()
     L = inputs.random_layer("o", 512, 512, 256, 3, 0.05, 1.0, 0.05, (1,))
-    torch.cuda.synchronize()
+    _warm_library(L)
     free0 = torch.cuda.mem_get_info()[0]
     try:
         for nth in range(1, 11):
@@ -600,5 +614,97 @@ def test_backward_full_size_projection(gpu):
             err = _vec_rel(got, ref)
             _say(f"  {name} rel err {err:.3e}")
             assert err <= TOL, f"{name}: rel err {err:.3e}"
+    finally:
+        H.close()
+
+
+def test_backward_pack_allocation_failures_leak_nothing(gpu):
+    """dbf_pack_ex with DBF_PACK_BACKWARD: a failure at any of its device
+    allocations (the layer's, the transposed layer's, the gradient workspace)
+    returns DBF_ERR_OOM and frees everything already allocated."""
+    torch = _torch()
+    L = inputs.random_layer("ob", 300, 200, 130, 3, 0.05, 1.0, 0.05, (1,))
+    _warm_library(L, dbf.DBF_PACK_BACKWARD)
+    free0 = torch.cuda.mem_get_info()[0]
+    try:
+        n_alloc = 22   # 10 for the layer, 10 for the transposed layer, t and the batch-sum partials
+        for nth in range(1, n_alloc + 1):
+            _say(f"backward pack: inject allocation failure #{nth}")
+            os.environ["DBF_TEST_FAIL_ALLOC"] = str(nth)
+            with pytest.raises(dbf.DbfError) as e:
+                dbf.dbf_pack(L.n, L.m, L.k, L.A, L.B, L.a, L.mid, L.b, 64, dbf.DBF_PACK_BACKWARD)
+            assert e.value.status == dbf.DBF_ERR_OOM
+        os.environ["DBF_TEST_FAIL_ALLOC"] = str(n_alloc + 1)
+        h = dbf.dbf_pack(L.n, L.m, L.k, L.A, L.B, L.a, L.mid, L.b, 64, dbf.DBF_PACK_BACKWARD)
+        info = dbf.dbf_get_info(h)
+        assert info["workspace_bytes"] > 0 and info["packed_bytes"] > 0
+        dbf.dbf_free(h)
+    finally:
+        os.environ.pop("DBF_TEST_FAIL_ALLOC", None)
+    torch.cuda.synchronize()
+    free1 = torch.cuda.mem_get_info()[0]
+    assert abs(free1 - free0) < (8 << 20), (free0, free1)
+
+
+def test_graph_replay_of_prefill_and_backward(gpu):
+    """Prefill forwards and gradient calls captured in a HIP graph and
+    replayed several times, with eager work between the replays, give the
+    eager results every time."""
+    torch = _torch()
+    n, m, k, bt = 320, 256, 192, 96
+    X, A, B, a, mid, b = inputs.tiny_case(515, n, m, k, bt, signed_scales=True)
+    dY = np.random.default_rng(9).uniform(-2, 2, (bt, n)).astype(np.float16)
+    H = dbf.Layer(A, B, a, mid, b, max_batch=bt, backward=True)
+    try:
+        _say("graph replay prefill + backward")
+        x = torch.from_numpy(X).cuda()
+        dy = torch.from_numpy(dY).cuda()
+        want_y = H.forward(x).cpu().numpy()
+        want_g = [t.cpu().numpy() for t in H.backward(x, dy)]
+        y = torch.empty((bt, n), dtype=torch.float16, device="cuda")
+        dx = torch.empty((bt, m), dtype=torch.float16, device="cuda")
+        da = torch.empty(n, dtype=torch.float32, device="cuda")
+        dmid = torch.empty(k, dtype=torch.float32, device="cuda")
+        db = torch.empty(m, dtype=torch.float32, device="cuda")
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                H.forward(x, out=y)
+                dbf.dbf_linear_backward(H.handle, x.data_ptr(), dy.data_ptr(), dx.data_ptr(), da.data_ptr(),
+                                        dmid.data_ptr(), db.data_ptr(), bt, s.cuda_stream)
+        torch.cuda.current_stream().wait_stream(s)
+        for rep in range(4):
+            for t in (y, dx):
+                t.fill_(3.0)
+            for t in (da, dmid, db):
+                t.fill_(3.0)
+            g.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(y.cpu().numpy().view(np.uint16), want_y.view(np.uint16)), rep
+            for got, want in zip((dx, da, dmid, db), want_g):
+                assert np.array_equal(got.cpu().numpy().view(np.uint8), want.view(np.uint8)), rep
+            H.forward(x)   # eager work between replays
+            torch.cuda.synchronize()
+    finally:
+        H.close()
+
+
+def test_non_default_stream(gpu):
+    """Forwards enqueued on a side stream give the default-stream results."""
+    torch = _torch()
+    L = inputs.random_layer("st", 500, 400, 300, 12, 0.05, 1.0, 0.05, (1, 7, 64))
+    H = dbf.Layer(L.A, L.B, L.a, L.mid, L.b, max_batch=64)
+    try:
+        _say("side stream")
+        for bt in (1, 7, 64):
+            x = torch.from_numpy(L.X[bt]).cuda()
+            want = H.forward(x).cpu().numpy()
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                y = H.forward(x)
+            s.synchronize()
+            assert np.array_equal(y.cpu().numpy().view(np.uint16), want.view(np.uint16)), bt
     finally:
         H.close()
