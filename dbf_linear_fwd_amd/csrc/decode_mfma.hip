@@ -5,14 +5,18 @@
 // run here as 16x16x32 f16 MFMA products: the sign matrix is the A operand,
 // expanded from its bits to ±1.0 in registers, and the activations are the B
 // operand with the batch as the (at most 16 wide) N dimension.
+// Batch 1..8:
 //   stage 1: u = x ⊙ b is formed in fp32 (exact: a product of two fp16) and
 //            split into u_hi = rne16(u) and u_lo = rne16(u - u_hi), which
 //            carry about 22 significant bits; t = B u_hi + B u_lo in fp32;
 //            the epilogue forms v = t * mid and stores it the same way, as
 //            fp16 planes v_hi, v_lo.
 //   stage 2: s = A v_hi + A v_lo in fp32; y = rne16(s * a).
-// For batch <= 8 the hi and lo parts ride in columns r and r + 8 of one
-// MFMA; for batch 9..16 they take two MFMAs.
+//   The hi and lo parts ride in columns r and r + 8 of one MFMA.
+// Batch 9..16 (the 16 columns are all batch rows): the sign operand of
+// stage 1 carries ±b (b's fp16 sign bit flipped, exact), so x enters the
+// product as it is and t = (B ⊙ b) x; v = rne16(t * mid) is one fp16 plane
+// and s = A v -- the numerics of the prefill path.
 //
 // Work split.  A workgroup of 8 waves owns 16*RT rows of the sign matrix and
 // its whole reduction dimension, taken in rounds that fit LDS (one round for
@@ -77,6 +81,17 @@ __device__ __forceinline__ f16x8 expand_pm1(uint32_t word, int g, uint32_t mask,
     return __builtin_bit_cast(f16x8, r);
 }
 
+// Halves 8g..8g+7 of a sign word as the operand ±sc (scale pairs sc[p],
+// single-plane stage 1: ±b, exact): each sign pair is XORed onto the fp16
+// sign bits of its scale pair.
+__device__ __forceinline__ f16x8 expand_scaled(uint32_t word, int g, const u32x4 &sc, uint32_t mask) {
+    const uint32_t sh = word << (12 - 4 * g);
+    u32x4 r;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) r[p] = sc[p] ^ ((sh << (3 - p)) & mask);
+    return __builtin_bit_cast(f16x8, r);
+}
+
 // The two constants of expand_pm1 as register values the compiler cannot
 // fold back into literals: the sign mask in a scalar register, +1.0 pair in
 // a vector register.  Called once at kernel entry, before any MFMA has been
@@ -94,22 +109,34 @@ __device__ __forceinline__ ExpandConsts expand_consts() {
 
 __device__ __forceinline__ f16x8 zero8() { return __builtin_bit_cast(f16x8, u32x4{0u, 0u, 0u, 0u}); }
 
+// Operand forms by batch size:
+//   NB <= 8  : hi and lo fp16 planes of u = x ⊙ b (stage 1) and v (stage 2)
+//              ride in columns r and r + 8 of one MFMA (kShared);
+//   NB 9..16 : one plane (kSP): stage 1 multiplies x itself, with b folded
+//              into the expanded signs as ±b (exact, as on the prefill
+//              path), and stage 2 multiplies v rounded once to fp16; one
+//              MFMA per sign fragment with the batch rows as its columns.
 template <int NB>
 struct Acc {
-    static constexpr bool kShared = NB <= 8;  // hi and lo in one MFMA (columns r and r + 8)
-    static constexpr int N = kShared ? 1 : 2;
+    static constexpr bool kShared = NB <= 8;
+    static constexpr bool kSP = NB > 8;
+    static constexpr int N = 1;
+    // activation bytes per word pair in LDS: 2 planes x NB rows x 64 halves;
+    // single plane: NB rows + one row of b (stage 1)
+    static constexpr int kActPair = kSP ? 128 * NB + 128 : 256 * NB;
 };
 
 // LDS layout of one round of PR pairs:
 //   signs  [PR][16*RT rows][2 words]           PR * 128 * RT bytes
 //   planes [2][NB][64*PR] fp16 (hi, lo)         PR * 256 * NB bytes
+//          (single plane: [NB + 1][64*PR], the last row b)
 // and, after the last round, over the same bytes:
 //   reduce [Acc::N][kNW][RT][64 lanes][4] fp32  Acc::N * kNW * RT * 1 KiB
 // followed by kLdsTail bytes for workgroup-wide scalars.
 constexpr size_t kLdsTail = 64;
 template <int NB, int RT>
 __host__ __device__ constexpr size_t lds_round_bytes(int PR) {
-    return static_cast<size_t>(PR) * (128 * RT + 256 * NB);
+    return static_cast<size_t>(PR) * (128 * RT + Acc<NB>::kActPair);
 }
 template <int NB, int RT>
 __host__ __device__ constexpr size_t lds_reduce_bytes() {
@@ -125,7 +152,7 @@ __host__ __device__ constexpr size_t lds_bytes(int PR) {
 // Pairs per round that fit the LDS budget.
 template <int NB, int RT>
 int round_pairs() {
-    return static_cast<int>((kLdsBudget - kLdsTail) / (128 * RT + 256 * NB));
+    return static_cast<int>((kLdsBudget - kLdsTail) / (128 * RT + Acc<NB>::kActPair));
 }
 
 // Issue the loads of this thread's 16-byte sign items of the round, items
@@ -155,20 +182,22 @@ __device__ __forceinline__ void store_sign_items(const u32x4 (&v)[kMaxItems], ui
 }
 
 // One round: pairs [pr0, pr1) of rows r0..r0+16RT-1 from the LDS copies.
-template <int NB, int RT>
+template <int NB, int RT, bool STAGE1>
 __device__ __forceinline__ void round_mma(f32x4 (&acc)[Acc<NB>::N][RT], const uint32_t *sgn, const _Float16 *act,
                                           int KR, int pr0, int pr1, int wave, int li, int g, ExpandConsts ec) {
     constexpr bool kShared = Acc<NB>::kShared;
+    constexpr bool kSP = Acc<NB>::kSP;
     // Activation rows this lane feeds.  Column c of the B operand only
     // reaches output column c, so lanes of unused columns simply repeat a
     // valid row (no branches, no zeroing); those outputs are never read.
     const int r = (li & 7) < NB ? (li & 7) : NB - 1;
     const _Float16 *arow0 = kShared ? act + ((li < 8 ? 0 : NB) + r) * KR : act + (li < NB ? li : NB - 1) * KR;
-    const _Float16 *arow1 = kShared ? arow0 : act + (NB + (li < NB ? li : NB - 1)) * KR;
+    const _Float16 *brow = act + NB * KR;  // single plane, stage 1: the b row
     // operands of one word pair from LDS
     struct PairOps {
         uint2 w[RT];
-        f16x8 v0[2], v1[2];
+        f16x8 v0[2];
+        u32x4 sc[2];  // single-plane stage 1: b of the lane's 8 elements
     };
     auto load_pair = [&](int p, PairOps &o) {
         const int pl = p - pr0;
@@ -178,7 +207,7 @@ __device__ __forceinline__ void round_mma(f32x4 (&acc)[Acc<NB>::N][RT], const ui
         for (int h = 0; h < 2; ++h) {
             const int e = 64 * pl + 32 * h + 8 * g;
             o.v0[h] = *reinterpret_cast<const f16x8 *>(arow0 + e);
-            o.v1[h] = kShared ? o.v0[h] : *reinterpret_cast<const f16x8 *>(arow1 + e);
+            if constexpr (kSP && STAGE1) o.sc[h] = *reinterpret_cast<const u32x4 *>(brow + e);
         }
     };
     auto mma_pair = [&](const PairOps &o) {
@@ -186,11 +215,10 @@ __device__ __forceinline__ void round_mma(f32x4 (&acc)[Acc<NB>::N][RT], const ui
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int t = 0; t < RT; ++t) {
-                const f16x8 sv = expand_pm1(h ? o.w[t].y : o.w[t].x, g, ec.mask, ec.one);
+                f16x8 sv;
+                if constexpr (kSP && STAGE1) sv = expand_scaled(h ? o.w[t].y : o.w[t].x, g, o.sc[h], ec.mask);
+                else sv = expand_pm1(h ? o.w[t].y : o.w[t].x, g, ec.mask, ec.one);
                 acc[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sv, o.v0[h], acc[0][t], 0, 0, 0);
-                if (!kShared)
-                    acc[Acc<NB>::N - 1][t] =
-                        __builtin_amdgcn_mfma_f32_16x16x32_f16(sv, o.v1[h], acc[Acc<NB>::N - 1][t], 0, 0, 0);
             }
     };
     // two pairs per iteration: the LDS reads of both are issued before
@@ -238,13 +266,13 @@ __device__ __forceinline__ void reduce_waves(const f32x4 (&acc)[Acc<NB>::N][RT],
 template <int NB, int RT>
 __device__ __forceinline__ f32x4 total(const float *red, int t, int lane) {
     const f32x4 dh = *reinterpret_cast<const f32x4 *>(&red[t * 256 + lane * 4]);
-    const f32x4 dl = Acc<NB>::kShared ? *reinterpret_cast<const f32x4 *>(&red[t * 256 + (lane + 8) * 4])
-                                      : *reinterpret_cast<const f32x4 *>(&red[(kNW * RT + t) * 256 + lane * 4]);
+    if constexpr (Acc<NB>::kSP) return dh;
+    const f32x4 dl = *reinterpret_cast<const f32x4 *>(&red[t * 256 + (lane + 8) * 4]);
     return dh + dl;
 }
 
 // Stage 1 for row block `blk` (rows 16*RT*blk ..): v = mid * (B (x ⊙ b)),
-// stored as fp16 hi/lo planes [2][NB][k_pad].
+// stored as fp16 hi/lo planes [2][NB][k_pad] (single plane: [NB][k_pad]).
 template <int NB, int RT>
 __device__ __forceinline__ void stage1_body(int blk, char *base, const uint32_t *__restrict__ Bt, int Wm,
                                             const __half *__restrict__ x, int m, const __half *__restrict__ b,
@@ -315,6 +343,20 @@ __device__ __forceinline__ void stage1_body(int blk, char *base, const uint32_t 
                 }
             }
             store_sign_items(v, sgn, nitems, item0);
+            if constexpr (Acc<NB>::kSP) {
+                // x as it is (b goes into the signs); row 0's items also store b
+#pragma unroll
+                for (int q = 0; q < kMaxAct; ++q) {
+                    const int it = act0 + threadIdx.x + kThreads * q;
+                    if (it < nact) {
+                        const int r = it / per_row;
+                        const int e = (it - r * per_row) * 8;
+                        *reinterpret_cast<f16x8 *>(act + r * KR + e) = xv[q];
+                        if (r == 0) *reinterpret_cast<f16x8 *>(act + NB * KR + e) = bv[q];
+                    }
+                }
+                continue;
+            }
             // u = x ⊙ b (exact in fp32) as hi/lo planes
 #pragma unroll
             for (int q = 0; q < kMaxAct; ++q) {
@@ -335,7 +377,7 @@ __device__ __forceinline__ void stage1_body(int blk, char *base, const uint32_t 
             }
         }
         __syncthreads();
-        round_mma<NB, RT>(acc, sgn, act, KR, pr0, pr1, wave, li, g, ec);
+        round_mma<NB, RT, true>(acc, sgn, act, KR, pr0, pr1, wave, li, g, ec);
     }
 
     reduce_waves<NB, RT>(acc, red, wave, lane);
@@ -353,12 +395,13 @@ __device__ __forceinline__ void stage1_body(int blk, char *base, const uint32_t 
                 lo[v] = static_cast<_Float16>(val - static_cast<float>(hi[v]));
             }
             *reinterpret_cast<f16x4 *>(v16 + static_cast<size_t>(li) * k_pad + row0) = hi;
-            *reinterpret_cast<f16x4 *>(v16 + static_cast<size_t>(NB + li) * k_pad + row0) = lo;
+            if constexpr (!Acc<NB>::kSP)
+                *reinterpret_cast<f16x4 *>(v16 + static_cast<size_t>(NB + li) * k_pad + row0) = lo;
         }
     }
 }
 
-// Stage 2 for row block `blk`: y = rne16(a ⊙ (A (v_hi + v_lo))).
+// Stage 2 for row block `blk`: y = rne16(a ⊙ (A (v_hi + v_lo))) (single plane: A v).
 template <int NB, int RT>
 __device__ __forceinline__ void stage2_body(int blk, char *base, const uint32_t *__restrict__ At, int Wk,
                                             const __half *__restrict__ v16, int k_pad, const __half *__restrict__ a,
@@ -395,7 +438,8 @@ __device__ __forceinline__ void stage2_body(int blk, char *base, const uint32_t 
         const int nitems = (pr1 - pr0) * 8 * RT;
         if (pr0 > 0) __syncthreads();
         const int k0 = 64 * pr0, len = 64 * (pr1 - pr0);
-        const int nact = 2 * NB * (len >> 3);  // 16-byte plane items: hi rows then lo rows
+        // 16-byte plane items: hi rows then lo rows (one plane of NB rows in the single-plane form)
+        const int nact = (Acc<NB>::kSP ? 1 : 2) * NB * (len >> 3);
         const int per_row = len >> 3;
         // all loads of a batch (sign items, v_hi / v_lo items) are issued first
         for (int item0 = 0, act0 = 0; item0 < nitems || act0 < nact;
@@ -422,7 +466,7 @@ __device__ __forceinline__ void stage2_body(int blk, char *base, const uint32_t 
             }
         }
         __syncthreads();
-        round_mma<NB, RT>(acc, sgn, act, KR, pr0, pr1, wave, li, g, ec);
+        round_mma<NB, RT, false>(acc, sgn, act, KR, pr0, pr1, wave, li, g, ec);
     }
 
     reduce_waves<NB, RT>(acc, red, wave, lane);
@@ -567,16 +611,12 @@ void allow_lds(K kernel, size_t bytes) {
 }
 
 // Rows per workgroup: 16, 32 or 64, the smallest that keeps the grid within
-// one workgroup per CU of the 256-CU MI355X (batch <= 4; larger use 16).
-template <int NB>
+// one workgroup per CU of the 256-CU MI355X.  Every workgroup stages the
+// whole activation block, so fewer, taller workgroups also cut that traffic.
 int split_rt(int rows) {
-    if constexpr (NB <= 4) {
-        if (rows / 16 <= DBF_DECODE_ONE_ROUND) return 1;
-        if (rows / 32 <= DBF_DECODE_ONE_ROUND) return 2;
-        return 4;
-    } else {
-        return 1;
-    }
+    if (rows / 16 <= DBF_DECODE_ONE_ROUND) return 1;
+    if (rows / 32 <= DBF_DECODE_ONE_ROUND) return 2;
+    return 4;
 }
 
 template <int NB, int RT>
@@ -590,7 +630,7 @@ int launch_rt(const MfmaDecodeArgs &d, hipStream_t s, int which) {
         Stage2Readahead ra{};
         ra.A = reinterpret_cast<const uint4 *>(d.A_dev);
         ra.pairs = d.k_pad / 64;
-        const int rt2 = split_rt<NB>(d.n_pad);
+        const int rt2 = split_rt(d.n_pad);
         ra.rows_per_wg = 16 * rt2;
         ra.groups = d.n_pad / (16 * rt2);
         // the read-ahead blocks take the CUs stage 1 leaves free, if there are
@@ -618,11 +658,9 @@ int launch_rt(const MfmaDecodeArgs &d, hipStream_t s, int which) {
 
 template <int NB>
 int launch_nb(const MfmaDecodeArgs &d, hipStream_t s, int which) {
-    const int rt = split_rt<NB>(which == 1 ? d.k_pad : d.n_pad);
-    if constexpr (NB <= 4) {
-        if (rt == 2) return launch_rt<NB, 2>(d, s, which);
-        if (rt == 4) return launch_rt<NB, 4>(d, s, which);
-    }
+    const int rt = split_rt(which == 1 ? d.k_pad : d.n_pad);
+    if (rt == 2) return launch_rt<NB, 2>(d, s, which);
+    if (rt == 4) return launch_rt<NB, 4>(d, s, which);
     return launch_rt<NB, 1>(d, s, which);
 }
 
@@ -669,11 +707,9 @@ template <int NB>
 int launch_group_nb(const MfmaGroupArgs &g, hipStream_t s, int which) {
     int rows = 0;
     for (int i = 0; i < g.count; ++i) rows += which == 1 ? g.L[i].k_pad : g.L[i].n_pad;
-    const int rt = split_rt<NB>(rows);
-    if constexpr (NB <= 4) {
-        if (rt == 2) return launch_group_rt<NB, 2>(g, s, which);
-        if (rt == 4) return launch_group_rt<NB, 4>(g, s, which);
-    }
+    const int rt = split_rt(rows);
+    if (rt == 2) return launch_group_rt<NB, 2>(g, s, which);
+    if (rt == 4) return launch_group_rt<NB, 4>(g, s, which);
     return launch_group_rt<NB, 1>(g, s, which);
 }
 

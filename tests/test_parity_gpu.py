@@ -81,9 +81,15 @@ def assert_bits(y16, ref64, what):
                            f"got {y16[tuple(bad[0])]} want {want[tuple(bad[0])]}")
 
 
+def fp16_intermediate(path, batch) -> bool:
+    """Whether the path rounds v = mid * t to fp16 once (prefill, and the
+    matrix-core decode at batch 9..16) instead of keeping it as hi/lo planes."""
+    return path == dbf.DBF_PATH_PREFILL or (path == dbf.DBF_PATH_DECODE and batch > 8)
+
+
 def integer_preconditions(layer, X, prefill: bool):
     """The realized data keep every partial sum an exact integer in fp32 and
-    (for the matrix-core path) the fp16 intermediate exact."""
+    (where the path rounds it to fp16: `prefill`) the intermediate v exact."""
     u, t, v, s, y = O.factored_intermediate(X, layer.A, layer.B, layer.a, layer.mid, layer.b)
     m, k = layer.m, layer.k
     assert np.all(np.abs(u) <= 4) and np.abs(t).max() + np.abs(u).sum(axis=1).max() < 2 ** 24
@@ -131,11 +137,13 @@ ROW_TILE_SHAPES = [
     (4160, 96, 64),     # stage 2: 32-row workgroups
     (70, 100, 8256),    # stage 1: 64-row workgroups
     (8256, 130, 200),   # stage 2: 64-row workgroups, ragged n
+    (70, 100, 16448),   # stage 1: more 64-row blocks (257) than CUs, so no read-ahead blocks
 ]
 
 
 @pytest.mark.parametrize("n,m,k", ROW_TILE_SHAPES)
-@pytest.mark.parametrize("batch", [1, 4, 9])   # 9: 16-row blocks, more stage-1 blocks than CUs (k >= 4160)
+# 1..8: hi/lo planes in one MFMA; 9: the single-plane form
+@pytest.mark.parametrize("batch", [1, 6, 9])
 def test_decode_row_tile_variants(gpu, n, m, k, batch):
     _say(f"decode row tiles n={n} m={m} k={k} batch={batch}")
     X, A, B, a, mid, b = inputs.tiny_case(3000 + n + m + k + batch, n, m, k, batch, signed_scales=True)
@@ -172,7 +180,7 @@ def test_integer_bit_exact_small(gpu, n, m, k, batch, path):
     L = inputs.integer_layer("i", n, m, k, 77 + n, (batch,), a_vals=(0.5, 1.0), mid_vals=(1.0, 2.0),
                              b_vals=(1.0, 2.0))
     X = L.X[batch]
-    integer_preconditions(L, X, prefill=path == dbf.DBF_PATH_PREFILL)
+    integer_preconditions(L, X, prefill=fp16_intermediate(path, batch))
     y = run(L, X, path)
     assert_bits(y, O.factored_forward(X, L.A, L.B, L.a, L.mid, L.b), f"integer {n}x{m}x{k}")
 
@@ -200,7 +208,7 @@ def test_integer_bit_exact_full_size(gpu, name, n, m, k, vals, batch, path):
     rows = np.arange(batch) if batch <= 16 else np.random.default_rng(1).choice(batch, 12, replace=False)
     ref = O.sampled_forward(X, L.A, L.B, L.a, L.mid, L.b, rows, np.arange(n))
     assert np.abs(ref).max() <= 65504
-    if path == dbf.DBF_PATH_PREFILL:
+    if fp16_intermediate(path, batch):
         u, t, v, s, y = O.factored_intermediate(X[rows], L.A, L.B, L.a, L.mid, L.b)
         assert np.abs(v).max() <= 2048
     y = run(L, X, path)
@@ -248,12 +256,26 @@ def test_determinism_and_batch_independence(gpu):
             y1 = H.forward(x, path=path).cpu().numpy()
             y2 = H.forward(x, path=path).cpu().numpy()
             assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
+            if path == dbf.DBF_PATH_DECODE:
+                # batch 9..16 share one kernel form (one fp16 plane), and so
+                # do batch 1..8 (hi/lo planes); within a form every output
+                # column is summed in the same order: identical bits
+                y9 = H.forward(x[:9].clone(), path=path).cpu().numpy()
+                assert np.array_equal(y9.view(np.uint16), y1[:9].view(np.uint16))
+                y8 = H.forward(x[:8].clone(), path=path).cpu().numpy()
             for r in (0, 5, bt - 1):
                 yr = H.forward(x[r:r + 1].clone(), path=path).cpu().numpy()
-                if path != dbf.DBF_PATH_DECODE_TABLE:
+                if path == dbf.DBF_PATH_PREFILL:
                     # the same kernel code serves both batch sizes and every
                     # output column is summed in the same order: identical bits
                     assert np.array_equal(yr[0].view(np.uint16), y1[r].view(np.uint16)), f"row {r}"
+                elif path == dbf.DBF_PATH_DECODE:
+                    if r < 8:
+                        assert np.array_equal(yr[0].view(np.uint16), y8[r].view(np.uint16)), f"row {r}"
+                    # batch 1 keeps v to about 22 bits, batch 16 rounds it to
+                    # fp16 once: equal within the parity tolerance
+                    d = np.abs(yr[0].astype(np.float64) - y1[r].astype(np.float64)).max()
+                    assert d <= TOL * np.abs(y1[r].astype(np.float64)).max(), f"row {r}"
                 else:
                     # batch 1 and batch 16 run different table-path kernels
                     # (lookups vs one add per sign): fp32 sums in another order,
