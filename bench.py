@@ -54,6 +54,9 @@ def parse():
                    help="only run a plain device copy of this size (counter scaling) and exit")
     p.add_argument("--no-block", action="store_true", help="skip the decoder-block measurement")
     p.add_argument("--no-backward", action="store_true", help="skip the gradient measurement")
+    p.add_argument("--all-configs", action="store_true",
+                   help="instead of the headline line: one JSON line per workload layer and batch "
+                        "(decode at batch 1 and 16, prefill at batch 2048)")
     p.add_argument("--only", choices=("decode", "prefill", "block", "backward"), default=None,
                    help="run one leg only (for profiling)")
     p.add_argument("--decode-path", choices=("mfma", "table"), default="mfma",
@@ -265,6 +268,64 @@ def backward_leg():
                                        "(dX, da, dmid, db)"}
 
 
+def all_configs(args):
+    """Every layer of the five workloads: decode (batch 1 and 16, weights
+    rotated over >= rotate-mb of copies, graph replay) and prefill (batch
+    2048).  One JSON line each."""
+    import torch
+
+    import dbf_linear_fwd_amd as dbf
+    from tests import inputs
+
+    for cid in inputs.CONFIG_IDS:
+        cfg = inputs.config(cid)
+        for layer in cfg.layers:
+            bytes_step = layer.sign_bytes + layer.scale_bytes
+            # copies streamed from HBM (at most 256: the 256x256 correctness layer stays cache-resident)
+            R = min(256, max(2, -(-args.rotate_mb * (1 << 20) // bytes_step)))
+            copies = [dbf.Layer(layer.A, layer.B, layer.a, layer.mid, layer.b, max_batch=16) for _ in range(R)]
+            for bt in (1, 16):
+                X = layer.X.get(bt)
+                if X is None:
+                    X = np.random.default_rng(bt).standard_normal((bt, layer.m)).astype(np.float16)
+                x = torch.from_numpy(X).cuda()
+                y = torch.empty((bt, layer.n), dtype=torch.float16, device="cuda")
+
+                def fwd(i):
+                    copies[i % R].forward(x, out=y)
+                fwd.period = R
+                el, done = time_steps(fwd, max(R, min(args.steps, 10 * R)), min(args.warmup, R), "graph")
+                print(json.dumps({"config": cid, "layer": layer.name, "n": layer.n, "m": layer.m, "k": layer.k,
+                                  "batch": bt, "path": "decode", "us_per_forward": el * 1e6 / done,
+                                  "packed_gbs": bytes_step * done / el / 1e9,
+                                  "frac_of_hbm_peak": bytes_step * done / el / 1e9 / HBM_PEAK_GBS,
+                                  "copies": R}), flush=True)
+            for c in copies:
+                c.close()
+            del copies
+            torch.cuda.synchronize()
+            if 2048 in cfg.batches or cid == 3:
+                bt = 2048
+                L = dbf.Layer(layer.A, layer.B, layer.a, layer.mid, layer.b, max_batch=bt)
+                X = layer.X.get(bt)
+                if X is None:
+                    X = np.random.default_rng(bt).standard_normal((bt, layer.m)).astype(np.float16)
+                x = torch.from_numpy(X).cuda()
+                y = torch.empty((bt, layer.n), dtype=torch.float16, device="cuda")
+
+                def pf(i):
+                    L.forward(x, out=y)
+                el, done = time_steps(pf, 30, 5, "eager")
+                flops = 2 * bt * layer.k * (layer.n + layer.m)
+                print(json.dumps({"config": cid, "layer": layer.name, "n": layer.n, "m": layer.m, "k": layer.k,
+                                  "batch": bt, "path": "prefill", "us_per_forward": el * 1e6 / done,
+                                  "tflops_eq": flops * done / el / 1e12,
+                                  "frac_of_mfma_peak": flops * done / el / 1e12 / MFMA_F16_PEAK_TFLOPS}),
+                      flush=True)
+                L.close()
+                torch.cuda.synchronize()
+
+
 def copy_probe(mb):
     import torch
     n = mb * (1 << 20) // 4
@@ -290,6 +351,9 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_probe_mb:
         copy_probe(args.copy_probe_mb)
+        return
+    if args.all_configs:
+        all_configs(args)
         return
 
     result = {}

@@ -138,9 +138,26 @@ inline void launch_kernel(K kernel, dim3 grid, dim3 block, size_t lds, hipStream
 //   of sum * Q[i][c] over each group of 64 rows i (Q fp16 or fp32 as dq_f32,
 //   leading dimension lddq), dpart[(i / 64) * n_out + c], to be finished by
 //   launch_colsum_finish(dpart, M, n_out, ...).
+//   split (may be null; fp16 output only, no out32 or dpart): where the
+//   grid of output tiles is too small to fill the GPU, the K range is cut
+//   into split->nsplit parts that run as separate workgroups and write
+//   their unscaled fp32 sums to split->ws[s][M][split->ldw]; the caller then
+//   runs launch_split_finish, which adds the parts in order s = 0, 1, ...
+//   and writes out.  split->nsplit is set to 1 when no split was taken.
+struct SplitK {
+    float *ws = nullptr;  // workspace of cap floats
+    size_t cap = 0;
+    int nsplit = 1;       // set by launch_sign_gemm
+    int ldw = 0;
+};
 int launch_sign_gemm(const void *P, int ldp, int M, int K, const uint32_t *S, int words, int n_rows_pad,
                      const void *sk, const void *sn, void *out, int ldo, int n_out, float *out32, int ldo32,
-                     const void *dq, int dq_f32, int lddq, float *dpart, void *stream);
+                     const void *dq, int dq_f32, int lddq, float *dpart, void *stream, SplitK *split = nullptr);
+// Floats of split workspace that launch_sign_gemm would use for this
+// product (0: it would not split), assuming 16-byte aligned rows of P.
+size_t sign_gemm_split_elems(int M, int K, int words, int n_out);
+// out[i][c] = rne16(sn[c] * (ws[0][i][c] + ws[1][i][c] + ...)), i < M, c < n_out.
+int launch_split_finish(const SplitK &split, int M, int n_out, const void *sn, void *out, int ldo, void *stream);
 
 // Batch sums of the gradients: out[c] = sum over g < ceil(rows / 64) of
 // partial[g * ld + c] for c < cols, added in g order (the partials are

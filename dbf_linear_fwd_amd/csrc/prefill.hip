@@ -24,9 +24,17 @@
 // sign_gemm_kernel (any K, any alignment): block 128 x 256, four waves of
 // 64 x 128, P tile staged through registers into a double-buffered LDS tile,
 // signs loaded into registers one step ahead.
+//
+// Split-K: a grid of few tiles (small batch) leaves most CUs idle while each
+// workgroup walks the whole K.  Such grids are cut along K into parts that
+// run as separate workgroups of the DMA kernel and store unscaled fp32 sums;
+// split_finish_kernel adds the parts of each output in part order and
+// applies the epilogue.
 
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
+
+#include <algorithm>
 
 #include "dbf_internal.h"
 
@@ -141,6 +149,46 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[MF_][NF_], const fl
             if (kg == 0 && col < n_out && row0 < M) dot.part[static_cast<size_t>(row0 / 64) * n_out + col] = sum;
         }
     }
+}
+
+// Split-K parts: the unscaled sums of the tile, part[row * ldw + col].
+template <int MF_, int NF_>
+__device__ __forceinline__ void store_partial(const f32x16 (&acc)[MF_][NF_], int M, int n_out, int row0, int col0,
+                                              int l32, int kg, float *__restrict__ part, int ldw) {
+#pragma unroll
+    for (int i = 0; i < MF_; ++i)
+#pragma unroll
+        for (int f = 0; f < NF_; ++f) {
+            const int col = col0 + f * 32 + l32;
+            if (col >= n_out) continue;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = row0 + i * 32 + 8 * (v >> 2) + 4 * kg + (v & 3);
+                if (row < M) part[static_cast<size_t>(row) * ldw + col] = acc[i][f][v];
+            }
+        }
+}
+
+// Sum of the split-K parts in part order, scaled and rounded once: one
+// thread per output, the loads of up to eight parts in flight at a time.
+__global__ __launch_bounds__(256) void split_finish_kernel(const float *__restrict__ part, int nsplit, int M,
+                                                           int n_out, int ldw, const __half *__restrict__ sn,
+                                                           __half *__restrict__ out, int ldo) {
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= M * n_out) return;
+    const int row = idx / n_out, col = idx - row * n_out;
+    const size_t plane = static_cast<size_t>(M) * ldw;
+    const float *p = part + static_cast<size_t>(row) * ldw + col;
+    float s = 0.0f;
+    for (int k0 = 0; k0 < nsplit; k0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = k0 + u < nsplit ? p[(k0 + u) * plane] : 0.0f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (k0 + u < nsplit) s += v[u];
+    }
+    out[static_cast<size_t>(row) * ldo + col] = __float2half_rn(s * __half2float(sn[col]));
 }
 
 // C = P S'ᵀ (see the file comment).  P: fp16 [M][ldp], K valid columns
@@ -427,16 +475,21 @@ __global__ __launch_bounds__(kDThreads) void sign_gemm_dma_kernel(const __half *
                                                                  const __half *__restrict__ sn,
                                                                  __half *__restrict__ out, int ldo, int n_out,
                                                                  float *__restrict__ out32, int ldo32, const DotArgs dot,
-                                                                 int nbm, int nbn) {
+                                                                 int nbm, int nbn, float *__restrict__ part,
+                                                                 int nsplit, int ldw) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     using C = DmaStep<KP>;
     constexpr int D = C::PI + C::SI + (HAS_SK ? 1 : 0);  // loads per step and wave
 
     const ExpandConsts ec = expand_consts();
-    const int G = nbm * nbn;
+    // XCD-aware order over (split, tile), tile fastest: the blocks of one XCD
+    // take consecutive indexes, so they share a K range (and rows of P)
+    const int T = nbm * nbn;
+    const int G = T * nsplit;
     const int b = blockIdx.x;
     const int xcd = b % kXcds, slot = b / kXcds, q = G / kXcds, rem = G % kXcds;
-    const int tile = xcd * q + min(xcd, rem) + slot;
+    const int idx = xcd * q + min(xcd, rem) + slot;
+    const int split = idx / T, tile = idx - split * T;
     const int bm = tile / nbn, bn = tile - (tile / nbn) * nbn;
     const int m0 = bm * BM, n0 = bn * DBN;
 
@@ -444,7 +497,10 @@ __global__ __launch_bounds__(kDThreads) void sign_gemm_dma_kernel(const __half *
     const int wave = tid >> 6, lane = tid & 63;
     const int wm = wave / DWGN, wn = wave % DWGN;
     const int l32 = lane & 31, kg = lane >> 5;
-    const int nk = words / (2 * KP);
+    // K steps [kb, kb + nk) of this split
+    const int nk_all = words / (2 * KP);
+    const int kb = split * nk_all / nsplit;
+    const int nk = (split + 1) * nk_all / nsplit - kb;
 
     // per-lane source offsets of the step loads (a step adds K halves / KP word pairs)
     const __half *psrc[C::PI];
@@ -464,7 +520,8 @@ __global__ __launch_bounds__(kDThreads) void sign_gemm_dma_kernel(const __half *
         ssrc[h] = S + (static_cast<size_t>(t) * (words >> 1) + j) * 128 + (rem & 1) * 64 + lane;
     }
     // load q (0 <= q < D) of this wave for step kt into stage st
-    auto issue_one = [&](int kt, char *st, int q) {
+    auto issue_one = [&](int kl, char *st, int q) {
+        const int kt = kb + kl;
         if (q < C::PI) {
             dma16(psrc[q] + kt * C::K, st + (wave * C::PI + q) * 1024);
         } else if (q < C::PI + C::SI) {
@@ -510,6 +567,11 @@ __global__ __launch_bounds__(kDThreads) void sign_gemm_dma_kernel(const __half *
                                 lds + (kt % kStages) * C::StageBytes, issue_one, acc, wm, wn, l32, kg, ec);
     }
 
+    if (part) {
+        store_partial<DMF, DNF>(acc, M, n_out, m0 + wm * 32 * DMF, n0 + wn * 32 * DNF, l32, kg,
+                                part + static_cast<size_t>(split) * M * ldw, ldw);
+        return;
+    }
     epilogue<DMF, DNF>(acc, snv, M, n_out, m0 + wm * 32 * DMF, n0 + wn * 32 * DNF, l32, kg, out, ldo, out32, ldo32,
                        dot);
 }
@@ -517,7 +579,7 @@ __global__ __launch_bounds__(kDThreads) void sign_gemm_dma_kernel(const __half *
 template <bool HAS_SK, int KP>
 void launch_dma(const void *P, int ldp, int M, const uint32_t *S, int words, int n_rows_pad, const void *sk,
                 const void *sn, void *out, int ldo, int n_out, float *out32, int ldo32, const DotArgs &dot,
-            hipStream_t s) {
+                hipStream_t s, float *part = nullptr, int nsplit = 1, int ldw = 0) {
     using C = DmaStep<KP>;
     static const bool once =
         ((void)hipFuncSetAttribute(reinterpret_cast<const void *>(sign_gemm_dma_kernel<HAS_SK, KP>),
@@ -526,22 +588,90 @@ void launch_dma(const void *P, int ldp, int M, const uint32_t *S, int words, int
     (void)once;
     const int nbm = (M + BM - 1) / BM;
     const int nbn = (n_out + DBN - 1) / DBN;
-    launch_kernel((sign_gemm_dma_kernel<HAS_SK, KP>), dim3(nbm * nbn), dim3(kDThreads), C::Lds, s,
+    launch_kernel((sign_gemm_dma_kernel<HAS_SK, KP>), dim3(nbm * nbn * nsplit), dim3(kDThreads), C::Lds, s,
                   static_cast<const __half *>(P), ldp, M, S, words, n_rows_pad, static_cast<const __half *>(sk),
-                  static_cast<const __half *>(sn), static_cast<__half *>(out), ldo, n_out, out32, ldo32, dot, nbm, nbn);
+                  static_cast<const __half *>(sn), static_cast<__half *>(out), ldo, n_out, out32, ldo32, dot, nbm, nbn,
+                  part, nsplit, ldw);
+}
+
+#ifndef DBF_SPLIT_BELOW
+#define DBF_SPLIT_BELOW 128
+#endif
+#ifndef DBF_SPLIT_TARGET
+#define DBF_SPLIT_TARGET 256
+#endif
+#ifndef DBF_SPLIT_MIN_STEPS
+#define DBF_SPLIT_MIN_STEPS 2
+#endif
+
+// Word pairs per step of the DMA kernel for this product.
+int dma_pairs(int M, int words, int n_out) {
+    if constexpr (kDmaPairs == 2) {
+        const int tiles = ((M + BM - 1) / BM) * ((n_out + DBN - 1) / DBN);
+        if (words % 4 == 0 && tiles <= 256) return 2;
+    }
+    return 1;
+}
+
+// K parts of the split-K form: grids of fewer than DBF_SPLIT_BELOW tiles are
+// cut along K into about DBF_SPLIT_TARGET workgroups in all, each with at
+// least DBF_SPLIT_MIN_STEPS steps.
+int split_parts(int M, int words, int n_out) {
+    const int tiles = ((M + BM - 1) / BM) * ((n_out + DBN - 1) / DBN);
+    if (tiles >= DBF_SPLIT_BELOW) return 1;
+    const int nk = words / (2 * dma_pairs(M, words, n_out));
+    return std::max(1, std::min(DBF_SPLIT_TARGET / tiles, nk / DBF_SPLIT_MIN_STEPS));
 }
 
 }  // namespace
 
+size_t sign_gemm_split_elems(int M, int K, int words, int n_out) {
+#ifndef DBF_PREFILL_NO_DMA
+    if (M <= 0 || K % BK != 0 || K != words * 32) return 0;
+    const int parts = split_parts(M, words, n_out);
+    if (parts <= 1) return 0;
+    return static_cast<size_t>(parts) * M * ((n_out + 3) & ~3);
+#else
+    (void)M, (void)K, (void)words, (void)n_out;
+    return 0;
+#endif
+}
+
+int launch_split_finish(const SplitK &split, int M, int n_out, const void *sn, void *out, int ldo, void *stream) {
+    const int items = M * n_out;
+    if (items == 0) return 0;
+    launch_kernel(split_finish_kernel, dim3((items + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream),
+                  static_cast<const float *>(split.ws), split.nsplit, M, n_out, split.ldw,
+                  static_cast<const __half *>(sn), static_cast<__half *>(out), ldo);
+    return static_cast<int>(hipGetLastError());
+}
+
 int launch_sign_gemm(const void *P, int ldp, int M, int K, const uint32_t *S, int words, int n_rows_pad,
                      const void *sk, const void *sn, void *out, int ldo, int n_out, float *out32, int ldo32,
-                     const void *dq, int dq_f32, int lddq, float *dpart, void *stream) {
+                     const void *dq, int dq_f32, int lddq, float *dpart, void *stream, SplitK *split) {
     const DotArgs dot{dq, dq_f32, lddq, dpart};
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool pvec = (ldp & 7) == 0;
     const bool kfull = pvec && (K % BK) == 0;
+    if (split) split->nsplit = 1;
 #ifndef DBF_PREFILL_NO_DMA
     if (kfull && (reinterpret_cast<uintptr_t>(P) & 15) == 0 && K == words * 32) {
+        if (split && split->ws && out && sn && !out32 && !dpart) {
+            const int parts = split_parts(M, words, n_out);
+            const int ldw = (n_out + 3) & ~3;
+            if (parts > 1 && static_cast<size_t>(parts) * M * ldw <= split->cap) {
+                split->nsplit = parts;
+                split->ldw = ldw;
+                if (dma_pairs(M, words, n_out) == 2) {
+                    if (sk) launch_dma<true, 2>(P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, dot, s, split->ws, parts, ldw);
+                    else launch_dma<false, 2>(P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, dot, s, split->ws, parts, ldw);
+                } else {
+                    if (sk) launch_dma<true, 1>(P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, dot, s, split->ws, parts, ldw);
+                    else launch_dma<false, 1>(P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, dot, s, split->ws, parts, ldw);
+                }
+                return static_cast<int>(hipGetLastError());
+            }
+        }
         // K steps of 128 where K allows and the tiles fit one wave of
         // workgroups over the 256 CUs; else steps of 64, whose 74 KiB of LDS
         // lets two workgroups share a CU (a partial last wave of tiles then

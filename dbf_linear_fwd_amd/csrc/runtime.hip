@@ -35,6 +35,8 @@ struct dbf_layer {
     uint16_t *T = nullptr;    // prefill intermediate    [max_batch][k_pad] fp16
     unsigned *tickets = nullptr;  // per 64-row tile of A; zero between calls
     uint16_t *v16 = nullptr;      // matrix-core decode intermediate [2][16][k_pad] fp16
+    float *split = nullptr;       // split-K parts of the prefill products (small grids)
+    size_t split_cap = 0;         // floats
     size_t packed_bytes = 0, scale_bytes = 0, workspace_bytes = 0;
     // backward (dbf_pack_ex with DBF_PACK_BACKWARD): the transposed layer
     // Wᵀ = diag(b) Bᵀ diag(mid) Aᵀ diag(a), and fp32 intermediates of the
@@ -95,6 +97,7 @@ void release(dbf_layer *h) {
     (void)hipFree(h->T);
     (void)hipFree(h->tickets);
     (void)hipFree(h->v16);
+    (void)hipFree(h->split);
     (void)hipFree(h->t32);
     (void)hipFree(h->red);
     release(h->bwd);
@@ -292,7 +295,21 @@ static dbf_status_t pack_layer(int32_t n, int32_t m, int32_t k, const int8_t *A_
     if (st == DBF_OK && hipDeviceSynchronize() != hipSuccess) st = DBF_ERR_HIP;
     const size_t v16_bytes = sizeof(uint16_t) * 2 * size_t(dec_b) * k_pad;
     if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->v16), v16_bytes);
-    if (st == DBF_OK) h->workspace_bytes = tpart_bytes + ypart_bytes + T_bytes + ticket_bytes + v16_bytes;
+    // split-K parts: the most that either prefill product takes at any batch
+    // <= max_batch (the part count depends on the batch through its 128-row
+    // tiles only, so the largest batch of each tile count is the worst case)
+    size_t split_elems = 64;
+    for (int32_t mb = 1; st == DBF_OK; mb += 128) {
+        const int32_t M = std::min(max_batch, mb + 127);
+        split_elems = std::max(split_elems, dbf::sign_gemm_split_elems(M, m, h->Wm, k_pad));
+        split_elems = std::max(split_elems, dbf::sign_gemm_split_elems(M, k_pad, h->Wk, n));
+        if (M >= max_batch) break;
+    }
+    if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->split), sizeof(float) * split_elems);
+    if (st == DBF_OK) h->split_cap = split_elems;
+    if (st == DBF_OK)
+        h->workspace_bytes =
+            tpart_bytes + ypart_bytes + T_bytes + ticket_bytes + v16_bytes + sizeof(float) * split_elems;
 
     if (st != DBF_OK) {
         release(h);
@@ -447,16 +464,28 @@ static dbf_status_t forward_decode(dbf_layer *h, const void *x, void *y, int32_t
 
 static dbf_status_t forward_prefill(dbf_layer *h, const void *x, void *y, int32_t batch, hipStream_t stream) {
     // T = rne16(mid ⊙ (X (B ⊙ b)ᵀ)), all k_pad columns (padded ones are 0).
+    dbf::SplitK sp;
+    sp.ws = h->split;
+    sp.cap = h->split_cap;
     dbf_status_t st = timed_launch(h, "prefill_gemm1", stream, [&] {
         return dbf::launch_sign_gemm(x, h->m, batch, h->m, h->B_dev, h->Wm, h->k_pad, h->b_dev, h->mid_dev, h->T,
-                                     h->k_pad, h->k_pad, nullptr, 0, nullptr, 0, 0, nullptr, stream);
+                                     h->k_pad, h->k_pad, nullptr, 0, nullptr, 0, 0, nullptr, stream, &sp);
     });
+    if (st == DBF_OK && sp.nsplit > 1)
+        st = timed_launch(h, "prefill_split1", stream, [&] {
+            return dbf::launch_split_finish(sp, batch, h->k_pad, h->mid_dev, h->T, h->k_pad, stream);
+        });
     if (st != DBF_OK) return st;
     // Y = rne16(a ⊙ (T Aᵀ)).
-    return timed_launch(h, "prefill_gemm2", stream, [&] {
+    st = timed_launch(h, "prefill_gemm2", stream, [&] {
         return dbf::launch_sign_gemm(h->T, h->k_pad, batch, h->k_pad, h->A_dev, h->Wk, h->n_pad, nullptr,
-                                     h->a_dev, y, h->n, h->n, nullptr, 0, nullptr, 0, 0, nullptr, stream);
+                                     h->a_dev, y, h->n, h->n, nullptr, 0, nullptr, 0, 0, nullptr, stream, &sp);
     });
+    if (st == DBF_OK && sp.nsplit > 1)
+        st = timed_launch(h, "prefill_split2", stream, [&] {
+            return dbf::launch_split_finish(sp, batch, h->n, h->a_dev, y, h->n, stream);
+        });
+    return st;
 }
 
 extern "C" dbf_status_t dbf_linear_forward_ex(dbf_handle_t h, const void *x, void *y, int32_t batch, int32_t path,

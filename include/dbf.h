@@ -23,9 +23,10 @@
  * Numerics: fp16 in and out, fp32 accumulation, one round-to-nearest-even
  * to fp16 at the end; no flush-to-zero.  The intermediate v = t * mid
  * (batch x k) is an operand of 16-bit matrix-core products: on the decode
- * path it is kept as the sum of two fp16 numbers (about 22 significant bits),
- * on the prefill path it is rounded once to fp16.  On both it must stay
- * inside the fp16 range (|v| < 65520); the table path keeps it in fp32.
+ * path at batch <= 8 it is kept as the sum of two fp16 numbers (about 22
+ * significant bits); at decode batch 9..16 and on the prefill path it is
+ * rounded once to fp16.  On both it must stay inside the fp16 range
+ * (|v| < 65520); the table path keeps it in fp32.
  *
  * Packed sign format (the pages fix none; this is the library's own)
  * ----------------------------------------------------------------------
@@ -71,7 +72,8 @@ typedef enum {
 typedef enum {
     DBF_PATH_AUTO = 0,         /* batch <= 16: DBF_PATH_DECODE; batch > 16: DBF_PATH_PREFILL */
     DBF_PATH_DECODE = 1,       /* small-batch kernels: batch as the MFMA N dimension, intermediate
-                                  kept as an fp16 hi+lo pair; batch must be <= 16 */
+                                  kept as an fp16 hi+lo pair (batch <= 8) or rounded once to fp16
+                                  (batch 9..16); batch must be <= 16 */
     DBF_PATH_PREFILL = 2,      /* tiled MFMA products, intermediate rounded once to fp16; any batch */
     DBF_PATH_DECODE_TABLE = 3  /* vector-ALU signed sums (4-sign lookup tables for batch <= 4, one
                                   add per sign above), intermediate in fp32; batch must be <= 16 */

@@ -163,6 +163,44 @@ def test_prefill_small_shapes(gpu, n, m, k, batch):
     assert_tol(y, O.dense_forward(X, A, B, a, mid, b), f"prefill {n}x{m}x{k} b{batch}")
 
 
+# Intermediate batches on shapes whose prefill grids are small (a few
+# 128 x 256 output tiles), so both products take the split-K form: stage 1
+# (K = 4096) in 16 parts, stage 2 (K = 1024) in 4, ragged n.
+SPLIT_SHAPE = (1000, 4096, 1000)
+
+
+@pytest.mark.parametrize("batch", [17, 100, 130, 300])
+def test_prefill_split_k(gpu, batch):
+    n, m, k = SPLIT_SHAPE
+    _say(f"prefill split-K n={n} m={m} k={k} batch={batch}")
+    X, A, B, a, mid, b = inputs.tiny_case(4000 + batch, n, m, k, batch, signed_scales=True)
+    L = inputs.Layer("s", n, m, k, A, B, a, mid, b, {})
+    y = run(L, X, dbf.DBF_PATH_PREFILL)
+    assert_tol(y, O.dense_forward(X, A, B, a, mid, b), f"prefill split-K b{batch}")
+
+
+def test_prefill_split_k_determinism(gpu):
+    """The parts are added in a fixed order and their count depends on the
+    batch only through its 128-row tiles: repeated calls give identical bits,
+    and so do batches within one tile count."""
+    torch = _torch()
+    n, m, k = SPLIT_SHAPE
+    X, A, B, a, mid, b = inputs.tiny_case(4999, n, m, k, 256, signed_scales=True)
+    H = dbf.Layer(A, B, a, mid, b, max_batch=256)
+    try:
+        x = torch.from_numpy(X).cuda()
+        y100 = H.forward(x[:100], path=dbf.DBF_PATH_PREFILL).cpu().numpy()
+        assert np.array_equal(y100.view(np.uint16),
+                              H.forward(x[:100], path=dbf.DBF_PATH_PREFILL).cpu().numpy().view(np.uint16))
+        y17 = H.forward(x[:17], path=dbf.DBF_PATH_PREFILL).cpu().numpy()
+        assert np.array_equal(y17.view(np.uint16), y100[:17].view(np.uint16))
+        y256 = H.forward(x, path=dbf.DBF_PATH_PREFILL).cpu().numpy()
+        y130 = H.forward(x[:130], path=dbf.DBF_PATH_PREFILL).cpu().numpy()
+        assert np.array_equal(y130.view(np.uint16), y256[:130].view(np.uint16))
+    finally:
+        H.close()
+
+
 # --------------------------------------------------------------------------- integer sub-suite (bit-exact)
 
 INT_SHAPES = [
@@ -387,14 +425,14 @@ def test_injected_allocation_failure_leaks_nothing(gpu):
     _warm_library(L)
     free0 = torch.cuda.mem_get_info()[0]
     try:
-        for nth in range(1, 11):
+        for nth in range(1, 12):
             _say(f"inject allocation failure #{nth}")
             os.environ["DBF_TEST_FAIL_ALLOC"] = str(nth)
             with pytest.raises(dbf.DbfError) as e:
                 dbf.dbf_pack(L.n, L.m, L.k, L.A, L.B, L.a, L.mid, L.b, 64)
             assert e.value.status == dbf.DBF_ERR_OOM
         os.environ["DBF_TEST_FAIL_ALLOC"] = "100"
-        h = dbf.dbf_pack(L.n, L.m, L.k, L.A, L.B, L.a, L.mid, L.b, 64)   # a pack makes 10 allocations
+        h = dbf.dbf_pack(L.n, L.m, L.k, L.A, L.B, L.a, L.mid, L.b, 64)   # a pack makes 11 allocations
         dbf.dbf_free(h)
     finally:
         os.environ.pop("DBF_TEST_FAIL_ALLOC", None)
@@ -649,7 +687,7 @@ def test_backward_pack_allocation_failures_leak_nothing(gpu):
     _warm_library(L, dbf.DBF_PACK_BACKWARD)
     free0 = torch.cuda.mem_get_info()[0]
     try:
-        n_alloc = 22   # 10 for the layer, 10 for the transposed layer, t and the batch-sum partials
+        n_alloc = 24   # 11 for the layer, 11 for the transposed layer, t and the batch-sum partials
         for nth in range(1, n_alloc + 1):
             _say(f"backward pack: inject allocation failure #{nth}")
             os.environ["DBF_TEST_FAIL_ALLOC"] = str(nth)
