@@ -38,6 +38,8 @@ __all__ = [
     "integer_x",
     "C5_LAYERS",
     "tiny_case",
+    "BqqLayer",
+    "bqq_layer",
 ]
 
 
@@ -198,3 +200,62 @@ def config(cid: int) -> Config:
                   for i, ((name, n, m), k) in enumerate(zip(C5_LAYERS, ks))]
         return Config(5, "Llama-3-8B-shaped block of 7 DBF linears, per-layer k", layers, (1, 2048))
     raise ValueError(f"unknown config {cid}")
+
+
+# --------------------------------------------------------------------------- binary-quadratic (BQQ-form) layers
+
+@dataclasses.dataclass
+class BqqLayer:
+    name: str
+    n: int                      # output features
+    m: int                      # input features
+    d: int                      # inner dimension of each binary product
+    p: int                      # number of binary products
+    Y: np.ndarray               # uint8 (p, n, d), entries 0/1
+    Z: np.ndarray               # uint8 (p, d, m), entries 0/1
+    r: np.ndarray               # float16 (p,)
+    s: np.ndarray               # float16 (p,)
+    t: np.ndarray               # float16 (p,)
+    u: np.float16
+    X: Dict[int, np.ndarray]    # batch -> float16 (batch, m)
+
+    @property
+    def bit_bytes(self) -> int:
+        return self.p * self.d * (self.n + self.m) // 8
+
+
+def bqq_layer(name: str, n: int, m: int, d: int, p: int, seed, batches: Sequence[int],
+              sigma: float = 0.02, jitter: float = 0.05, integer: bool = False) -> BqqLayer:
+    """A seeded BQQ-form layer.
+
+    Draw order with one ``Generator(PCG64(seed))``: Y bits (p, n, d), Z bits
+    (p, d, m), then per term rho_i ~ U[0.5, 1.5] * sigma / sqrt(d) and the
+    jitters e_s, e_t (p each) and e_u ~ U[-jitter, jitter], then X per batch.
+    The scalars are r = 4 rho, s = -2 rho (1 + e_s), t = -2 rho (1 + e_t),
+    u = d * sum(rho) * (1 + e_u), rounded to fp16: with zero jitter a term is
+    rho times a product of two +/-1 matrices (centred entries of size
+    sigma, like trained weights); the jitter keeps every term of the formula
+    in play.  ``integer=True`` instead draws r, s, t from {-2, -1, 1, 2}, u
+    from {-4, ..., 4} and X from {-1, 0, 1}, so every partial sum is a small
+    integer (exact in fp32 in any order).
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    Y = rng.integers(0, 2, size=(p, n, d), dtype=np.uint8)
+    Z = rng.integers(0, 2, size=(p, d, m), dtype=np.uint8)
+    if integer:
+        r = rng.choice([-2.0, -1.0, 1.0, 2.0], size=p).astype(np.float16)
+        s = rng.choice([-2.0, -1.0, 1.0, 2.0], size=p).astype(np.float16)
+        t = rng.choice([-2.0, -1.0, 1.0, 2.0], size=p).astype(np.float16)
+        u = np.float16(rng.integers(-4, 5))
+        X = {bt: integer_x(rng, bt, m) for bt in batches}
+    else:
+        rho = rng.uniform(0.5, 1.5, size=p) * sigma / math.sqrt(d)
+        e_s = rng.uniform(-jitter, jitter, size=p)
+        e_t = rng.uniform(-jitter, jitter, size=p)
+        e_u = rng.uniform(-jitter, jitter)
+        r = (4.0 * rho).astype(np.float16)
+        s = (-2.0 * rho * (1.0 + e_s)).astype(np.float16)
+        t = (-2.0 * rho * (1.0 + e_t)).astype(np.float16)
+        u = np.float16(d * rho.sum() * (1.0 + e_u))
+        X = {bt: random_x(rng, bt, m) for bt in batches}
+    return BqqLayer(name, n, m, d, p, Y, Z, r, s, t, u, X)
