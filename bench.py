@@ -57,7 +57,8 @@ def parse():
     p.add_argument("--all-configs", action="store_true",
                    help="instead of the headline line: one JSON line per workload layer and batch "
                         "(decode at batch 1 and 16, prefill at batch 2048)")
-    p.add_argument("--only", choices=("decode", "prefill", "block", "backward"), default=None,
+    p.add_argument("--no-bqq", action="store_true", help="skip the BQQ-form layer measurement")
+    p.add_argument("--only", choices=("decode", "prefill", "block", "backward", "bqq"), default=None,
                    help="run one leg only (for profiling)")
     p.add_argument("--decode-path", choices=("mfma", "table"), default="mfma",
                    help="decode kernels: matrix cores (default) or vector-ALU lookup tables")
@@ -326,6 +327,60 @@ def all_configs(args):
                 torch.cuda.synchronize()
 
 
+def bqq_leg(args):
+    """A BQQ-form layer (sum of scaled 0/1 matrix products plus rank-one
+    terms) of shape 4096x4096 with p = 2 products of inner dimension 1024 --
+    2 MiB of bits, the size of the 4096x4096, k = 2048 DBF layer: batch-1
+    decode over rotated weight copies (GB/s of bits + scales per forward)
+    and batch-2048 prefill (TFLOP/s-equivalent 2 * batch * p d (n + m))."""
+    import torch
+
+    import dbf_linear_fwd_amd as dbf
+    from tests import inputs
+
+    n, m, d, p = 4096, 4096, 1024, 2
+    L = inputs.bqq_layer("bqq", n, m, d, p, 7300, (1, 2048))
+    bytes_step = L.bit_bytes + 2 * (n + p * d + m) + 4 * (n + m)
+    R = max(1, -(-args.rotate_mb * (1 << 20) // bytes_step))
+    print(f"[bench] bqq: {n}x{m} d={d} p={p}, {R} copies", file=sys.stderr, flush=True)
+    copies = [dbf.Layer.bqq(L.Y, L.Z, L.r, L.s, L.t, L.u, max_batch=1) for _ in range(R)]
+    x = torch.from_numpy(L.X[1]).cuda()
+    y = torch.empty((1, n), dtype=torch.float16, device="cuda")
+
+    def fwd(i):
+        copies[i % R].forward(x, out=y)
+    fwd.period = R
+    el, done = time_steps(fwd, max(R, min(args.steps, 10 * R)), min(args.warmup, R), args.mode)
+    kt = kernel_times(copies, fwd, min(args.steps, 2 * R))
+    res = {"workload": "BQQ-form layer 4096x4096, p=2 products of d=1024 (2 MiB of bits)",
+           "decode_b1": {"us_per_forward": el * 1e6 / done, "gbs": bytes_step * done / el / 1e9,
+                         "frac_of_hbm_peak": bytes_step * done / el / 1e9 / HBM_PEAK_GBS, "kernels": kt,
+                         "bytes_per_forward": bytes_step, "copies": R}}
+    print(f"[bench] bqq decode: {res['decode_b1']['us_per_forward']:.2f} us, {res['decode_b1']['gbs']:.1f} GB/s; "
+          f"kernels {kt}", file=sys.stderr, flush=True)
+    for c in copies:
+        c.close()
+    del copies
+    torch.cuda.synchronize()
+    bt = 2048
+    H = dbf.Layer.bqq(L.Y, L.Z, L.r, L.s, L.t, L.u, max_batch=bt)
+    x = torch.from_numpy(L.X[bt]).cuda()
+    y = torch.empty((bt, n), dtype=torch.float16, device="cuda")
+
+    def pf(i):
+        H.forward(x, out=y)
+    el, done = time_steps(pf, 30, 5, "eager")
+    kt = kernel_times([H], pf, 10)
+    flops = 2 * bt * p * d * (n + m)
+    res["prefill_b2048"] = {"us_per_forward": el * 1e6 / done, "tflops_eq": flops * done / el / 1e12,
+                            "frac_of_mfma_peak": flops * done / el / 1e12 / MFMA_F16_PEAK_TFLOPS, "kernels": kt}
+    print(f"[bench] bqq prefill: {res['prefill_b2048']['tflops_eq']:.1f} TFLOP/s-eq; kernels {kt}",
+          file=sys.stderr, flush=True)
+    H.close()
+    torch.cuda.synchronize()
+    return res
+
+
 def copy_probe(mb):
     import torch
     n = mb * (1 << 20) // 4
@@ -438,6 +493,10 @@ def main():
     if args.only in (None, "block") and not args.no_block:
         result["block"] = block_leg(args)
 
+    # ---------------------------------------------------------------- BQQ-form layer (secondary)
+    if args.only in (None, "bqq") and not args.no_bqq:
+        result["bqq"] = bqq_leg(args)
+
     if args.only is not None:
         print(json.dumps({k: {kk: vv for kk, vv in v.items() if kk not in ("layer", "copies")}
                           for k, v in result.items()}, default=str))
@@ -477,6 +536,8 @@ def main():
         line["decode_block_b1"] = result["block"]
     if "backward" in result:
         line["backward_batch2048"] = result["backward"]
+    if "bqq" in result:
+        line["bqq_form"] = result["bqq"]
     print(json.dumps(line))
 
 

@@ -28,7 +28,7 @@ __all__ = [
     "dbf_pack", "dbf_linear_forward", "dbf_linear_forward_ex", "dbf_free", "dbf_get_info",
     "dbf_status_string", "dbf_pack_signs", "dbf_layout_signs", "dbf_layout_words",
     "dbf_timing_enable", "dbf_timing_read", "Layer", "dbf_linear_forward_group", "forward_group",
-    "dbf_pack_ex", "dbf_linear_backward_data", "dbf_linear_backward", "DBF_PACK_BACKWARD",
+    "dbf_pack_ex", "dbf_linear_backward_data", "dbf_linear_backward", "DBF_PACK_BACKWARD", "dbf_bqq_pack",
 ]
 
 DBF_OK = 0
@@ -51,6 +51,7 @@ EXPORTED_SYMBOLS = (
     "dbf_pack", "dbf_pack_ex", "dbf_linear_forward", "dbf_linear_forward_ex", "dbf_linear_forward_group",
     "dbf_linear_backward_data", "dbf_linear_backward", "dbf_free", "dbf_get_info", "dbf_status_string",
     "dbf_pack_signs", "dbf_layout_signs", "dbf_layout_words", "dbf_timing_enable", "dbf_timing_read",
+    "dbf_bqq_pack",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -101,6 +102,8 @@ def lib() -> ctypes.CDLL:
     L.dbf_linear_forward_ex.restype = ctypes.c_int
     L.dbf_pack_ex.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, i32, i32, ctypes.POINTER(vp)]
     L.dbf_pack_ex.restype = ctypes.c_int
+    L.dbf_bqq_pack.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, ctypes.c_uint16, i32, ctypes.POINTER(vp)]
+    L.dbf_bqq_pack.restype = ctypes.c_int
     L.dbf_linear_backward_data.argtypes = [vp, vp, vp, i32, vp]
     L.dbf_linear_backward_data.restype = ctypes.c_int
     L.dbf_linear_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp]
@@ -168,6 +171,23 @@ def dbf_pack(n: int, m: int, k: int, A_signs, B_signs, a, mid, b, max_batch: int
         st = lib().dbf_pack(n, m, k, _ptr(A), _ptr(B), _ptr(a16), _ptr(mid16), _ptr(b16), max_batch,
                             ctypes.byref(h))
     _check(st, "dbf_pack")
+    return h.value
+
+
+def dbf_bqq_pack(n: int, m: int, d: int, p: int, Y, Z, r, s, t, u, max_batch: int) -> int:
+    """Handle of a BQQ-form layer (see dbf_bqq_pack in include/dbf.h): Y (p, n, d) and
+    Z (p, d, m) of 0/1, fp16 scalars r, s, t (p each) and u."""
+    Y8 = np.ascontiguousarray(np.asarray(Y), dtype=np.uint8)
+    Z8 = np.ascontiguousarray(np.asarray(Z), dtype=np.uint8)
+    if Y8.size != p * n * d or Z8.size != p * d * m:
+        raise ValueError("Y must hold p*n*d and Z p*d*m entries")
+    r16, s16, t16 = _as_half_bits(r), _as_half_bits(s), _as_half_bits(t)
+    if r16.size != p or s16.size != p or t16.size != p:
+        raise ValueError("r, s, t must have p entries")
+    u16 = int(_as_half_bits(np.asarray([u]))[0])
+    h = ctypes.c_void_p()
+    _check(lib().dbf_bqq_pack(n, m, d, p, _ptr(Y8), _ptr(Z8), _ptr(r16), _ptr(s16), _ptr(t16), u16, max_batch,
+                              ctypes.byref(h)), "dbf_bqq_pack")
     return h.value
 
 
@@ -285,6 +305,22 @@ class Layer:
         self.max_batch = int(max_batch)
         self.handle = dbf_pack(self.n, self.m, self.k, A, B, a, mid, b, self.max_batch,
                                DBF_PACK_BACKWARD if backward else 0)
+
+    @classmethod
+    def bqq(cls, Y, Z, r, s, t, u, max_batch: int = 2048) -> "Layer":
+        """A layer with the BQQ-form weight sum_i (r_i Y_i Z_i + s_i Y_i 1 + t_i 1 Z_i) + u 1:
+        Y (p, n, d) and Z (p, d, m) of 0/1; forward only."""
+        Y = np.asarray(Y)
+        Z = np.asarray(Z)
+        if Y.ndim != 3 or Z.ndim != 3 or Y.shape[0] != Z.shape[0] or Y.shape[2] != Z.shape[1]:
+            raise ValueError("Y must be (p, n, d) and Z (p, d, m)")
+        self = cls.__new__(cls)
+        p, self.n, d = Y.shape
+        self.m = Z.shape[2]
+        self.k = p * d
+        self.max_batch = int(max_batch)
+        self.handle = dbf_bqq_pack(self.n, self.m, d, p, Y, Z, r, s, t, u, self.max_batch)
+        return self
 
     def info(self) -> Dict[str, int]:
         return dbf_get_info(self.handle)

@@ -1,0 +1,64 @@
+// Per-row statistics of the input for the forward of a binary-quadratic
+// (BQQ-form) weight matrix.
+//
+// The TL;DR of "Binary Quadratic Quantization: Beyond First-Order
+// Quantization for Real-Valued Matrix Compression" writes W as a sum of
+// scaled products of 0/1 matrices plus rank-one terms:
+//   W = Σ_i ( r_i Y_i Z_i + s_i Y_i 1 + t_i 1 Z_i ) + u 1.
+// The products go through the DBF kernels (0/1 flavour); the other terms
+// reduce, for an input row x, to E[o] * Σ_l x_l + Σ_l γ_l x_l with
+// E[o] = Σ_i s_i (row o of Y_i summed) + u and γ_l = Σ_i t_i (column l of
+// Z_i summed), both fixed at pack time.  This kernel forms the two sums per
+// row; the products' epilogue adds the term before the one rounding.
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+
+#include "dbf_internal.h"
+
+namespace dbf {
+namespace {
+
+constexpr int kStatThreads = 256;
+
+// stats[2r] = Σ_l x[r][l], stats[2r + 1] = Σ_l gamma[l] x[r][l], in fp32:
+// each thread sums a fixed stride of the row in order, then a fixed-order
+// tree over the threads, so every call gives the same bits.
+__global__ __launch_bounds__(kStatThreads) void bqq_rowstats_kernel(const __half *__restrict__ x, int m,
+                                                                    const float *__restrict__ gamma,
+                                                                    float *__restrict__ stats) {
+    __shared__ float sh[2][kStatThreads];
+    const int r = blockIdx.x, tid = threadIdx.x;
+    const __half *xr = x + static_cast<size_t>(r) * m;
+    float s = 0.0f, k = 0.0f;
+    for (int l = tid; l < m; l += kStatThreads) {
+        const float v = __half2float(xr[l]);
+        s += v;
+        k += gamma[l] * v;
+    }
+    sh[0][tid] = s;
+    sh[1][tid] = k;
+    __syncthreads();
+    for (int w = kStatThreads / 2; w > 0; w >>= 1) {
+        if (tid < w) {
+            sh[0][tid] += sh[0][tid + w];
+            sh[1][tid] += sh[1][tid + w];
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        stats[2 * r] = sh[0][0];
+        stats[2 * r + 1] = sh[1][0];
+    }
+}
+
+}  // namespace
+
+int launch_bqq_rowstats(const void *x, int batch, int m, const float *gamma, float *stats, void *stream) {
+    if (batch <= 0) return 0;
+    launch_kernel(bqq_rowstats_kernel, dim3(batch), dim3(kStatThreads), 0, static_cast<hipStream_t>(stream),
+                  static_cast<const __half *>(x), m, gamma, stats);
+    return static_cast<int>(hipGetLastError());
+}
+
+}  // namespace dbf

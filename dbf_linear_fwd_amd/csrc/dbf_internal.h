@@ -62,6 +62,12 @@ struct MfmaDecodeArgs {
     void *y;
     uint16_t *v16;       // [2][batch][k_pad] fp16: v_hi then v_lo planes
     int batch, n, m, n_pad, m_pad, k_pad;
+    // 0/1 matrices (bit 1 = 1, bit 0 = 0) instead of signs, expanded as
+    // {0, 2} (the factor 2 per product is folded into the scales)
+    int binary = 0;
+    // optional affine output term: y[r][i] = rne16(a_i s_ri + E[i] * stats[r].x + stats[r].y)
+    const float *aff_E = nullptr;
+    const float *aff_stats = nullptr;  // [batch][2]
 };
 
 // which = 1: stage 1 (writes v16); which = 2: stage 2 (writes y).
@@ -150,20 +156,36 @@ struct SplitK {
     int nsplit = 1;       // set by launch_sign_gemm
     int ldw = 0;
 };
+//   flavor (may be null): binary = S holds a 0/1 matrix (bit 1 = 1), the
+//   operand is then {0, 2} (callers fold the 2 into sn) and sk must be null;
+//   aff_E / aff_stats: out[i][c] = rne16(sn[c] * sum + aff_E[c] *
+//   aff_stats[2i] + aff_stats[2i + 1]).
+struct GemmFlavor {
+    int binary = 0;
+    const float *aff_E = nullptr;
+    const float *aff_stats = nullptr;
+};
 int launch_sign_gemm(const void *P, int ldp, int M, int K, const uint32_t *S, int words, int n_rows_pad,
                      const void *sk, const void *sn, void *out, int ldo, int n_out, float *out32, int ldo32,
-                     const void *dq, int dq_f32, int lddq, float *dpart, void *stream, SplitK *split = nullptr);
+                     const void *dq, int dq_f32, int lddq, float *dpart, void *stream, SplitK *split = nullptr,
+                     const GemmFlavor *flavor = nullptr);
 // Floats of split workspace that launch_sign_gemm would use for this
 // product (0: it would not split), assuming 16-byte aligned rows of P.
 size_t sign_gemm_split_elems(int M, int K, int words, int n_out);
-// out[i][c] = rne16(sn[c] * (ws[0][i][c] + ws[1][i][c] + ...)), i < M, c < n_out.
-int launch_split_finish(const SplitK &split, int M, int n_out, const void *sn, void *out, int ldo, void *stream);
+// out[i][c] = rne16(sn[c] * (ws[0][i][c] + ws[1][i][c] + ...)
+//                  [+ aff_E[c] * aff_stats[2i] + aff_stats[2i + 1]]), i < M, c < n_out.
+int launch_split_finish(const SplitK &split, int M, int n_out, const void *sn, void *out, int ldo, void *stream,
+                        const float *aff_E = nullptr, const float *aff_stats = nullptr);
 
 // Batch sums of the gradients: out[c] = sum over g < ceil(rows / 64) of
 // partial[g * ld + c] for c < cols, added in g order (the partials are
 // 64-row sums written by launch_sign_gemm's dpart epilogue).
 constexpr int kColChunk = 64;
 int launch_colsum_finish(const float *partial, int ld, int rows, int cols, float *out, void *stream);
+
+// BQQ-form layers: stats[2r] = sum of row r of x (fp16, batch x m), stats[2r + 1]
+// = Σ_l gamma[l] x[r][l]; fp32, fixed summation order.
+int launch_bqq_rowstats(const void *x, int batch, int m, const float *gamma, float *stats, void *stream);
 
 }  // namespace dbf
 

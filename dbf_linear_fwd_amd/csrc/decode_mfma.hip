@@ -92,19 +92,44 @@ __device__ __forceinline__ f16x8 expand_scaled(uint32_t word, int g, const u32x4
     return __builtin_bit_cast(f16x8, r);
 }
 
-// The two constants of expand_pm1 as register values the compiler cannot
-// fold back into literals: the sign mask in a scalar register, +1.0 pair in
-// a vector register.  Called once at kernel entry, before any MFMA has been
-// issued, so the vector move cannot collide with an MFMA still reading its
-// operands (the hazard recognizer does not see inside inline asm).
+// Halves 8g..8g+7 of a word of a 0/1 matrix as the operand {0, 2.0}: the
+// same pair moved one bit lower, onto the top exponent bit of each fp16
+// (0x4000 = 2.0).  The factor 2 of each product is folded into the scales.
+__device__ __forceinline__ f16x8 expand_01(uint32_t word, int g, uint32_t mask2) {
+    const uint32_t sh = word << (12 - 4 * g);
+    u32x4 r;
+#pragma unroll
+    for (int p = 0; p < 3; ++p) r[p] = (sh << (2 - p)) & mask2;
+    r[3] = (sh >> 1) & mask2;
+    return __builtin_bit_cast(f16x8, r);
+}
+
+// The constants of expand_pm1 / expand_01 as register values the compiler
+// cannot fold back into literals: the masks in scalar registers, +1.0 pair
+// in a vector register.  Called once at kernel entry, before any MFMA has
+// been issued, so the vector move cannot collide with an MFMA still reading
+// its operands (the hazard recognizer does not see inside inline asm).
 struct ExpandConsts {
-    uint32_t mask, one;
+    uint32_t mask, one, mask2;
 };
+template <bool BIN>
 __device__ __forceinline__ ExpandConsts expand_consts() {
     ExpandConsts c;
     asm volatile("s_mov_b32 %0, 0x80008000" : "=s"(c.mask));
     asm volatile("v_mov_b32 %0, 0x3c003c00" : "=v"(c.one));
+    if constexpr (BIN) asm volatile("s_mov_b32 %0, 0x40004000" : "=s"(c.mask2));
+    else c.mask2 = 0;
     return c;
+}
+
+// x as an fp32 value the compiler must materialize: a product rounded to
+// fp32 here is not fused into a following fp16 conversion (one mixed-
+// precision instruction rounding the exact product once), which the compiler
+// would otherwise do in some instantiations and not others -- every kernel
+// form then rounds alike.
+__device__ __forceinline__ float rounded(float x) {
+    asm volatile("" : "+v"(x));
+    return x;
 }
 
 __device__ __forceinline__ f16x8 zero8() { return __builtin_bit_cast(f16x8, u32x4{0u, 0u, 0u, 0u}); }
@@ -182,7 +207,7 @@ __device__ __forceinline__ void store_sign_items(const u32x4 (&v)[kMaxItems], ui
 }
 
 // One round: pairs [pr0, pr1) of rows r0..r0+16RT-1 from the LDS copies.
-template <int NB, int RT, bool STAGE1>
+template <int NB, int RT, bool STAGE1, bool BIN>
 __device__ __forceinline__ void round_mma(f32x4 (&acc)[Acc<NB>::N][RT], const uint32_t *sgn, const _Float16 *act,
                                           int KR, int pr0, int pr1, int wave, int li, int g, ExpandConsts ec) {
     constexpr bool kShared = Acc<NB>::kShared;
@@ -207,7 +232,7 @@ __device__ __forceinline__ void round_mma(f32x4 (&acc)[Acc<NB>::N][RT], const ui
         for (int h = 0; h < 2; ++h) {
             const int e = 64 * pl + 32 * h + 8 * g;
             o.v0[h] = *reinterpret_cast<const f16x8 *>(arow0 + e);
-            if constexpr (kSP && STAGE1) o.sc[h] = *reinterpret_cast<const u32x4 *>(brow + e);
+            if constexpr (kSP && STAGE1 && !BIN) o.sc[h] = *reinterpret_cast<const u32x4 *>(brow + e);
         }
     };
     auto mma_pair = [&](const PairOps &o) {
@@ -216,7 +241,8 @@ __device__ __forceinline__ void round_mma(f32x4 (&acc)[Acc<NB>::N][RT], const ui
 #pragma unroll
             for (int t = 0; t < RT; ++t) {
                 f16x8 sv;
-                if constexpr (kSP && STAGE1) sv = expand_scaled(h ? o.w[t].y : o.w[t].x, g, o.sc[h], ec.mask);
+                if constexpr (BIN) sv = expand_01(h ? o.w[t].y : o.w[t].x, g, ec.mask2);  // (b = 1)
+                else if constexpr (kSP && STAGE1) sv = expand_scaled(h ? o.w[t].y : o.w[t].x, g, o.sc[h], ec.mask);
                 else sv = expand_pm1(h ? o.w[t].y : o.w[t].x, g, ec.mask, ec.one);
                 acc[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sv, o.v0[h], acc[0][t], 0, 0, 0);
             }
@@ -273,7 +299,7 @@ __device__ __forceinline__ f32x4 total(const float *red, int t, int lane) {
 
 // Stage 1 for row block `blk` (rows 16*RT*blk ..): v = mid * (B (x ⊙ b)),
 // stored as fp16 hi/lo planes [2][NB][k_pad] (single plane: [NB][k_pad]).
-template <int NB, int RT>
+template <int NB, int RT, bool BIN>
 __device__ __forceinline__ void stage1_body(int blk, char *base, const uint32_t *__restrict__ Bt, int Wm,
                                             const __half *__restrict__ x, int m, const __half *__restrict__ b,
                                             const __half *__restrict__ mid, __half *__restrict__ v16, int k_pad,
@@ -287,7 +313,7 @@ __device__ __forceinline__ void stage1_body(int blk, char *base, const uint32_t 
     const int g = lane >> 4;
     const int li = lane & 15;
     const int j0 = blk * 16 * RT;
-    const ExpandConsts ec = expand_consts();
+    const ExpandConsts ec = expand_consts<BIN>();
 
     float mid_pre[RT][4];  // epilogue scales, fetched early
 #pragma unroll
@@ -377,7 +403,7 @@ __device__ __forceinline__ void stage1_body(int blk, char *base, const uint32_t 
             }
         }
         __syncthreads();
-        round_mma<NB, RT, true>(acc, sgn, act, KR, pr0, pr1, wave, li, g, ec);
+        round_mma<NB, RT, true, BIN>(acc, sgn, act, KR, pr0, pr1, wave, li, g, ec);
     }
 
     reduce_waves<NB, RT>(acc, red, wave, lane);
@@ -390,7 +416,7 @@ __device__ __forceinline__ void stage1_body(int blk, char *base, const uint32_t 
             f16x4 hi, lo;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const float val = d[v] * mid_pre[t][v];
+                const float val = rounded(d[v] * mid_pre[t][v]);
                 hi[v] = static_cast<_Float16>(val);
                 lo[v] = static_cast<_Float16>(val - static_cast<float>(hi[v]));
             }
@@ -402,10 +428,11 @@ __device__ __forceinline__ void stage1_body(int blk, char *base, const uint32_t 
 }
 
 // Stage 2 for row block `blk`: y = rne16(a ⊙ (A (v_hi + v_lo))) (single plane: A v).
-template <int NB, int RT>
+template <int NB, int RT, bool BIN>
 __device__ __forceinline__ void stage2_body(int blk, char *base, const uint32_t *__restrict__ At, int Wk,
                                             const __half *__restrict__ v16, int k_pad, const __half *__restrict__ a,
-                                            __half *__restrict__ y, int n, int PR) {
+                                            __half *__restrict__ y, int n, int PR, const float *__restrict__ aff_E,
+                                            const float *__restrict__ aff_stats) {
     const int KR = 64 * PR;
     uint32_t *sgn = reinterpret_cast<uint32_t *>(base);
     _Float16 *act = reinterpret_cast<_Float16 *>(base + static_cast<size_t>(PR) * 128 * RT);
@@ -415,7 +442,7 @@ __device__ __forceinline__ void stage2_body(int blk, char *base, const uint32_t 
     const int g = lane >> 4;
     const int li = lane & 15;
     const int i0 = blk * 16 * RT;
-    const ExpandConsts ec = expand_consts();
+    const ExpandConsts ec = expand_consts<BIN>();
 
     float a_pre[RT][4];  // epilogue scales, fetched early
 #pragma unroll
@@ -466,11 +493,13 @@ __device__ __forceinline__ void stage2_body(int blk, char *base, const uint32_t 
             }
         }
         __syncthreads();
-        round_mma<NB, RT, false>(acc, sgn, act, KR, pr0, pr1, wave, li, g, ec);
+        round_mma<NB, RT, false, BIN>(acc, sgn, act, KR, pr0, pr1, wave, li, g, ec);
     }
 
     reduce_waves<NB, RT>(acc, red, wave, lane);
     if (wave == 0 && li < NB) {
+        // affine term (if any): E[row] * stats[li].x + stats[li].y, added before the one rounding
+        const float2 st = aff_E ? *reinterpret_cast<const float2 *>(aff_stats + 2 * li) : float2{0.0f, 0.0f};
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
             const int row0 = i0 + 16 * t + 4 * g;
@@ -478,7 +507,11 @@ __device__ __forceinline__ void stage2_body(int blk, char *base, const uint32_t 
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int row = row0 + v;
-                if (row < n) y[static_cast<size_t>(li) * n + row] = __float2half_rn(d[v] * a_pre[t][v]);
+                if (row < n) {
+                    float val = rounded(d[v] * a_pre[t][v]);
+                    if (aff_E) val = rounded(val + (aff_E[row] * st.x + st.y));
+                    y[static_cast<size_t>(li) * n + row] = __float2half_rn(val);
+                }
             }
         }
     }
@@ -528,7 +561,7 @@ __device__ __forceinline__ void readahead_stage2(const Stage2Readahead &ra, int 
 }
 
 // Stage 1; workgroups past the k / (16 RT) row blocks read ahead for stage 2.
-template <int NB, int RT>
+template <int NB, int RT, bool BIN>
 __global__ __launch_bounds__(kThreads) void mfma_stage1_kernel(const uint32_t *__restrict__ Bt, int Wm,
                                                                const __half *__restrict__ x, int m,
                                                                const __half *__restrict__ b,
@@ -541,16 +574,19 @@ __global__ __launch_bounds__(kThreads) void mfma_stage1_kernel(const uint32_t *_
         readahead_stage2(ra, blockIdx.x, (blockIdx.x - G1) >> 3);
         return;
     }
-    stage1_body<NB, RT>(blockIdx.x, reinterpret_cast<char *>(lds), Bt, Wm, x, m, b, mid, v16, k_pad, PR);
+    stage1_body<NB, RT, BIN>(blockIdx.x, reinterpret_cast<char *>(lds), Bt, Wm, x, m, b, mid, v16, k_pad, PR);
 }
 
-template <int NB, int RT>
+template <int NB, int RT, bool BIN>
 __global__ __launch_bounds__(kThreads) void mfma_stage2_kernel(const uint32_t *__restrict__ At, int Wk,
                                                                const __half *__restrict__ v16, int k_pad,
                                                                const __half *__restrict__ a,
-                                                               __half *__restrict__ y, int n, int PR) {
+                                                               __half *__restrict__ y, int n, int PR,
+                                                               const float *__restrict__ aff_E,
+                                                               const float *__restrict__ aff_stats) {
     extern __shared__ float lds[];
-    stage2_body<NB, RT>(blockIdx.x, reinterpret_cast<char *>(lds), At, Wk, v16, k_pad, a, y, n, PR);
+    stage2_body<NB, RT, BIN>(blockIdx.x, reinterpret_cast<char *>(lds), At, Wk, v16, k_pad, a, y, n, PR, aff_E,
+                             aff_stats);
 }
 
 // Grouped form: one launch runs a stage for several layers that share the
@@ -591,8 +627,8 @@ __global__ __launch_bounds__(kThreads) void mfma_group_stage1_kernel(const Group
     extern __shared__ float lds[];
     const int l = group_layer(g);
     const GroupStage1Layer &L = g.L[l];
-    stage1_body<NB, RT>(blockIdx.x - L.blk0, reinterpret_cast<char *>(lds), L.Bt, g.Wm, g.x, g.m, L.b, L.mid, L.v16,
-                        L.k_pad, g.PR);
+    stage1_body<NB, RT, false>(blockIdx.x - L.blk0, reinterpret_cast<char *>(lds), L.Bt, g.Wm, g.x, g.m, L.b, L.mid,
+                               L.v16, L.k_pad, g.PR);
 }
 
 template <int NB, int RT>
@@ -600,8 +636,8 @@ __global__ __launch_bounds__(kThreads) void mfma_group_stage2_kernel(const Group
     extern __shared__ float lds[];
     const int l = group_layer(g);
     const GroupStage2Layer &L = g.L[l];
-    stage2_body<NB, RT>(blockIdx.x - L.blk0, reinterpret_cast<char *>(lds), L.At, L.Wk, L.v16, L.k_pad, L.a, L.y, L.n,
-                        L.PR);
+    stage2_body<NB, RT, false>(blockIdx.x - L.blk0, reinterpret_cast<char *>(lds), L.At, L.Wk, L.v16, L.k_pad, L.a,
+                               L.y, L.n, L.PR, nullptr, nullptr);
 }
 
 template <typename K>
@@ -619,10 +655,10 @@ int split_rt(int rows) {
     return 4;
 }
 
-template <int NB, int RT>
+template <int NB, int RT, bool BIN>
 int launch_rt(const MfmaDecodeArgs &d, hipStream_t s, int which) {
     if (which == 1) {
-        static const bool once = (allow_lds(mfma_stage1_kernel<NB, RT>, kLdsBudget), true);
+        static const bool once = (allow_lds(mfma_stage1_kernel<NB, RT, BIN>, kLdsBudget), true);
         (void)once;
         const int PR = std::min(d.m_pad / 64, round_pairs<NB, RT>());
         const size_t lds = lds_bytes<NB, RT>(PR);
@@ -641,17 +677,18 @@ int launch_rt(const MfmaDecodeArgs &d, hipStream_t s, int which) {
             if (items > static_cast<size_t>(kReadaheadMax) * 8 * ra.per_xcd * kThreads) ra.per_xcd = 0;
         }
         // the read-ahead blocks start on XCD G1 mod 8; 8 * per_xcd of them cover every XCD equally
-        launch_kernel((mfma_stage1_kernel<NB, RT>), dim3(G1 + 8 * ra.per_xcd), dim3(kThreads), lds, s, d.B_dev,
+        launch_kernel((mfma_stage1_kernel<NB, RT, BIN>), dim3(G1 + 8 * ra.per_xcd), dim3(kThreads), lds, s, d.B_dev,
                       d.m_pad / 32, static_cast<const __half *>(d.x), d.m, static_cast<const __half *>(d.b_dev),
                       static_cast<const __half *>(d.mid_dev), reinterpret_cast<__half *>(d.v16), d.k_pad, PR, ra);
     } else {
-        static const bool once = (allow_lds(mfma_stage2_kernel<NB, RT>, kLdsBudget), true);
+        static const bool once = (allow_lds(mfma_stage2_kernel<NB, RT, BIN>, kLdsBudget), true);
         (void)once;
         const int PR = std::min(d.k_pad / 64, round_pairs<NB, RT>());
         const size_t lds = lds_bytes<NB, RT>(PR);
-        launch_kernel((mfma_stage2_kernel<NB, RT>), dim3(d.n_pad / (16 * RT)), dim3(kThreads), lds, s, d.A_dev,
+        launch_kernel((mfma_stage2_kernel<NB, RT, BIN>), dim3(d.n_pad / (16 * RT)), dim3(kThreads), lds, s, d.A_dev,
                       d.k_pad / 32, reinterpret_cast<const __half *>(d.v16), d.k_pad,
-                      static_cast<const __half *>(d.a_dev), static_cast<__half *>(d.y), d.n, PR);
+                      static_cast<const __half *>(d.a_dev), static_cast<__half *>(d.y), d.n, PR, d.aff_E,
+                      d.aff_stats);
     }
     return static_cast<int>(hipGetLastError());
 }
@@ -659,9 +696,14 @@ int launch_rt(const MfmaDecodeArgs &d, hipStream_t s, int which) {
 template <int NB>
 int launch_nb(const MfmaDecodeArgs &d, hipStream_t s, int which) {
     const int rt = split_rt(which == 1 ? d.k_pad : d.n_pad);
-    if (rt == 2) return launch_rt<NB, 2>(d, s, which);
-    if (rt == 4) return launch_rt<NB, 4>(d, s, which);
-    return launch_rt<NB, 1>(d, s, which);
+    if (d.binary) {
+        if (rt == 2) return launch_rt<NB, 2, true>(d, s, which);
+        if (rt == 4) return launch_rt<NB, 4, true>(d, s, which);
+        return launch_rt<NB, 1, true>(d, s, which);
+    }
+    if (rt == 2) return launch_rt<NB, 2, false>(d, s, which);
+    if (rt == 4) return launch_rt<NB, 4, false>(d, s, which);
+    return launch_rt<NB, 1, false>(d, s, which);
 }
 
 template <int NB, int RT>

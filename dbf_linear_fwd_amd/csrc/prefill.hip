@@ -65,15 +65,18 @@ constexpr int kThreads = 256;
 constexpr int kXcds = 8;             // MI355X: blocks are dispatched round-robin over 8 XCDs
 
 struct ExpandConsts {
-    uint32_t mask, one;
+    uint32_t mask, one, mask2;
 };
 
 // The constants of the sign expansion as register values (see expand()).
 // Called once at kernel entry, before any MFMA is issued.
+template <bool BIN>
 __device__ __forceinline__ ExpandConsts expand_consts() {
     ExpandConsts c;
     asm volatile("s_mov_b32 %0, 0x80008000" : "=s"(c.mask));
     asm volatile("v_mov_b32 %0, 0x3c003c00" : "=v"(c.one));
+    if constexpr (BIN) asm volatile("s_mov_b32 %0, 0x40004000" : "=s"(c.mask2));
+    else c.mask2 = 0;
     return c;
 }
 
@@ -81,17 +84,40 @@ __device__ __forceinline__ ExpandConsts expand_consts() {
 // pairs, SCALED) or ±1.0.  Element 2q sits at bit q and element 2q+1 at bit
 // 16+q; after one shift by 12-4g the pair (8g+2p, 8g+2p+1) is at bits
 // (12+p, 28+p) and a further shift by 3-p puts it on the fp16 sign bits.
-template <bool SCALED>
+// BIN: the word is a row of a 0/1 matrix and the operand is {0, 2.0}: the
+// pair one bit lower, on the top exponent bit of each fp16 (0x4000 = 2.0);
+// the factor 2 is folded into the scales.
+template <bool SCALED, bool BIN>
 __device__ __forceinline__ f16x8 expand(uint32_t word, int g, const u32x4 &sc, ExpandConsts ec) {
     const uint32_t sh = word << (12 - 4 * g);
     u32x4 r;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const uint32_t m = (sh << (3 - p)) & ec.mask;
-        r[p] = SCALED ? (sc[p] ^ m) : (m | ec.one);
+        if constexpr (BIN) {
+            r[p] = (p < 3 ? sh << (2 - p) : sh >> 1) & ec.mask2;
+        } else {
+            const uint32_t m = (sh << (3 - p)) & ec.mask;
+            r[p] = SCALED ? (sc[p] ^ m) : (m | ec.one);
+        }
     }
     return __builtin_bit_cast(f16x8, r);
 }
+
+// x as an fp32 value the compiler must materialize: the product rounded to
+// fp32 is then converted to fp16, in every kernel form alike (the compiler
+// may otherwise fuse product and conversion into one mixed-precision
+// instruction that rounds the exact product once, in some forms only).
+__device__ __forceinline__ float rounded(float x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+// Optional affine output term: out[r][c] = rne16(sn[c] * C[r][c] + E[c] *
+// stats[r].x + stats[r].y) (E null: none).
+struct Affine {
+    const float *E;
+    const float *stats;  // [M][2]
+};
 
 // Batch-sum epilogue (gradients): for every output column c, the sum over
 // the wave's 64 rows of C[r][c] * Q[r][c], written to part[(r0 / 64) * n_out
@@ -108,7 +134,8 @@ struct DotArgs {
 template <int MF_, int NF_>
 __device__ __forceinline__ void epilogue(const f32x16 (&acc)[MF_][NF_], const float (&snv)[NF_], int M, int n_out,
                                          int row0, int col0, int l32, int kg, __half *__restrict__ out, int ldo,
-                                         float *__restrict__ out32, int ldo32, const DotArgs &dot) {
+                                         float *__restrict__ out32, int ldo32, const DotArgs &dot,
+                                         const Affine &aff) {
     static_assert(32 * MF_ == 64, "batch-sum groups are the waves' 64 rows");
 #pragma unroll
     for (int i = 0; i < MF_; ++i) {
@@ -120,7 +147,11 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[MF_][NF_], const fl
             for (int v = 0; v < 16; ++v) {
                 const int row = row0 + i * 32 + 8 * (v >> 2) + 4 * kg + (v & 3);
                 if (row < M) {
-                    if (out) out[static_cast<size_t>(row) * ldo + col] = __float2half_rn(acc[i][f][v] * snv[f]);
+                    if (out) {
+                        float val = rounded(acc[i][f][v] * snv[f]);
+                        if (aff.E) val = rounded(val + (aff.E[col] * aff.stats[2 * row] + aff.stats[2 * row + 1]));
+                        out[static_cast<size_t>(row) * ldo + col] = __float2half_rn(val);
+                    }
                     if (out32) out32[static_cast<size_t>(row) * ldo32 + col] = acc[i][f][v];
                 }
             }
@@ -173,7 +204,7 @@ __device__ __forceinline__ void store_partial(const f32x16 (&acc)[MF_][NF_], int
 // thread per output, the loads of up to eight parts in flight at a time.
 __global__ __launch_bounds__(256) void split_finish_kernel(const float *__restrict__ part, int nsplit, int M,
                                                            int n_out, int ldw, const __half *__restrict__ sn,
-                                                           __half *__restrict__ out, int ldo) {
+                                                           __half *__restrict__ out, int ldo, const Affine aff) {
     const int idx = blockIdx.x * 256 + threadIdx.x;
     if (idx >= M * n_out) return;
     const int row = idx / n_out, col = idx - row * n_out;
@@ -188,7 +219,9 @@ __global__ __launch_bounds__(256) void split_finish_kernel(const float *__restri
         for (int u = 0; u < 8; ++u)
             if (k0 + u < nsplit) s += v[u];
     }
-    out[static_cast<size_t>(row) * ldo + col] = __float2half_rn(s * __half2float(sn[col]));
+    float val = rounded(s * __half2float(sn[col]));
+    if (aff.E) val = rounded(val + (aff.E[col] * aff.stats[2 * row] + aff.stats[2 * row + 1]));
+    out[static_cast<size_t>(row) * ldo + col] = __float2half_rn(val);
 }
 
 // C = P S'ᵀ (see the file comment).  P: fp16 [M][ldp], K valid columns
@@ -197,19 +230,18 @@ __global__ __launch_bounds__(256) void split_finish_kernel(const float *__restri
 // per output column.  out: fp16 [M][ldo], columns < n_out written.
 // PVEC: rows of P are 16-byte aligned (ldp % 8 == 0).  KFULL: also K % 64
 // == 0, so every K step loads whole 16-byte items with no bounds test.
-template <bool HAS_SK, bool PVEC, bool KFULL>
+template <bool HAS_SK, bool PVEC, bool KFULL, bool BIN>
 __global__ __launch_bounds__(kThreads, DBF_PREFILL_OCC) void sign_gemm_kernel(const __half *__restrict__ P, int ldp, int M, int K,
                                                              const uint32_t *__restrict__ S, int words,
                                                              int n_rows_pad, const __half *__restrict__ sk,
                                                              const __half *__restrict__ sn,
                                                              __half *__restrict__ out, int ldo, int n_out,
                                                              float *__restrict__ out32, int ldo32, const DotArgs dot,
-                                                             int nbm,
-                                                             int nbn) {
+                                                             const Affine aff, int nbm, int nbn) {
     __shared__ _Float16 Ps[2][BM * LDP];
     __shared__ uint32_t Ss[2][BK / 2];  // sk of the K step, as half pairs
 
-    const ExpandConsts ec = expand_consts();
+    const ExpandConsts ec = expand_consts<BIN>();
     // XCD-aware tile order: the blocks of one XCD take consecutive tiles.
     const int G = nbm * nbn;
     const int b = blockIdx.x;
@@ -308,7 +340,7 @@ __global__ __launch_bounds__(kThreads, DBF_PREFILL_OCC) void sign_gemm_kernel(co
             const int g = 2 * (s & 1) + kg;  // which 8 elements of the 32-element word
 #pragma unroll
             for (int f = 0; f < NF; ++f) {
-                const f16x8 bf = expand<HAS_SK>(s < 2 ? wcur[f].x : wcur[f].y, g, sc, ec);
+                const f16x8 bf = expand<HAS_SK, BIN>(s < 2 ? wcur[f].x : wcur[f].y, g, sc, ec);
 #pragma unroll
                 for (int i = 0; i < MF; ++i)
                     acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf, acc[i][f], 0, 0, 0);
@@ -322,19 +354,33 @@ __global__ __launch_bounds__(kThreads, DBF_PREFILL_OCC) void sign_gemm_kernel(co
         __syncthreads();
     }
 
-    epilogue<MF, NF>(acc, snv, M, n_out, m0 + wm * 32 * MF, n0 + wn * 32 * NF, l32, kg, out, ldo, out32, ldo32, dot);
+    epilogue<MF, NF>(acc, snv, M, n_out, m0 + wm * 32 * MF, n0 + wn * 32 * NF, l32, kg, out, ldo, out32, ldo32, dot,
+                     aff);
 }
 
-template <bool HAS_SK, bool PVEC, bool KFULL>
-void launch(const void *P, int ldp, int M, int K, const uint32_t *S, int words, int n_rows_pad, const void *sk,
-            const void *sn, void *out, int ldo, int n_out, float *out32, int ldo32, const DotArgs &dot,
-            hipStream_t s) {
-    const int nbm = (M + BM - 1) / BM;
-    const int nbn = (n_out + BN - 1) / BN;
-    launch_kernel((sign_gemm_kernel<HAS_SK, PVEC, KFULL>), dim3(nbm * nbn), dim3(kThreads), 0, s,
-                       static_cast<const __half *>(P), ldp, M, K, S, words, n_rows_pad,
-                       static_cast<const __half *>(sk), static_cast<const __half *>(sn), static_cast<__half *>(out),
-                       ldo, n_out, out32, ldo32, dot, nbm, nbn);
+// Host-side arguments of one product launch.
+struct GemmLaunch {
+    const void *P;
+    int ldp, M, K;
+    const uint32_t *S;
+    int words, n_rows_pad;
+    const void *sk, *sn;
+    void *out;
+    int ldo, n_out;
+    float *out32;
+    int ldo32;
+    DotArgs dot;
+    Affine aff;
+};
+
+template <bool HAS_SK, bool PVEC, bool KFULL, bool BIN>
+void launch(const GemmLaunch &a, hipStream_t s) {
+    const int nbm = (a.M + BM - 1) / BM;
+    const int nbn = (a.n_out + BN - 1) / BN;
+    launch_kernel((sign_gemm_kernel<HAS_SK, PVEC, KFULL, BIN>), dim3(nbm * nbn), dim3(kThreads), 0, s,
+                  static_cast<const __half *>(a.P), a.ldp, a.M, a.K, a.S, a.words, a.n_rows_pad,
+                  static_cast<const __half *>(a.sk), static_cast<const __half *>(a.sn), static_cast<__half *>(a.out),
+                  a.ldo, a.n_out, a.out32, a.ldo32, a.dot, a.aff, nbm, nbn);
 }
 
 
@@ -432,7 +478,7 @@ __device__ __forceinline__ void wait_step(int y) {
 // stage pointers are restrict-qualified: they never overlap, and the compiler
 // then does not hold the LDS reads of `src` back until the loads into `dst`
 // have landed (the kernel orders them itself with vmcnt and the barrier).
-template <bool HAS_SK, int KP, int D, typename IssueOne>
+template <bool HAS_SK, int KP, int D, bool BIN, typename IssueOne>
 __device__ __forceinline__ void dma_step(bool go, int nxt, char *__restrict__ dst, const char *__restrict__ src,
                                          IssueOne &issue_one, f32x16 (&acc)[DMF][DNF], int wm, int wn, int l32,
                                          int kg, ExpandConsts ec) {
@@ -459,7 +505,7 @@ __device__ __forceinline__ void dma_step(bool go, int nxt, char *__restrict__ ds
         const int g = 2 * (s & 1) + kg;
 #pragma unroll
         for (int f = 0; f < DNF; ++f) {
-            const f16x8 bf = expand<HAS_SK>((s & 3) < 2 ? w[f].x : w[f].y, g, sc, ec);
+            const f16x8 bf = expand<HAS_SK, BIN>((s & 3) < 2 ? w[f].x : w[f].y, g, sc, ec);
 #pragma unroll
             for (int i = 0; i < DMF; ++i)
                 acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf, acc[i][f], 0, 0, 0);
@@ -468,20 +514,20 @@ __device__ __forceinline__ void dma_step(bool go, int nxt, char *__restrict__ ds
     }
 }
 
-template <bool HAS_SK, int KP>
+template <bool HAS_SK, int KP, bool BIN>
 __global__ __launch_bounds__(kDThreads) void sign_gemm_dma_kernel(const __half *__restrict__ P, int ldp, int M,
                                                                  const uint32_t *__restrict__ S, int words,
                                                                  int n_rows_pad, const __half *__restrict__ sk,
                                                                  const __half *__restrict__ sn,
                                                                  __half *__restrict__ out, int ldo, int n_out,
                                                                  float *__restrict__ out32, int ldo32, const DotArgs dot,
-                                                                 int nbm, int nbn, float *__restrict__ part,
-                                                                 int nsplit, int ldw) {
+                                                                 const Affine aff, int nbm, int nbn,
+                                                                 float *__restrict__ part, int nsplit, int ldw) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     using C = DmaStep<KP>;
     constexpr int D = C::PI + C::SI + (HAS_SK ? 1 : 0);  // loads per step and wave
 
-    const ExpandConsts ec = expand_consts();
+    const ExpandConsts ec = expand_consts<BIN>();
     // XCD-aware order over (split, tile), tile fastest: the blocks of one XCD
     // take consecutive indexes, so they share a K range (and rows of P)
     const int T = nbm * nbn;
@@ -563,7 +609,7 @@ __global__ __launch_bounds__(kDThreads) void sign_gemm_dma_kernel(const __half *
         __builtin_amdgcn_s_barrier();  // ... and every other wave's; step kt - 1's buffer is free
         asm volatile("" ::: "memory");
         const int nxt = kt + kStages - 1;
-        dma_step<HAS_SK, KP, D>(nxt < nk, nxt, lds + (nxt % kStages) * C::StageBytes,
+        dma_step<HAS_SK, KP, D, BIN>(nxt < nk, nxt, lds + (nxt % kStages) * C::StageBytes,
                                 lds + (kt % kStages) * C::StageBytes, issue_one, acc, wm, wn, l32, kg, ec);
     }
 
@@ -573,25 +619,23 @@ __global__ __launch_bounds__(kDThreads) void sign_gemm_dma_kernel(const __half *
         return;
     }
     epilogue<DMF, DNF>(acc, snv, M, n_out, m0 + wm * 32 * DMF, n0 + wn * 32 * DNF, l32, kg, out, ldo, out32, ldo32,
-                       dot);
+                       dot, aff);
 }
 
-template <bool HAS_SK, int KP>
-void launch_dma(const void *P, int ldp, int M, const uint32_t *S, int words, int n_rows_pad, const void *sk,
-                const void *sn, void *out, int ldo, int n_out, float *out32, int ldo32, const DotArgs &dot,
-                hipStream_t s, float *part = nullptr, int nsplit = 1, int ldw = 0) {
+template <bool HAS_SK, int KP, bool BIN>
+void launch_dma(const GemmLaunch &a, hipStream_t s, float *part = nullptr, int nsplit = 1, int ldw = 0) {
     using C = DmaStep<KP>;
     static const bool once =
-        ((void)hipFuncSetAttribute(reinterpret_cast<const void *>(sign_gemm_dma_kernel<HAS_SK, KP>),
+        ((void)hipFuncSetAttribute(reinterpret_cast<const void *>(sign_gemm_dma_kernel<HAS_SK, KP, BIN>),
                                    hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(C::Lds)),
          true);
     (void)once;
-    const int nbm = (M + BM - 1) / BM;
-    const int nbn = (n_out + DBN - 1) / DBN;
-    launch_kernel((sign_gemm_dma_kernel<HAS_SK, KP>), dim3(nbm * nbn * nsplit), dim3(kDThreads), C::Lds, s,
-                  static_cast<const __half *>(P), ldp, M, S, words, n_rows_pad, static_cast<const __half *>(sk),
-                  static_cast<const __half *>(sn), static_cast<__half *>(out), ldo, n_out, out32, ldo32, dot, nbm, nbn,
-                  part, nsplit, ldw);
+    const int nbm = (a.M + BM - 1) / BM;
+    const int nbn = (a.n_out + DBN - 1) / DBN;
+    launch_kernel((sign_gemm_dma_kernel<HAS_SK, KP, BIN>), dim3(nbm * nbn * nsplit), dim3(kDThreads), C::Lds, s,
+                  static_cast<const __half *>(a.P), a.ldp, a.M, a.S, a.words, a.n_rows_pad,
+                  static_cast<const __half *>(a.sk), static_cast<const __half *>(a.sn), static_cast<__half *>(a.out),
+                  a.ldo, a.n_out, a.out32, a.ldo32, a.dot, a.aff, nbm, nbn, part, nsplit, ldw);
 }
 
 #ifndef DBF_SPLIT_BELOW
@@ -637,38 +681,38 @@ size_t sign_gemm_split_elems(int M, int K, int words, int n_out) {
 #endif
 }
 
-int launch_split_finish(const SplitK &split, int M, int n_out, const void *sn, void *out, int ldo, void *stream) {
+int launch_split_finish(const SplitK &split, int M, int n_out, const void *sn, void *out, int ldo, void *stream,
+                        const float *aff_E, const float *aff_stats) {
     const int items = M * n_out;
     if (items == 0) return 0;
     launch_kernel(split_finish_kernel, dim3((items + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream),
                   static_cast<const float *>(split.ws), split.nsplit, M, n_out, split.ldw,
-                  static_cast<const __half *>(sn), static_cast<__half *>(out), ldo);
+                  static_cast<const __half *>(sn), static_cast<__half *>(out), ldo, Affine{aff_E, aff_stats});
     return static_cast<int>(hipGetLastError());
 }
 
-int launch_sign_gemm(const void *P, int ldp, int M, int K, const uint32_t *S, int words, int n_rows_pad,
-                     const void *sk, const void *sn, void *out, int ldo, int n_out, float *out32, int ldo32,
-                     const void *dq, int dq_f32, int lddq, float *dpart, void *stream, SplitK *split) {
-    const DotArgs dot{dq, dq_f32, lddq, dpart};
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool pvec = (ldp & 7) == 0;
-    const bool kfull = pvec && (K % BK) == 0;
-    if (split) split->nsplit = 1;
+namespace {
+
+template <bool HAS_SK, bool BIN>
+void dispatch_dma(const GemmLaunch &a, hipStream_t s, int kp, float *part = nullptr, int nsplit = 1, int ldw = 0) {
+    if (kp == 2) launch_dma<HAS_SK, 2, BIN>(a, s, part, nsplit, ldw);
+    else launch_dma<HAS_SK, 1, BIN>(a, s, part, nsplit, ldw);
+}
+
+template <bool HAS_SK, bool BIN>
+int dispatch(const GemmLaunch &a, hipStream_t s, SplitK *split) {
+    const bool pvec = (a.ldp & 7) == 0;
+    const bool kfull = pvec && (a.K % BK) == 0;
 #ifndef DBF_PREFILL_NO_DMA
-    if (kfull && (reinterpret_cast<uintptr_t>(P) & 15) == 0 && K == words * 32) {
-        if (split && split->ws && out && sn && !out32 && !dpart) {
-            const int parts = split_parts(M, words, n_out);
-            const int ldw = (n_out + 3) & ~3;
-            if (parts > 1 && static_cast<size_t>(parts) * M * ldw <= split->cap) {
+    if (kfull && (reinterpret_cast<uintptr_t>(a.P) & 15) == 0 && a.K == a.words * 32) {
+        const int kp = dma_pairs(a.M, a.words, a.n_out);
+        if (split && split->ws && a.out && a.sn && !a.out32 && !a.dot.part) {
+            const int parts = split_parts(a.M, a.words, a.n_out);
+            const int ldw = (a.n_out + 3) & ~3;
+            if (parts > 1 && static_cast<size_t>(parts) * a.M * ldw <= split->cap) {
                 split->nsplit = parts;
                 split->ldw = ldw;
-                if (dma_pairs(M, words, n_out) == 2) {
-                    if (sk) launch_dma<true, 2>(P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, dot, s, split->ws, parts, ldw);
-                    else launch_dma<false, 2>(P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, dot, s, split->ws, parts, ldw);
-                } else {
-                    if (sk) launch_dma<true, 1>(P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, dot, s, split->ws, parts, ldw);
-                    else launch_dma<false, 1>(P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, dot, s, split->ws, parts, ldw);
-                }
+                dispatch_dma<HAS_SK, BIN>(a, s, kp, split->ws, parts, ldw);
                 return static_cast<int>(hipGetLastError());
             }
         }
@@ -676,32 +720,33 @@ int launch_sign_gemm(const void *P, int ldp, int M, int K, const uint32_t *S, in
         // workgroups over the 256 CUs; else steps of 64, whose 74 KiB of LDS
         // lets two workgroups share a CU (a partial last wave of tiles then
         // runs beside the first instead of after it)
-        if constexpr (kDmaPairs == 2) {
-            const int tiles = ((M + BM - 1) / BM) * ((n_out + DBN - 1) / DBN);
-            if (words % 4 == 0 && tiles <= 256) {
-                if (sk) launch_dma<true, 2>(P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, dot, s);
-                else launch_dma<false, 2>(P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, dot, s);
-                return static_cast<int>(hipGetLastError());
-            }
-        }
-        {
-            if (sk) launch_dma<true, 1>(P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, dot, s);
-            else launch_dma<false, 1>(P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, dot, s);
-        }
+        dispatch_dma<HAS_SK, BIN>(a, s, kp);
         return static_cast<int>(hipGetLastError());
     }
 #endif
-    if (sk) {
-        if (kfull) launch<true, true, true>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, dot, s);
-        else if (pvec) launch<true, true, false>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, dot, s);
-        else launch<true, false, false>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, dot, s);
-    } else {
-        // the second product's K is k_pad, a multiple of 64
-        if (kfull) launch<false, true, true>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, dot, s);
-        else if (pvec) launch<false, true, false>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, dot, s);
-        else launch<false, false, false>(P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, dot, s);
-    }
+    if (kfull) launch<HAS_SK, true, true, BIN>(a, s);
+    else if (pvec) launch<HAS_SK, true, false, BIN>(a, s);
+    else launch<HAS_SK, false, false, BIN>(a, s);
     return static_cast<int>(hipGetLastError());
+}
+
+}  // namespace
+
+int launch_sign_gemm(const void *P, int ldp, int M, int K, const uint32_t *S, int words, int n_rows_pad,
+                     const void *sk, const void *sn, void *out, int ldo, int n_out, float *out32, int ldo32,
+                     const void *dq, int dq_f32, int lddq, float *dpart, void *stream, SplitK *split,
+                     const GemmFlavor *flavor) {
+    const GemmLaunch a{P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32,
+                       DotArgs{dq, dq_f32, lddq, dpart},
+                       Affine{flavor ? flavor->aff_E : nullptr, flavor ? flavor->aff_stats : nullptr}};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (split) split->nsplit = 1;
+    if (flavor && flavor->binary) {
+        if (sk) return static_cast<int>(hipErrorInvalidValue);  // 0/1 matrices take no per-K scale
+        return dispatch<false, true>(a, s, split);
+    }
+    if (sk) return dispatch<true, false>(a, s, split);
+    return dispatch<false, false>(a, s, split);
 }
 
 }  // namespace dbf

@@ -10,6 +10,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
+#include <limits>
 #include <cstdlib>
 #include <cstring>
 #include <map>
@@ -37,6 +39,10 @@ struct dbf_layer {
     uint16_t *v16 = nullptr;      // matrix-core decode intermediate [2][16][k_pad] fp16
     float *split = nullptr;       // split-K parts of the prefill products (small grids)
     size_t split_cap = 0;         // floats
+    // BQQ-form layer (dbf_bqq_pack): A, B hold 0/1 matrices, and the output
+    // gains E[o] * Σx + γ·x (per-row sums in bqq_stats [max_batch][2])
+    bool binary = false;
+    float *bqq_E = nullptr, *bqq_gamma = nullptr, *bqq_stats = nullptr;
     size_t packed_bytes = 0, scale_bytes = 0, workspace_bytes = 0;
     // backward (dbf_pack_ex with DBF_PACK_BACKWARD): the transposed layer
     // Wᵀ = diag(b) Bᵀ diag(mid) Aᵀ diag(a), and fp32 intermediates of the
@@ -98,6 +104,9 @@ void release(dbf_layer *h) {
     (void)hipFree(h->tickets);
     (void)hipFree(h->v16);
     (void)hipFree(h->split);
+    (void)hipFree(h->bqq_E);
+    (void)hipFree(h->bqq_gamma);
+    (void)hipFree(h->bqq_stats);
     (void)hipFree(h->t32);
     (void)hipFree(h->red);
     release(h->bwd);
@@ -204,6 +213,16 @@ dbf_status_t timed_launch(dbf_layer *h, const char *name, hipStream_t stream, F 
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// The value of an fp16 bit pattern, exactly, as a double.
+double half_bits_value(uint16_t h) {
+    const int ex = (h >> 10) & 31, man = h & 1023;
+    double v;
+    if (ex == 0) v = std::ldexp(double(man), -24);
+    else if (ex == 31) v = man ? std::numeric_limits<double>::quiet_NaN() : std::numeric_limits<double>::infinity();
+    else v = std::ldexp(double(man + 1024), ex - 25);
+    return (h & 0x8000) ? -v : v;
+}
 
 }  // namespace
 
@@ -368,6 +387,83 @@ extern "C" dbf_status_t dbf_pack_ex(int32_t n, int32_t m, int32_t k, const int8_
     return DBF_OK;
 }
 
+extern "C" dbf_status_t dbf_bqq_pack(int32_t n, int32_t m, int32_t d, int32_t p, const uint8_t *Y,
+                                     const uint8_t *Z, const uint16_t *r, const uint16_t *s, const uint16_t *t,
+                                     uint16_t u, int32_t max_batch, dbf_handle_t *out) {
+    if (out) *out = nullptr;
+    if (!out || !Y || !Z || !r || !s || !t) return DBF_ERR_INVALID_ARG;
+    if (n < 1 || m < 1 || d < 1 || p < 1 || max_batch < 1) return DBF_ERR_INVALID_ARG;
+    const int64_t k = int64_t(p) * d;
+    if (k > (int64_t(1) << 30)) return DBF_ERR_SHAPE;
+    for (int64_t i = 0; i < int64_t(p) * n * d; ++i)
+        if (Y[i] > 1) return DBF_ERR_INVALID_ARG;
+    for (int64_t i = 0; i < int64_t(p) * d * m; ++i)
+        if (Z[i] > 1) return DBF_ERR_INVALID_ARG;
+    g_alloc_calls = 0;
+    // The p products as one: Y_0 .. Y_{p-1} side by side (n x p d), Z_i
+    // stacked (p d x m), in the packed-sign encoding (bit 1 <-> entry 1,
+    // passed as -1).  Both products expand to {0, 2}: mid = r_i and
+    // a = 1/4 undo the two factors of 2; b = 1.
+    std::vector<int8_t> As, Bs;
+    std::vector<uint16_t> a16, mid16, b16;
+    std::vector<double> E(static_cast<size_t>(n)), gamma(static_cast<size_t>(m), 0.0);
+    try {
+        As.resize(static_cast<size_t>(n) * k);
+        Bs.resize(static_cast<size_t>(k) * m);
+        a16.assign(static_cast<size_t>(n), 0x3400);  // fp16 0.25
+        b16.assign(static_cast<size_t>(m), 0x3C00);  // fp16 1.0
+        mid16.resize(static_cast<size_t>(k));
+    } catch (const std::bad_alloc &) {
+        return DBF_ERR_OOM;
+    }
+    const double uu = half_bits_value(u);
+    for (int64_t o = 0; o < n; ++o) E[o] = uu;
+    for (int64_t i = 0; i < p; ++i) {
+        const double si = half_bits_value(s[i]), ti = half_bits_value(t[i]);
+        for (int64_t j = 0; j < d; ++j) mid16[i * d + j] = r[i];
+        for (int64_t o = 0; o < n; ++o) {
+            const uint8_t *yrow = Y + (i * n + o) * d;
+            int64_t deg = 0;
+            for (int64_t j = 0; j < d; ++j) {
+                As[o * k + i * d + j] = yrow[j] ? -1 : 1;
+                deg += yrow[j];
+            }
+            E[o] += si * double(deg);
+        }
+        for (int64_t j = 0; j < d; ++j) {
+            const uint8_t *zrow = Z + (i * d + j) * m;
+            int8_t *brow = Bs.data() + (i * d + j) * m;
+            for (int64_t l = 0; l < m; ++l) {
+                brow[l] = zrow[l] ? -1 : 1;
+                gamma[l] += ti * double(zrow[l]);
+            }
+        }
+    }
+    dbf_layer *h = nullptr;
+    dbf_status_t st = pack_layer(n, m, static_cast<int32_t>(k), As.data(), Bs.data(), a16.data(), mid16.data(),
+                                 b16.data(), max_batch, &h);
+    if (st != DBF_OK) return st;
+    std::vector<int8_t>().swap(As);
+    std::vector<int8_t>().swap(Bs);
+    h->binary = true;
+    std::vector<float> E32(E.begin(), E.end()), g32(gamma.begin(), gamma.end());
+    if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->bqq_E), sizeof(float) * E32.size());
+    if (st == DBF_OK) st = upload(h->bqq_E, E32.data(), sizeof(float) * E32.size());
+    if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->bqq_gamma), sizeof(float) * g32.size());
+    if (st == DBF_OK) st = upload(h->bqq_gamma, g32.data(), sizeof(float) * g32.size());
+    if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->bqq_stats), sizeof(float) * 2 * size_t(max_batch));
+    if (st == DBF_OK) {
+        h->scale_bytes += sizeof(float) * (E32.size() + g32.size());
+        h->workspace_bytes += sizeof(float) * 2 * size_t(max_batch);
+    }
+    if (st != DBF_OK) {
+        release(h);
+        return st;
+    }
+    *out = h;
+    return DBF_OK;
+}
+
 extern "C" void dbf_free(dbf_handle_t h) {
     if (!h) return;
     int cur = 0;
@@ -414,6 +510,9 @@ static dbf_status_t forward_decode_mfma(dbf_layer *h, const void *x, void *y, in
     d.n_pad = h->n_pad;
     d.m_pad = h->m_pad;
     d.k_pad = h->k_pad;
+    d.binary = h->binary ? 1 : 0;
+    d.aff_E = h->bqq_E;
+    d.aff_stats = h->bqq_stats;
     dbf_status_t st = timed_launch(h, "decode_stage1", stream, [&] { return dbf::launch_mfma_decode(d, stream, 1); });
     if (st != DBF_OK) return st;
     return timed_launch(h, "decode_stage2", stream, [&] { return dbf::launch_mfma_decode(d, stream, 2); });
@@ -464,12 +563,19 @@ static dbf_status_t forward_decode(dbf_layer *h, const void *x, void *y, int32_t
 
 static dbf_status_t forward_prefill(dbf_layer *h, const void *x, void *y, int32_t batch, hipStream_t stream) {
     // T = rne16(mid ⊙ (X (B ⊙ b)ᵀ)), all k_pad columns (padded ones are 0).
+    // (BQQ-form layers: 0/1 matrices, b = 1 so no per-K scale, and the
+    // affine term in the second product's epilogue)
     dbf::SplitK sp;
     sp.ws = h->split;
     sp.cap = h->split_cap;
+    dbf::GemmFlavor f1, f2;
+    f1.binary = f2.binary = h->binary ? 1 : 0;
+    f2.aff_E = h->bqq_E;
+    f2.aff_stats = h->bqq_stats;
+    const void *sk = h->binary ? nullptr : h->b_dev;
     dbf_status_t st = timed_launch(h, "prefill_gemm1", stream, [&] {
-        return dbf::launch_sign_gemm(x, h->m, batch, h->m, h->B_dev, h->Wm, h->k_pad, h->b_dev, h->mid_dev, h->T,
-                                     h->k_pad, h->k_pad, nullptr, 0, nullptr, 0, 0, nullptr, stream, &sp);
+        return dbf::launch_sign_gemm(x, h->m, batch, h->m, h->B_dev, h->Wm, h->k_pad, sk, h->mid_dev, h->T,
+                                     h->k_pad, h->k_pad, nullptr, 0, nullptr, 0, 0, nullptr, stream, &sp, &f1);
     });
     if (st == DBF_OK && sp.nsplit > 1)
         st = timed_launch(h, "prefill_split1", stream, [&] {
@@ -479,11 +585,11 @@ static dbf_status_t forward_prefill(dbf_layer *h, const void *x, void *y, int32_
     // Y = rne16(a ⊙ (T Aᵀ)).
     st = timed_launch(h, "prefill_gemm2", stream, [&] {
         return dbf::launch_sign_gemm(h->T, h->k_pad, batch, h->k_pad, h->A_dev, h->Wk, h->n_pad, nullptr,
-                                     h->a_dev, y, h->n, h->n, nullptr, 0, nullptr, 0, 0, nullptr, stream, &sp);
+                                     h->a_dev, y, h->n, h->n, nullptr, 0, nullptr, 0, 0, nullptr, stream, &sp, &f2);
     });
     if (st == DBF_OK && sp.nsplit > 1)
         st = timed_launch(h, "prefill_split2", stream, [&] {
-            return dbf::launch_split_finish(sp, batch, h->n, h->a_dev, y, h->n, stream);
+            return dbf::launch_split_finish(sp, batch, h->n, h->a_dev, y, h->n, stream, h->bqq_E, h->bqq_stats);
         });
     return st;
 }
@@ -502,7 +608,16 @@ extern "C" dbf_status_t dbf_linear_forward_ex(dbf_handle_t h, const void *x, voi
     int cur = -1;
     if (hipGetDevice(&cur) != hipSuccess) return DBF_ERR_HIP;
     if (cur != h->device) return DBF_ERR_INVALID_ARG;
-    if (path == DBF_PATH_DECODE_TABLE) return forward_decode(h, x, y, batch, stream);
+    if (path == DBF_PATH_DECODE_TABLE) {
+        if (h->binary) return DBF_ERR_UNSUPPORTED;
+        return forward_decode(h, x, y, batch, stream);
+    }
+    if (h->binary) {
+        const dbf_status_t st = timed_launch(h, "bqq_rowstats", stream, [&] {
+            return dbf::launch_bqq_rowstats(x, batch, h->m, h->bqq_gamma, h->bqq_stats, stream);
+        });
+        if (st != DBF_OK) return st;
+    }
     const bool decode = path == DBF_PATH_DECODE || (path == DBF_PATH_AUTO && batch <= dbf::kDecodeMaxBatch);
     return decode ? forward_decode_mfma(h, x, y, batch, stream) : forward_prefill(h, x, y, batch, stream);
 }
@@ -514,6 +629,7 @@ extern "C" dbf_status_t dbf_linear_forward_group(const dbf_handle_t *hs, int32_t
         if (!hs[i]) return DBF_ERR_INVALID_ARG;
         if (hs[i]->m != hs[0]->m || hs[i]->device != hs[0]->device || batch > hs[i]->max_batch)
             return DBF_ERR_INVALID_ARG;
+        if (hs[i]->binary) return DBF_ERR_UNSUPPORTED;
     }
     if (batch == 0) return DBF_OK;
     if (!x || !aligned16(x)) return DBF_ERR_INVALID_ARG;

@@ -172,6 +172,35 @@ dbf_status_t dbf_pack_ex(int32_t n, int32_t m, int32_t k,
                          int32_t max_batch, int32_t flags, dbf_handle_t *out);
 
 /*
+ * dbf_bqq_pack -- a layer whose weight is in the binary-quadratic form of
+ * the TL;DR of "Binary Quadratic Quantization: Beyond First-Order
+ * Quantization for Real-Valued Matrix Compression" (sciencestack.ai page):
+ *   W = Σ_{i<p} ( r_i Y_i Z_i + s_i Y_i 1 + t_i 1 Z_i ) + u 1        (n x m)
+ * with Y_i (n x d) and Z_i (d x m) 0/1 matrices and 1 an all-ones matrix of
+ * the shape that fits.  The returned handle takes dbf_linear_forward and
+ * dbf_linear_forward_ex (paths AUTO, DECODE, PREFILL) with the contract of a
+ * DBF layer: y = rne16(x Wᵀ), fp32 accumulation, one final rounding.
+ *   Y      host uint8, p x n x d (row-major, term-major), entries 0 or 1.
+ *   Z      host uint8, p x d x m, entries 0 or 1.
+ *   r,s,t  host fp16 bit patterns, p each; u one fp16 bit pattern.
+ * The p products run as one DBF product with middle dimension p*d on the
+ * DBF kernels (0/1 operands, mid = r_i per term); the other terms reduce to
+ * E[o] * Σx + γ·x with E[o] = Σ_i s_i (row o of Y_i summed) + u and
+ * γ[l] = Σ_i t_i (column l of Z_i summed), formed at pack time in double
+ * precision and kept in fp32; the per-row sums Σx and γ·x (fp32, one small
+ * kernel per forward) enter the output epilogue before its rounding.  The
+ * intermediate (batch x p d) follows the DBF path rules (hi+lo pair at
+ * decode batch <= 8, else one fp16 rounding) and must stay in fp16 range.
+ * Errors: DBF_ERR_INVALID_ARG (null pointers, sizes < 1, entries not 0/1),
+ * DBF_ERR_SHAPE, DBF_ERR_OOM, DBF_ERR_HIP.  The table path, grouped
+ * forwards and gradients return DBF_ERR_UNSUPPORTED for such a handle.
+ */
+dbf_status_t dbf_bqq_pack(int32_t n, int32_t m, int32_t d, int32_t p,
+                          const uint8_t *Y, const uint8_t *Z,
+                          const uint16_t *r, const uint16_t *s, const uint16_t *t, uint16_t u,
+                          int32_t max_batch, dbf_handle_t *out);
+
+/*
  * dbf_linear_backward_data -- dX = dY W (batch x m, fp16) for an upstream
  * gradient dY (batch x n, fp16): the forward of the transposed layer, with
  * the same kernels and numerics as dbf_linear_forward.  Fine-tuning of the

@@ -161,3 +161,34 @@ def test_backward_entries_validate_before_any_device_call():
     # null handles
     assert L.dbf_linear_backward_data(None, None, None, 1, None) == dbf.DBF_ERR_INVALID_ARG
     assert L.dbf_linear_backward(None, None, None, None, None, None, None, 1, None) == dbf.DBF_ERR_INVALID_ARG
+
+
+def test_bqq_pack_validates_before_any_device_call():
+    """dbf_bqq_pack reports argument errors (null pointers, sizes, entries
+    other than 0/1) without touching a GPU; with valid arguments and no GPU
+    it reports a HIP error and returns no handle."""
+    L = dbf.lib()
+    p, n, d, m = 2, 4, 3, 5
+    Y = np.ones((p, n, d), np.uint8)
+    Z = np.zeros((p, d, m), np.uint8)
+    r = np.ones(p, np.float16).view(np.uint16)
+    h = ctypes.c_void_p()
+    P = lambda arr: arr.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
+    E = dbf.DBF_ERR_INVALID_ARG
+    assert L.dbf_bqq_pack(n, m, d, p, P(Y), P(Z), P(r), P(r), P(r), 0x3C00, 4, None) == E
+    assert L.dbf_bqq_pack(n, m, d, p, None, P(Z), P(r), P(r), P(r), 0x3C00, 4, ctypes.byref(h)) == E
+    assert L.dbf_bqq_pack(n, m, d, p, P(Y), P(Z), None, P(r), P(r), 0x3C00, 4, ctypes.byref(h)) == E
+    for bad in ((0, m, d, p), (n, 0, d, p), (n, m, 0, p), (n, m, d, 0)):
+        assert L.dbf_bqq_pack(*bad, P(Y), P(Z), P(r), P(r), P(r), 0x3C00, 4, ctypes.byref(h)) == E
+    assert L.dbf_bqq_pack(n, m, d, p, P(Y), P(Z), P(r), P(r), P(r), 0x3C00, 0, ctypes.byref(h)) == E
+    Y2 = Y.copy()
+    Y2[1, 2, 0] = 2
+    assert L.dbf_bqq_pack(n, m, d, p, P(Y2), P(Z), P(r), P(r), P(r), 0x3C00, 4, ctypes.byref(h)) == E
+    Z2 = Z.copy()
+    Z2[0, 1, 4] = 255
+    assert L.dbf_bqq_pack(n, m, d, p, P(Y), P(Z2), P(r), P(r), P(r), 0x3C00, 4, ctypes.byref(h)) == E
+    assert h.value is None
+    if not _have_gpu():
+        assert L.dbf_bqq_pack(n, m, d, p, P(Y), P(Z), P(r), P(r), P(r), 0x3C00, 4,
+                              ctypes.byref(h)) == dbf.DBF_ERR_HIP
+        assert h.value is None
