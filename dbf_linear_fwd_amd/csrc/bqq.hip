@@ -14,6 +14,7 @@
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
+#include "bqq_rowstats.h"
 #include "dbf_internal.h"
 
 namespace dbf {
@@ -21,35 +22,14 @@ namespace {
 
 constexpr int kStatThreads = 256;
 
-// stats[2r] = Σ_l x[r][l], stats[2r + 1] = Σ_l gamma[l] x[r][l], in fp32:
-// each thread sums a fixed stride of the row in order, then a fixed-order
-// tree over the threads, so every call gives the same bits.
+// One workgroup per row of x: stats[2r] = Σ_l x[r][l], stats[2r + 1] =
+// Σ_l gamma[l] x[r][l] (bqq_rowstats.h).
 __global__ __launch_bounds__(kStatThreads) void bqq_rowstats_kernel(const __half *__restrict__ x, int m,
                                                                     const float *__restrict__ gamma,
                                                                     float *__restrict__ stats) {
-    __shared__ float sh[2][kStatThreads];
-    const int r = blockIdx.x, tid = threadIdx.x;
-    const __half *xr = x + static_cast<size_t>(r) * m;
-    float s = 0.0f, k = 0.0f;
-    for (int l = tid; l < m; l += kStatThreads) {
-        const float v = __half2float(xr[l]);
-        s += v;
-        k += gamma[l] * v;
-    }
-    sh[0][tid] = s;
-    sh[1][tid] = k;
-    __syncthreads();
-    for (int w = kStatThreads / 2; w > 0; w >>= 1) {
-        if (tid < w) {
-            sh[0][tid] += sh[0][tid + w];
-            sh[1][tid] += sh[1][tid + w];
-        }
-        __syncthreads();
-    }
-    if (tid == 0) {
-        stats[2 * r] = sh[0][0];
-        stats[2 * r + 1] = sh[1][0];
-    }
+    __shared__ float sh[2 * kStatThreads];
+    const int r = blockIdx.x;
+    bqq_rowstats_row<kStatThreads>(x + static_cast<size_t>(r) * m, m, gamma, stats + 2 * r, sh);
 }
 
 }  // namespace

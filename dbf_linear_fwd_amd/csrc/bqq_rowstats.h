@@ -1,0 +1,75 @@
+// Per-row input sums of the BQQ-form layer (device code, shared by the
+// standalone kernel and the decode stage-1 kernel).
+//
+// For one row x of the input (m fp16 values): sigma = Σ_l x_l and
+// kappa = Σ_l gamma_l x_l in fp32.  A workgroup of `threads` threads takes
+// 8-element chunks c = tid + threads * q, issuing the loads of up to four
+// chunks before adding them, then the threads' partial sums meet in a
+// fixed-order tree in LDS: every call gives the same bits.
+
+#ifndef DBF_BQQ_ROWSTATS_H_
+#define DBF_BQQ_ROWSTATS_H_
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+
+namespace dbf {
+
+template <int THREADS>
+__device__ __forceinline__ void bqq_rowstats_row(const __half *__restrict__ xr, int m,
+                                                 const float *__restrict__ gamma, float *__restrict__ out2,
+                                                 float *sh /* LDS, 2 * THREADS floats */) {
+    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+    const int tid = threadIdx.x;
+    float s = 0.0f, k = 0.0f;
+    if ((m & 7) == 0 && (reinterpret_cast<uintptr_t>(xr) & 15) == 0) {
+        const int nch = m >> 3;
+        for (int c0 = 0; c0 < nch; c0 += 4 * THREADS) {
+            h8 xv[4];
+            float4 g0[4], g1[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int c = min(c0 + tid + THREADS * q, nch - 1);  // past the end: a valid chunk, not added
+                xv[q] = *reinterpret_cast<const h8 *>(xr + 8 * c);
+                g0[q] = *reinterpret_cast<const float4 *>(gamma + 8 * c);
+                g1[q] = *reinterpret_cast<const float4 *>(gamma + 8 * c + 4);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (c0 + tid + THREADS * q < nch) {
+                    const float gv[8] = {g0[q].x, g0[q].y, g0[q].z, g0[q].w, g1[q].x, g1[q].y, g1[q].z, g1[q].w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float v = static_cast<float>(xv[q][e]);
+                        s += v;
+                        k += gv[e] * v;
+                    }
+                }
+            }
+        }
+    } else {
+        for (int l = tid; l < m; l += THREADS) {
+            const float v = __half2float(xr[l]);
+            s += v;
+            k += gamma[l] * v;
+        }
+    }
+    sh[tid] = s;
+    sh[THREADS + tid] = k;
+    __syncthreads();
+    for (int w = THREADS / 2; w > 0; w >>= 1) {
+        if (tid < w) {
+            sh[tid] += sh[tid + w];
+            sh[THREADS + tid] += sh[THREADS + tid + w];
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        out2[0] = sh[0];
+        out2[1] = sh[THREADS];
+    }
+}
+
+}  // namespace dbf
+
+#endif  // DBF_BQQ_ROWSTATS_H_

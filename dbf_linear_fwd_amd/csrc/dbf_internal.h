@@ -68,6 +68,10 @@ struct MfmaDecodeArgs {
     // optional affine output term: y[r][i] = rne16(a_i s_ri + E[i] * stats[r].x + stats[r].y)
     const float *aff_E = nullptr;
     const float *aff_stats = nullptr;  // [batch][2]
+    // 0/1 layers: stage 1 also forms the per-row sums of x the affine term
+    // needs, stats_out[2r] = Σ_l x[r][l], stats_out[2r + 1] = Σ_l gamma[l] x[r][l]
+    const float *gamma = nullptr;
+    float *stats_out = nullptr;
 };
 
 // which = 1: stage 1 (writes v16); which = 2: stage 2 (writes y).

@@ -35,6 +35,7 @@
 
 #include <algorithm>
 
+#include "bqq_rowstats.h"
 #include "dbf_internal.h"
 
 namespace dbf {
@@ -452,6 +453,20 @@ __device__ __forceinline__ void stage2_body(int blk, char *base, const uint32_t 
             const int row = i0 + 16 * t + 4 * g + v;
             a_pre[t][v] = row < n ? __half2float(a[row]) : 0.0f;
         }
+    // affine term (if any), fetched early too: E of this lane's rows, the
+    // row sums of batch row li
+    float e_pre[RT][4];
+    float2 st = float2{0.0f, 0.0f};
+    if (aff_E) {
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int row = i0 + 16 * t + 4 * g + v;
+                e_pre[t][v] = row < n ? aff_E[row] : 0.0f;
+            }
+        if (li < NB) st = *reinterpret_cast<const float2 *>(aff_stats + 2 * li);
+    }
 
     f32x4 acc[Acc<NB>::N][RT];
 #pragma unroll
@@ -499,7 +514,6 @@ __device__ __forceinline__ void stage2_body(int blk, char *base, const uint32_t 
     reduce_waves<NB, RT>(acc, red, wave, lane);
     if (wave == 0 && li < NB) {
         // affine term (if any): E[row] * stats[li].x + stats[li].y, added before the one rounding
-        const float2 st = aff_E ? *reinterpret_cast<const float2 *>(aff_stats + 2 * li) : float2{0.0f, 0.0f};
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
             const int row0 = i0 + 16 * t + 4 * g;
@@ -509,7 +523,7 @@ __device__ __forceinline__ void stage2_body(int blk, char *base, const uint32_t 
                 const int row = row0 + v;
                 if (row < n) {
                     float val = rounded(d[v] * a_pre[t][v]);
-                    if (aff_E) val = rounded(val + (aff_E[row] * st.x + st.y));
+                    if (aff_E) val = rounded(val + (e_pre[t][v] * st.x + st.y));
                     y[static_cast<size_t>(li) * n + row] = __float2half_rn(val);
                 }
             }
@@ -567,11 +581,20 @@ __global__ __launch_bounds__(kThreads) void mfma_stage1_kernel(const uint32_t *_
                                                                const __half *__restrict__ b,
                                                                const __half *__restrict__ mid,
                                                                __half *__restrict__ v16, int k_pad, int PR,
-                                                               const Stage2Readahead ra) {
+                                                               const Stage2Readahead ra,
+                                                               const float *__restrict__ gamma,
+                                                               float *__restrict__ stats) {
     extern __shared__ float lds[];
     const int G1 = k_pad / (16 * RT);
     if (static_cast<int>(blockIdx.x) >= G1) {
-        readahead_stage2(ra, blockIdx.x, (blockIdx.x - G1) >> 3);
+        const int extra = blockIdx.x - G1;
+        if (BIN && extra >= 8 * ra.per_xcd) {
+            // 0/1 layers: one block per batch row forms the row sums of x
+            const int r = extra - 8 * ra.per_xcd;
+            bqq_rowstats_row<kThreads>(x + static_cast<size_t>(r) * m, m, gamma, stats + 2 * r, lds);
+            return;
+        }
+        readahead_stage2(ra, blockIdx.x, extra >> 3);
         return;
     }
     stage1_body<NB, RT, BIN>(blockIdx.x, reinterpret_cast<char *>(lds), Bt, Wm, x, m, b, mid, v16, k_pad, PR);
@@ -676,10 +699,13 @@ int launch_rt(const MfmaDecodeArgs &d, hipStream_t s, int which) {
             const size_t items = static_cast<size_t>(d.n_pad) * (d.k_pad / 32) / 4;
             if (items > static_cast<size_t>(kReadaheadMax) * 8 * ra.per_xcd * kThreads) ra.per_xcd = 0;
         }
-        // the read-ahead blocks start on XCD G1 mod 8; 8 * per_xcd of them cover every XCD equally
-        launch_kernel((mfma_stage1_kernel<NB, RT, BIN>), dim3(G1 + 8 * ra.per_xcd), dim3(kThreads), lds, s, d.B_dev,
-                      d.m_pad / 32, static_cast<const __half *>(d.x), d.m, static_cast<const __half *>(d.b_dev),
-                      static_cast<const __half *>(d.mid_dev), reinterpret_cast<__half *>(d.v16), d.k_pad, PR, ra);
+        // the read-ahead blocks start on XCD G1 mod 8; 8 * per_xcd of them cover every XCD equally;
+        // 0/1 layers add one block per batch row for the row sums of x
+        const int stat_blocks = BIN ? NB : 0;
+        launch_kernel((mfma_stage1_kernel<NB, RT, BIN>), dim3(G1 + 8 * ra.per_xcd + stat_blocks), dim3(kThreads), lds,
+                      s, d.B_dev, d.m_pad / 32, static_cast<const __half *>(d.x), d.m,
+                      static_cast<const __half *>(d.b_dev), static_cast<const __half *>(d.mid_dev),
+                      reinterpret_cast<__half *>(d.v16), d.k_pad, PR, ra, d.gamma, d.stats_out);
     } else {
         static const bool once = (allow_lds(mfma_stage2_kernel<NB, RT, BIN>, kLdsBudget), true);
         (void)once;

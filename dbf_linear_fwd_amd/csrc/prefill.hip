@@ -201,27 +201,49 @@ __device__ __forceinline__ void store_partial(const f32x16 (&acc)[MF_][NF_], int
 }
 
 // Sum of the split-K parts in part order, scaled and rounded once: one
-// thread per output, the loads of up to eight parts in flight at a time.
+// thread per four outputs of a row (16-byte loads of each part, eight
+// parts' loads in flight at a time, one 8-byte store).
 __global__ __launch_bounds__(256) void split_finish_kernel(const float *__restrict__ part, int nsplit, int M,
                                                            int n_out, int ldw, const __half *__restrict__ sn,
                                                            __half *__restrict__ out, int ldo, const Affine aff) {
+    const int cq = ldw >> 2;
     const int idx = blockIdx.x * 256 + threadIdx.x;
-    if (idx >= M * n_out) return;
-    const int row = idx / n_out, col = idx - row * n_out;
+    if (idx >= M * cq) return;
+    const int row = idx / cq, c0 = (idx - row * cq) * 4;
     const size_t plane = static_cast<size_t>(M) * ldw;
-    const float *p = part + static_cast<size_t>(row) * ldw + col;
-    float s = 0.0f;
+    const float *p = part + static_cast<size_t>(row) * ldw + c0;
+    float4 s = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int k0 = 0; k0 < nsplit; k0 += 8) {
-        float v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = k0 + u < nsplit ? p[(k0 + u) * plane] : 0.0f;
+        float4 v[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u)
-            if (k0 + u < nsplit) s += v[u];
+            v[u] = *reinterpret_cast<const float4 *>(p + static_cast<size_t>(min(k0 + u, nsplit - 1)) * plane);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (k0 + u < nsplit) {
+                s.x += v[u].x;
+                s.y += v[u].y;
+                s.z += v[u].z;
+                s.w += v[u].w;
+            }
     }
-    float val = rounded(s * __half2float(sn[col]));
-    if (aff.E) val = rounded(val + (aff.E[col] * aff.stats[2 * row] + aff.stats[2 * row + 1]));
-    out[static_cast<size_t>(row) * ldo + col] = __float2half_rn(val);
+    const float sv[4] = {s.x, s.y, s.z, s.w};
+    __half o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int col = min(c0 + e, n_out - 1);
+        float val = rounded(sv[e] * __half2float(sn[col]));
+        if (aff.E) val = rounded(val + (aff.E[col] * aff.stats[2 * row] + aff.stats[2 * row + 1]));
+        o[e] = __float2half_rn(val);
+    }
+    __half *dst = out + static_cast<size_t>(row) * ldo + c0;
+    if (c0 + 4 <= n_out && ((reinterpret_cast<uintptr_t>(dst) & 7) == 0)) {
+        *reinterpret_cast<uint2 *>(dst) = *reinterpret_cast<const uint2 *>(o);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (c0 + e < n_out) dst[e] = o[e];
+    }
 }
 
 // C = P S'ᵀ (see the file comment).  P: fp16 [M][ldp], K valid columns
@@ -639,7 +661,7 @@ void launch_dma(const GemmLaunch &a, hipStream_t s, float *part = nullptr, int n
 }
 
 #ifndef DBF_SPLIT_BELOW
-#define DBF_SPLIT_BELOW 128
+#define DBF_SPLIT_BELOW 129
 #endif
 #ifndef DBF_SPLIT_TARGET
 #define DBF_SPLIT_TARGET 256
@@ -657,9 +679,10 @@ int dma_pairs(int M, int words, int n_out) {
     return 1;
 }
 
-// K parts of the split-K form: grids of fewer than DBF_SPLIT_BELOW tiles are
-// cut along K into about DBF_SPLIT_TARGET workgroups in all, each with at
-// least DBF_SPLIT_MIN_STEPS steps.
+// K parts of the split-K form: grids of fewer than DBF_SPLIT_BELOW tiles (at
+// most 128: half the CUs or less) are cut along K into about
+// DBF_SPLIT_TARGET workgroups in all, each with at least DBF_SPLIT_MIN_STEPS
+// steps.
 int split_parts(int M, int words, int n_out) {
     const int tiles = ((M + BM - 1) / BM) * ((n_out + DBN - 1) / DBN);
     if (tiles >= DBF_SPLIT_BELOW) return 1;
@@ -683,7 +706,7 @@ size_t sign_gemm_split_elems(int M, int K, int words, int n_out) {
 
 int launch_split_finish(const SplitK &split, int M, int n_out, const void *sn, void *out, int ldo, void *stream,
                         const float *aff_E, const float *aff_stats) {
-    const int items = M * n_out;
+    const int items = M * (split.ldw >> 2);
     if (items == 0) return 0;
     launch_kernel(split_finish_kernel, dim3((items + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream),
                   static_cast<const float *>(split.ws), split.nsplit, M, n_out, split.ldw,

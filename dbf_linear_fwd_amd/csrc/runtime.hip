@@ -513,6 +513,8 @@ static dbf_status_t forward_decode_mfma(dbf_layer *h, const void *x, void *y, in
     d.binary = h->binary ? 1 : 0;
     d.aff_E = h->bqq_E;
     d.aff_stats = h->bqq_stats;
+    d.gamma = h->bqq_gamma;       // (0/1 layers: stage 1 forms the row sums)
+    d.stats_out = h->bqq_stats;
     dbf_status_t st = timed_launch(h, "decode_stage1", stream, [&] { return dbf::launch_mfma_decode(d, stream, 1); });
     if (st != DBF_OK) return st;
     return timed_launch(h, "decode_stage2", stream, [&] { return dbf::launch_mfma_decode(d, stream, 2); });
@@ -612,13 +614,14 @@ extern "C" dbf_status_t dbf_linear_forward_ex(dbf_handle_t h, const void *x, voi
         if (h->binary) return DBF_ERR_UNSUPPORTED;
         return forward_decode(h, x, y, batch, stream);
     }
-    if (h->binary) {
+    const bool decode = path == DBF_PATH_DECODE || (path == DBF_PATH_AUTO && batch <= dbf::kDecodeMaxBatch);
+    if (h->binary && !decode) {
+        // (on the decode path the stage-1 launch forms the row sums itself)
         const dbf_status_t st = timed_launch(h, "bqq_rowstats", stream, [&] {
             return dbf::launch_bqq_rowstats(x, batch, h->m, h->bqq_gamma, h->bqq_stats, stream);
         });
         if (st != DBF_OK) return st;
     }
-    const bool decode = path == DBF_PATH_DECODE || (path == DBF_PATH_AUTO && batch <= dbf::kDecodeMaxBatch);
     return decode ? forward_decode_mfma(h, x, y, batch, stream) : forward_prefill(h, x, y, batch, stream);
 }
 
