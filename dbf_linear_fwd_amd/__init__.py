@@ -29,6 +29,7 @@ __all__ = [
     "dbf_status_string", "dbf_pack_signs", "dbf_layout_signs", "dbf_layout_words",
     "dbf_timing_enable", "dbf_timing_read", "Layer", "dbf_linear_forward_group", "forward_group",
     "dbf_pack_ex", "dbf_linear_backward_data", "dbf_linear_backward", "DBF_PACK_BACKWARD", "dbf_bqq_pack",
+    "dbf_factorize", "factorize",
 ]
 
 DBF_OK = 0
@@ -51,7 +52,7 @@ EXPORTED_SYMBOLS = (
     "dbf_pack", "dbf_pack_ex", "dbf_linear_forward", "dbf_linear_forward_ex", "dbf_linear_forward_group",
     "dbf_linear_backward_data", "dbf_linear_backward", "dbf_free", "dbf_get_info", "dbf_status_string",
     "dbf_pack_signs", "dbf_layout_signs", "dbf_layout_words", "dbf_timing_enable", "dbf_timing_read",
-    "dbf_bqq_pack",
+    "dbf_bqq_pack", "dbf_factorize",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -104,6 +105,9 @@ def lib() -> ctypes.CDLL:
     L.dbf_pack_ex.restype = ctypes.c_int
     L.dbf_bqq_pack.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, ctypes.c_uint16, i32, ctypes.POINTER(vp)]
     L.dbf_bqq_pack.restype = ctypes.c_int
+    L.dbf_factorize.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, ctypes.c_float, i32, i32, i32,
+                                vp, vp, vp, vp, vp, vp, vp]
+    L.dbf_factorize.restype = ctypes.c_int
     L.dbf_linear_backward_data.argtypes = [vp, vp, vp, i32, vp]
     L.dbf_linear_backward_data.restype = ctypes.c_int
     L.dbf_linear_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp]
@@ -189,6 +193,47 @@ def dbf_bqq_pack(n: int, m: int, d: int, p: int, Y, Z, r, s, t, u, max_batch: in
     _check(lib().dbf_bqq_pack(n, m, d, p, _ptr(Y8), _ptr(Z8), _ptr(r16), _ptr(s16), _ptr(t16), u16, max_batch,
                               ctypes.byref(h)), "dbf_bqq_pack")
     return h.value
+
+
+def dbf_factorize(W_ptr: int, n: int, m: int, k: int, U0_ptr: int, V0_ptr: int, dout_ptr: int, din_ptr: int,
+                  rho_rel: float, outer: int, inner: int, power_iters: int, A_ptr: int, B_ptr: int, a_ptr: int,
+                  mid_ptr: int, b_ptr: int, err_ptr: int, stream: int = 0) -> None:
+    _check(lib().dbf_factorize(W_ptr, n, m, k, U0_ptr, V0_ptr, dout_ptr or None, din_ptr or None, rho_rel, outer,
+                               inner, power_iters, A_ptr, B_ptr, a_ptr, mid_ptr, b_ptr, err_ptr or None, stream),
+           "dbf_factorize")
+
+
+def factorize(W, k: int, U0, V0, rho_rel: float = 1.0, outer: int = 2, inner: int = 4, power_iters: int = 8,
+              d_out=None, d_in=None):
+    """DBF factors of W (CUDA float32 tensor, n x m) from the starting factors
+    U0 (n x k) and V0 (k x m): returns (A, B, a, mid, b, err) as CUDA tensors
+    (int8 +/-1, int8 +/-1, float16 x 3, float32 [outer])."""
+    import torch
+
+    def dev32(t, shape, what):
+        if t is None:
+            return None
+        if t.dtype != torch.float32 or not t.is_cuda or tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"{what} must be a contiguous CUDA float32 tensor of shape {shape}")
+        return t
+    n, m = W.shape
+    dev32(W, (n, m), "W")
+    dev32(U0, (n, k), "U0")
+    dev32(V0, (k, m), "V0")
+    dev32(d_out, (n,), "d_out")
+    dev32(d_in, (m,), "d_in")
+    dev = W.device
+    A = torch.empty((n, k), dtype=torch.int8, device=dev)
+    B = torch.empty((k, m), dtype=torch.int8, device=dev)
+    a = torch.empty(n, dtype=torch.float16, device=dev)
+    mid = torch.empty(k, dtype=torch.float16, device=dev)
+    b = torch.empty(m, dtype=torch.float16, device=dev)
+    err = torch.empty(outer, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    dbf_factorize(W.data_ptr(), n, m, k, U0.data_ptr(), V0.data_ptr(), d_out.data_ptr() if d_out is not None else 0,
+                  d_in.data_ptr() if d_in is not None else 0, rho_rel, outer, inner, power_iters, A.data_ptr(),
+                  B.data_ptr(), a.data_ptr(), mid.data_ptr(), b.data_ptr(), err.data_ptr(), stream)
+    return A, B, a, mid, b, err
 
 
 def dbf_linear_forward(h: int, x_ptr: int, y_ptr: int, batch: int, stream: int = 0) -> None:

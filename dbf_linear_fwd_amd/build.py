@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdbf.so")
 
-HIP_SOURCES = ["runtime.hip", "decode.hip", "decode_mfma.hip", "prefill.hip", "grad.hip", "bqq.hip"]
+HIP_SOURCES = ["runtime.hip", "decode.hip", "decode_mfma.hip", "prefill.hip", "grad.hip", "bqq.hip", "factor.hip"]
 CXX_SOURCES = ["pack.cpp"]
 
 ARCH = "gfx950"
@@ -82,7 +82,9 @@ def build(verbose: bool = False) -> str:
     if failed:
         raise RuntimeError(f"compilation failed: {failed}")
     tmp = LIB + ".tmp"
-    link = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    # rocBLAS: the plain fp32 GEMMs of the factorization
+    link = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, "-L/opt/rocm/lib", "-lrocblas",
+            "-Wl,-rpath,/opt/rocm/lib"]
     if verbose:
         print(" ".join(link), flush=True)
     res = subprocess.run(link, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)

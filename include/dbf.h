@@ -201,6 +201,43 @@ dbf_status_t dbf_bqq_pack(int32_t n, int32_t m, int32_t d, int32_t p,
                           int32_t max_batch, dbf_handle_t *out);
 
 /*
+ * dbf_factorize -- the DBF factors of a weight matrix W (n x m), the step
+ * before packing.  Technical summary (gist.science) of "Addition is almost
+ * all you need", §2.2: alternating minimization of the two factors, ADMM
+ * for each constrained subproblem, SVID projection onto sign matrices with
+ * a rank-one scaling, importance scaling of rows and columns.  With
+ * T = diag(d_out) W diag(d_in) and W ~ U V, U = diag(a) A diag(c_u),
+ * V = diag(c_v) B diag(b), each of `outer` iterations updates U with V
+ * fixed and then V with U fixed by `inner` ADMM iterations:
+ *   X = (T' F + rho (Z - L)) (F^T F + rho I)^{-1},  Z = SVID(X + L),
+ *   L = L + X - Z,   rho = rho_rel * trace(F^T F) / k,
+ * starting from the current factor (Z) and L = 0; SVID(M) = sign(M) times
+ * the rank-one approximation of |M| from `power_iters` power-method steps
+ * (sign(0) = +1).  mid = c_u * c_v; a and b are divided by their RMS and
+ * mid multiplied by both before the one rounding to fp16.
+ *   W      device fp32, n x m row-major.
+ *   U0, V0 device fp32, n x k and k x m row-major: the starting factors.
+ *   d_out, d_in  device fp32 row / column importance (n, m), or NULL (1).
+ *   A, B   device int8 outputs, n x k and k x m, entries +1 / -1 (the input
+ *          format of dbf_pack).
+ *   a, mid, b  device fp16 outputs (n, k, m).
+ *   err    device fp32 [outer] or NULL: ||T - U V||_F / ||T||_F after each
+ *          outer iteration.
+ * fp32 arithmetic: dense products on rocBLAS GEMMs, (F^T F + rho I)^{-1} by
+ * Newton-Schulz iteration, the rest in the library's kernels; reductions in
+ * a fixed order (repeated calls give identical results).  Allocates its
+ * workspace (about 4 n m + 8 max(n, m) k + 4 k^2 floats) and frees it before
+ * returning; synchronizes `stream`.
+ * Errors: DBF_ERR_INVALID_ARG (null pointers, sizes or counts < 1,
+ * rho_rel <= 0), DBF_ERR_SHAPE, DBF_ERR_OOM, DBF_ERR_HIP.
+ */
+dbf_status_t dbf_factorize(const float *W, int32_t n, int32_t m, int32_t k,
+                           const float *U0, const float *V0, const float *d_out, const float *d_in,
+                           float rho_rel, int32_t outer, int32_t inner, int32_t power_iters,
+                           int8_t *A, int8_t *B, uint16_t *a, uint16_t *mid, uint16_t *b, float *err,
+                           hipStream_t stream);
+
+/*
  * dbf_linear_backward_data -- dX = dY W (batch x m, fp16) for an upstream
  * gradient dY (batch x n, fp16): the forward of the transposed layer, with
  * the same kernels and numerics as dbf_linear_forward.  Fine-tuning of the

@@ -192,3 +192,20 @@ def test_bqq_pack_validates_before_any_device_call():
         assert L.dbf_bqq_pack(n, m, d, p, P(Y), P(Z), P(r), P(r), P(r), 0x3C00, 4,
                               ctypes.byref(h)) == dbf.DBF_ERR_HIP
         assert h.value is None
+
+
+def test_factorize_validates_before_any_device_call():
+    L = dbf.lib()
+    E = dbf.DBF_ERR_INVALID_ARG
+    f = ctypes.c_float
+    p = ctypes.c_void_p(16)  # never dereferenced: every call below fails validation first
+    assert L.dbf_factorize(None, 4, 4, 2, p, p, None, None, f(1.0), 1, 1, 1, p, p, p, p, p, None, None) == E
+    assert L.dbf_factorize(p, 4, 4, 2, p, p, None, None, f(1.0), 1, 1, 1, None, p, p, p, p, None, None) == E
+    for n, m, k in ((0, 4, 2), (4, 0, 2), (4, 4, 0)):
+        assert L.dbf_factorize(p, n, m, k, p, p, None, None, f(1.0), 1, 1, 1, p, p, p, p, p, None, None) == E
+    for outer, inner, pw in ((0, 1, 1), (1, 0, 1), (1, 1, 0)):
+        assert L.dbf_factorize(p, 4, 4, 2, p, p, None, None, f(1.0), outer, inner, pw, p, p, p, p, p, None,
+                               None) == E
+    assert L.dbf_factorize(p, 4, 4, 2, p, p, None, None, f(0.0), 1, 1, 1, p, p, p, p, p, None, None) == E
+    assert L.dbf_factorize(p, 1 << 20, 1 << 20, 2, p, p, None, None, f(1.0), 1, 1, 1, p, p, p, p, p, None,
+                           None) == dbf.DBF_ERR_SHAPE
