@@ -58,7 +58,10 @@ def parse():
                    help="instead of the headline line: one JSON line per workload layer and batch "
                         "(decode at batch 1 and 16, prefill at batch 2048)")
     p.add_argument("--no-bqq", action="store_true", help="skip the BQQ-form layer measurement")
-    p.add_argument("--only", choices=("decode", "prefill", "block", "backward", "bqq"), default=None,
+    p.add_argument("--no-factorize", action="store_true", help="skip the factorization measurement")
+    p.add_argument("--factor-cpu", action="store_true",
+                   help="also time the factorization oracle (one outer x one inner iteration) on the host")
+    p.add_argument("--only", choices=("decode", "prefill", "block", "backward", "bqq", "factorize"), default=None,
                    help="run one leg only (for profiling)")
     p.add_argument("--decode-path", choices=("mfma", "table"), default="mfma",
                    help="decode kernels: matrix cores (default) or vector-ALU lookup tables")
@@ -381,6 +384,49 @@ def bqq_leg(args):
     return res
 
 
+def factorize_leg(args):
+    """The factorization of a 4096x4096 matrix into DBF factors with k = 2048
+    (about 1 bit per weight): 2 outer iterations of 4 ADMM steps with 8
+    power-method steps per SVID, from a seeded random start; wall time per
+    call (it synchronizes) and per outer iteration, and the error after each
+    outer iteration.  W is a synthetic matrix of i.i.d. N(0, 0.02^2) entries
+    (no trained weights are used)."""
+    import torch
+
+    import dbf_linear_fwd_amd as dbf
+
+    n = m = 4096
+    k = 2048
+    g = torch.Generator(device="cpu").manual_seed(21)
+    W = (0.02 * torch.randn((n, m), generator=g)).cuda()
+    U0 = (torch.randn((n, k), generator=g) * (0.02 / k) ** 0.5).cuda()
+    V0 = torch.randn((k, m), generator=g).cuda()
+    outer, inner, power = 2, 4, 8
+    dbf.factorize(W, k, U0, V0, outer=1, inner=1, power_iters=2)   # library warm-up
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    A, B, a, mid, b, err = dbf.factorize(W, k, U0, V0, outer=outer, inner=inner, power_iters=power)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    res = {"workload": f"DBF factorization of a {n}x{m} fp32 matrix (i.i.d. normal), k={k}, {outer} outer x "
+                       f"{inner} ADMM iterations, {power} power-method steps per SVID",
+           "seconds": el, "ms_per_outer_iteration": el * 1e3 / outer,
+           "rel_err_per_outer": [float(e) for e in err.cpu()]}
+    print(f"[bench] factorize: {el * 1e3:.1f} ms ({el * 1e3 / outer:.1f} ms per outer iteration), "
+          f"err {res['rel_err_per_outer']}", file=sys.stderr, flush=True)
+    if args.factor_cpu:
+        from oracle import factor_oracle as FO
+        t0 = time.perf_counter()
+        FO.factorize(W.cpu().double().numpy(), k, U0.cpu().double().numpy(), V0.cpu().double().numpy(),
+                     outer=1, inner=1, power_iters=power)
+        cel = time.perf_counter() - t0
+        res["cpu_oracle_one_outer_one_inner_s"] = cel
+        print(f"[bench] factorize oracle (1 outer x 1 inner): {cel:.1f} s", file=sys.stderr, flush=True)
+    del W, U0, V0, A, B
+    torch.cuda.synchronize()
+    return res
+
+
 def copy_probe(mb):
     import torch
     n = mb * (1 << 20) // 4
@@ -497,6 +543,10 @@ def main():
     if args.only in (None, "bqq") and not args.no_bqq:
         result["bqq"] = bqq_leg(args)
 
+    # ---------------------------------------------------------------- factorization (secondary)
+    if args.only in (None, "factorize") and not args.no_factorize:
+        result["factorize"] = factorize_leg(args)
+
     if args.only is not None:
         print(json.dumps({k: {kk: vv for kk, vv in v.items() if kk not in ("layer", "copies")}
                           for k, v in result.items()}, default=str))
@@ -538,6 +588,8 @@ def main():
         line["backward_batch2048"] = result["backward"]
     if "bqq" in result:
         line["bqq_form"] = result["bqq"]
+    if "factorize" in result:
+        line["factorization"] = result["factorize"]
     print(json.dumps(line))
 
 
