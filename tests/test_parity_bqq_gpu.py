@@ -92,6 +92,21 @@ def test_bqq_prefill_path_at_decode_batch(gpu, batch):
     _assert_tol(_run(L, X, dbf.DBF_PATH_PREFILL), ref, f"bqq prefill b{batch}")
 
 
+# Small prefill grids: both products take the split-K form, the second with
+# the affine term in the finish kernel.
+@pytest.mark.parametrize("batch", [17, 130])
+def test_bqq_split_k(gpu, batch):
+    n, m, d, p = 1000, 4096, 512, 2
+    _say(f"bqq split-K n={n} m={m} d={d} p={p} batch={batch}")
+    L = inputs.bqq_layer("k", n, m, d, p, 7050 + batch, (batch,))
+    X = L.X[batch]
+    ref = Q.bqq_forward(X, L.Y, L.Z, L.r, L.s, L.t, L.u)
+    _assert_tol(_run(L, X), ref, f"bqq split-K b{batch}")
+    Li = inputs.bqq_layer("ki", n, m, d, p, 7060 + batch, (batch,), integer=True)
+    Xi = Li.X[batch]
+    _assert_bits(_run(Li, Xi), _integer_preconditions(Li, Xi, True), f"bqq split-K integer b{batch}")
+
+
 def _integer_preconditions(L, X, fp16_intermediate):
     """Every partial sum is an integer far inside fp32's exact range, the
     kernel's intermediate v = 2 r_i (Z_i x) is exact where it is rounded to
