@@ -59,9 +59,11 @@ def parse():
                         "(decode at batch 1 and 16, prefill at batch 2048)")
     p.add_argument("--no-bqq", action="store_true", help="skip the BQQ-form layer measurement")
     p.add_argument("--no-factorize", action="store_true", help="skip the factorization measurement")
+    p.add_argument("--no-context", action="store_true", help="skip the fp16-matvec and device-copy context")
     p.add_argument("--factor-cpu", action="store_true",
                    help="also time the factorization oracle (one outer x one inner iteration) on the host")
-    p.add_argument("--only", choices=("decode", "prefill", "block", "backward", "bqq", "factorize"), default=None,
+    p.add_argument("--only", choices=("decode", "prefill", "block", "backward", "bqq", "factorize", "context"),
+                   default=None,
                    help="run one leg only (for profiling)")
     p.add_argument("--decode-path", choices=("mfma", "table"), default="mfma",
                    help="decode kernels: matrix cores (default) or vector-ALU lookup tables")
@@ -427,6 +429,79 @@ def factorize_leg(args):
     return res
 
 
+def fp16_context_leg(args):
+    """Context for the pages' headline (DBF matvec speedup over an fp16
+    matvec): on the same GPU, the batch-1 forward of fp16 dense 4096x4096
+    and 14336x4096 layers (torch's library matvec) against the DBF decode of
+    the 4096x4096 layer at k = 2048 (~1 bit/weight) and k = 4096 (~2
+    bits/weight) and of the 14336x4096 MLP layer at k = 4800, each over >=
+    rotate-mb of distinct weight copies replayed from a graph; and the
+    bandwidth of a plain 1 GiB device copy (the attainable HBM rate)."""
+    import torch
+
+    import dbf_linear_fwd_amd as dbf
+    from tests import inputs
+
+    res = {}
+    g = torch.Generator(device="cpu").manual_seed(5)
+
+    def fp16_us(n, m):
+        R = max(2, -(-args.rotate_mb * (1 << 20) // (2 * n * m)))
+        Ws = [(0.02 * torch.randn((n, m), generator=g)).half().cuda() for _ in range(R)]
+        x = torch.randn((1, m), generator=g).half().cuda()
+        yy = torch.empty((1, n), dtype=torch.float16, device="cuda")
+
+        def dense(i):
+            torch.matmul(x, Ws[i % R].t(), out=yy)
+        dense.period = R
+        el, done = time_steps(dense, max(R, min(args.steps, 20 * R)), min(args.warmup, R), "graph")
+        del Ws
+        torch.cuda.empty_cache()
+        return el * 1e6 / done, 2 * n * m * done / el / 1e9
+
+    t16, gbs16 = fp16_us(4096, 4096)
+    res["fp16_matvec_4096x4096_us"] = t16
+    res["fp16_matvec_4096x4096_gbs"] = gbs16
+    t16_up, gbs16_up = fp16_us(14336, 4096)
+    res["fp16_matvec_14336x4096_us"] = t16_up
+    res["fp16_matvec_14336x4096_gbs"] = gbs16_up
+    for cid, li, tag, tref in ((2, 0, "4096x4096_k2048_1bit", t16), (3, 0, "4096x4096_k4096_2bit", t16),
+                               (4, 0, "14336x4096_k4800_1.5bit", t16_up)):
+        layer = inputs.config(cid).layers[li]
+        y = torch.empty((1, layer.n), dtype=torch.float16, device="cuda")
+        bytes_step = layer.sign_bytes + layer.scale_bytes
+        Rd = max(1, -(-args.rotate_mb * (1 << 20) // bytes_step))
+        copies = [dbf.Layer(layer.A, layer.B, layer.a, layer.mid, layer.b, max_batch=1) for _ in range(Rd)]
+        xd = torch.from_numpy(layer.X[1]).cuda()
+
+        def fwd(i):
+            copies[i % Rd].forward(xd, out=y)
+        fwd.period = Rd
+        el, done = time_steps(fwd, max(Rd, min(args.steps, 10 * Rd)), min(args.warmup, Rd), "graph")
+        td = el * 1e6 / done
+        res[f"dbf_{tag}_us"] = td
+        res[f"speedup_{tag}"] = tref / td
+        for c in copies:
+            c.close()
+        del copies
+        torch.cuda.synchronize()
+    buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(buf)
+    dst.copy_(buf)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(buf)
+    e1.record()
+    torch.cuda.synchronize()
+    res["device_copy_1GiB_gbs"] = 10 * 2 * buf.numel() * 4 / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del buf, dst
+    torch.cuda.empty_cache()
+    print(f"[bench] fp16 context: {res}", file=sys.stderr, flush=True)
+    return res
+
+
 def copy_probe(mb):
     import torch
     n = mb * (1 << 20) // 4
@@ -543,6 +618,10 @@ def main():
     if args.only in (None, "bqq") and not args.no_bqq:
         result["bqq"] = bqq_leg(args)
 
+    # ---------------------------------------------------------------- fp16 matvec and copy context
+    if args.only in (None, "context") and not args.no_context:
+        result["context"] = fp16_context_leg(args)
+
     # ---------------------------------------------------------------- factorization (secondary)
     if args.only in (None, "factorize") and not args.no_factorize:
         result["factorize"] = factorize_leg(args)
@@ -590,6 +669,8 @@ def main():
         line["bqq_form"] = result["bqq"]
     if "factorize" in result:
         line["factorization"] = result["factorize"]
+    if "context" in result:
+        line["context_same_gpu"] = result["context"]
     print(json.dumps(line))
 
 

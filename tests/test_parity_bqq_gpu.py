@@ -102,7 +102,10 @@ def test_bqq_split_k(gpu, batch):
     X = L.X[batch]
     ref = Q.bqq_forward(X, L.Y, L.Z, L.r, L.s, L.t, L.u)
     _assert_tol(_run(L, X), ref, f"bqq split-K b{batch}")
-    Li = inputs.bqq_layer("ki", n, m, d, p, 7060 + batch, (batch,), integer=True)
+    # integer data on a narrower layer (still split: K = 1024 and 512), s, t = ±1 so the output fits fp16
+    Li = inputs.bqq_layer("ki", n, 1024, 256, p, 7060 + batch, (batch,), integer=True)
+    Li.s = np.sign(Li.s).astype(np.float16)
+    Li.t = np.sign(Li.t).astype(np.float16)
     Xi = Li.X[batch]
     _assert_bits(_run(Li, Xi), _integer_preconditions(Li, Xi, True), f"bqq split-K integer b{batch}")
 
