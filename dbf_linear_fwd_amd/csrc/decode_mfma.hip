@@ -269,6 +269,75 @@ __device__ __forceinline__ void round_mma(f32x4 (&acc)[Acc<NB>::N][RT], const ui
     }
 }
 
+// Direct form of a stage's multiply: all activations of the reduction
+// dimension are in LDS (pair p's 64 columns at 64 p), and each wave loads the
+// sign words of its own pairs (p = wave, wave + 8, ...) straight from global
+// memory into the operand registers, kDirect pairs ahead of the MFMAs -- no
+// LDS copy of the signs and no barrier between their arrival and use.  The
+// MFMAs run in the same order as in round_mma, so both forms give the same
+// bits.  r0: the workgroup's first row (its 16 RT rows lie in one 64-row tile).
+#ifndef DBF_DECODE_DIRECT_DEPTH
+#define DBF_DECODE_DIRECT_DEPTH 4
+#endif
+constexpr int kDirect = DBF_DECODE_DIRECT_DEPTH;
+template <int NB, int RT, bool STAGE1, bool BIN>
+__device__ __forceinline__ void direct_mma(f32x4 (&acc)[Acc<NB>::N][RT], const uint32_t *__restrict__ S, int words,
+                                           int r0, int npairs, const _Float16 *act, int KR, int wave, int li, int g,
+                                           ExpandConsts ec) {
+    constexpr bool kShared = Acc<NB>::kShared;
+    constexpr bool kSP = Acc<NB>::kSP;
+    const int r = (li & 7) < NB ? (li & 7) : NB - 1;
+    const _Float16 *arow0 = kShared ? act + ((li < 8 ? 0 : NB) + r) * KR : act + (li < NB ? li : NB - 1) * KR;
+    const _Float16 *brow = act + NB * KR;
+    // word pair p of row r0 + 16 t + li: uint2 at ((tile * words / 2 + p) * 64 + (r0 & 63) + 16 t + li)
+    const uint2 *src = reinterpret_cast<const uint2 *>(S) + static_cast<size_t>(r0 >> 6) * (words >> 1) * 64 +
+                       (r0 & 63) + li;
+    const int np = npairs > wave ? (npairs - wave + kNW - 1) / kNW : 0;  // this wave's pairs
+    if (np == 0) return;
+    uint2 wa[kDirect][RT], wb[kDirect][RT];
+    auto load_group = [&](uint2 (&w)[kDirect][RT], int i0) {
+#pragma unroll
+        for (int ii = 0; ii < kDirect; ++ii) {
+            const int p = wave + kNW * min(i0 + ii, np - 1);  // past the end: a valid pair, not used
+#pragma unroll
+            for (int t = 0; t < RT; ++t) w[ii][t] = src[static_cast<size_t>(p) * 64 + 16 * t];
+        }
+    };
+    auto mma_group = [&](const uint2 (&w)[kDirect][RT], int i0) {
+#pragma unroll
+        for (int ii = 0; ii < kDirect; ++ii) {
+            if (i0 + ii >= np) break;
+            const int p = wave + kNW * (i0 + ii);
+            f16x8 v0[2];
+            u32x4 sc[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int e = 64 * p + 32 * h + 8 * g;
+                v0[h] = *reinterpret_cast<const f16x8 *>(arow0 + e);
+                if constexpr (kSP && STAGE1 && !BIN) sc[h] = *reinterpret_cast<const u32x4 *>(brow + e);
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int t = 0; t < RT; ++t) {
+                    f16x8 sv;
+                    if constexpr (BIN) sv = expand_01(h ? w[ii][t].y : w[ii][t].x, g, ec.mask2);
+                    else if constexpr (kSP && STAGE1) sv = expand_scaled(h ? w[ii][t].y : w[ii][t].x, g, sc[h], ec.mask);
+                    else sv = expand_pm1(h ? w[ii][t].y : w[ii][t].x, g, ec.mask, ec.one);
+                    acc[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sv, v0[h], acc[0][t], 0, 0, 0);
+                }
+        }
+    };
+    load_group(wa, 0);
+    for (int i0 = 0; i0 < np; i0 += 2 * kDirect) {
+        if (i0 + kDirect < np) load_group(wb, i0 + kDirect);
+        mma_group(wa, i0);
+        if (i0 + kDirect >= np) break;
+        if (i0 + 2 * kDirect < np) load_group(wa, i0 + 2 * kDirect);
+        mma_group(wb, i0 + kDirect);
+    }
+}
+
 // Sum the waves' accumulators through LDS in a fixed wave order; wave 0's
 // slots then hold the workgroup totals.
 template <int NB, int RT>
@@ -338,12 +407,12 @@ __device__ __forceinline__ void stage1_body(int blk, char *base, const uint32_t 
         u32x4 v[kMaxItems];
         f16x8 xv[kMaxAct], bv[kMaxAct];
     };
-    auto issue = [&](Batch &B, int pr0, int pr1, int item0, int act0) {
+    auto issue = [&](Batch &B, int pr0, int pr1, int item0, int act0, bool with_signs = true) {
         const int nitems = (pr1 - pr0) * 8 * RT;
         const int k0 = 64 * pr0, len = 64 * (pr1 - pr0);
         const int nact = NB * (len >> 3);  // 8-element activation items
         const int per_row = len >> 3;
-        load_sign_items<RT>(B.v, Bt, Wm, j0, pr0, nitems, item0);
+        if (with_signs) load_sign_items<RT>(B.v, Bt, Wm, j0, pr0, nitems, item0);
         if (xvec) {
             // rows of x are 16-byte aligned: clamped, unconditional vector loads
 #pragma unroll
@@ -369,12 +438,13 @@ __device__ __forceinline__ void stage1_body(int blk, char *base, const uint32_t 
             }
         }
     };
-    auto stash = [&](const Batch &B, uint32_t *sgn_b, _Float16 *act_b, int pr0, int pr1, int item0, int act0) {
+    auto stash = [&](const Batch &B, uint32_t *sgn_b, _Float16 *act_b, int pr0, int pr1, int item0, int act0,
+                     bool with_signs = true) {
         const int nitems = (pr1 - pr0) * 8 * RT;
         const int len = 64 * (pr1 - pr0);
         const int nact = NB * (len >> 3);
         const int per_row = len >> 3;
-        store_sign_items(B.v, sgn_b, nitems, item0);
+        if (with_signs) store_sign_items(B.v, sgn_b, nitems, item0);
         if constexpr (Acc<NB>::kSP) {
             // x as it is (b goes into the signs); row 0's items also store b
 #pragma unroll
@@ -408,7 +478,18 @@ __device__ __forceinline__ void stage1_body(int blk, char *base, const uint32_t 
             }
         }
     };
-    if (pipe) {
+    if (pipe == 2) {
+        // direct form: the activations of all of m in LDS, the signs straight to registers
+        _Float16 *act_all = reinterpret_cast<_Float16 *>(base);
+        const int nact = NB * 8 * npairs;
+        for (int act0 = 0; act0 < nact; act0 += kThreads * kMaxAct) {
+            Batch B;
+            issue(B, 0, npairs, 0, act0, false);
+            stash(B, nullptr, act_all, 0, npairs, 0, act0, false);
+        }
+        __syncthreads();
+        direct_mma<NB, RT, true, BIN>(acc, Bt, Wm, j0, npairs, act_all, 64 * npairs, wave, li, g, ec);
+    } else if (pipe) {
         // Rounds of PR pairs, each one batch, through two LDS buffers: the
         // loads of round r + 1 are in flight while round r is multiplied.
         const size_t RB = lds_round_bytes<NB, RT>(PR);
@@ -518,12 +599,12 @@ __device__ __forceinline__ void stage2_body(int blk, char *base, const uint32_t 
         u32x4 v[kMaxItems];
         f16x8 av[kMaxAct];
     };
-    auto issue = [&](Batch &B, int pr0, int pr1, int item0, int act0) {
+    auto issue = [&](Batch &B, int pr0, int pr1, int item0, int act0, bool with_signs = true) {
         const int nitems = (pr1 - pr0) * 8 * RT;
         const int k0 = 64 * pr0, len = 64 * (pr1 - pr0);
         const int nact = kPlanes * NB * (len >> 3);  // 16-byte plane items: hi rows then lo rows
         const int per_row = len >> 3;
-        load_sign_items<RT>(B.v, At, Wk, i0, pr0, nitems, item0);
+        if (with_signs) load_sign_items<RT>(B.v, At, Wk, i0, pr0, nitems, item0);
 #pragma unroll
         for (int q = 0; q < kMaxAct; ++q) {
             const int it = min(act0 + static_cast<int>(threadIdx.x) + kThreads * q, nact - 1);
@@ -532,12 +613,13 @@ __device__ __forceinline__ void stage2_body(int blk, char *base, const uint32_t 
             B.av[q] = *reinterpret_cast<const f16x8 *>(v16 + static_cast<size_t>(r) * k_pad + k0 + e);
         }
     };
-    auto stash = [&](const Batch &B, uint32_t *sgn_b, _Float16 *act_b, int pr0, int pr1, int item0, int act0) {
+    auto stash = [&](const Batch &B, uint32_t *sgn_b, _Float16 *act_b, int pr0, int pr1, int item0, int act0,
+                     bool with_signs = true) {
         const int nitems = (pr1 - pr0) * 8 * RT;
         const int len = 64 * (pr1 - pr0);
         const int nact = kPlanes * NB * (len >> 3);
         const int per_row = len >> 3;
-        store_sign_items(B.v, sgn_b, nitems, item0);
+        if (with_signs) store_sign_items(B.v, sgn_b, nitems, item0);
 #pragma unroll
         for (int q = 0; q < kMaxAct; ++q) {
             const int it = act0 + threadIdx.x + kThreads * q;
@@ -548,7 +630,18 @@ __device__ __forceinline__ void stage2_body(int blk, char *base, const uint32_t 
             }
         }
     };
-    if (pipe) {
+    if (pipe == 2) {
+        // direct form: v of all of k in LDS, the signs straight to registers
+        _Float16 *act_all = reinterpret_cast<_Float16 *>(base);
+        const int nact = kPlanes * NB * 8 * npairs;
+        for (int act0 = 0; act0 < nact; act0 += kThreads * kMaxAct) {
+            Batch B;
+            issue(B, 0, npairs, 0, act0, false);
+            stash(B, nullptr, act_all, 0, npairs, 0, act0, false);
+        }
+        __syncthreads();
+        direct_mma<NB, RT, false, BIN>(acc, At, Wk, i0, npairs, act_all, 64 * npairs, wave, li, g, ec);
+    } else if (pipe) {
         // two LDS buffers: round r + 1's loads in flight while round r is multiplied
         const size_t RB = lds_round_bytes<NB, RT>(PR);
         const int nr = (npairs + PR - 1) / PR;
@@ -759,10 +852,28 @@ struct RoundPlan {
     int PR, pipe;
     size_t lds;
 };
+#ifndef DBF_DECODE_DIRECT
+#define DBF_DECODE_DIRECT 1
+#endif
+#ifndef DBF_DECODE_DIRECT_MIN_NB
+#define DBF_DECODE_DIRECT_MIN_NB 2
+#endif
 template <int NB, int RT>
-RoundPlan plan_rounds(int npairs, int act_rows) {
+RoundPlan plan_rounds(int npairs, int act_rows, int lds_rows) {
     RoundPlan p{};
     const int budget = round_pairs<NB, RT>();
+    // Direct form at batch >= 2 when the activations of the whole reduction
+    // dimension (lds_rows rows of 64 halves per pair) fit LDS.  (Measured:
+    // 4096x4096 k = 2048 at batch 16, 19.4 -> 15.1 us per forward, batch 4
+    // 11.5 -> 10.9 us; at batch 1 the one-shot staging through LDS is as
+    // fast or faster -- 8 times fewer load instructions for the big layers.)
+    const size_t act_all = static_cast<size_t>(lds_rows) * 64 * npairs * sizeof(_Float16);
+    if (DBF_DECODE_DIRECT && NB >= DBF_DECODE_DIRECT_MIN_NB && act_all + kLdsTail <= kLdsBudget) {
+        p.PR = npairs;
+        p.pipe = 2;
+        p.lds = std::max(act_all, lds_reduce_bytes<NB, RT>()) + kLdsTail;
+        return p;
+    }
     if (Acc<NB>::kSP && DBF_DECODE_PIPE_KB > 0 &&
         static_cast<size_t>(npairs) * 128 * RT >= size_t(DBF_DECODE_PIPE_KB) * 1024) {
         const int cap = std::min({budget / 2, kThreads * kMaxItems / (8 * RT), kThreads * kMaxAct / (8 * act_rows)});
@@ -794,7 +905,7 @@ int launch_rt(const MfmaDecodeArgs &d, hipStream_t s, int which) {
     if (which == 1) {
         static const bool once = (allow_lds(mfma_stage1_kernel<NB, RT, BIN>, kLdsBudget), true);
         (void)once;
-        const RoundPlan rp = plan_rounds<NB, RT>(d.m_pad / 64, NB);
+        const RoundPlan rp = plan_rounds<NB, RT>(d.m_pad / 64, NB, Acc<NB>::kSP ? NB + 1 : 2 * NB);
         const int G1 = d.k_pad / (16 * RT);
         Stage2Readahead ra{};
         ra.A = reinterpret_cast<const uint4 *>(d.A_dev);
@@ -819,7 +930,7 @@ int launch_rt(const MfmaDecodeArgs &d, hipStream_t s, int which) {
     } else {
         static const bool once = (allow_lds(mfma_stage2_kernel<NB, RT, BIN>, kLdsBudget), true);
         (void)once;
-        const RoundPlan rp = plan_rounds<NB, RT>(d.k_pad / 64, (Acc<NB>::kSP ? 1 : 2) * NB);
+        const RoundPlan rp = plan_rounds<NB, RT>(d.k_pad / 64, (Acc<NB>::kSP ? 1 : 2) * NB, (Acc<NB>::kSP ? 1 : 2) * NB);
         launch_kernel((mfma_stage2_kernel<NB, RT, BIN>), dim3(d.n_pad / (16 * RT)), dim3(kThreads), rp.lds, s,
                       d.A_dev, d.k_pad / 32, reinterpret_cast<const __half *>(d.v16), d.k_pad,
                       static_cast<const __half *>(d.a_dev), static_cast<__half *>(d.y), d.n, rp.PR, rp.pipe,
@@ -851,7 +962,7 @@ int launch_group_rt(const MfmaGroupArgs &g, hipStream_t s, int which) {
         a.x = static_cast<const __half *>(g.x);
         a.m = g.m;
         a.Wm = g.m_pad / 32;
-        const RoundPlan rp = plan_rounds<NB, RT>(g.m_pad / 64, NB);
+        const RoundPlan rp = plan_rounds<NB, RT>(g.m_pad / 64, NB, Acc<NB>::kSP ? NB + 1 : 2 * NB);
         a.PR = rp.PR;
         a.pipe = rp.pipe;
         int blocks = 0;
@@ -871,7 +982,8 @@ int launch_group_rt(const MfmaGroupArgs &g, hipStream_t s, int which) {
         size_t lds = 0;
         for (int i = 0; i < g.count; ++i) {
             const MfmaGroupLayer &L = g.L[i];
-            const RoundPlan rp = plan_rounds<NB, RT>(L.k_pad / 64, (Acc<NB>::kSP ? 1 : 2) * NB);
+            const RoundPlan rp =
+                plan_rounds<NB, RT>(L.k_pad / 64, (Acc<NB>::kSP ? 1 : 2) * NB, (Acc<NB>::kSP ? 1 : 2) * NB);
             a.L[i] = {L.A_dev, reinterpret_cast<const __half *>(L.v16), static_cast<const __half *>(L.a_dev),
                       static_cast<__half *>(L.y), L.k_pad / 32, L.k_pad, L.n, rp.PR, rp.pipe, blocks};
             blocks += L.n_pad / (16 * RT);
