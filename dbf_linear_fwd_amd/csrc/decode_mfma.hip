@@ -5,7 +5,7 @@
 // run here as 16x16x32 f16 MFMA products: the sign matrix is the A operand,
 // expanded from its bits to ±1.0 in registers, and the activations are the B
 // operand with the batch as the (at most 16 wide) N dimension.
-// Batch 1..8:
+// Batch 1:
 //   stage 1: u = x ⊙ b is formed in fp32 (exact: a product of two fp16) and
 //            split into u_hi = rne16(u) and u_lo = rne16(u - u_hi), which
 //            carry about 22 significant bits; t = B u_hi + B u_lo in fp32;
@@ -13,7 +13,7 @@
 //            fp16 planes v_hi, v_lo.
 //   stage 2: s = A v_hi + A v_lo in fp32; y = rne16(s * a).
 //   The hi and lo parts ride in columns r and r + 8 of one MFMA.
-// Batch 9..16 (the 16 columns are all batch rows): the sign operand of
+// Batch 2..16 (the columns are batch rows): the sign operand of
 // stage 1 carries ±b (b's fp16 sign bit flipped, exact), so x enters the
 // product as it is and t = (B ⊙ b) x; v = rne16(t * mid) is one fp16 plane
 // and s = A v -- the numerics of the prefill path.
@@ -135,17 +135,23 @@ __device__ __forceinline__ float rounded(float x) {
 
 __device__ __forceinline__ f16x8 zero8() { return __builtin_bit_cast(f16x8, u32x4{0u, 0u, 0u, 0u}); }
 
-// Operand forms by batch size:
-//   NB <= 8  : hi and lo fp16 planes of u = x ⊙ b (stage 1) and v (stage 2)
+// Operand forms by batch size (NB < DBF_DECODE_SP_MIN: the first form):
+//   NB = 1   : hi and lo fp16 planes of u = x ⊙ b (stage 1) and v (stage 2)
 //              ride in columns r and r + 8 of one MFMA (kShared);
-//   NB 9..16 : one plane (kSP): stage 1 multiplies x itself, with b folded
+//   NB 2..16 : one plane (kSP): stage 1 multiplies x itself, with b folded
 //              into the expanded signs as ±b (exact, as on the prefill
 //              path), and stage 2 multiplies v rounded once to fp16; one
 //              MFMA per sign fragment with the batch rows as its columns.
+//              (Half the activation bytes: measured 5-25 % faster than the
+//              hi/lo form at batch 2-8 on the 4096- and 14336-wide layers.)
+#ifndef DBF_DECODE_SP_MIN
+#define DBF_DECODE_SP_MIN 2
+#endif
 template <int NB>
 struct Acc {
-    static constexpr bool kShared = NB <= 8;
-    static constexpr bool kSP = NB > 8;
+    static_assert(DBF_DECODE_SP_MIN >= 2 && DBF_DECODE_SP_MIN <= 9, "hi/lo planes need 2 NB <= 16 columns");
+    static constexpr bool kSP = NB >= DBF_DECODE_SP_MIN;
+    static constexpr bool kShared = !kSP;
     static constexpr int N = 1;
     // activation bytes per word pair in LDS: 2 planes x NB rows x 64 halves;
     // single plane: NB rows + one row of b (stage 1)
@@ -840,13 +846,13 @@ void allow_lds(K kernel, size_t bytes) {
 #define DBF_DECODE_PIPE_ROUNDS 3
 #endif
 
-// Rounds of a stage: at batch 9..16 a workgroup whose block of sign words
+// Rounds of a stage: in the single-plane form a workgroup whose block of sign words
 // reaches DBF_DECODE_PIPE_KB takes it in at least DBF_DECODE_PIPE_ROUNDS
 // rounds, each one batch of loads, through two LDS buffers (the next round's
 // loads fly while the current round is multiplied); otherwise one round when
-// LDS allows.  (Measured: at batch 16 the MLP layers gain 6-10 %; at batch
-// 1-8, where a round's MFMA work is shorter than the memory latency, the
-// extra round trips cost more than the overlap saves.)  act_rows: activation
+// LDS allows.  (Measured: at batch 16 the MLP layers gain 6-10 %; in the
+// hi/lo form, where a round's MFMA work is shorter than the memory latency,
+// the extra round trips cost more than the overlap saves.)  act_rows: activation
 // rows staged per word pair.
 struct RoundPlan {
     int PR, pipe;

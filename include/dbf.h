@@ -23,8 +23,8 @@
  * Numerics: fp16 in and out, fp32 accumulation, one round-to-nearest-even
  * to fp16 at the end; no flush-to-zero.  The intermediate v = t * mid
  * (batch x k) is an operand of 16-bit matrix-core products: on the decode
- * path at batch <= 8 it is kept as the sum of two fp16 numbers (about 22
- * significant bits); at decode batch 9..16 and on the prefill path it is
+ * path at batch 1 it is kept as the sum of two fp16 numbers (about 22
+ * significant bits); at decode batch 2..16 and on the prefill path it is
  * rounded once to fp16.  On both it must stay inside the fp16 range
  * (|v| < 65520); the table path keeps it in fp32.
  *
@@ -72,8 +72,8 @@ typedef enum {
 typedef enum {
     DBF_PATH_AUTO = 0,         /* batch <= 16: DBF_PATH_DECODE; batch > 16: DBF_PATH_PREFILL */
     DBF_PATH_DECODE = 1,       /* small-batch kernels: batch as the MFMA N dimension, intermediate
-                                  kept as an fp16 hi+lo pair (batch <= 8) or rounded once to fp16
-                                  (batch 9..16); batch must be <= 16 */
+                                  kept as an fp16 hi+lo pair (batch 1) or rounded once to fp16
+                                  (batch 2..16); batch must be <= 16 */
     DBF_PATH_PREFILL = 2,      /* tiled MFMA products, intermediate rounded once to fp16; any batch */
     DBF_PATH_DECODE_TABLE = 3  /* vector-ALU signed sums (4-sign lookup tables for batch <= 4, one
                                   add per sign above), intermediate in fp32; batch must be <= 16 */
@@ -190,7 +190,7 @@ dbf_status_t dbf_pack_ex(int32_t n, int32_t m, int32_t k,
  * precision and kept in fp32; the per-row sums Σx and γ·x (fp32, one small
  * kernel per forward) enter the output epilogue before its rounding.  The
  * intermediate (batch x p d) follows the DBF path rules (hi+lo pair at
- * decode batch <= 8, else one fp16 rounding) and must stay in fp16 range.
+ * decode batch 1, else one fp16 rounding) and must stay in fp16 range.
  * Errors: DBF_ERR_INVALID_ARG (null pointers, sizes < 1, entries not 0/1),
  * DBF_ERR_SHAPE, DBF_ERR_OOM, DBF_ERR_HIP.  The table path, grouped
  * forwards and gradients return DBF_ERR_UNSUPPORTED for such a handle.

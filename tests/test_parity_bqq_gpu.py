@@ -131,7 +131,7 @@ def test_bqq_integer_bit_exact(gpu, n, m, d, p, batch, path):
     _say(f"bqq integer n={n} m={m} d={d} p={p} batch={batch} path={path}")
     L = inputs.bqq_layer("i", n, m, d, p, 7200 + n + batch, (batch,), integer=True)
     X = L.X[batch]
-    fp16_v = path == dbf.DBF_PATH_PREFILL or batch > 8
+    fp16_v = path == dbf.DBF_PATH_PREFILL or batch > 1
     ref = _integer_preconditions(L, X, fp16_v)
     _assert_bits(_run(L, X, path), ref, f"bqq integer {n}x{m} d{d} p{p} b{batch}")
 
