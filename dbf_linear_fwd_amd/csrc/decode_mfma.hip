@@ -49,6 +49,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kNW = 8;                      // waves per workgroup
 constexpr int kThreads = kNW * 64;
 constexpr int kMaxItems = 8;                // 16-byte sign loads per thread in flight per batch
+#ifndef DBF_DECODE_TRIM_LOADS
+#define DBF_DECODE_TRIM_LOADS 1
+#endif
 constexpr int kMaxAct = 4;                  // activation items (8 elements) per thread per batch
 #ifndef DBF_DECODE_LDS_KB
 #define DBF_DECODE_LDS_KB 144
@@ -189,15 +192,21 @@ int round_pairs() {
 
 // Issue the loads of this thread's 16-byte sign items of the round, items
 // it = item0 + threadIdx.x + kThreads * q (q < kMaxItems) of the block
-// [pairs][rows].  Items past the end load a valid item instead (the index is
-// clamped) and are not stored: the loads are straight-line code, so they are
-// all in flight together instead of waiting on one another at branch joins.
+// [pairs][rows].  Slots that no thread of the workgroup needs are skipped (a
+// uniform branch; measured 2-5 % faster at batch 1 than loading them); in
+// the last slot, items past the end load a valid item instead (the index is
+// clamped) and are not stored, so the loads stay unconditional per lane and
+// are all in flight together.
 template <int RT>
 __device__ __forceinline__ void load_sign_items(u32x4 (&v)[kMaxItems], const uint32_t *__restrict__ S, int words,
                                                 int r0, int pr0, int nitems, int item0) {
     const int tile = r0 >> 6, roff = r0 & 63;
 #pragma unroll
     for (int q = 0; q < kMaxItems; ++q) {
+#if DBF_DECODE_TRIM_LOADS
+        // slots no lane of the workgroup needs are not loaded (a uniform branch)
+        if (item0 + kThreads * q >= nitems) break;
+#endif
         const int it = min(item0 + static_cast<int>(threadIdx.x) + kThreads * q, nitems - 1);
         const int p = pr0 + it / (8 * RT);
         const int off = (it % (8 * RT)) * 4;  // in words
@@ -423,6 +432,9 @@ __device__ __forceinline__ void stage1_body(int blk, char *base, const uint32_t 
             // rows of x are 16-byte aligned: clamped, unconditional vector loads
 #pragma unroll
             for (int q = 0; q < kMaxAct; ++q) {
+#if DBF_DECODE_TRIM_LOADS
+                if (act0 + kThreads * q >= nact) break;
+#endif
                 const int it = min(act0 + static_cast<int>(threadIdx.x) + kThreads * q, nact - 1);
                 const int r = NB == 1 ? 0 : it / per_row;
                 const int l = k0 + (it - r * per_row) * 8;
@@ -613,6 +625,9 @@ __device__ __forceinline__ void stage2_body(int blk, char *base, const uint32_t 
         if (with_signs) load_sign_items<RT>(B.v, At, Wk, i0, pr0, nitems, item0);
 #pragma unroll
         for (int q = 0; q < kMaxAct; ++q) {
+#if DBF_DECODE_TRIM_LOADS
+            if (act0 + kThreads * q >= nact) break;
+#endif
             const int it = min(act0 + static_cast<int>(threadIdx.x) + kThreads * q, nact - 1);
             const int r = it / per_row;
             const int e = (it - r * per_row) * 8;
