@@ -485,6 +485,24 @@ def fp16_context_leg(args):
             c.close()
         del copies
         torch.cuda.synchronize()
+    # the library's dense fp16 GEMM on the batch-2048 shape of the 4096x4096
+    # layer: the MFMA rate a plain GEMM attains on this chip under this load
+    Xg = torch.randn((2048, 4096), generator=g).half().cuda()
+    Wg = (0.02 * torch.randn((4096, 4096), generator=g)).half().cuda()
+    Yg = torch.empty((2048, 4096), dtype=torch.float16, device="cuda")
+    for _ in range(5):
+        torch.matmul(Xg, Wg.t(), out=Yg)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(50):
+        torch.matmul(Xg, Wg.t(), out=Yg)
+    e1.record()
+    torch.cuda.synchronize()
+    tg = e0.elapsed_time(e1) * 1e3 / 50
+    res["fp16_gemm_2048x4096x4096_us"] = tg
+    res["fp16_gemm_2048x4096x4096_tflops"] = 2 * 2048 * 4096 * 4096 / (tg * 1e-6) / 1e12
+    del Xg, Wg, Yg
     buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(buf)
     dst.copy_(buf)

@@ -496,12 +496,12 @@ __device__ __forceinline__ void wait_step(int y) {
 }
 
 // One K step of sign_gemm_dma_kernel: start the loads of step `nxt` into
-// stage `dst` (if `go`), then multiply the operands in stage `src`.  The two
+// stage `dst` (if GO), then multiply the operands in stage `src`.  The two
 // stage pointers are restrict-qualified: they never overlap, and the compiler
 // then does not hold the LDS reads of `src` back until the loads into `dst`
 // have landed (the kernel orders them itself with vmcnt and the barrier).
-template <bool HAS_SK, int KP, int D, bool BIN, typename IssueOne>
-__device__ __forceinline__ void dma_step(bool go, int nxt, char *__restrict__ dst, const char *__restrict__ src,
+template <bool HAS_SK, int KP, int D, bool BIN, bool GO, typename IssueOne>
+__device__ __forceinline__ void dma_step(int nxt, char *__restrict__ dst, const char *__restrict__ src,
                                          IssueOne &issue_one, f32x16 (&acc)[DMF][DNF], int wm, int wn, int l32,
                                          int kg, ExpandConsts ec) {
     using C = DmaStep<KP>;
@@ -517,7 +517,7 @@ __device__ __forceinline__ void dma_step(bool go, int nxt, char *__restrict__ ds
         for (int s = 4 * j; s < 4 * j + 4; ++s) {  // K sub-steps of 16
         // the loads of step nxt go out one per sub-step, between the MFMAs,
         // so that the memory pipeline works while the matrix cores do
-        if (go && s < D) issue_one(nxt, dst, s);
+        if (GO && s < D) issue_one(nxt, dst, s);
         const int pc = ((2 * s + kg) ^ (l32 & 7)) * 16;
         f16x8 af[DMF];
 #pragma unroll
@@ -624,15 +624,32 @@ __global__ __launch_bounds__(kDThreads) void sign_gemm_dma_kernel(const __half *
     for (int s0 = 0; s0 < kStages - 1; ++s0)
         if (s0 < nk) issue(s0, lds + s0 * C::StageBytes);
 
-    for (int kt = 0; kt < nk; ++kt) {
-        // this wave's loads of step kt have landed; younger steps may be in flight
-        wait_step<D, kStages - 2>(min(kStages - 2, nk - 1 - kt));
+    // Steps that start the loads of a later step, then the last kStages - 1
+    // steps that start none: no branch inside a step's body, so the
+    // compiler schedules a whole step as one block (LDS reads of the next K
+    // sub-step ahead of the current one's MFMAs; 4096x14336 MLP products
+    // 7-9 % faster than with the loads under a per-step condition).
+    int kt = 0;
+    for (; kt < nk - (kStages - 1); ++kt) {
+        // this wave's loads of step kt have landed, those of the kStages - 2
+        // younger steps may be in flight; the barrier: every other wave's too,
+        // and step kt - 1's buffer is free
+        wait_vm<(kStages - 2) * D>();
         asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();  // ... and every other wave's; step kt - 1's buffer is free
+        __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         const int nxt = kt + kStages - 1;
-        dma_step<HAS_SK, KP, D, BIN>(nxt < nk, nxt, lds + (nxt % kStages) * C::StageBytes,
-                                lds + (kt % kStages) * C::StageBytes, issue_one, acc, wm, wn, l32, kg, ec);
+        dma_step<HAS_SK, KP, D, BIN, true>(nxt, lds + (nxt % kStages) * C::StageBytes,
+                                           lds + (kt % kStages) * C::StageBytes, issue_one, acc, wm, wn, l32, kg,
+                                           ec);
+    }
+    for (; kt < nk; ++kt) {
+        wait_step<D, kStages - 2>(min(kStages - 2, nk - 1 - kt));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        dma_step<HAS_SK, KP, D, BIN, false>(0, lds, lds + (kt % kStages) * C::StageBytes, issue_one, acc, wm, wn,
+                                            l32, kg, ec);
     }
 
     if (part) {
