@@ -126,11 +126,12 @@ struct LaunchEvents {
 LaunchEvents &launch_events();
 
 #if defined(__HIPCC__)
-// Launch through hipExtLaunchKernel when launch events are set, plainly otherwise.
+// Launch through hipExtLaunchKernel when a launch event is set (start: recorded
+// as the kernel starts, stop: as it ends), plainly otherwise.
 template <typename K, typename... Args>
 inline void launch_kernel(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, Args... args) {
     const LaunchEvents &e = launch_events();
-    if (e.start && e.stop)
+    if (e.start || e.stop)
         hipExtLaunchKernelGGL(kernel, grid, block, static_cast<uint32_t>(lds), s, static_cast<hipEvent_t>(e.start),
                               static_cast<hipEvent_t>(e.stop), 0u, args...);
     else
@@ -153,12 +154,16 @@ inline void launch_kernel(K kernel, dim3 grid, dim3 block, size_t lds, hipStream
 //   into split->nsplit parts that run as separate workgroups and write
 //   their unscaled fp32 sums to split->ws[s][M][split->ldw]; the caller then
 //   runs launch_split_finish, which adds the parts in order s = 0, 1, ...
-//   and writes out.  split->nsplit is set to 1 when no split was taken.
+//   and writes out.  Where the grid is one wave of workgroups plus a small
+//   partial one, only the output columns from split->col0 on (the tail) are
+//   split; the columns before it are written directly.  split->nsplit is
+//   set to 1 when no split was taken.
 struct SplitK {
     float *ws = nullptr;  // workspace of cap floats
     size_t cap = 0;
     int nsplit = 1;       // set by launch_sign_gemm
     int ldw = 0;
+    int col0 = 0;         // first output column of the split part (set by launch_sign_gemm)
 };
 //   flavor (may be null): binary = S holds a 0/1 matrix (bit 1 = 1), the
 //   operand is then {0, 2} (callers fold the 2 into sn) and sk must be null;
@@ -176,8 +181,8 @@ int launch_sign_gemm(const void *P, int ldp, int M, int K, const uint32_t *S, in
 // Floats of split workspace that launch_sign_gemm would use for this
 // product (0: it would not split), assuming 16-byte aligned rows of P.
 size_t sign_gemm_split_elems(int M, int K, int words, int n_out);
-// out[i][c] = rne16(sn[c] * (ws[0][i][c] + ws[1][i][c] + ...)
-//                  [+ aff_E[c] * aff_stats[2i] + aff_stats[2i + 1]]), i < M, c < n_out.
+// out[i][c] = rne16(sn[c] * (ws[0][i][c - col0] + ws[1][i][c - col0] + ...)
+//                  [+ aff_E[c] * aff_stats[2i] + aff_stats[2i + 1]]), i < M, split.col0 <= c < n_out.
 int launch_split_finish(const SplitK &split, int M, int n_out, const void *sn, void *out, int ldo, void *stream,
                         const float *aff_E = nullptr, const float *aff_stats = nullptr);
 

@@ -707,14 +707,49 @@ int split_parts(int M, int words, int n_out) {
     return std::max(1, std::min(DBF_SPLIT_TARGET / tiles, nk / DBF_SPLIT_MIN_STEPS));
 }
 
+#ifndef DBF_PREFILL_TAIL
+#define DBF_PREFILL_TAIL 1
+#endif
+#ifndef DBF_TAIL_BELOW
+#define DBF_TAIL_BELOW 512
+#endif
+
+// Head and tail of a grid of 257 to DBF_TAIL_BELOW - 1 tiles (one wave of
+// workgroups over the CUs plus a partial one): the first column tiles, at
+// most 256 tiles, run whole-K as one wave, and the remaining columns run
+// split-K in about DBF_SPLIT_TARGET workgroups instead of as a second,
+// mostly empty wave.  Returns the first tail column (0: no head and tail)
+// and sets *parts to the tail's part count.  Measured at batch 2048 (304
+// tiles in the first product of the k = 4800 MLP layers): 4096x14336
+// 406 -> 336 us per forward, 14336x4096 341 -> 335 us.  Grids of 512 tiles
+// and more keep K steps of 64 and two workgroups per CU (a head of whole
+// waves with a split tail measured no faster there).
+int tail_split(int M, int words, int n_out, int *parts) {
+    *parts = 1;
+    if (!DBF_PREFILL_TAIL || kDmaPairs != 2 || words % 4 != 0) return 0;
+    const int nbm = (M + BM - 1) / BM, nbn = (n_out + DBN - 1) / DBN;
+    const int tiles = nbm * nbn;
+    if (tiles <= 256 || tiles >= DBF_TAIL_BELOW) return 0;
+    const int head = 256 / nbm;  // column tiles of the head
+    if (head < 1 || head >= nbn) return 0;
+    const int tail_tiles = nbm * (nbn - head);
+    if (tail_tiles >= DBF_SPLIT_BELOW) return 0;
+    const int nk = words / 4;
+    *parts = std::max(1, std::min(DBF_SPLIT_TARGET / tail_tiles, nk / DBF_SPLIT_MIN_STEPS));
+    if (*parts <= 1) return 0;
+    return head * DBN;
+}
+
 }  // namespace
 
 size_t sign_gemm_split_elems(int M, int K, int words, int n_out) {
 #ifndef DBF_PREFILL_NO_DMA
     if (M <= 0 || K % BK != 0 || K != words * 32) return 0;
-    const int parts = split_parts(M, words, n_out);
-    if (parts <= 1) return 0;
-    return static_cast<size_t>(parts) * M * ((n_out + 3) & ~3);
+    int parts = split_parts(M, words, n_out);
+    if (parts > 1) return static_cast<size_t>(parts) * M * ((n_out + 3) & ~3);
+    const int col0 = tail_split(M, words, n_out, &parts);
+    if (col0 > 0) return static_cast<size_t>(parts) * M * ((n_out - col0 + 3) & ~3);
+    return 0;
 #else
     (void)M, (void)K, (void)words, (void)n_out;
     return 0;
@@ -725,9 +760,11 @@ int launch_split_finish(const SplitK &split, int M, int n_out, const void *sn, v
                         const float *aff_E, const float *aff_stats) {
     const int items = M * (split.ldw >> 2);
     if (items == 0) return 0;
+    const int c0 = split.col0;
     launch_kernel(split_finish_kernel, dim3((items + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream),
-                  static_cast<const float *>(split.ws), split.nsplit, M, n_out, split.ldw,
-                  static_cast<const __half *>(sn), static_cast<__half *>(out), ldo, Affine{aff_E, aff_stats});
+                  static_cast<const float *>(split.ws), split.nsplit, M, n_out - c0, split.ldw,
+                  static_cast<const __half *>(sn) + c0, static_cast<__half *>(out) + c0, ldo,
+                  Affine{aff_E ? aff_E + c0 : nullptr, aff_stats});
     return static_cast<int>(hipGetLastError());
 }
 
@@ -755,6 +792,31 @@ int dispatch(const GemmLaunch &a, hipStream_t s, SplitK *split) {
                 dispatch_dma<HAS_SK, BIN>(a, s, kp, split->ws, parts, ldw);
                 return static_cast<int>(hipGetLastError());
             }
+            int tparts = 1;
+            const int c0 = tail_split(a.M, a.words, a.n_out, &tparts);
+            const int ldt = (a.n_out - c0 + 3) & ~3;
+            if (c0 > 0 && static_cast<size_t>(tparts) * a.M * ldt <= split->cap) {
+                // timed as one product: the start event on the head, the stop event on the tail
+                const LaunchEvents ev = launch_events();
+                launch_events() = {ev.start, nullptr};
+                GemmLaunch head = a;  // columns [0, c0), whole K
+                head.n_out = c0;
+                dispatch_dma<HAS_SK, BIN>(head, s, 2);
+                launch_events() = {nullptr, ev.stop};
+                GemmLaunch tail = a;  // columns [c0, n_out): sign rows from 64-row tile c0 / 64 on
+                tail.S = a.S + static_cast<size_t>(c0 / 64) * (a.words >> 1) * 128;
+                tail.n_rows_pad = a.n_rows_pad - c0;
+                tail.sn = static_cast<const __half *>(a.sn) + c0;
+                tail.out = static_cast<__half *>(a.out) + c0;
+                tail.n_out = a.n_out - c0;
+                tail.aff.E = a.aff.E ? a.aff.E + c0 : nullptr;
+                dispatch_dma<HAS_SK, BIN>(tail, s, 2, split->ws, tparts, ldt);
+                launch_events() = ev;
+                split->nsplit = tparts;
+                split->ldw = ldt;
+                split->col0 = c0;
+                return static_cast<int>(hipGetLastError());
+            }
         }
         // K steps of 128 where K allows and the tiles fit one wave of
         // workgroups over the 256 CUs; else steps of 64, whose 74 KiB of LDS
@@ -780,7 +842,10 @@ int launch_sign_gemm(const void *P, int ldp, int M, int K, const uint32_t *S, in
                        DotArgs{dq, dq_f32, lddq, dpart},
                        Affine{flavor ? flavor->aff_E : nullptr, flavor ? flavor->aff_stats : nullptr}};
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (split) split->nsplit = 1;
+    if (split) {
+        split->nsplit = 1;
+        split->col0 = 0;
+    }
     if (flavor && flavor->binary) {
         if (sk) return static_cast<int>(hipErrorInvalidValue);  // 0/1 matrices take no per-K scale
         return dispatch<false, true>(a, s, split);

@@ -110,6 +110,18 @@ def test_bqq_split_k(gpu, batch):
     _assert_bits(_run(Li, Xi), _integer_preconditions(Li, Xi, True), f"bqq split-K integer b{batch}")
 
 
+# A large batch on a layer whose second product is one wave of output tiles
+# plus a partial one (n = 4400: 18 column tiles of 256 at 16 row tiles): its
+# tail columns take the split-K finish, with the affine term.
+def test_bqq_head_tail(gpu):
+    n, m, d, p, batch = 4400, 512, 2240, 2, 2048
+    _say(f"bqq head/tail n={n} m={m} d={d} p={p} batch={batch}")
+    L = inputs.bqq_layer("h", n, m, d, p, 7080, (batch,))
+    X = L.X[batch]
+    ref = Q.bqq_forward(X, L.Y, L.Z, L.r, L.s, L.t, L.u)
+    _assert_tol(_run(L, X), ref, f"bqq head/tail b{batch}")
+
+
 def _integer_preconditions(L, X, fp16_intermediate):
     """Every partial sum is an integer far inside fp32's exact range, the
     kernel's intermediate v = 2 r_i (Z_i x) is exact where it is rounded to

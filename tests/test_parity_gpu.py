@@ -201,6 +201,42 @@ def test_prefill_split_k_determinism(gpu):
         H.close()
 
 
+# Large batches on a shape whose prefill grids are one wave of 128 x 256
+# output tiles plus a small partial one: the first column tiles (at most 256
+# tiles) run whole-K, the remaining columns split-K.  Stage 1: N = k = 4480
+# (18 column tiles; the tail from column 4096 at batch 2048, from 4352 at
+# batch 1920, ragged); stage 2: N = n = 4400 (18 column tiles, ragged tail).
+HEAD_TAIL_SHAPE = (4400, 512, 4480)
+
+
+@pytest.mark.parametrize("batch", [1920, 2048])
+def test_prefill_head_tail(gpu, batch):
+    n, m, k = HEAD_TAIL_SHAPE
+    _say(f"prefill head/tail n={n} m={m} k={k} batch={batch}")
+    X, A, B, a, mid, b = inputs.tiny_case(4100 + batch, n, m, k, batch, signed_scales=True)
+    L = inputs.Layer("s", n, m, k, A, B, a, mid, b, {})
+    y = run(L, X)
+    assert_tol(y, O.dense_forward(X, A, B, a, mid, b), f"prefill head/tail b{batch}")
+
+
+def test_prefill_head_tail_determinism(gpu):
+    """The head/tail split depends on the batch only through its 128-row
+    tiles: batches of one tile count give identical bits."""
+    torch = _torch()
+    n, m, k = HEAD_TAIL_SHAPE
+    X, A, B, a, mid, b = inputs.tiny_case(4199, n, m, k, 2048, signed_scales=True)
+    H = dbf.Layer(A, B, a, mid, b, max_batch=2048)
+    try:
+        _say("prefill head/tail determinism")
+        x = torch.from_numpy(X).cuda()
+        y2048 = H.forward(x).cpu().numpy()
+        assert np.array_equal(y2048.view(np.uint16), H.forward(x).cpu().numpy().view(np.uint16))
+        y1930 = H.forward(x[:1930]).cpu().numpy()
+        assert np.array_equal(y1930.view(np.uint16), y2048[:1930].view(np.uint16))
+    finally:
+        H.close()
+
+
 # --------------------------------------------------------------------------- integer sub-suite (bit-exact)
 
 INT_SHAPES = [
