@@ -169,12 +169,16 @@ def prefill_kernel_flops(layer, batch):
 
 def cpu_baseline(layer, seconds):
     """The fp64 oracle (dense reconstruction + X W^T, one batch-1 forward per
-    call) on the host, repeated for about `seconds`; GB/s of packed weights."""
+    call) on the host, repeated for about `seconds`; GB/s of packed weights.
+    Also its two parts on their own (the W reconstruction, 2nmk flops, and
+    the product X W^T with W built, 2nm flops per batch row) and one forward
+    on a single core."""
     from oracle import dbf_oracle as O
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     except Exception:
+        threadpool_limits = None
         threads = os.cpu_count() or 1
     X = layer.X[1]
     calls = 0
@@ -186,9 +190,28 @@ def cpu_baseline(layer, seconds):
         if el >= seconds:
             break
     gbs = (layer.sign_bytes + layer.scale_bytes) * calls / el / 1e9
+    t1 = time.perf_counter()
+    W = O.dense_weight(layer.A, layer.B, layer.a, layer.mid, layer.b)
+    w_s = time.perf_counter() - t1
+    X64 = X.astype(np.float64)
+    xw = []
+    for _ in range(21):
+        t2 = time.perf_counter()
+        X64 @ W.T
+        xw.append(time.perf_counter() - t2)
+    del W
+    one = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            t3 = time.perf_counter()
+            O.dense_forward(X, layer.A, layer.B, layer.a, layer.mid, layer.b)
+            one = time.perf_counter() - t3
     return {"value": gbs, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{calls} batch-1 forwards of the 4096x4096 k=2048 layer through the fp64 dense oracle "
-                      f"(W rebuilt each call) in {el:.1f} s"}
+                      f"(W rebuilt each call) in {el:.1f} s",
+            "w_rebuild_s": round(w_s, 3), "xwt_median_ms": round(1e3 * float(np.median(xw)), 3),
+            "one_core_forward_s": None if one is None else round(one, 3),
+            "host_cpu_count": os.cpu_count()}
 
 
 def block_leg(args):
@@ -575,6 +598,24 @@ def main():
         el_e, done_e = time_steps(fwd, min(args.steps, 2 * R), min(args.warmup, R), "eager")
         kt = kernel_times(copies, fwd, min(args.steps, 2 * R))
         print(f"[bench] kernel event times: {kt}", file=sys.stderr, flush=True)
+        # cold calls: each after a 512 MiB write (evicts the L2s and the
+        # Infinity Cache); a GPU-side spin covers the host's enqueue, so the
+        # events time the forward's kernels and the gap between them
+        scrub = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        cold = []
+        for i in range(9):
+            scrub.fill_(i & 255)
+            torch.cuda.synchronize()
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(200000)
+            c0.record()
+            fwd(i)
+            c1.record()
+            torch.cuda.synchronize()
+            cold.append(c0.elapsed_time(c1) * 1e3)
+        del scrub
+        torch.cuda.empty_cache()
+        print(f"[bench] cold calls (us): {[round(c, 1) for c in cold]}", file=sys.stderr, flush=True)
         kb = decode_kernel_bytes(layer, 1)
         if args.decode_path == "table":
             kb = {"table_" + kname.split("_", 1)[1]: v for kname, v in kb.items()}
@@ -583,6 +624,7 @@ def main():
         result["decode"] = {
             "value": gbs, "ms_per_step": el * 1e3 / done, "steps": done,
             "eager_gbs": bytes_step * done_e / el_e / 1e9,
+            "cold_call_us_median": float(np.median(cold)),
             "kernels": kt, "dominant": dom,
             "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": ach / HBM_PEAK_GBS, "traffic": recorded_traffic(dom), "kernel": dom,
@@ -676,6 +718,7 @@ def main():
         "cpu_baseline": cpu,
         "decode_kernels_us": d["kernels"],
         "eager_gbs": d["eager_gbs"],
+        "cold_call_us_median": d["cold_call_us_median"],
     }
     if "prefill" in result:
         line["prefill_batch2048"] = result["prefill"]
