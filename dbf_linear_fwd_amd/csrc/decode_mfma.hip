@@ -53,6 +53,20 @@ constexpr int kMaxItems = 8;                // 16-byte sign loads per thread in 
 #define DBF_DECODE_TRIM_LOADS 1
 #endif
 constexpr int kMaxAct = 4;                  // activation items (8 elements) per thread per batch
+#ifndef DBF_DECODE_WIDE_ACT_NB
+#define DBF_DECODE_WIDE_ACT_NB 8
+#endif
+#ifndef DBF_DECODE_WIDE_ACT
+#define DBF_DECODE_WIDE_ACT 8
+#endif
+// Activation items per thread per batch at batch NB: twice as many from
+// batch 8 on, so that the rounds of the pipelined form are half as many
+// (14336-wide reductions at batch 16: 48 -> 43 us per forward for the
+// 4096x14336 layer; 207 VGPRs, no spills; 16 items spill).
+template <int NB>
+__host__ __device__ constexpr int act_slots() {
+    return NB >= DBF_DECODE_WIDE_ACT_NB ? DBF_DECODE_WIDE_ACT : kMaxAct;
+}
 #ifndef DBF_DECODE_LDS_KB
 #define DBF_DECODE_LDS_KB 144
 #endif
@@ -420,7 +434,7 @@ __device__ __forceinline__ void stage1_body(int blk, char *base, const uint32_t 
     // the loads of one batch: sign items and the x / b fragments of the round
     struct Batch {
         u32x4 v[kMaxItems];
-        f16x8 xv[kMaxAct], bv[kMaxAct];
+        f16x8 xv[act_slots<NB>()], bv[act_slots<NB>()];
     };
     auto issue = [&](Batch &B, int pr0, int pr1, int item0, int act0, bool with_signs = true) {
         const int nitems = (pr1 - pr0) * 8 * RT;
@@ -431,7 +445,7 @@ __device__ __forceinline__ void stage1_body(int blk, char *base, const uint32_t 
         if (xvec) {
             // rows of x are 16-byte aligned: clamped, unconditional vector loads
 #pragma unroll
-            for (int q = 0; q < kMaxAct; ++q) {
+            for (int q = 0; q < act_slots<NB>(); ++q) {
 #if DBF_DECODE_TRIM_LOADS
                 if (act0 + kThreads * q >= nact) break;
 #endif
@@ -444,7 +458,7 @@ __device__ __forceinline__ void stage1_body(int blk, char *base, const uint32_t 
             }
         } else {
 #pragma unroll
-            for (int q = 0; q < kMaxAct; ++q) {
+            for (int q = 0; q < act_slots<NB>(); ++q) {
                 const int it = min(act0 + static_cast<int>(threadIdx.x) + kThreads * q, nact - 1);
                 const int r = NB == 1 ? 0 : it / per_row;
                 const int l = k0 + (it - r * per_row) * 8;
@@ -466,7 +480,7 @@ __device__ __forceinline__ void stage1_body(int blk, char *base, const uint32_t 
         if constexpr (Acc<NB>::kSP) {
             // x as it is (b goes into the signs); row 0's items also store b
 #pragma unroll
-            for (int q = 0; q < kMaxAct; ++q) {
+            for (int q = 0; q < act_slots<NB>(); ++q) {
                 const int it = act0 + threadIdx.x + kThreads * q;
                 if (it < nact) {
                     const int r = it / per_row;
@@ -478,7 +492,7 @@ __device__ __forceinline__ void stage1_body(int blk, char *base, const uint32_t 
         } else {
             // u = x ⊙ b (exact in fp32) as hi/lo planes
 #pragma unroll
-            for (int q = 0; q < kMaxAct; ++q) {
+            for (int q = 0; q < act_slots<NB>(); ++q) {
                 const int it = act0 + threadIdx.x + kThreads * q;
                 if (it < nact) {
                     const int r = NB == 1 ? 0 : it / per_row;
@@ -500,7 +514,7 @@ __device__ __forceinline__ void stage1_body(int blk, char *base, const uint32_t 
         // direct form: the activations of all of m in LDS, the signs straight to registers
         _Float16 *act_all = reinterpret_cast<_Float16 *>(base);
         const int nact = NB * 8 * npairs;
-        for (int act0 = 0; act0 < nact; act0 += kThreads * kMaxAct) {
+        for (int act0 = 0; act0 < nact; act0 += kThreads * act_slots<NB>()) {
             Batch B;
             issue(B, 0, npairs, 0, act0, false);
             stash(B, nullptr, act_all, 0, npairs, 0, act0, false);
@@ -534,7 +548,7 @@ __device__ __forceinline__ void stage1_body(int blk, char *base, const uint32_t 
             // before any of it is used; one batch covers the layer shapes of
             // interest, so the workgroup waits for memory once per round.
             for (int item0 = 0, act0 = 0; item0 < nitems || act0 < nact;
-                 item0 += kThreads * kMaxItems, act0 += kThreads * kMaxAct) {
+                 item0 += kThreads * kMaxItems, act0 += kThreads * act_slots<NB>()) {
                 Batch B;
                 issue(B, pr0, pr1, item0, act0);
                 stash(B, sgn, act, pr0, pr1, item0, act0);
@@ -615,7 +629,7 @@ __device__ __forceinline__ void stage2_body(int blk, char *base, const uint32_t 
     constexpr int kPlanes = Acc<NB>::kSP ? 1 : 2;  // hi and lo rows (one plane in the single-plane form)
     struct Batch {
         u32x4 v[kMaxItems];
-        f16x8 av[kMaxAct];
+        f16x8 av[act_slots<NB>()];
     };
     auto issue = [&](Batch &B, int pr0, int pr1, int item0, int act0, bool with_signs = true) {
         const int nitems = (pr1 - pr0) * 8 * RT;
@@ -624,7 +638,7 @@ __device__ __forceinline__ void stage2_body(int blk, char *base, const uint32_t 
         const int per_row = len >> 3;
         if (with_signs) load_sign_items<RT>(B.v, At, Wk, i0, pr0, nitems, item0);
 #pragma unroll
-        for (int q = 0; q < kMaxAct; ++q) {
+        for (int q = 0; q < act_slots<NB>(); ++q) {
 #if DBF_DECODE_TRIM_LOADS
             if (act0 + kThreads * q >= nact) break;
 #endif
@@ -642,7 +656,7 @@ __device__ __forceinline__ void stage2_body(int blk, char *base, const uint32_t 
         const int per_row = len >> 3;
         if (with_signs) store_sign_items(B.v, sgn_b, nitems, item0);
 #pragma unroll
-        for (int q = 0; q < kMaxAct; ++q) {
+        for (int q = 0; q < act_slots<NB>(); ++q) {
             const int it = act0 + threadIdx.x + kThreads * q;
             if (it < nact) {
                 const int r = it / per_row;
@@ -655,7 +669,7 @@ __device__ __forceinline__ void stage2_body(int blk, char *base, const uint32_t 
         // direct form: v of all of k in LDS, the signs straight to registers
         _Float16 *act_all = reinterpret_cast<_Float16 *>(base);
         const int nact = kPlanes * NB * 8 * npairs;
-        for (int act0 = 0; act0 < nact; act0 += kThreads * kMaxAct) {
+        for (int act0 = 0; act0 < nact; act0 += kThreads * act_slots<NB>()) {
             Batch B;
             issue(B, 0, npairs, 0, act0, false);
             stash(B, nullptr, act_all, 0, npairs, 0, act0, false);
@@ -686,7 +700,7 @@ __device__ __forceinline__ void stage2_body(int blk, char *base, const uint32_t 
             if (pr0 > 0) __syncthreads();
             // all loads of a batch (sign items, v_hi / v_lo items) are issued first
             for (int item0 = 0, act0 = 0; item0 < nitems || act0 < nact;
-                 item0 += kThreads * kMaxItems, act0 += kThreads * kMaxAct) {
+                 item0 += kThreads * kMaxItems, act0 += kThreads * act_slots<NB>()) {
                 Batch B;
                 issue(B, pr0, pr1, item0, act0);
                 stash(B, sgn, act, pr0, pr1, item0, act0);
@@ -897,7 +911,7 @@ RoundPlan plan_rounds(int npairs, int act_rows, int lds_rows) {
     }
     if (Acc<NB>::kSP && DBF_DECODE_PIPE_KB > 0 &&
         static_cast<size_t>(npairs) * 128 * RT >= size_t(DBF_DECODE_PIPE_KB) * 1024) {
-        const int cap = std::min({budget / 2, kThreads * kMaxItems / (8 * RT), kThreads * kMaxAct / (8 * act_rows)});
+        const int cap = std::min({budget / 2, kThreads * kMaxItems / (8 * RT), kThreads * act_slots<NB>() / (8 * act_rows)});
         if (cap >= 1) {
             const int nr = std::max(DBF_DECODE_PIPE_ROUNDS, (npairs + cap - 1) / cap);
             p.PR = std::min(cap, ((npairs + nr - 1) / nr + kNW - 1) / kNW * kNW);  // whole waves' worth
