@@ -948,16 +948,18 @@ int launch_rt(const MfmaDecodeArgs &d, hipStream_t s, int which) {
         const int rt2 = split_rt(d.n_pad);
         ra.rows_per_wg = 16 * rt2;
         ra.groups = d.n_pad / (16 * rt2);
-        // the read-ahead blocks take the CUs stage 1 leaves free, if there are
-        // enough of them to read stage 2's words in a few batches
-        ra.per_xcd = kReadahead ? std::max(0, (kCUs - G1) / 8) : 0;  // none when stage 1 fills the CUs
+        // 0/1 layers add one block per batch row for the row sums of x
+        const int stat_blocks = BIN ? NB : 0;
+        // the read-ahead blocks take the CUs stage 1 and the row-sum blocks
+        // leave free (a block beyond one per CU would wait for a CU: the
+        // kernel's registers allow one block per CU), if there are enough of
+        // them to read stage 2's words in a few batches
+        ra.per_xcd = kReadahead ? std::max(0, (kCUs - G1 - stat_blocks) / 8) : 0;  // none when stage 1 fills the CUs
         if (ra.per_xcd > 0) {
             const size_t items = static_cast<size_t>(d.n_pad) * (d.k_pad / 32) / 4;
             if (items > static_cast<size_t>(kReadaheadMax) * 8 * ra.per_xcd * kThreads) ra.per_xcd = 0;
         }
-        // the read-ahead blocks start on XCD G1 mod 8; 8 * per_xcd of them cover every XCD equally;
-        // 0/1 layers add one block per batch row for the row sums of x
-        const int stat_blocks = BIN ? NB : 0;
+        // the read-ahead blocks start on XCD G1 mod 8; 8 * per_xcd of them cover every XCD equally
         launch_kernel((mfma_stage1_kernel<NB, RT, BIN>), dim3(G1 + 8 * ra.per_xcd + stat_blocks), dim3(kThreads),
                       rp.lds, s, d.B_dev, d.m_pad / 32, static_cast<const __half *>(d.x), d.m,
                       static_cast<const __half *>(d.b_dev), static_cast<const __half *>(d.mid_dev),
