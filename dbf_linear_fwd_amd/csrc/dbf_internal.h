@@ -72,7 +72,20 @@ struct MfmaDecodeArgs {
     // needs, stats_out[2r] = Σ_l x[r][l], stats_out[2r + 1] = Σ_l gamma[l] x[r][l]
     const float *gamma = nullptr;
     float *stats_out = nullptr;
+    // stage-1 reduction parts (mfma_stage1_parts): fp32 partials of
+    // s1_part_cap floats and s1_ntickets per-row-block tickets, zero between calls
+    float *s1_part = nullptr;
+    size_t s1_part_cap = 0;
+    unsigned *s1_tickets = nullptr;
+    int s1_ntickets = 0;
 };
+
+// Parts into which the matrix-core decode cuts stage 1's reduction (over m)
+// at this batch: a function of the layer's shape and of the batch's numeric
+// form only (1: not cut).  Wide reductions at batch >= 2 are cut so that
+// more CUs share them; the handle then needs parts * kDecodeMaxBatch * k_pad
+// floats of stage-1 partials and k_pad / 16 tickets.
+int mfma_stage1_parts(int m_pad, int k_pad, int batch);
 
 // which = 1: stage 1 (writes v16); which = 2: stage 2 (writes y).
 int launch_mfma_decode(const MfmaDecodeArgs &d, void *stream, int which);

@@ -304,15 +304,17 @@ __device__ __forceinline__ void round_mma(f32x4 (&acc)[Acc<NB>::N][RT], const ui
 // memory into the operand registers, kDirect pairs ahead of the MFMAs -- no
 // LDS copy of the signs and no barrier between their arrival and use.  The
 // MFMAs run in the same order as in round_mma, so both forms give the same
-// bits.  r0: the workgroup's first row (its 16 RT rows lie in one 64-row tile).
+// bits.  r0: the workgroup's first row (its 16 RT rows lie in one 64-row tile);
+// the pairs are p0 .. p0 + npairs - 1 (p0 a multiple of kNW), the activations
+// of pair p0 + q at 64 q.
 #ifndef DBF_DECODE_DIRECT_DEPTH
 #define DBF_DECODE_DIRECT_DEPTH 4
 #endif
 constexpr int kDirect = DBF_DECODE_DIRECT_DEPTH;
 template <int NB, int RT, bool STAGE1, bool BIN>
 __device__ __forceinline__ void direct_mma(f32x4 (&acc)[Acc<NB>::N][RT], const uint32_t *__restrict__ S, int words,
-                                           int r0, int npairs, const _Float16 *act, int KR, int wave, int li, int g,
-                                           ExpandConsts ec) {
+                                           int r0, int p0, int npairs, const _Float16 *act, int KR, int wave, int li,
+                                           int g, ExpandConsts ec) {
     constexpr bool kShared = Acc<NB>::kShared;
     constexpr bool kSP = Acc<NB>::kSP;
     const int r = (li & 7) < NB ? (li & 7) : NB - 1;
@@ -320,7 +322,7 @@ __device__ __forceinline__ void direct_mma(f32x4 (&acc)[Acc<NB>::N][RT], const u
     const _Float16 *brow = act + NB * KR;
     // word pair p of row r0 + 16 t + li: uint2 at ((tile * words / 2 + p) * 64 + (r0 & 63) + 16 t + li)
     const uint2 *src = reinterpret_cast<const uint2 *>(S) + static_cast<size_t>(r0 >> 6) * (words >> 1) * 64 +
-                       (r0 & 63) + li;
+                       static_cast<size_t>(p0) * 64 + (r0 & 63) + li;
     const int np = npairs > wave ? (npairs - wave + kNW - 1) / kNW : 0;  // this wave's pairs
     if (np == 0) return;
     uint2 wa[kDirect][RT], wb[kDirect][RT];
@@ -399,13 +401,25 @@ __device__ __forceinline__ f32x4 total(const float *red, int t, int lane) {
     return dh + dl;
 }
 
+// Reduction parts of stage 1: part `s` of `parts` takes word pairs
+// [pb0, pb1) (whole groups of kNW pairs, so pair p still belongs to wave
+// p mod kNW) and writes its unscaled sums to part[(s * NB + r) * k_pad + j];
+// the last part of a row block to finish (a ticket per row block) adds the
+// parts in order s = 0, 1, ... and writes v.  parts == 1: no split.
+struct S1Split {
+    float *part;
+    unsigned *tickets;
+    int parts;
+};
+
 // Stage 1 for row block `blk` (rows 16*RT*blk ..): v = mid * (B (x ⊙ b)),
 // stored as fp16 hi/lo planes [2][NB][k_pad] (single plane: [NB][k_pad]).
 template <int NB, int RT, bool BIN>
 __device__ __forceinline__ void stage1_body(int blk, char *base, const uint32_t *__restrict__ Bt, int Wm,
                                             const __half *__restrict__ x, int m, const __half *__restrict__ b,
                                             const __half *__restrict__ mid, __half *__restrict__ v16, int k_pad,
-                                            int PR, int pipe) {
+                                            int PR, int pipe, const S1Split sp = S1Split{nullptr, nullptr, 1},
+                                            int part = 0) {
     const int KR = 64 * PR;
     uint32_t *sgn = reinterpret_cast<uint32_t *>(base);
     _Float16 *act = reinterpret_cast<_Float16 *>(base + static_cast<size_t>(PR) * 128 * RT);
@@ -430,6 +444,10 @@ __device__ __forceinline__ void stage1_body(int blk, char *base, const uint32_t 
         for (int t = 0; t < RT; ++t) acc[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int npairs = Wm >> 1;
+    // this part's word pairs [pb0, pb1)
+    const int ngroups = (npairs + kNW - 1) / kNW;
+    const int pb0 = min(npairs, part * ngroups / sp.parts * kNW);
+    const int pb1 = min(npairs, (part + 1) * ngroups / sp.parts * kNW);
     const bool xvec = (m & 7) == 0;
     // the loads of one batch: sign items and the x / b fragments of the round
     struct Batch {
@@ -513,37 +531,38 @@ __device__ __forceinline__ void stage1_body(int blk, char *base, const uint32_t 
     if (pipe == 2) {
         // direct form: the activations of all of m in LDS, the signs straight to registers
         _Float16 *act_all = reinterpret_cast<_Float16 *>(base);
-        const int nact = NB * 8 * npairs;
+        const int nact = NB * 8 * (pb1 - pb0);
         for (int act0 = 0; act0 < nact; act0 += kThreads * act_slots<NB>()) {
             Batch B;
-            issue(B, 0, npairs, 0, act0, false);
-            stash(B, nullptr, act_all, 0, npairs, 0, act0, false);
+            issue(B, pb0, pb1, 0, act0, false);
+            stash(B, nullptr, act_all, pb0, pb1, 0, act0, false);
         }
         __syncthreads();
-        direct_mma<NB, RT, true, BIN>(acc, Bt, Wm, j0, npairs, act_all, 64 * npairs, wave, li, g, ec);
+        // (rows of act_all at the stride KR = 64 PR the plan sized for the largest part)
+        direct_mma<NB, RT, true, BIN>(acc, Bt, Wm, j0, pb0, pb1 - pb0, act_all, KR, wave, li, g, ec);
     } else if (pipe) {
         // Rounds of PR pairs, each one batch, through two LDS buffers: the
         // loads of round r + 1 are in flight while round r is multiplied.
         const size_t RB = lds_round_bytes<NB, RT>(PR);
-        const int nr = (npairs + PR - 1) / PR;
+        const int nr = (pb1 - pb0 + PR - 1) / PR;
         Batch B;
-        issue(B, 0, min(PR, npairs), 0, 0);
+        if (nr > 0) issue(B, pb0, min(pb0 + PR, pb1), 0, 0);
         for (int r = 0; r < nr; ++r) {
-            const int pr0 = r * PR, pr1 = min(pr0 + PR, npairs);
+            const int pr0 = pb0 + r * PR, pr1 = min(pr0 + PR, pb1);
             char *buf = base + (r & 1) * RB;
             uint32_t *sgn_b = reinterpret_cast<uint32_t *>(buf);
             _Float16 *act_b = reinterpret_cast<_Float16 *>(buf + static_cast<size_t>(PR) * 128 * RT);
             stash(B, sgn_b, act_b, pr0, pr1, 0, 0);
             __syncthreads();  // round r staged; every wave is done with round r - 1's buffer
-            if (r + 1 < nr) issue(B, pr1, min(pr1 + PR, npairs), 0, 0);
+            if (r + 1 < nr) issue(B, pr1, min(pr1 + PR, pb1), 0, 0);
             round_mma<NB, RT, true, BIN>(acc, sgn_b, act_b, KR, pr0, pr1, wave, li, g, ec);
         }
     } else {
-        for (int pr0 = 0; pr0 < npairs; pr0 += PR) {
-            const int pr1 = min(pr0 + PR, npairs);
+        for (int pr0 = pb0; pr0 < pb1; pr0 += PR) {
+            const int pr1 = min(pr0 + PR, pb1);
             const int nitems = (pr1 - pr0) * 8 * RT;
             const int nact = NB * 8 * (pr1 - pr0);
-            if (pr0 > 0) __syncthreads();  // the previous round is done with LDS
+            if (pr0 > pb0) __syncthreads();  // the previous round is done with LDS
             // Every load of a batch (sign items, x and b fragments) is issued
             // before any of it is used; one batch covers the layer shapes of
             // interest, so the workgroup waits for memory once per round.
@@ -559,12 +578,55 @@ __device__ __forceinline__ void stage1_body(int blk, char *base, const uint32_t 
     }
 
     reduce_waves<NB, RT>(acc, red, wave, lane);
+    f32x4 dsum[RT];
+    if (sp.parts > 1) {
+        // publish this part's sums, take a ticket; the last part of the row
+        // block adds all parts in order (the flag overlays the reduction
+        // slots, whose totals are read before it is written; a static LDS
+        // variable would put the dynamic LDS off its 16-byte alignment)
+        int &s_last = *reinterpret_cast<int *>(red);
+        // The sums go out as agent-scope atomic stores (written through to
+        // memory, where the other XCDs' agent-scope loads read them), and
+        // the ticket is taken only after they have completed (vmcnt 0); no
+        // release fence, whose write-back of the whole L2 costs microseconds
+        // per workgroup on this chip.
+        if (wave == 0 && li < NB) {
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+                const f32x4 d = total<NB, RT>(red, t, lane);
+                float *dst = sp.part + (static_cast<size_t>(part) * NB + li) * k_pad + j0 + 16 * t + 4 * g;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) __hip_atomic_store(dst + v, d[v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);  // every counter: this thread's stores have completed
+        __syncthreads();
+        if (threadIdx.x == 0)
+            s_last = __hip_atomic_fetch_add(&sp.tickets[blk], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                     static_cast<unsigned>(sp.parts - 1);
+        __syncthreads();
+        if (!s_last) return;
+        if (wave == 0 && li < NB) {
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+                dsum[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int q = 0; q < sp.parts; ++q) {
+                    const float *src = sp.part + (static_cast<size_t>(q) * NB + li) * k_pad + j0 + 16 * t + 4 * g;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        dsum[t][v] += __hip_atomic_load(src + v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+        }
+        if (threadIdx.x == 0)  // ready for the next call
+            __hip_atomic_store(&sp.tickets[blk], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     // epilogue (wave 0): D[row 4g+v][col li] of row tile t is t[li][j0 + 16t + 4g + v]
     if (wave == 0 && li < NB) {
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
             const int row0 = j0 + 16 * t + 4 * g;
-            const f32x4 d = total<NB, RT>(red, t, lane);
+            const f32x4 d = sp.parts > 1 ? dsum[t] : total<NB, RT>(red, t, lane);
             f16x4 hi, lo;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
@@ -675,7 +737,7 @@ __device__ __forceinline__ void stage2_body(int blk, char *base, const uint32_t 
             stash(B, nullptr, act_all, 0, npairs, 0, act0, false);
         }
         __syncthreads();
-        direct_mma<NB, RT, false, BIN>(acc, At, Wk, i0, npairs, act_all, 64 * npairs, wave, li, g, ec);
+        direct_mma<NB, RT, false, BIN>(acc, At, Wk, i0, 0, npairs, act_all, 64 * npairs, wave, li, g, ec);
     } else if (pipe) {
         // two LDS buffers: round r + 1's loads in flight while round r is multiplied
         const size_t RB = lds_round_bytes<NB, RT>(PR);
@@ -773,7 +835,7 @@ __device__ __forceinline__ void readahead_stage2(const Stage2Readahead &ra, int 
     asm volatile("" ::"v"(acc));  // the loads are the point: keep them
 }
 
-// Stage 1; workgroups past the k / (16 RT) row blocks read ahead for stage 2.
+// Stage 1; workgroups past the (row block, part) ones read ahead for stage 2.
 template <int NB, int RT, bool BIN>
 __global__ __launch_bounds__(kThreads) void mfma_stage1_kernel(const uint32_t *__restrict__ Bt, int Wm,
                                                                const __half *__restrict__ x, int m,
@@ -782,11 +844,12 @@ __global__ __launch_bounds__(kThreads) void mfma_stage1_kernel(const uint32_t *_
                                                                __half *__restrict__ v16, int k_pad, int PR, int pipe,
                                                                const Stage2Readahead ra,
                                                                const float *__restrict__ gamma,
-                                                               float *__restrict__ stats) {
+                                                               float *__restrict__ stats, const S1Split sp) {
     extern __shared__ float lds[];
     const int G1 = k_pad / (16 * RT);
-    if (static_cast<int>(blockIdx.x) >= G1) {
-        const int extra = blockIdx.x - G1;
+    const int GC = G1 * sp.parts;  // (row block, part) workgroups, row block fastest
+    if (static_cast<int>(blockIdx.x) >= GC) {
+        const int extra = blockIdx.x - GC;
         if (BIN && extra >= 8 * ra.per_xcd) {
             // 0/1 layers: one block per batch row forms the row sums of x
             const int r = extra - 8 * ra.per_xcd;
@@ -796,7 +859,8 @@ __global__ __launch_bounds__(kThreads) void mfma_stage1_kernel(const uint32_t *_
         readahead_stage2(ra, blockIdx.x, extra >> 3);
         return;
     }
-    stage1_body<NB, RT, BIN>(blockIdx.x, reinterpret_cast<char *>(lds), Bt, Wm, x, m, b, mid, v16, k_pad, PR, pipe);
+    stage1_body<NB, RT, BIN>(blockIdx.x % G1, reinterpret_cast<char *>(lds), Bt, Wm, x, m, b, mid, v16, k_pad, PR,
+                             pipe, sp, blockIdx.x / G1);
 }
 
 template <int NB, int RT, bool BIN>
@@ -935,13 +999,47 @@ int split_rt(int rows) {
     return 4;
 }
 
+// Stage 1's reduction cut into parts (batch >= 2, signed layers): where m
+// spans at least DBF_DECODE_S1_SPLIT_PAIRS word pairs, 3 or else 2 parts
+// with the smallest rows per workgroup that keep (row block, part)
+// workgroups within the CUs.  At batch 16 the 14336-wide activations (458
+// KiB) do not fit LDS and each workgroup streamed all of them in rounds that
+// wait on memory; a part streams a third of them, on three times the CUs.
+#ifndef DBF_DECODE_S1_SPLIT_PAIRS
+#define DBF_DECODE_S1_SPLIT_PAIRS 160
+#endif
+struct S1Plan {
+    int rt, parts;
+};
+S1Plan s1_plan(int m_pad, int k_pad) {
+    S1Plan p{split_rt(k_pad), 1};
+    if (DBF_DECODE_S1_SPLIT_PAIRS <= 0 || m_pad / 64 < DBF_DECODE_S1_SPLIT_PAIRS) return p;
+    for (int parts = 3; parts >= 2; --parts)
+        for (int rt = 1; rt <= 4; rt *= 2)
+            if ((k_pad / (16 * rt)) * parts <= kCUs) return S1Plan{rt, parts};
+    return p;
+}
+
+}  // namespace
+
+int mfma_stage1_parts(int m_pad, int k_pad, int batch) {
+    if (batch < DBF_DECODE_SP_MIN) return 1;
+    return s1_plan(m_pad, k_pad).parts;
+}
+
+namespace {
+
 template <int NB, int RT, bool BIN>
-int launch_rt(const MfmaDecodeArgs &d, hipStream_t s, int which) {
+int launch_rt(const MfmaDecodeArgs &d, hipStream_t s, int which, int parts = 1) {
     if (which == 1) {
         static const bool once = (allow_lds(mfma_stage1_kernel<NB, RT, BIN>, kLdsBudget), true);
         (void)once;
-        const RoundPlan rp = plan_rounds<NB, RT>(d.m_pad / 64, NB, Acc<NB>::kSP ? NB + 1 : 2 * NB);
+        // the largest part's word pairs (parts take whole groups of kNW pairs)
+        const int npairs = d.m_pad / 64;
+        const int part_pairs = std::min(npairs, ((npairs + kNW - 1) / kNW + parts - 1) / parts * kNW);
+        const RoundPlan rp = plan_rounds<NB, RT>(part_pairs, NB, Acc<NB>::kSP ? NB + 1 : 2 * NB);
         const int G1 = d.k_pad / (16 * RT);
+        const int GC = G1 * parts;
         Stage2Readahead ra{};
         ra.A = reinterpret_cast<const uint4 *>(d.A_dev);
         ra.pairs = d.k_pad / 64;
@@ -954,16 +1052,17 @@ int launch_rt(const MfmaDecodeArgs &d, hipStream_t s, int which) {
         // leave free (a block beyond one per CU would wait for a CU: the
         // kernel's registers allow one block per CU), if there are enough of
         // them to read stage 2's words in a few batches
-        ra.per_xcd = kReadahead ? std::max(0, (kCUs - G1 - stat_blocks) / 8) : 0;  // none when stage 1 fills the CUs
+        ra.per_xcd = kReadahead ? std::max(0, (kCUs - GC - stat_blocks) / 8) : 0;  // none when stage 1 fills the CUs
         if (ra.per_xcd > 0) {
             const size_t items = static_cast<size_t>(d.n_pad) * (d.k_pad / 32) / 4;
             if (items > static_cast<size_t>(kReadaheadMax) * 8 * ra.per_xcd * kThreads) ra.per_xcd = 0;
         }
-        // the read-ahead blocks start on XCD G1 mod 8; 8 * per_xcd of them cover every XCD equally
-        launch_kernel((mfma_stage1_kernel<NB, RT, BIN>), dim3(G1 + 8 * ra.per_xcd + stat_blocks), dim3(kThreads),
+        // the read-ahead blocks start on XCD GC mod 8; 8 * per_xcd of them cover every XCD equally
+        launch_kernel((mfma_stage1_kernel<NB, RT, BIN>), dim3(GC + 8 * ra.per_xcd + stat_blocks), dim3(kThreads),
                       rp.lds, s, d.B_dev, d.m_pad / 32, static_cast<const __half *>(d.x), d.m,
                       static_cast<const __half *>(d.b_dev), static_cast<const __half *>(d.mid_dev),
-                      reinterpret_cast<__half *>(d.v16), d.k_pad, rp.PR, rp.pipe, ra, d.gamma, d.stats_out);
+                      reinterpret_cast<__half *>(d.v16), d.k_pad, rp.PR, rp.pipe, ra, d.gamma, d.stats_out,
+                      S1Split{d.s1_part, d.s1_tickets, parts});
     } else {
         static const bool once = (allow_lds(mfma_stage2_kernel<NB, RT, BIN>, kLdsBudget), true);
         (void)once;
@@ -978,7 +1077,16 @@ int launch_rt(const MfmaDecodeArgs &d, hipStream_t s, int which) {
 
 template <int NB>
 int launch_nb(const MfmaDecodeArgs &d, hipStream_t s, int which) {
-    const int rt = split_rt(which == 1 ? d.k_pad : d.n_pad);
+    int rt = split_rt(which == 1 ? d.k_pad : d.n_pad);
+    if (which == 1 && !d.binary && mfma_stage1_parts(d.m_pad, d.k_pad, NB) > 1) {
+        const S1Plan p = s1_plan(d.m_pad, d.k_pad);
+        if (!d.s1_part || !d.s1_tickets || static_cast<size_t>(p.parts) * NB * d.k_pad > d.s1_part_cap ||
+            d.k_pad / (16 * p.rt) > d.s1_ntickets)
+            return static_cast<int>(hipErrorInvalidValue);  // the handle's workspace is sized for the parts
+        if (p.rt == 1) return launch_rt<NB, 1, false>(d, s, which, p.parts);
+        if (p.rt == 2) return launch_rt<NB, 2, false>(d, s, which, p.parts);
+        return launch_rt<NB, 4, false>(d, s, which, p.parts);
+    }
     if (d.binary) {
         if (rt == 2) return launch_rt<NB, 2, true>(d, s, which);
         if (rt == 4) return launch_rt<NB, 4, true>(d, s, which);

@@ -32,10 +32,12 @@ struct dbf_layer {
     uint32_t *B_dev = nullptr;
     uint16_t *a_dev = nullptr, *mid_dev = nullptr, *b_dev = nullptr;
     // workspace
-    float *tpart = nullptr;   // decode stage-1 partials [nchunk_m][16][k_pad]
+    float *tpart = nullptr;   // decode stage-1 partials [nchunk_m][16][k_pad] (or [parts][16][k_pad])
+    size_t tpart_cap = 0;     // floats
+    int ntickets = 0;
     float *ypart = nullptr;   // decode stage-2 partials [nchunk_k][16][n_pad]
     uint16_t *T = nullptr;    // prefill intermediate    [max_batch][k_pad] fp16
-    unsigned *tickets = nullptr;  // per 64-row tile of A; zero between calls
+    unsigned *tickets = nullptr;  // per 64-row tile of A or 16-row block of B; zero between calls
     uint16_t *v16 = nullptr;      // matrix-core decode intermediate [2][16][k_pad] fp16
     float *split = nullptr;       // split-K parts of the prefill products (small grids)
     size_t split_cap = 0;         // floats
@@ -302,11 +304,17 @@ static dbf_status_t pack_layer(int32_t n, int32_t m, int32_t k, const int8_t *A_
         tpart_elems = std::max(tpart_elems, size_t(lp.nchunk_m) * nb * k_pad);
         ypart_elems = std::max(ypart_elems, size_t(lp.nchunk_k) * nb * n_pad);
     }
+    // stage-1 reduction parts of the matrix-core decode (wide m, batch >= 2)
+    const int s1_parts = dbf::mfma_stage1_parts(m_pad, k_pad, dbf::kDecodeMaxBatch);
+    if (s1_parts > 1) tpart_elems = std::max(tpart_elems, size_t(s1_parts) * dbf::kDecodeMaxBatch * k_pad);
     const size_t tpart_bytes = sizeof(float) * tpart_elems;
     const size_t ypart_bytes = sizeof(float) * ypart_elems;
-    const size_t ticket_bytes = sizeof(unsigned) * size_t(n_pad / 64);
+    const int ntickets = std::max(n_pad / 64, k_pad / 16);
+    const size_t ticket_bytes = sizeof(unsigned) * size_t(ntickets);
     const size_t T_bytes = sizeof(uint16_t) * size_t(max_batch) * k_pad;
     if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->tpart), tpart_bytes);
+    if (st == DBF_OK) h->tpart_cap = tpart_elems;
+    h->ntickets = ntickets;
     if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->ypart), ypart_bytes);
     if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->T), T_bytes);
     if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->tickets), ticket_bytes);
@@ -515,6 +523,10 @@ static dbf_status_t forward_decode_mfma(dbf_layer *h, const void *x, void *y, in
     d.aff_stats = h->bqq_stats;
     d.gamma = h->bqq_gamma;       // (0/1 layers: stage 1 forms the row sums)
     d.stats_out = h->bqq_stats;
+    d.s1_part = h->tpart;
+    d.s1_part_cap = h->tpart_cap;
+    d.s1_tickets = h->tickets;
+    d.s1_ntickets = h->ntickets;
     dbf_status_t st = timed_launch(h, "decode_stage1", stream, [&] { return dbf::launch_mfma_decode(d, stream, 1); });
     if (st != DBF_OK) return st;
     return timed_launch(h, "decode_stage2", stream, [&] { return dbf::launch_mfma_decode(d, stream, 2); });
@@ -647,6 +659,18 @@ extern "C" dbf_status_t dbf_linear_forward_group(const dbf_handle_t *hs, int32_t
             if (st != DBF_OK) return st;
         }
         return DBF_OK;
+    }
+    // layers whose stage 1 is cut into reduction parts run their own
+    // forwards (the grouped kernels do not cut), so each output keeps the
+    // bits of the layer's own forward
+    for (int i = 0; i < count; ++i) {
+        if (dbf::mfma_stage1_parts(hs[i]->m_pad, hs[i]->k_pad, batch) > 1) {
+            for (int j = 0; j < count; ++j) {
+                const dbf_status_t st = forward_decode_mfma(hs[j], x, ys[j], batch, stream);
+                if (st != DBF_OK) return st;
+            }
+            return DBF_OK;
+        }
     }
     dbf::MfmaGroupArgs g{};
     g.count = count;

@@ -201,6 +201,52 @@ def test_prefill_split_k_determinism(gpu):
         H.close()
 
 
+# A reduction wide enough (m spans at least 160 word pairs) that stage 1 of
+# the matrix-core decode at batch >= 2 is cut into parts (3 here) whose sums
+# the last part of each row block adds in order; ragged m.  Batches 2 and 5
+# take the direct form, 9 and 16 the pipelined rounds.
+WIDE_SHAPE = (300, 10300, 600)
+
+
+@pytest.mark.parametrize("batch", [2, 5, 9, 16])
+def test_decode_wide_reduction_parts(gpu, batch):
+    n, m, k = WIDE_SHAPE
+    _say(f"decode wide reduction n={n} m={m} k={k} batch={batch}")
+    X, A, B, a, mid, b = inputs.tiny_case(4300 + batch, n, m, k, batch, signed_scales=True)
+    L = inputs.Layer("w", n, m, k, A, B, a, mid, b, {})
+    y = run(L, X, dbf.DBF_PATH_DECODE)
+    assert_tol(y, O.dense_forward(X, A, B, a, mid, b), f"decode wide b{batch}")
+
+
+def test_decode_wide_reduction_batch_independence(gpu):
+    """The parts do not depend on the batch (2..16): sub-batches give the
+    rows of the full batch bit for bit, repeated calls the same bits, and a
+    grouped forward the layer's own bits."""
+    torch = _torch()
+    n, m, k = WIDE_SHAPE
+    X, A, B, a, mid, b = inputs.tiny_case(4399, n, m, k, 16, signed_scales=True)
+    H = dbf.Layer(A, B, a, mid, b, max_batch=16)
+    H2 = dbf.Layer(A[:100], B, a[:100], mid, b, max_batch=16)
+    try:
+        _say("decode wide reduction batch independence")
+        x = torch.from_numpy(X).cuda()
+        y16 = H.forward(x, path=dbf.DBF_PATH_DECODE).cpu().numpy()
+        assert np.array_equal(y16.view(np.uint16), H.forward(x, path=dbf.DBF_PATH_DECODE).cpu().numpy().view(np.uint16))
+        for bt in (2, 5, 12):
+            yb = H.forward(x[:bt], path=dbf.DBF_PATH_DECODE).cpu().numpy()
+            assert np.array_equal(yb.view(np.uint16), y16[:bt].view(np.uint16)), f"batch {bt}"
+        _say("decode wide reduction grouped")
+        for bt in (1, 9):
+            ys = dbf.forward_group([H, H2], x[:bt])
+            assert np.array_equal(ys[0].cpu().numpy().view(np.uint16),
+                                  H.forward(x[:bt], path=dbf.DBF_PATH_DECODE).cpu().numpy().view(np.uint16))
+            assert np.array_equal(ys[1].cpu().numpy().view(np.uint16),
+                                  H2.forward(x[:bt], path=dbf.DBF_PATH_DECODE).cpu().numpy().view(np.uint16))
+    finally:
+        H.close()
+        H2.close()
+
+
 # Large batches on a shape whose prefill grids are one wave of 128 x 256
 # output tiles plus a small partial one: the first column tiles (at most 256
 # tiles) run whole-K, the remaining columns split-K.  Stage 1: N = k = 4480
