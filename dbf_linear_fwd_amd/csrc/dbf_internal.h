@@ -21,7 +21,6 @@ namespace dbf {
 constexpr int kDecodeMaxBatch = 16;
 // Decode chunking: words of 32 signs handled by one workgroup along a
 // reduction dimension (1024 elements); bounds the LDS copy of the activations.
-constexpr int kChunkWords = 32;
 
 uint32_t reorder_word(uint32_t canonical);
 
@@ -35,11 +34,6 @@ DBF_HD inline size_t tiled_index(int row, int w, int words) {
 constexpr int kLutMaxBatch = 4;
 // Upper bound on the words of one lookup-table chunk (register budget).
 constexpr int kMaxLutChunkWords = 124;
-
-struct DecodePlan {
-    int nchunk_m;   // chunks along m (stage 1)
-    int nchunk_k;   // chunks along k (stage 2)
-};
 
 // Arguments of the decode kernels for one forward.
 struct DecodeArgs {
@@ -116,19 +110,6 @@ int launch_lut_stage1(const DecodeArgs &d, void *stream);
 int launch_lut_stage2(const DecodeArgs &d, void *stream);
 
 // ---- kernel launchers (return hipError_t as int to keep HIP types out of here)
-
-// Stage 1 of the decode path: partial t[c][r][j] = sum over chunk c of
-// B[j][l] * x[r][l] * b[l]  for j < k_pad, r < batch.
-int launch_decode_stage1(const uint32_t *B_dev, const void *x, const void *b_dev, float *tpart,
-                         int batch, int m, int m_pad, int k_pad, int nchunk_m, void *stream);
-
-// Stage 2: v = mid * sum_c tpart[c]; partial y[c][r][i] = sum over chunk c of A[i][j] * v[r][j].
-int launch_decode_stage2(const uint32_t *A_dev, const float *tpart, const void *mid_dev, float *ypart,
-                         int batch, int n_pad, int k_pad, int nchunk_m, int nchunk_k, void *stream);
-
-// Final: y[r][i] = rne16(a[i] * sum_c ypart[c][r][i]) for i < n.
-int launch_decode_final(const float *ypart, const void *a_dev, void *y, int batch, int n, int n_pad,
-                        int nchunk_k, void *stream);
 
 // Events that bracket the next kernel launch when the runtime times kernels
 // (null otherwise).  They are handed to the launch itself, so the elapsed time

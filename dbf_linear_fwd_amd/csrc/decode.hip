@@ -14,10 +14,11 @@
 // of a chunk go to the workspace and are added in a fixed order, so results
 // are deterministic and independent of the other batch rows.
 //
-// Small batches (<= 4 rows) use a lookup table instead of one add per sign:
-// for every group of 4 activations that share a nibble of a sign word, the
-// 16 signed sums of those 4 values are tabulated in LDS, and a lane adds one
-// table entry per nibble of its row's word.  All lanes of a wave read the
+// A launch takes up to 4 batch rows (larger batches run as groups of rows)
+// and uses lookup tables instead of one add per sign: for every group of 4
+// activations that share a nibble of a sign word, the 16 signed sums of
+// those 4 values are tabulated in LDS, and a lane adds one table entry per
+// nibble of its row's word.  All lanes of a wave read the
 // table of the same word at the same time, so a wave's 64 reads touch at most
 // 16 distinct LDS words (broadcast, no bank conflicts).
 //
@@ -249,19 +250,23 @@ __global__ __launch_bounds__(kThreads) void lut_stage2_kernel(const uint32_t *__
     }
     if (wave == 0) {
 #pragma unroll
-        for (int rb = 0; rb < NB; ++rb) ypart[(static_cast<size_t>(c) * NB + rb) * n_pad + i] = acc[rb];
+        for (int rb = 0; rb < NB; ++rb)
+            __hip_atomic_store(&ypart[(static_cast<size_t>(c) * NB + rb) * n_pad + i], acc[rb], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     }
-    // Publish the partial, then take a ticket; the last of the tile's chunks
-    // adds all partials of the tile in chunk order.
-    __threadfence();
+    // Publish the partial (agent-scope atomic stores, written through to
+    // memory, completed before the ticket: no release fence, whose write-back
+    // of the whole L2 costs microseconds per workgroup), then take a ticket;
+    // the last of the tile's chunks adds all partials of the tile in chunk
+    // order with agent-scope loads.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) {
-        const unsigned prev = atomicAdd(&tickets[tile], 1u);
+        const unsigned prev = __hip_atomic_fetch_add(&tickets[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         *s_last = prev == static_cast<unsigned>(nchunk_k - 1);
     }
     __syncthreads();
     if (!*s_last) return;
-    __threadfence();
     if (wave == 0 && i < n) {
         const float sa = __half2float(a[i]);
 #pragma unroll
@@ -274,115 +279,9 @@ __global__ __launch_bounds__(kThreads) void lut_stage2_kernel(const uint32_t *__
             y[static_cast<size_t>(rb) * n + i] = __float2half_rn(s * sa);
         }
     }
-    if (threadIdx.x == 0) tickets[tile] = 0u;  // ready for the next call (kernel end publishes it)
+    if (threadIdx.x == 0) __hip_atomic_store(&tickets[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// ------------------------------------------------------------------ batch 5..16: one add per sign
-
-constexpr int kMaxB = kDecodeMaxBatch;
-constexpr int kChunkElems = kChunkWords * 32;
-
-__global__ __launch_bounds__(64) void decode_stage1_kernel(const uint32_t *__restrict__ Bt,
-                                                           const __half *__restrict__ x,
-                                                           const __half *__restrict__ b,
-                                                           float *__restrict__ tpart, int batch, int m,
-                                                           int Wm, int k_pad) {
-    __shared__ float u[kMaxB * kChunkElems];
-    const int c = blockIdx.y;
-    const int w0 = c * kChunkWords;
-    const int w1 = min(w0 + kChunkWords, Wm);
-    const int ncols = (w1 - w0) * 32;
-    for (int idx = threadIdx.x; idx < batch * ncols; idx += blockDim.x) {
-        const int r = idx / ncols;
-        const int e = idx - r * ncols;
-        const int l = w0 * 32 + e;
-        u[r * kChunkElems + e] =
-            l < m ? __half2float(x[static_cast<size_t>(r) * m + l]) * __half2float(b[l]) : 0.0f;
-    }
-    __syncthreads();
-
-    const int j = blockIdx.x * 64 + threadIdx.x;
-    float acc[kMaxB];
-#pragma unroll
-    for (int r = 0; r < kMaxB; ++r) acc[r] = 0.0f;
-    for (int w = w0; w < w1; ++w) {
-        const uint32_t word = Bt[tiled_index(j, w, Wm)];
-        const int base = (w - w0) * 32;
-        for (int q = 0; q < 32; ++q) {
-            const bool neg = (word >> q) & 1u;
-            const int e = base + element_of_bit(q);
-#pragma unroll
-            for (int r = 0; r < kMaxB; ++r) {
-                if (r < batch) {
-                    const float v = u[r * kChunkElems + e];
-                    acc[r] += neg ? -v : v;
-                }
-            }
-        }
-    }
-#pragma unroll
-    for (int r = 0; r < kMaxB; ++r) {
-        if (r < batch) tpart[(static_cast<size_t>(c) * batch + r) * k_pad + j] = acc[r];
-    }
-}
-
-__global__ __launch_bounds__(64) void decode_stage2_kernel(const uint32_t *__restrict__ At,
-                                                           const float *__restrict__ tpart,
-                                                           const __half *__restrict__ mid,
-                                                           float *__restrict__ ypart, int batch, int Wk,
-                                                           int n_pad, int k_pad, int nchunk_m) {
-    __shared__ float v[kMaxB * kChunkElems];
-    const int c = blockIdx.y;
-    const int w0 = c * kChunkWords;
-    const int w1 = min(w0 + kChunkWords, Wk);
-    const int ncols = (w1 - w0) * 32;
-    for (int idx = threadIdx.x; idx < batch * ncols; idx += blockDim.x) {
-        const int r = idx / ncols;
-        const int e = idx - r * ncols;
-        const int j = w0 * 32 + e;
-        float t = 0.0f;
-        for (int cm = 0; cm < nchunk_m; ++cm) t += tpart[(static_cast<size_t>(cm) * batch + r) * k_pad + j];
-        v[r * kChunkElems + e] = t * __half2float(mid[j]);
-    }
-    __syncthreads();
-
-    const int i = blockIdx.x * 64 + threadIdx.x;
-    float acc[kMaxB];
-#pragma unroll
-    for (int r = 0; r < kMaxB; ++r) acc[r] = 0.0f;
-    for (int w = w0; w < w1; ++w) {
-        const uint32_t word = At[tiled_index(i, w, Wk)];
-        const int base = (w - w0) * 32;
-        for (int q = 0; q < 32; ++q) {
-            const bool neg = (word >> q) & 1u;
-            const int e = base + element_of_bit(q);
-#pragma unroll
-            for (int r = 0; r < kMaxB; ++r) {
-                if (r < batch) {
-                    const float s = v[r * kChunkElems + e];
-                    acc[r] += neg ? -s : s;
-                }
-            }
-        }
-    }
-#pragma unroll
-    for (int r = 0; r < kMaxB; ++r) {
-        if (r < batch) ypart[(static_cast<size_t>(c) * batch + r) * n_pad + i] = acc[r];
-    }
-}
-
-__global__ __launch_bounds__(256) void decode_final_kernel(const float *__restrict__ ypart,
-                                                           const __half *__restrict__ a,
-                                                           __half *__restrict__ y, int batch, int n,
-                                                           int n_pad, int nchunk_k) {
-    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= batch * n) return;
-    const int r = idx / n;
-    const int i = idx - r * n;
-    float s = 0.0f;
-    for (int c = 0; c < nchunk_k; ++c) s += ypart[(static_cast<size_t>(c) * batch + r) * n_pad + i];
-    y[idx] = __float2half_rn(s * __half2float(a[i]));
-}
 
 template <int NB>
 size_t lut_lds_bytes(int CW) {
@@ -435,34 +334,6 @@ int launch_lut_stage2(const DecodeArgs &d, void *stream) {
         case 4: return lut_stage2<4>(d, s);
         default: return static_cast<int>(hipErrorInvalidValue);
     }
-}
-
-int launch_decode_stage1(const uint32_t *B_dev, const void *x, const void *b_dev, float *tpart, int batch,
-                         int m, int m_pad, int k_pad, int nchunk_m, void *stream) {
-    dim3 grid(k_pad / 64, nchunk_m);
-    launch_kernel(decode_stage1_kernel, grid, dim3(64), 0, static_cast<hipStream_t>(stream), B_dev,
-                       static_cast<const __half *>(x), static_cast<const __half *>(b_dev), tpart, batch, m,
-                       m_pad / 32, k_pad);
-    return static_cast<int>(hipGetLastError());
-}
-
-int launch_decode_stage2(const uint32_t *A_dev, const float *tpart, const void *mid_dev, float *ypart,
-                         int batch, int n_pad, int k_pad, int nchunk_m, int nchunk_k, void *stream) {
-    dim3 grid(n_pad / 64, nchunk_k);
-    launch_kernel(decode_stage2_kernel, grid, dim3(64), 0, static_cast<hipStream_t>(stream), A_dev,
-                       tpart, static_cast<const __half *>(mid_dev), ypart, batch, k_pad / 32, n_pad, k_pad,
-                       nchunk_m);
-    return static_cast<int>(hipGetLastError());
-}
-
-int launch_decode_final(const float *ypart, const void *a_dev, void *y, int batch, int n, int n_pad,
-                        int nchunk_k, void *stream) {
-    const int total = batch * n;
-    dim3 grid((total + 255) / 256);
-    launch_kernel(decode_final_kernel, grid, dim3(256), 0, static_cast<hipStream_t>(stream), ypart,
-                       static_cast<const __half *>(a_dev), static_cast<__half *>(y), batch, n, n_pad,
-                       nchunk_k);
-    return static_cast<int>(hipGetLastError());
 }
 
 }  // namespace dbf

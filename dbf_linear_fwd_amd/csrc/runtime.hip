@@ -52,7 +52,6 @@ struct dbf_layer {
     dbf_layer *bwd = nullptr;
     float *t32 = nullptr;     // (X ⊙ b) Bᵀ in fp32          [max_batch][k_pad]
     float *red = nullptr;     // batch-sum partials [ceil(max_batch / 64)][max(n, k_pad, m)]
-    dbf::DecodePlan plan{};   // one-add-per-sign decode kernels (batch 5..16)
     struct LutPlan {
         int cw_m, nchunk_m, cw_k, nchunk_k;
     } lut[dbf::kLutMaxBatch + 1]{};
@@ -272,8 +271,6 @@ static dbf_status_t pack_layer(int32_t n, int32_t m, int32_t k, const int8_t *A_
     h->max_batch = max_batch;
     h->Wk = k_pad / 32;
     h->Wm = m_pad / 32;
-    h->plan.nchunk_m = (h->Wm + dbf::kChunkWords - 1) / dbf::kChunkWords;
-    h->plan.nchunk_k = (h->Wk + dbf::kChunkWords - 1) / dbf::kChunkWords;
 
     dbf_status_t st = DBF_OK;
     if (hipGetDevice(&h->device) != hipSuccess) st = DBF_ERR_HIP;
@@ -294,8 +291,7 @@ static dbf_status_t pack_layer(int32_t n, int32_t m, int32_t k, const int8_t *A_
     if (st == DBF_OK) h->scale_bytes = 2 * size_t(n_pad + k_pad + m_pad);
 
     const int32_t dec_b = max_batch < dbf::kDecodeMaxBatch ? max_batch : dbf::kDecodeMaxBatch;
-    size_t tpart_elems = size_t(h->plan.nchunk_m) * dec_b * k_pad;
-    size_t ypart_elems = size_t(h->plan.nchunk_k) * dec_b * n_pad;
+    size_t tpart_elems = 64, ypart_elems = 64;
     for (int nb = 1; nb <= dbf::kLutMaxBatch && nb <= max_batch; ++nb) {
         auto &lp = h->lut[nb];
         const int maxcw = dbf::lut_max_chunk_words(nb);
@@ -533,20 +529,24 @@ static dbf_status_t forward_decode_mfma(dbf_layer *h, const void *x, void *y, in
 }
 
 static dbf_status_t forward_decode(dbf_layer *h, const void *x, void *y, int32_t batch, hipStream_t stream) {
-    if (batch <= dbf::kLutMaxBatch) {
-        const auto &lp = h->lut[batch];
+    // Lookup-table decode, up to kLutMaxBatch rows per pair of launches;
+    // larger batches run as groups of rows (each row's result is the same
+    // in any group).
+    for (int32_t r0 = 0; r0 < batch; r0 += dbf::kLutMaxBatch) {
+        const int32_t nb = std::min<int32_t>(dbf::kLutMaxBatch, batch - r0);
+        const auto &lp = h->lut[nb];
         dbf::DecodeArgs d{};
         d.A_dev = h->A_dev;
         d.B_dev = h->B_dev;
         d.a_dev = h->a_dev;
         d.mid_dev = h->mid_dev;
         d.b_dev = h->b_dev;
-        d.x = x;
-        d.y = y;
+        d.x = static_cast<const uint16_t *>(x) + static_cast<size_t>(r0) * h->m;
+        d.y = static_cast<uint16_t *>(y) + static_cast<size_t>(r0) * h->n;
         d.tpart = h->tpart;
         d.ypart = h->ypart;
         d.tickets = h->tickets;
-        d.batch = batch;
+        d.batch = nb;
         d.n = h->n;
         d.m = h->m;
         d.n_pad = h->n_pad;
@@ -558,21 +558,10 @@ static dbf_status_t forward_decode(dbf_layer *h, const void *x, void *y, int32_t
         d.nchunk_k = lp.nchunk_k;
         dbf_status_t st = timed_launch(h, "table_stage1", stream, [&] { return dbf::launch_lut_stage1(d, stream); });
         if (st != DBF_OK) return st;
-        return timed_launch(h, "table_stage2", stream, [&] { return dbf::launch_lut_stage2(d, stream); });
+        st = timed_launch(h, "table_stage2", stream, [&] { return dbf::launch_lut_stage2(d, stream); });
+        if (st != DBF_OK) return st;
     }
-    dbf_status_t st = timed_launch(h, "decode_add_stage1", stream, [&] {
-        return dbf::launch_decode_stage1(h->B_dev, x, h->b_dev, h->tpart, batch, h->m, h->m_pad, h->k_pad,
-                                         h->plan.nchunk_m, stream);
-    });
-    if (st != DBF_OK) return st;
-    st = timed_launch(h, "decode_add_stage2", stream, [&] {
-        return dbf::launch_decode_stage2(h->A_dev, h->tpart, h->mid_dev, h->ypart, batch, h->n_pad, h->k_pad,
-                                         h->plan.nchunk_m, h->plan.nchunk_k, stream);
-    });
-    if (st != DBF_OK) return st;
-    return timed_launch(h, "decode_add_final", stream, [&] {
-        return dbf::launch_decode_final(h->ypart, h->a_dev, y, batch, h->n, h->n_pad, h->plan.nchunk_k, stream);
-    });
+    return DBF_OK;
 }
 
 static dbf_status_t forward_prefill(dbf_layer *h, const void *x, void *y, int32_t batch, hipStream_t stream) {
