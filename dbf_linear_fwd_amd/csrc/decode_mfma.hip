@@ -1008,6 +1008,9 @@ int split_rt(int rows) {
 #ifndef DBF_DECODE_S1_SPLIT_PAIRS
 #define DBF_DECODE_S1_SPLIT_PAIRS 160
 #endif
+#ifndef DBF_DECODE_S1_SPLIT_MIN_NB
+#define DBF_DECODE_S1_SPLIT_MIN_NB DBF_DECODE_SP_MIN
+#endif
 struct S1Plan {
     int rt, parts;
 };
@@ -1023,7 +1026,7 @@ S1Plan s1_plan(int m_pad, int k_pad) {
 }  // namespace
 
 int mfma_stage1_parts(int m_pad, int k_pad, int batch) {
-    if (batch < DBF_DECODE_SP_MIN) return 1;
+    if (batch < DBF_DECODE_S1_SPLIT_MIN_NB) return 1;
     return s1_plan(m_pad, k_pad).parts;
 }
 
