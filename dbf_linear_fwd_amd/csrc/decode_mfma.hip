@@ -401,6 +401,13 @@ __device__ __forceinline__ f32x4 total(const float *red, int t, int lane) {
     return dh + dl;
 }
 
+#ifndef DBF_DECODE_S1_SPLIT_PAIRS
+#define DBF_DECODE_S1_SPLIT_PAIRS 160
+#endif
+#ifndef DBF_DECODE_S1_SPLIT_MIN_NB
+#define DBF_DECODE_S1_SPLIT_MIN_NB DBF_DECODE_SP_MIN
+#endif
+
 // Reduction parts of stage 1: part `s` of `parts` takes word pairs
 // [pb0, pb1) (whole groups of kNW pairs, so pair p still belongs to wave
 // p mod kNW) and writes its unscaled sums to part[(s * NB + r) * k_pad + j];
@@ -444,10 +451,12 @@ __device__ __forceinline__ void stage1_body(int blk, char *base, const uint32_t 
         for (int t = 0; t < RT; ++t) acc[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int npairs = Wm >> 1;
-    // this part's word pairs [pb0, pb1)
+    // this part's word pairs [pb0, pb1) (batches below the parts' threshold
+    // never take parts: their code keeps the whole range)
+    constexpr bool kParts = NB >= DBF_DECODE_S1_SPLIT_MIN_NB;
     const int ngroups = (npairs + kNW - 1) / kNW;
-    const int pb0 = min(npairs, part * ngroups / sp.parts * kNW);
-    const int pb1 = min(npairs, (part + 1) * ngroups / sp.parts * kNW);
+    const int pb0 = kParts ? min(npairs, part * ngroups / sp.parts * kNW) : 0;
+    const int pb1 = kParts ? min(npairs, (part + 1) * ngroups / sp.parts * kNW) : npairs;
     const bool xvec = (m & 7) == 0;
     // the loads of one batch: sign items and the x / b fragments of the round
     struct Batch {
@@ -579,7 +588,7 @@ __device__ __forceinline__ void stage1_body(int blk, char *base, const uint32_t 
 
     reduce_waves<NB, RT>(acc, red, wave, lane);
     f32x4 dsum[RT];
-    if (sp.parts > 1) {
+    if (kParts && sp.parts > 1) {
         // publish this part's sums, take a ticket; the last part of the row
         // block adds all parts in order (the flag overlays the reduction
         // slots, whose totals are read before it is written; a static LDS
@@ -626,7 +635,7 @@ __device__ __forceinline__ void stage1_body(int blk, char *base, const uint32_t 
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
             const int row0 = j0 + 16 * t + 4 * g;
-            const f32x4 d = sp.parts > 1 ? dsum[t] : total<NB, RT>(red, t, lane);
+            const f32x4 d = kParts && sp.parts > 1 ? dsum[t] : total<NB, RT>(red, t, lane);
             f16x4 hi, lo;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
@@ -1005,12 +1014,7 @@ int split_rt(int rows) {
 // workgroups within the CUs.  At batch 16 the 14336-wide activations (458
 // KiB) do not fit LDS and each workgroup streamed all of them in rounds that
 // wait on memory; a part streams a third of them, on three times the CUs.
-#ifndef DBF_DECODE_S1_SPLIT_PAIRS
-#define DBF_DECODE_S1_SPLIT_PAIRS 160
-#endif
-#ifndef DBF_DECODE_S1_SPLIT_MIN_NB
-#define DBF_DECODE_S1_SPLIT_MIN_NB DBF_DECODE_SP_MIN
-#endif
+
 struct S1Plan {
     int rt, parts;
 };
