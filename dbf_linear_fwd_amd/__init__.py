@@ -26,7 +26,8 @@ __all__ = [
     "DBF_PATH_AUTO", "DBF_PATH_DECODE", "DBF_PATH_PREFILL", "DBF_PATH_DECODE_TABLE", "EXPORTED_SYMBOLS",
     "DbfError", "lib", "library_path",
     "dbf_pack", "dbf_linear_forward", "dbf_linear_forward_ex", "dbf_free", "dbf_get_info",
-    "dbf_status_string", "dbf_pack_signs", "dbf_layout_signs", "dbf_layout_words",
+    "dbf_status_string", "dbf_pack_signs", "dbf_layout_signs", "dbf_layout_words", "dbf_layout_signs_dec",
+    "dbf_layout_words_dec",
     "dbf_timing_enable", "dbf_timing_read", "Layer", "dbf_linear_forward_group", "forward_group",
     "dbf_pack_ex", "dbf_linear_backward_data", "dbf_linear_backward", "DBF_PACK_BACKWARD", "dbf_bqq_pack",
     "dbf_factorize", "factorize",
@@ -51,8 +52,8 @@ DECODE_MAX_BATCH = 16
 EXPORTED_SYMBOLS = (
     "dbf_pack", "dbf_pack_ex", "dbf_linear_forward", "dbf_linear_forward_ex", "dbf_linear_forward_group",
     "dbf_linear_backward_data", "dbf_linear_backward", "dbf_free", "dbf_get_info", "dbf_status_string",
-    "dbf_pack_signs", "dbf_layout_signs", "dbf_layout_words", "dbf_timing_enable", "dbf_timing_read",
-    "dbf_bqq_pack", "dbf_factorize",
+    "dbf_pack_signs", "dbf_layout_signs", "dbf_layout_words", "dbf_layout_signs_dec", "dbf_layout_words_dec",
+    "dbf_timing_enable", "dbf_timing_read", "dbf_bqq_pack", "dbf_factorize",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -126,6 +127,10 @@ def lib() -> ctypes.CDLL:
     L.dbf_layout_signs.restype = ctypes.c_int
     L.dbf_layout_words.argtypes = [i32, i32]
     L.dbf_layout_words.restype = sz
+    L.dbf_layout_signs_dec.argtypes = [vp, i32, i32, i32, i32, i32, vp]
+    L.dbf_layout_signs_dec.restype = ctypes.c_int
+    L.dbf_layout_words_dec.argtypes = [i32, i32]
+    L.dbf_layout_words_dec.restype = sz
     L.dbf_timing_enable.argtypes = [vp, i32]
     L.dbf_timing_enable.restype = ctypes.c_int
     L.dbf_timing_read.argtypes = [vp, ctypes.POINTER(_KernelTime), i32, ctypes.POINTER(i32)]
@@ -317,6 +322,20 @@ def dbf_layout_signs(packed: np.ndarray) -> np.ndarray:
     return out
 
 
+def dbf_layout_words_dec(rows_pad: int, cols_pad: int) -> int:
+    return int(lib().dbf_layout_words_dec(rows_pad, cols_pad))
+
+
+def dbf_layout_signs_dec(packed: np.ndarray, cols: int, rows_pad: int, cols_pad: int) -> np.ndarray:
+    """The batch-1 decode kernels' copy of packed signs (host only)."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint32)
+    rows, words = packed.shape
+    out = np.zeros(max(dbf_layout_words_dec(rows_pad, cols_pad), 1), dtype=np.uint32)
+    _check(lib().dbf_layout_signs_dec(_ptr(packed), rows, cols, words, rows_pad, cols_pad, _ptr(out)),
+           "dbf_layout_signs_dec")
+    return out
+
+
 def dbf_timing_enable(h: int, enable: bool = True) -> None:
     _check(lib().dbf_timing_enable(h, 1 if enable else 0), "dbf_timing_enable")
 
@@ -379,8 +398,9 @@ class Layer:
         batch = x.shape[0]
         if out is None:
             out = torch.empty((batch, self.n), dtype=torch.float16, device=x.device)
-        elif out.shape != (batch, self.n) or out.dtype != torch.float16 or not out.is_contiguous():
-            raise ValueError("out must be a contiguous float16 tensor of shape (batch, n)")
+        elif (out.shape != (batch, self.n) or out.dtype != torch.float16 or not out.is_contiguous()
+              or not out.is_cuda or out.device != x.device):
+            raise ValueError("out must be a contiguous float16 tensor of shape (batch, n) on x's device")
         stream = torch.cuda.current_stream(x.device).cuda_stream
         dbf_linear_forward_ex(self.handle, x.data_ptr(), out.data_ptr(), batch, path, stream)
         return out

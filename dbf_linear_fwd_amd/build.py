@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdbf.so")
 
-HIP_SOURCES = ["runtime.hip", "decode.hip", "decode_mfma.hip", "prefill.hip", "grad.hip", "bqq.hip", "factor.hip"]
+HIP_SOURCES = ["runtime.hip", "decode.hip", "decode_mfma.hip", "decode_i8.hip", "prefill.hip", "grad.hip", "bqq.hip", "factor.hip"]
 CXX_SOURCES = ["pack.cpp"]
 
 ARCH = "gfx950"

@@ -10,9 +10,11 @@
 #if defined(__HIPCC__)
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
+#include <hip/hip_fp16.h>
 #define DBF_HD __host__ __device__
 #else
 #define DBF_HD
+struct __half;
 #endif
 
 namespace dbf {
@@ -29,6 +31,45 @@ uint32_t reorder_word(uint32_t canonical);
 DBF_HD inline size_t tiled_index(int row, int w, int words) {
     return ((static_cast<size_t>(row >> 6) * (words >> 1) + (w >> 1)) * 64 + (row & 63)) * 2 + (w & 1);
 }
+
+// ---- batch-1 decode on the int8 matrix cores (decode_i8.hip)
+
+DBF_HD inline int round_up_int(int v, int q) { return (v + q - 1) / q * q; }
+
+// Superchunks (512 reduction columns) of the decode layout: the reduction
+// length is padded to a multiple of 128, at most kI8MaxSC superchunks.
+constexpr int kI8MaxSC = 64;
+int i8_superchunks(int K);
+
+// One layer of a decode stage.  Stage 1: rows = k_pad output rows (v),
+// K = m, vec = x (fp16), bsc = b, osc = mid, out = v (fp32).  Stage 2:
+// rows = n, K = k_pad, vec = v (fp32), osc = a, out = y (fp16).
+struct I8Layer {
+    const uint32_t *S = nullptr;   // signs in the dbf_layout_signs_dec layout
+    const void *vec = nullptr;
+    const __half *bsc = nullptr;
+    const __half *osc = nullptr;
+    void *out = nullptr;
+    const float *aff_E = nullptr;      // stage 2 of a 0/1 layer: y += E[row] * stats[0] + stats[1]
+    const float *aff_stats = nullptr;
+    int rows = 0, K = 0;
+    int SC = 0, wlast = 0;             // superchunks; words per lane of the last one (1..4)
+    int ntiles = 0;                    // 16-row tiles
+    int wg0 = 0, nwg = 0;              // set by launch_decode_i8
+};
+struct I8Args {
+    I8Layer L[8];
+    int count = 0;
+    // stage 1 of a 0/1 layer: one more workgroup forms the row sums of x
+    // (stats[0] = Σ x, stats[1] = Σ gamma x); stat_wg >= 0 asks for it
+    const __half *stat_x = nullptr;
+    int stat_m = 0;
+    const float *gamma = nullptr;
+    float *stats = nullptr;
+    int stat_wg = -1;
+};
+// stage = 1 or 2; bin: 0/1 matrices (Z instead of U - 2 Z, times 2).
+int launch_decode_i8(I8Args &a, int stage, bool bin, void *stream);
 
 // Largest batch served by the lookup-table decode kernels.
 constexpr int kLutMaxBatch = 4;

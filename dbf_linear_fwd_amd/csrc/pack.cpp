@@ -78,3 +78,49 @@ extern "C" dbf_status_t dbf_layout_signs(const uint32_t *in, int32_t rows, int32
     }
     return DBF_OK;
 }
+
+// Layout of the batch-1 decode kernels (int8 matrix cores).  Rows in tiles
+// of 16; the reduction dimension, padded to cols_pad (a multiple of 128), in
+// superchunks of 512 columns (the last one may hold 128, 256 or 384).  In
+// superchunk s of tile T, lane l = r + 16 g holds W_s words (W_s = 4 except
+// in a short last superchunk), word i at
+//     T * cols_pad / 2 + 256 s + W_s l + i,
+// and bit 8 b + j of that word is the sign bit of column
+// 512 s + 128 i + 16 j + 4 g + b of row 16 T + r (j < 8, b < 4).  AND-ing a
+// word with 0x01010101 << j then gives the four int8 operand values of
+// columns 16 j + 4 g + b, b < 4, of each of its 128-column blocks.
+extern "C" size_t dbf_layout_words_dec(int32_t rows_pad, int32_t cols_pad) {
+    if (rows_pad < 16 || cols_pad < 128 || (rows_pad % 16) || (cols_pad % 128)) return 0;
+    return static_cast<size_t>(rows_pad / 16) * (cols_pad / 2) + 4;  // + 4: room for a full-width read of the tail
+}
+
+extern "C" dbf_status_t dbf_layout_signs_dec(const uint32_t *in, int32_t rows, int32_t cols, int32_t words,
+                                             int32_t rows_pad, int32_t cols_pad, uint32_t *out) {
+    if (!in || !out || rows < 1 || cols < 1 || words < (static_cast<int64_t>(cols) + 31) / 32) return DBF_ERR_INVALID_ARG;
+    if (rows_pad < rows || cols_pad < cols || (rows_pad % 16) || (cols_pad % 128)) return DBF_ERR_INVALID_ARG;
+    const int64_t tiles = rows_pad / 16;
+    const int64_t tile_words = cols_pad / 2;
+    const int64_t nsc = (cols_pad + 511) / 512;
+    const int64_t wlast = (cols_pad - 512 * (nsc - 1)) / 128;
+    std::memset(out, 0, sizeof(uint32_t) * dbf_layout_words_dec(rows_pad, cols_pad));
+    for (int64_t t = 0; t < tiles; ++t) {
+        for (int64_t s = 0; s < nsc; ++s) {
+            const int64_t W = s + 1 < nsc ? 4 : wlast;
+            for (int64_t l = 0; l < 64; ++l) {
+                const int64_t r = l & 15, g = l >> 4, row = 16 * t + r;
+                if (row >= rows) continue;
+                const uint32_t *src = in + row * static_cast<int64_t>(words);
+                for (int64_t i = 0; i < W; ++i) {
+                    uint32_t word = 0;
+                    for (int64_t j = 0; j < 8; ++j)
+                        for (int64_t b = 0; b < 4; ++b) {
+                            const int64_t col = 512 * s + 128 * i + 16 * j + 4 * g + b;
+                            if (col < cols && ((src[col >> 5] >> (col & 31)) & 1u)) word |= 1u << (8 * b + j);
+                        }
+                    out[t * tile_words + 256 * s + W * l + i] = word;
+                }
+            }
+        }
+    }
+    return DBF_OK;
+}

@@ -39,6 +39,13 @@ struct dbf_layer {
     uint16_t *T = nullptr;    // prefill intermediate    [max_batch][k_pad] fp16
     unsigned *tickets = nullptr;  // per 64-row tile of A or 16-row block of B; zero between calls
     uint16_t *v16 = nullptr;      // matrix-core decode intermediate [2][16][k_pad] fp16
+    // batch-1 decode (int8 matrix cores): A and B in the dbf_layout_signs_dec
+    // layout (A: round_up(n, 16) rows along k_pad; B: k_pad rows along m) and
+    // the fp32 intermediate v [k_pad]
+    uint32_t *A_i8 = nullptr, *B_i8 = nullptr;
+    float *v32 = nullptr;
+    int32_t A_i8_rows = 0;
+    bool i8_ok = false;           // m and k_pad within the batch-1 kernels' reduction limit
     float *split = nullptr;       // split-K parts of the prefill products (small grids)
     size_t split_cap = 0;         // floats
     // BQQ-form layer (dbf_bqq_pack): A, B hold 0/1 matrices, and the output
@@ -104,6 +111,9 @@ void release(dbf_layer *h) {
     (void)hipFree(h->T);
     (void)hipFree(h->tickets);
     (void)hipFree(h->v16);
+    (void)hipFree(h->A_i8);
+    (void)hipFree(h->B_i8);
+    (void)hipFree(h->v32);
     (void)hipFree(h->split);
     (void)hipFree(h->bqq_E);
     (void)hipFree(h->bqq_gamma);
@@ -137,19 +147,26 @@ void choose_chunks(int tiles, int words, int max_cw, int &cw, int &nchunk) {
     nchunk = (words + cw - 1) / cw;
 }
 
-// Pack a +/-1 matrix (rows x cols) along cols and tile it for the device.
+// Pack a +/-1 matrix (rows x cols) along cols and tile it for the device:
+// `tiled` in the dbf_layout_signs layout and, when dec_rows > 0, `dec` in the
+// dbf_layout_signs_dec layout (dec_rows x dec_cols, padded sizes).
 dbf_status_t pack_tiled(const int8_t *S, int32_t rows, int32_t cols, int32_t words,
-                        std::vector<uint32_t> &tiled) {
+                        std::vector<uint32_t> &tiled, int32_t dec_rows, int32_t dec_cols,
+                        std::vector<uint32_t> &dec) {
     std::vector<uint32_t> canon;
     try {
         canon.assign(static_cast<size_t>(rows) * words, 0u);
         tiled.assign(dbf_layout_words(rows, words), 0u);
+        if (dec_rows > 0) dec.assign(dbf_layout_words_dec(dec_rows, dec_cols), 0u);
+        else dec.clear();
     } catch (const std::bad_alloc &) {
         return DBF_ERR_OOM;
     }
     dbf_status_t st = dbf_pack_signs(S, rows, cols, canon.data(), words);
     if (st != DBF_OK) return st;
-    return dbf_layout_signs(canon.data(), rows, words, tiled.data());
+    st = dbf_layout_signs(canon.data(), rows, words, tiled.data());
+    if (st != DBF_OK || dec_rows <= 0) return st;
+    return dbf_layout_signs_dec(canon.data(), rows, cols, words, dec_rows, dec_cols, dec.data());
 }
 
 dbf_status_t upload(void *dst, const void *src, size_t bytes) {
@@ -275,16 +292,28 @@ static dbf_status_t pack_layer(int32_t n, int32_t m, int32_t k, const int8_t *A_
     dbf_status_t st = DBF_OK;
     if (hipGetDevice(&h->device) != hipSuccess) st = DBF_ERR_HIP;
 
-    std::vector<uint32_t> tiled;
-    if (st == DBF_OK) st = pack_tiled(A_signs, n, k, h->Wk, tiled);
+    // batch-1 decode layouts: reduction lengths (m, k_pad) padded to 128,
+    // within the kernels' limit of kI8MaxSC superchunks of 512
+    const int32_t m128 = dbf::round_up_int(m, 128), k128 = dbf::round_up_int(k_pad, 128);
+    h->i8_ok = m128 <= 512 * dbf::kI8MaxSC && k128 <= 512 * dbf::kI8MaxSC;
+    h->A_i8_rows = dbf::round_up_int(n, 16);
+    std::vector<uint32_t> tiled, dec;
+    if (st == DBF_OK) st = pack_tiled(A_signs, n, k, h->Wk, tiled, h->i8_ok ? h->A_i8_rows : 0, k128, dec);
     if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->A_dev), tiled.size() * 4);
     if (st == DBF_OK) st = upload(h->A_dev, tiled.data(), tiled.size() * 4);
     if (st == DBF_OK) h->packed_bytes += tiled.size() * 4;
-    if (st == DBF_OK) st = pack_tiled(B_signs, k, m, h->Wm, tiled);
+    if (st == DBF_OK && h->i8_ok) st = dev_alloc(reinterpret_cast<void **>(&h->A_i8), dec.size() * 4);
+    if (st == DBF_OK && h->i8_ok) st = upload(h->A_i8, dec.data(), dec.size() * 4);
+    if (st == DBF_OK) h->packed_bytes += dec.size() * 4;
+    if (st == DBF_OK) st = pack_tiled(B_signs, k, m, h->Wm, tiled, h->i8_ok ? k_pad : 0, m128, dec);
     if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->B_dev), tiled.size() * 4);
     if (st == DBF_OK) st = upload(h->B_dev, tiled.data(), tiled.size() * 4);
     if (st == DBF_OK) h->packed_bytes += tiled.size() * 4;
+    if (st == DBF_OK && h->i8_ok) st = dev_alloc(reinterpret_cast<void **>(&h->B_i8), dec.size() * 4);
+    if (st == DBF_OK && h->i8_ok) st = upload(h->B_i8, dec.data(), dec.size() * 4);
+    if (st == DBF_OK) h->packed_bytes += dec.size() * 4;
     std::vector<uint32_t>().swap(tiled);
+    std::vector<uint32_t>().swap(dec);
     if (st == DBF_OK) st = upload_scales(&h->a_dev, a, n, n_pad);
     if (st == DBF_OK) st = upload_scales(&h->mid_dev, mid, k, k_pad);
     if (st == DBF_OK) st = upload_scales(&h->b_dev, b, m, m_pad);
@@ -318,6 +347,8 @@ static dbf_status_t pack_layer(int32_t n, int32_t m, int32_t k, const int8_t *A_
     if (st == DBF_OK && hipDeviceSynchronize() != hipSuccess) st = DBF_ERR_HIP;
     const size_t v16_bytes = sizeof(uint16_t) * 2 * size_t(dec_b) * k_pad;
     if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->v16), v16_bytes);
+    const size_t v32_bytes = sizeof(float) * size_t(k_pad);
+    if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->v32), v32_bytes);
     // split-K parts: the most that either prefill product takes at any batch
     // <= max_batch (the part count depends on the batch through its 128-row
     // tiles only, so the largest batch of each tile count is the worst case)
@@ -332,7 +363,7 @@ static dbf_status_t pack_layer(int32_t n, int32_t m, int32_t k, const int8_t *A_
     if (st == DBF_OK) h->split_cap = split_elems;
     if (st == DBF_OK)
         h->workspace_bytes =
-            tpart_bytes + ypart_bytes + T_bytes + ticket_bytes + v16_bytes + sizeof(float) * split_elems;
+            tpart_bytes + ypart_bytes + T_bytes + ticket_bytes + v16_bytes + v32_bytes + sizeof(float) * split_elems;
 
     if (st != DBF_OK) {
         release(h);
@@ -497,8 +528,57 @@ extern "C" dbf_status_t dbf_get_info(dbf_handle_t h, dbf_info_t *info) {
     return DBF_OK;
 }
 
+// The stage descriptions of one layer for the batch-1 decode kernels.
+static void i8_stages(const dbf_layer *h, const void *x, void *y, dbf::I8Layer &s1, dbf::I8Layer &s2) {
+    const int m128 = dbf::round_up_int(h->m, 128), k128 = dbf::round_up_int(h->k_pad, 128);
+    s1 = dbf::I8Layer{};
+    s1.S = h->B_i8;
+    s1.vec = x;
+    s1.bsc = reinterpret_cast<const __half *>(h->b_dev);
+    s1.osc = reinterpret_cast<const __half *>(h->mid_dev);
+    s1.out = h->v32;
+    s1.rows = h->k_pad;
+    s1.K = h->m;
+    s1.SC = dbf::i8_superchunks(h->m);
+    s1.wlast = (m128 - 512 * (s1.SC - 1)) / 128;
+    s1.ntiles = h->k_pad / 16;
+    s2 = dbf::I8Layer{};
+    s2.S = h->A_i8;
+    s2.vec = h->v32;
+    s2.osc = reinterpret_cast<const __half *>(h->a_dev);
+    s2.out = y;
+    s2.rows = h->n;
+    s2.K = h->k_pad;
+    s2.SC = dbf::i8_superchunks(h->k_pad);
+    s2.wlast = (k128 - 512 * (s2.SC - 1)) / 128;
+    s2.ntiles = h->A_i8_rows / 16;
+    if (h->binary) {
+        s2.aff_E = h->bqq_E;
+        s2.aff_stats = h->bqq_stats;
+    }
+}
+
+// Batch 1: two launches of the int8 matrix-core kernels (decode_i8.hip).
+static dbf_status_t forward_decode_i8(dbf_layer *h, const void *x, void *y, hipStream_t stream) {
+    dbf::I8Args a1{}, a2{};
+    a1.count = a2.count = 1;
+    i8_stages(h, x, y, a1.L[0], a2.L[0]);
+    if (h->binary) {
+        a1.stat_x = static_cast<const __half *>(x);
+        a1.stat_m = h->m;
+        a1.gamma = h->bqq_gamma;
+        a1.stats = h->bqq_stats;
+        a1.stat_wg = 0;
+    }
+    dbf_status_t st =
+        timed_launch(h, "decode_stage1", stream, [&] { return dbf::launch_decode_i8(a1, 1, h->binary, stream); });
+    if (st != DBF_OK) return st;
+    return timed_launch(h, "decode_stage2", stream, [&] { return dbf::launch_decode_i8(a2, 2, h->binary, stream); });
+}
+
 static dbf_status_t forward_decode_mfma(dbf_layer *h, const void *x, void *y, int32_t batch,
                                         hipStream_t stream) {
+    if (batch == 1 && h->i8_ok) return forward_decode_i8(h, x, y, stream);
     dbf::MfmaDecodeArgs d{};
     d.A_dev = h->A_dev;
     d.B_dev = h->B_dev;
@@ -648,6 +728,21 @@ extern "C" dbf_status_t dbf_linear_forward_group(const dbf_handle_t *hs, int32_t
             if (st != DBF_OK) return st;
         }
         return DBF_OK;
+    }
+    if (batch == 1) {
+        bool ok = true;
+        for (int i = 0; i < count; ++i) ok = ok && hs[i]->i8_ok;
+        if (ok) {
+            dbf::I8Args a1{}, a2{};
+            a1.count = a2.count = count;
+            for (int i = 0; i < count; ++i) i8_stages(hs[i], x, ys[i], a1.L[i], a2.L[i]);
+            dbf_layer *t = hs[0];  // kernel timing follows the first handle
+            dbf_status_t st = timed_launch(t, "decode_group_stage1", stream,
+                                           [&] { return dbf::launch_decode_i8(a1, 1, false, stream); });
+            if (st != DBF_OK) return st;
+            return timed_launch(t, "decode_group_stage2", stream,
+                                [&] { return dbf::launch_decode_i8(a2, 2, false, stream); });
+        }
     }
     // layers whose stage 1 is cut into reduction parts run their own
     // forwards (the grouped kernels do not cut), so each output keeps the

@@ -307,6 +307,29 @@ dbf_status_t dbf_layout_signs(const uint32_t *in, int32_t rows, int32_t words, u
 size_t dbf_layout_words(int32_t rows, int32_t words);
 
 /*
+ * dbf_layout_signs_dec -- host-only: the copy of packed signs that the
+ * batch-1 decode kernels read (int8 matrix cores).
+ *   in         host uint32, rows x words row-major, in the dbf_pack_signs format
+ *              (words >= ceil(cols / 32)).
+ *   rows, cols the matrix (>= 1); rows_pad >= rows, a multiple of 16;
+ *              cols_pad >= cols, a multiple of 128.
+ *   out        host uint32 of dbf_layout_words_dec(rows_pad, cols_pad) entries,
+ *              fully written (padding rows and columns hold 0 bits).
+ * Layout: rows in tiles of 16, columns in superchunks of 512 (the last one
+ * may hold 128, 256 or 384).  In superchunk s of tile T, lane l = r + 16 g
+ * (r < 16, g < 4) owns W words (W = 4, or (cols_pad - 512 s) / 128 in a short
+ * last superchunk); its word i is out[T * cols_pad / 2 + 256 s + W l + i], and
+ * bit 8 b + j of that word (j < 8, b < 4) is the sign bit of column
+ * 512 s + 128 i + 16 j + 4 g + b of row 16 T + r.  A word AND 0x01010101 << j
+ * then holds four int8 values 0 or 2^j, the operand of an int8 matrix-core
+ * product over those four columns.  The entry count includes 4 words of
+ * padding after the last tile.  Needs no GPU.
+ */
+dbf_status_t dbf_layout_signs_dec(const uint32_t *in, int32_t rows, int32_t cols, int32_t words,
+                                  int32_t rows_pad, int32_t cols_pad, uint32_t *out);
+size_t dbf_layout_words_dec(int32_t rows_pad, int32_t cols_pad);
+
+/*
  * Kernel timing (measurement support).  When enabled on a handle, every
  * kernel the handle launches carries a pair of HIP events on the launch itself
  * (hipExtLaunchKernel), so their elapsed time is that kernel's execution on

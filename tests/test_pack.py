@@ -115,3 +115,48 @@ def test_device_layout_pair_positions():
 def test_layout_rejects_odd_words():
     with pytest.raises(dbf.DbfError):
         dbf.dbf_layout_signs(np.zeros((2, 3), np.uint32))
+
+
+# --------------------------------------------------------------------------- batch-1 decode layout
+
+def layout_dec_reference(S: np.ndarray, rows_pad: int, cols_pad: int) -> np.ndarray:
+    """Independent construction from the statement in include/dbf.h: word i of
+    lane l = r + 16 g in superchunk s of tile T sits at
+    T * cols_pad / 2 + 256 s + W l + i, and its bit 8 b + j is the sign bit
+    (1 for -1) of column 512 s + 128 i + 16 j + 4 g + b of row 16 T + r."""
+    rows, cols = S.shape
+    neg = np.zeros((rows_pad, cols_pad), dtype=np.uint32)
+    neg[:rows, :cols] = (S == -1)
+    out = np.zeros(rows_pad // 16 * cols_pad // 2 + 4, dtype=np.uint32)
+    nsc = -(-cols_pad // 512)
+    for T in range(rows_pad // 16):
+        for s in range(nsc):
+            W = 4 if s + 1 < nsc else (cols_pad - 512 * s) // 128
+            for l in range(64):
+                r, g = l % 16, l // 16
+                for i in range(W):
+                    word = 0
+                    for j in range(8):
+                        for b in range(4):
+                            word |= int(neg[16 * T + r, 512 * s + 128 * i + 16 * j + 4 * g + b]) << (8 * b + j)
+                    out[T * cols_pad // 2 + 256 * s + W * l + i] = word
+    return out
+
+
+@pytest.mark.parametrize("rows,cols,rows_pad,cols_pad", [
+    (1, 1, 16, 128), (16, 128, 16, 128), (17, 300, 32, 384), (5, 512, 16, 512), (33, 640, 48, 640),
+    (20, 1408, 32, 1408), (16, 1000, 16, 1024), (3, 700, 64, 896)])
+def test_decode_layout_matches_statement(rows, cols, rows_pad, cols_pad):
+    rng = np.random.default_rng(rows * 7 + cols)
+    S = (1 - 2 * rng.integers(0, 2, size=(rows, cols))).astype(np.int8)
+    got = dbf.dbf_layout_signs_dec(dbf.dbf_pack_signs(S), cols, rows_pad, cols_pad)
+    assert got.size == dbf.dbf_layout_words_dec(rows_pad, cols_pad) == rows_pad // 16 * cols_pad // 2 + 4
+    assert np.array_equal(got, layout_dec_reference(S, rows_pad, cols_pad))
+
+
+def test_decode_layout_bad_arguments():
+    P = dbf.dbf_pack_signs(np.ones((4, 40), np.int8))
+    for cols, rp, cp in ((40, 8, 128), (40, 16, 100), (200, 16, 128), (40, 2, 128)):
+        with pytest.raises(dbf.DbfError):
+            dbf.dbf_layout_signs_dec(P, cols, rp, cp)
+    assert dbf.dbf_layout_words_dec(8, 128) == 0 and dbf.dbf_layout_words_dec(16, 64) == 0
