@@ -1,24 +1,31 @@
 """Benchmark of the DBF linear forward on one MI355X.
 
-Workload (default): the 4096x4096 projection at about 1 bit per weight
-(n = m = 4096, k = 2048), signs uniform +/-1, a, b ~ |N(0,1)|*0.02,
-mid ~ |N(0,1)|, x ~ N(0,1) in fp16, batch 1.  One step is one full forward
-(input scaling, both signed sums, middle and output scaling) of one layer.
-The step rotates over R distinct copies of the layer's packed weights,
+Headline workload: a Llama-3-8B-shaped decoder block of seven DBF linears
+(q 4096x4096, k and v 1024x4096, o 4096x4096, gate and up 14336x4096, down
+4096x14336) with a per-layer middle dimension drawn for 1.0-2.3 bits per
+weight, signs uniform +/-1, a, b ~ |N(0,1)|*0.02, mid ~ |N(0,1)|, x ~ N(0,1)
+in fp16, batch 1.  One step is one forward of the whole block in its
+dependency order on one stream: the layers that read the same input run as
+one grouped forward (q, k, v; gate, up), the groups one after another.  The
+steps rotate over R distinct copies of the block's packed weights,
 R * bytes >= 512 MB, so that the 256 MB Infinity Cache cannot hold them and
-every step streams its weights from HBM.  x is resident in HBM before the
-timed region starts.
+every step streams its weights from HBM.  The inputs are resident in HBM
+before the timed region starts.
 
-Metric: packed-weight GB/s = (n*k + k*m)/8 + 2*(n + k + m) bytes per step,
-divided by the wall time of the timed steps (events around K steps, after W
-warm-up steps).  A secondary measurement covers the batch-2048 half of the
-metric (TFLOP/s-equivalent = 2*batch*k*(n+m) per forward) on the 4096x4096
-projection at about 2 bits per weight (k = 4096).
+Metric: packed-weight GB/s = the block's (n*k + k*m)/8 + 2*(n + k + m) bytes
+per step, summed over its layers, times the steps, divided by the wall time
+of exactly --steps steps (one replay of a captured HIP graph of those steps,
+after --warmup untimed steps and one untimed replay that uploads the graph).
+Before any timing the outputs of the timed handles are checked against the
+fp64 oracle (every output of every layer, first and last copy); on a
+mismatch the bench prints no number and exits with status 1.
 
-Also reported: the roofline of the dominant kernel, from per-launch HIP
-events recorded by the library on the launch stream over a second pass of
-the same steps, and the CPU oracle (fp64, dense reconstruction) timed on the
-host on a bounded sample of the same workload.
+Secondary measurements in the same line: the batch-2048 half of the metric
+(TFLOP/s-equivalent = 2*batch*k*(n+m) per forward) on the MLP up and down
+projections (14336x4096 and 4096x14336, k = 4800), also parity-checked
+first; the roofline of the dominant decode kernel (per-launch HIP events on
+the launch stream); the CPU oracle timed on the host on a bounded sample of
+the same workload; gradients, the BQQ-form layer and the factorization.
 """
 
 from __future__ import annotations
@@ -42,8 +49,8 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix-core peak
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=4860)
-    p.add_argument("--warmup", type=int, default=486)
+    p.add_argument("--steps", type=int, default=240, help="timed decoder-block forwards (exactly)")
+    p.add_argument("--warmup", type=int, default=48)
     p.add_argument("--rotate-mb", type=int, default=512)
     p.add_argument("--mode", choices=("graph", "eager"), default="graph",
                    help="graph: the timed steps replay a captured HIP graph of forwards")
@@ -52,27 +59,19 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--copy-probe-mb", type=int, default=0,
                    help="only run a plain device copy of this size (counter scaling) and exit")
-    p.add_argument("--no-block", action="store_true", help="skip the decoder-block measurement")
     p.add_argument("--no-backward", action="store_true", help="skip the gradient measurement")
     p.add_argument("--all-configs", action="store_true",
                    help="instead of the headline line: one JSON line per workload layer and batch "
                         "(decode at batch 1 and 16, prefill at batch 2048)")
     p.add_argument("--no-bqq", action="store_true", help="skip the BQQ-form layer measurement")
     p.add_argument("--no-factorize", action="store_true", help="skip the factorization measurement")
-    p.add_argument("--no-context", action="store_true", help="skip the fp16-matvec and device-copy context")
+    p.add_argument("--no-context", action="store_true", help="skip the device-copy context")
     p.add_argument("--factor-cpu", action="store_true",
                    help="also time the factorization oracle (one outer x one inner iteration) on the host")
-    p.add_argument("--only", choices=("decode", "prefill", "block", "backward", "bqq", "factorize", "context"),
+    p.add_argument("--only", choices=("block", "layer", "prefill", "backward", "bqq", "factorize", "context"),
                    default=None,
                    help="run one leg only (for profiling)")
-    p.add_argument("--decode-path", choices=("mfma", "table"), default="mfma",
-                   help="decode kernels: matrix cores (default) or vector-ALU lookup tables")
     return p.parse_args()
-
-
-def layer_copies(layer, count):
-    import dbf_linear_fwd_amd as dbf
-    return [dbf.Layer(layer.A, layer.B, layer.a, layer.mid, layer.b, max_batch=max(layer.X)) for _ in range(count)]
 
 
 def time_steps(fwd, steps, warmup, mode):
@@ -133,15 +132,6 @@ def kernel_times(layers, fwd, steps):
     return {k: {"launches": v[0], "avg_us": 1e3 * v[1] / max(v[0], 1)} for k, v in tot.items()}
 
 
-def decode_kernel_bytes(layer, batch):
-    """Algorithmic bytes each decode kernel must move (signs + scales + activations)."""
-    n, m, k = layer.n, layer.m, layer.k
-    return {
-        "decode_stage1": k * m // 8 + 2 * m + 2 * batch * m,
-        "decode_stage2": n * k // 8 + 2 * k + 2 * n + 2 * batch * n,
-    }
-
-
 def recorded_traffic(kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     record (FETCH_SIZE and WRITE_SIZE scaled by a plain copy's reading), or
@@ -165,107 +155,6 @@ def recorded_traffic(kernel):
 def prefill_kernel_flops(layer, batch):
     n, m, k = layer.n, layer.m, layer.k
     return {"prefill_gemm1": 2 * batch * k * m, "prefill_gemm2": 2 * batch * k * n}
-
-
-def cpu_baseline(layer, seconds):
-    """The fp64 oracle (dense reconstruction + X W^T, one batch-1 forward per
-    call) on the host, repeated for about `seconds`; GB/s of packed weights.
-    Also its two parts on their own (the W reconstruction, 2nmk flops, and
-    the product X W^T with W built, 2nm flops per batch row) and one forward
-    on a single core."""
-    from oracle import dbf_oracle as O
-    try:
-        from threadpoolctl import threadpool_info, threadpool_limits
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    except Exception:
-        threadpool_limits = None
-        threads = os.cpu_count() or 1
-    X = layer.X[1]
-    calls = 0
-    t0 = time.perf_counter()
-    while True:
-        O.dense_forward(X, layer.A, layer.B, layer.a, layer.mid, layer.b)
-        calls += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    gbs = (layer.sign_bytes + layer.scale_bytes) * calls / el / 1e9
-    t1 = time.perf_counter()
-    W = O.dense_weight(layer.A, layer.B, layer.a, layer.mid, layer.b)
-    w_s = time.perf_counter() - t1
-    X64 = X.astype(np.float64)
-    xw = []
-    for _ in range(21):
-        t2 = time.perf_counter()
-        X64 @ W.T
-        xw.append(time.perf_counter() - t2)
-    del W
-    one = None
-    if threadpool_limits is not None:
-        with threadpool_limits(limits=1):
-            t3 = time.perf_counter()
-            O.dense_forward(X, layer.A, layer.B, layer.a, layer.mid, layer.b)
-            one = time.perf_counter() - t3
-    return {"value": gbs, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{calls} batch-1 forwards of the 4096x4096 k=2048 layer through the fp64 dense oracle "
-                      f"(W rebuilt each call) in {el:.1f} s",
-            "w_rebuild_s": round(w_s, 3), "xwt_median_ms": round(1e3 * float(np.median(xw)), 3),
-            "one_core_forward_s": None if one is None else round(one, 3),
-            "host_cpu_count": os.cpu_count()}
-
-
-def block_leg(args):
-    """The seven linears of a Llama-3-8B-shaped decoder block (q, k, v, o,
-    gate, up, down; per-layer k) at batch 1, one after another on one stream,
-    over enough copies of the block to stream from HBM: each layer on its own,
-    and with the layers that share an input (q, k, v; gate, up) grouped into
-    one pair of launches."""
-    import torch
-
-    import dbf_linear_fwd_amd as dbf
-    from tests import inputs
-
-    layers = inputs.config(5).layers
-    by = {L.name: L for L in layers}
-    block_bytes = sum(L.sign_bytes + L.scale_bytes for L in layers)
-    R = max(1, -(-args.rotate_mb * (1 << 20) // block_bytes))
-    print(f"[bench] block: 7 layers, {block_bytes / 2**20:.1f} MiB per block, {R} copies", file=sys.stderr, flush=True)
-    copies = [{L.name: dbf.Layer(L.A, L.B, L.a, L.mid, L.b, max_batch=1) for L in layers} for _ in range(R)]
-    xs = {L.name: torch.from_numpy(L.X[1]).cuda() for L in layers}
-    ys = {L.name: torch.empty((1, L.n), dtype=torch.float16, device="cuda") for L in layers}
-    order = ["q", "k", "v", "o", "gate", "up", "down"]
-    groups = [["q", "k", "v"], ["o"], ["gate", "up"], ["down"]]
-
-    def per_layer(i):
-        c = copies[i % R]
-        for name in order:
-            c[name].forward(xs[name], out=ys[name])
-    per_layer.period = R
-
-    def grouped(i):
-        c = copies[i % R]
-        for gr in groups:
-            if len(gr) == 1:
-                c[gr[0]].forward(xs[gr[0]], out=ys[gr[0]])
-            else:
-                dbf.forward_group([c[name] for name in gr], xs[gr[0]], [ys[name] for name in gr])
-    grouped.period = R
-
-    steps = max(R, min(args.steps // 7, 20 * R))
-    res = {"workload": "Llama-3-8B-shaped decoder block of 7 DBF linears (q 4096x4096, k/v 1024x4096, o 4096x4096, "
-                       "gate/up 14336x4096, down 4096x14336), k per layer from 1.0-2.3 bits/weight, batch 1",
-           "block_bytes": block_bytes, "copies": R}
-    for name, fn in (("per_layer", per_layer), ("grouped", grouped)):
-        el, done = time_steps(fn, steps, min(args.warmup, 2 * R), args.mode)
-        res[name] = {"us_per_block": el * 1e6 / done, "gbs": block_bytes * done / el / 1e9,
-                     "launches_per_block": 14 if name == "per_layer" else 8}
-        print(f"[bench] block {name}: {res[name]['us_per_block']:.1f} us per block, {res[name]['gbs']:.1f} GB/s",
-              file=sys.stderr, flush=True)
-    for c in copies:
-        for H in c.values():
-            H.close()
-    torch.cuda.synchronize()
-    return res
 
 
 def backward_leg():
@@ -452,97 +341,6 @@ def factorize_leg(args):
     return res
 
 
-def fp16_context_leg(args):
-    """Context for the pages' headline (DBF matvec speedup over an fp16
-    matvec): on the same GPU, the batch-1 forward of fp16 dense 4096x4096
-    and 14336x4096 layers (torch's library matvec) against the DBF decode of
-    the 4096x4096 layer at k = 2048 (~1 bit/weight) and k = 4096 (~2
-    bits/weight) and of the 14336x4096 MLP layer at k = 4800, each over >=
-    rotate-mb of distinct weight copies replayed from a graph; and the
-    bandwidth of a plain 1 GiB device copy (the attainable HBM rate)."""
-    import torch
-
-    import dbf_linear_fwd_amd as dbf
-    from tests import inputs
-
-    res = {}
-    g = torch.Generator(device="cpu").manual_seed(5)
-
-    def fp16_us(n, m):
-        R = max(2, -(-args.rotate_mb * (1 << 20) // (2 * n * m)))
-        Ws = [(0.02 * torch.randn((n, m), generator=g)).half().cuda() for _ in range(R)]
-        x = torch.randn((1, m), generator=g).half().cuda()
-        yy = torch.empty((1, n), dtype=torch.float16, device="cuda")
-
-        def dense(i):
-            torch.matmul(x, Ws[i % R].t(), out=yy)
-        dense.period = R
-        el, done = time_steps(dense, max(R, min(args.steps, 20 * R)), min(args.warmup, R), "graph")
-        del Ws
-        torch.cuda.empty_cache()
-        return el * 1e6 / done, 2 * n * m * done / el / 1e9
-
-    t16, gbs16 = fp16_us(4096, 4096)
-    res["fp16_matvec_4096x4096_us"] = t16
-    res["fp16_matvec_4096x4096_gbs"] = gbs16
-    t16_up, gbs16_up = fp16_us(14336, 4096)
-    res["fp16_matvec_14336x4096_us"] = t16_up
-    res["fp16_matvec_14336x4096_gbs"] = gbs16_up
-    for cid, li, tag, tref in ((2, 0, "4096x4096_k2048_1bit", t16), (3, 0, "4096x4096_k4096_2bit", t16),
-                               (4, 0, "14336x4096_k4800_1.5bit", t16_up)):
-        layer = inputs.config(cid).layers[li]
-        y = torch.empty((1, layer.n), dtype=torch.float16, device="cuda")
-        bytes_step = layer.sign_bytes + layer.scale_bytes
-        Rd = max(1, -(-args.rotate_mb * (1 << 20) // bytes_step))
-        copies = [dbf.Layer(layer.A, layer.B, layer.a, layer.mid, layer.b, max_batch=1) for _ in range(Rd)]
-        xd = torch.from_numpy(layer.X[1]).cuda()
-
-        def fwd(i):
-            copies[i % Rd].forward(xd, out=y)
-        fwd.period = Rd
-        el, done = time_steps(fwd, max(Rd, min(args.steps, 10 * Rd)), min(args.warmup, Rd), "graph")
-        td = el * 1e6 / done
-        res[f"dbf_{tag}_us"] = td
-        res[f"speedup_{tag}"] = tref / td
-        for c in copies:
-            c.close()
-        del copies
-        torch.cuda.synchronize()
-    # the library's dense fp16 GEMM on the batch-2048 shape of the 4096x4096
-    # layer: the MFMA rate a plain GEMM attains on this chip under this load
-    Xg = torch.randn((2048, 4096), generator=g).half().cuda()
-    Wg = (0.02 * torch.randn((4096, 4096), generator=g)).half().cuda()
-    Yg = torch.empty((2048, 4096), dtype=torch.float16, device="cuda")
-    for _ in range(5):
-        torch.matmul(Xg, Wg.t(), out=Yg)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(50):
-        torch.matmul(Xg, Wg.t(), out=Yg)
-    e1.record()
-    torch.cuda.synchronize()
-    tg = e0.elapsed_time(e1) * 1e3 / 50
-    res["fp16_gemm_2048x4096x4096_us"] = tg
-    res["fp16_gemm_2048x4096x4096_tflops"] = 2 * 2048 * 4096 * 4096 / (tg * 1e-6) / 1e12
-    del Xg, Wg, Yg
-    buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-    dst = torch.empty_like(buf)
-    dst.copy_(buf)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(10):
-        dst.copy_(buf)
-    e1.record()
-    torch.cuda.synchronize()
-    res["device_copy_1GiB_gbs"] = 10 * 2 * buf.numel() * 4 / (e0.elapsed_time(e1) / 1e3) / 1e9
-    del buf, dst
-    torch.cuda.empty_cache()
-    print(f"[bench] fp16 context: {res}", file=sys.stderr, flush=True)
-    return res
-
-
 def copy_probe(mb):
     import torch
     n = mb * (1 << 20) // 4
@@ -554,6 +352,320 @@ def copy_probe(mb):
     print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "launches": 3}))
 
 
+
+
+GROUPS = [["q", "k", "v"], ["o"], ["gate", "up"], ["down"]]
+TOL = 2e-3
+
+
+def block_bytes_of(layers):
+    return sum(L.sign_bytes + L.scale_bytes for L in layers)
+
+
+def stage_bytes(layers, batch):
+    """Algorithmic bytes of the two decode stages of a group of layers that
+    share an input: stage 1 reads B's signs, b, mid and x; stage 2 reads A's
+    signs and a and writes y (the intermediate is an implementation cost)."""
+    m = layers[0].m
+    s1 = sum(L.k * L.m // 8 + 2 * L.m + 2 * L.k for L in layers) + 2 * batch * m
+    s2 = sum(L.n * L.k // 8 + 2 * L.n + 2 * batch * L.n for L in layers)
+    return s1, s2
+
+
+def row_rel_err(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float((np.abs(got - ref).max(axis=1) / np.maximum(np.abs(ref).max(axis=1), 1e-300)).max())
+
+
+class Block:
+    """R copies of the decoder block's handles, with its inputs and outputs."""
+
+    def __init__(self, rotate_mb, max_batch=1):
+        import torch
+
+        import dbf_linear_fwd_amd as dbf
+        from tests import inputs
+        self.layers = inputs.config(5).layers
+        self.by = {L.name: L for L in self.layers}
+        self.bytes = block_bytes_of(self.layers)
+        self.R = max(1, -(-rotate_mb * (1 << 20) // self.bytes))
+        self.copies = [{L.name: dbf.Layer(L.A, L.B, L.a, L.mid, L.b, max_batch=max_batch) for L in self.layers}
+                       for _ in range(self.R)]
+        self.xs = {L.name: torch.from_numpy(L.X[1]).cuda() for L in self.layers}
+        self.ys = {L.name: torch.empty((1, L.n), dtype=torch.float16, device="cuda") for L in self.layers}
+
+    def step(self, i):
+        """One block forward on copy i mod R: the groups in dependency order."""
+        import dbf_linear_fwd_amd as dbf
+        c = self.copies[i % self.R]
+        for gr in GROUPS:
+            if len(gr) == 1:
+                c[gr[0]].forward(self.xs[gr[0]], out=self.ys[gr[0]])
+            else:
+                dbf.forward_group([c[n] for n in gr], self.xs[gr[0]], [self.ys[n] for n in gr])
+
+    def parity(self):
+        """Every output of every layer of the first and last copy against the
+        fp64 oracle (per-row infinity-norm relative error); the worst one."""
+        import torch
+
+        from oracle import dbf_oracle as O
+        worst = 0.0
+        # (a group's layers read the input of its first layer)
+        xin = {n: self.by[gr[0]].X[1] for gr in GROUPS for n in gr}
+        refs = {L.name: O.sampled_forward(xin[L.name], L.A, L.B, L.a, L.mid, L.b, [0], np.arange(L.n))
+                for L in self.layers}
+        for ci in sorted({0, self.R - 1}):
+            for y in self.ys.values():
+                y.fill_(float("nan"))
+            self.step(ci)
+            torch.cuda.synchronize()
+            for L in self.layers:
+                worst = max(worst, row_rel_err(self.ys[L.name].cpu().numpy(), refs[L.name]))
+        return worst
+
+    def close(self):
+        import torch
+        for c in self.copies:
+            for H in c.values():
+                H.close()
+        torch.cuda.synchronize()
+
+
+def time_exact(step, steps, warmup, start=0):
+    """`warmup` untimed eager steps, then exactly `steps` steps i = start +
+    warmup, ... captured in one HIP graph; one untimed replay uploads the
+    graph, one replay is timed with events.  Returns seconds."""
+    import torch
+    cur = torch.cuda.current_stream()
+    for i in range(warmup):
+        step(start + i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(cur)
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(steps):
+                step(start + warmup + i)
+    cur.wait_stream(s)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1e3
+
+
+def block_kernel_times(blk, rounds=2):
+    """Average per-launch time (us) of each decode kernel of the block, from
+    HIP events riding on the launches (eager steps over all copies)."""
+    import dbf_linear_fwd_amd as dbf
+    import torch
+    heads = {"qkv": "q", "o": "o", "gateup": "gate", "down": "down"}
+    for c in blk.copies:
+        for h in heads.values():
+            dbf.dbf_timing_enable(c[h].handle, True)
+            dbf.dbf_timing_read(c[h].handle)
+    torch.cuda.synchronize()
+    for i in range(rounds * blk.R):
+        blk.step(i)
+    torch.cuda.synchronize()
+    out = {}
+    for gname, h in heads.items():
+        tot = {}
+        for c in blk.copies:
+            for kname, v in dbf.dbf_timing_read(c[h].handle).items():
+                t = tot.setdefault(kname, [0, 0.0])
+                t[0] += v["launches"]
+                t[1] += v["total_ms"]
+            dbf.dbf_timing_enable(c[h].handle, False)
+        for kname, (n, ms) in tot.items():
+            stage = 1 if kname.endswith("stage1") else 2
+            out[f"{gname}_stage{stage}"] = {"launches": n, "avg_us": 1e3 * ms / max(n, 1)}
+    return out
+
+
+def block_leg(args):
+    """The headline: the decoder block at batch 1 (see the module docstring)."""
+    blk = Block(args.rotate_mb)
+    print(f"[bench] block: 7 layers, {blk.bytes / 2**20:.1f} MiB per block, {blk.R} copies", file=sys.stderr,
+          flush=True)
+    err = blk.parity()
+    print(f"[bench] block parity: worst row rel err {err:.3e}", file=sys.stderr, flush=True)
+    if not err <= TOL:
+        blk.close()
+        print(f"[bench] PARITY FAILED on the decoder block (worst row rel err {err:.3e} > {TOL}); no number",
+              file=sys.stderr, flush=True)
+        sys.exit(1)
+    el = time_exact(blk.step, args.steps, args.warmup, start=0)
+    gbs = blk.bytes * args.steps / el / 1e9
+    print(f"[bench] block: {args.steps} steps in {el * 1e3:.2f} ms -> {gbs:.1f} GB/s "
+          f"({el * 1e6 / args.steps:.1f} us per block)", file=sys.stderr, flush=True)
+    # beside it, a longer steady state over whole rotations
+    long_steps = 10 * blk.R
+    el_long = time_exact(blk.step, long_steps, blk.R, start=args.steps)
+    kt = block_kernel_times(blk)
+    print(f"[bench] block kernels: {kt}", file=sys.stderr, flush=True)
+    sb = {}
+    for gr, gname in zip(GROUPS, ("qkv", "o", "gateup", "down")):
+        s1, s2 = stage_bytes([blk.by[n] for n in gr], 1)
+        sb[f"{gname}_stage1"], sb[f"{gname}_stage2"] = s1, s2
+    dom = max(kt, key=lambda k: kt[k]["avg_us"])
+    ach = sb[dom] / (kt[dom]["avg_us"] * 1e-6) / 1e9
+    res = {
+        "value": gbs, "ms_per_step": el * 1e3 / args.steps, "steps": args.steps, "parity_worst_row_rel_err": err,
+        "steady_state": {"steps": long_steps, "gbs": blk.bytes * long_steps / el_long / 1e9,
+                         "us_per_block": el_long * 1e6 / long_steps},
+        "kernels": {k: dict(v, bytes=sb[k], gbs=sb[k] / (v["avg_us"] * 1e-6) / 1e9) for k, v in kt.items()},
+        "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": ach / HBM_PEAK_GBS, "traffic": recorded_traffic(dom), "kernel": dom,
+                     "algorithmic_bytes_per_launch": sb[dom]},
+        "block_bytes": blk.bytes, "copies": blk.R,
+    }
+    blk.close()
+    return res
+
+
+def layer_leg(args):
+    """Context: the single 4096x4096, k = 2048 layer (about 1 bit per weight)
+    at batch 1, steady state over rotated copies."""
+    import torch
+
+    import dbf_linear_fwd_amd as dbf
+    from tests import inputs
+    layer = inputs.config(2).layers[0]
+    bytes_step = layer.sign_bytes + layer.scale_bytes
+    R = max(1, -(-args.rotate_mb * (1 << 20) // bytes_step))
+    copies = [dbf.Layer(layer.A, layer.B, layer.a, layer.mid, layer.b, max_batch=1) for _ in range(R)]
+    x = torch.from_numpy(layer.X[1]).cuda()
+    y = torch.empty((1, layer.n), dtype=torch.float16, device="cuda")
+
+    def fwd(i):
+        copies[i % R].forward(x, out=y)
+    el = time_exact(fwd, 4 * R, R)
+    kt = kernel_times(copies, fwd, 2 * R)
+    res = {"workload": "DBF linear 4096x4096, k=2048 (~1 bit/weight), batch 1", "copies": R,
+           "us_per_forward": el * 1e6 / (4 * R), "gbs": bytes_step * 4 * R / el / 1e9, "kernels": kt}
+    print(f"[bench] layer 4096x4096 k2048: {res['us_per_forward']:.2f} us, {res['gbs']:.1f} GB/s; kernels {kt}",
+          file=sys.stderr, flush=True)
+    for c in copies:
+        c.close()
+    torch.cuda.synchronize()
+    return res
+
+
+def prefill_leg(args):
+    """The batch-2048 half of the metric on the MLP up (14336x4096) and down
+    (4096x14336) projections, k = 4800: outputs checked against the oracle
+    first (the first and last row of every 128-row tile and 16 random rows,
+    every output of each), then TFLOP/s-equivalent 2*batch*k*(n+m) per
+    forward over 20 forwards after 5 warm-ups, and the kernels' launch times."""
+    import torch
+
+    import dbf_linear_fwd_amd as dbf
+    from oracle import dbf_oracle as O
+    from tests import inputs
+    bt = 2048
+    out = {}
+    tot_flops, tot_s = 0, 0.0
+    kall = {}
+    for layer in inputs.config(4).layers:
+        L = dbf.Layer(layer.A, layer.B, layer.a, layer.mid, layer.b, max_batch=bt)
+        X = layer.X[bt]
+        x = torch.from_numpy(X).cuda()
+        y = torch.empty((bt, layer.n), dtype=torch.float16, device="cuda")
+        L.forward(x, out=y)
+        torch.cuda.synchronize()
+        rows = np.unique(np.concatenate([np.arange(0, bt, 128), np.arange(127, bt, 128),
+                                         np.random.default_rng(7).choice(bt, 16, replace=False)]))
+        err = row_rel_err(y.cpu().numpy()[rows],
+                          O.sampled_forward(X, layer.A, layer.B, layer.a, layer.mid, layer.b, rows,
+                                            np.arange(layer.n)))
+        print(f"[bench] prefill {layer.name} parity: worst row rel err {err:.3e} over {len(rows)} rows",
+              file=sys.stderr, flush=True)
+        if not err <= TOL:
+            print(f"[bench] PARITY FAILED on prefill {layer.name}; no number", file=sys.stderr, flush=True)
+            sys.exit(1)
+
+        def pf(i):
+            L.forward(x, out=y)
+        el, done = time_steps(pf, 20, 5, "eager")
+        flops = 2 * bt * layer.k * (layer.n + layer.m)
+        kt = kernel_times([L], pf, 10)
+        kf = prefill_kernel_flops(layer, bt)
+        out[layer.name] = {"us_per_forward": el * 1e6 / done, "tflops_eq": flops * done / el / 1e12,
+                           "parity_worst_row_rel_err": err, "kernels": kt}
+        for kname, v in kt.items():
+            if kname in kf:
+                kall[f"{layer.name}_{kname}"] = (kf[kname], v["avg_us"])
+        tot_flops += flops * done
+        tot_s += el
+        print(f"[bench] prefill {layer.name}: {out[layer.name]['tflops_eq']:.1f} TFLOP/s-eq; kernels {kt}",
+              file=sys.stderr, flush=True)
+        L.close()
+        torch.cuda.synchronize()
+    dom = max(kall, key=lambda k: kall[k][1])
+    ach = kall[dom][0] / (kall[dom][1] * 1e-6) / 1e12
+    tfs = tot_flops / tot_s / 1e12
+    return {"value": tfs, "unit": "TFLOP/s-eq", "frac_of_mfma_peak": tfs / MFMA_F16_PEAK_TFLOPS,
+            "workload": "MLP up 14336x4096 and down 4096x14336 projections, k=4800 (~1.5 bits/weight), batch 2048",
+            "layers": out,
+            "roofline": {"bound": "mfma", "achieved": ach, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": ach / MFMA_F16_PEAK_TFLOPS, "traffic": recorded_traffic(dom.split("_", 1)[1]),
+                         "kernel": dom, "algorithmic_flops_per_launch": kall[dom][0]}}
+
+
+def cpu_baseline(seconds):
+    """The fp64 oracle's factored forward (the §2.1 evaluation order) of the
+    decoder block's seven layers at batch 1, on the host's BLAS threads,
+    repeated for about `seconds`; GB/s of packed weights, the headline's unit."""
+    from oracle import dbf_oracle as O
+    from tests import inputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    layers = inputs.config(5).layers
+    nbytes = block_bytes_of(layers)
+    blocks = 0
+    t0 = time.perf_counter()
+    while True:
+        for L in layers:
+            O.factored_forward(L.X[1], L.A, L.B, L.a, L.mid, L.b)
+        blocks += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": nbytes * blocks / el / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{blocks} batch-1 forwards of the decoder block's 7 layers through the fp64 oracle "
+                      f"(factored evaluation order) in {el:.1f} s",
+            "host_cpu_count": os.cpu_count()}
+
+
+def context_leg():
+    """The attainable HBM rate on this GPU: a plain 1 GiB device copy."""
+    import torch
+    buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(buf)
+    dst.copy_(buf)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(buf)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 10 * 2 * buf.numel() * 4 / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del buf, dst
+    torch.cuda.empty_cache()
+    return {"device_copy_1GiB_gbs": gbs}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -561,10 +673,6 @@ def main():
               "(this build has no multi-GPU path; see the sharding notes in DESIGN.md)", file=sys.stderr)
         sys.exit(2)
     import torch
-
-    import dbf_linear_fwd_amd as dbf
-    from tests import inputs
-
     torch.cuda.set_device(0)
     if args.copy_probe_mb:
         copy_probe(args.copy_probe_mb)
@@ -572,130 +680,29 @@ def main():
     if args.all_configs:
         all_configs(args)
         return
-
     result = {}
-    # ---------------------------------------------------------------- decode, batch 1 (headline)
-    if args.only in (None, "decode"):
-        cfg = inputs.config(2)
-        layer = cfg.layers[0]
-        bytes_step = layer.sign_bytes + layer.scale_bytes
-        R = max(1, -(-args.rotate_mb * (1 << 20) // bytes_step))
-        print(f"[bench] decode: {layer.n}x{layer.m} k={layer.k}, {R} weight copies "
-              f"({R * bytes_step / 2**20:.0f} MiB), {args.steps} steps, mode={args.mode}", file=sys.stderr, flush=True)
-        copies = layer_copies(layer, R)
-        x = torch.from_numpy(layer.X[1]).cuda()
-        y = torch.empty((1, layer.n), dtype=torch.float16, device="cuda")
-
-        dpath = dbf.DBF_PATH_DECODE if args.decode_path == "mfma" else dbf.DBF_PATH_DECODE_TABLE
-
-        def fwd(i):
-            copies[i % R].forward(x, out=y, path=dpath)
-        fwd.period = R
-
-        el, done = time_steps(fwd, args.steps, args.warmup, args.mode)
-        gbs = bytes_step * done / el / 1e9
-        print(f"[bench] decode: {done} steps in {el * 1e3:.2f} ms -> {gbs:.1f} GB/s", file=sys.stderr, flush=True)
-        el_e, done_e = time_steps(fwd, min(args.steps, 2 * R), min(args.warmup, R), "eager")
-        kt = kernel_times(copies, fwd, min(args.steps, 2 * R))
-        print(f"[bench] kernel event times: {kt}", file=sys.stderr, flush=True)
-        # cold calls: each after a 512 MiB write (evicts the L2s and the
-        # Infinity Cache); a GPU-side spin covers the host's enqueue, so the
-        # events time the forward's kernels and the gap between them
-        scrub = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-        cold = []
-        for i in range(9):
-            scrub.fill_(i & 255)
-            torch.cuda.synchronize()
-            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda._sleep(200000)
-            c0.record()
-            fwd(i)
-            c1.record()
-            torch.cuda.synchronize()
-            cold.append(c0.elapsed_time(c1) * 1e3)
-        del scrub
-        torch.cuda.empty_cache()
-        print(f"[bench] cold calls (us): {[round(c, 1) for c in cold]}", file=sys.stderr, flush=True)
-        kb = decode_kernel_bytes(layer, 1)
-        if args.decode_path == "table":
-            kb = {"table_" + kname.split("_", 1)[1]: v for kname, v in kb.items()}
-        dom = max(kb, key=lambda kname: kt.get(kname, {"avg_us": 0})["avg_us"])
-        ach = kb[dom] / (kt[dom]["avg_us"] * 1e-6) / 1e9
-        result["decode"] = {
-            "value": gbs, "ms_per_step": el * 1e3 / done, "steps": done,
-            "eager_gbs": bytes_step * done_e / el_e / 1e9,
-            "cold_call_us_median": float(np.median(cold)),
-            "kernels": kt, "dominant": dom,
-            "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": ach / HBM_PEAK_GBS, "traffic": recorded_traffic(dom), "kernel": dom,
-                         "algorithmic_bytes_per_launch": kb[dom]},
-            "layer": layer, "copies": copies,
-        }
-        for c in copies:
-            c.close()
-        del copies
-        torch.cuda.synchronize()
-
-    # ---------------------------------------------------------------- prefill, batch 2048 (secondary)
+    if args.only in (None, "block"):
+        result["block"] = block_leg(args)
+    if args.only in (None, "layer"):
+        result["layer"] = layer_leg(args)
     if args.only in (None, "prefill") and not args.no_secondary:
-        layer = inputs.config(3).layers[0]
-        bt = 2048
-        print(f"[bench] prefill: {layer.n}x{layer.m} k={layer.k} batch {bt}", file=sys.stderr, flush=True)
-        L = dbf.Layer(layer.A, layer.B, layer.a, layer.mid, layer.b, max_batch=bt)
-        x = torch.from_numpy(layer.X[bt]).cuda()
-        y = torch.empty((bt, layer.n), dtype=torch.float16, device="cuda")
-
-        def pf(i):
-            L.forward(x, out=y)
-        reps = 50
-        el, done = time_steps(pf, reps, 10, "eager")
-        flops = 2 * bt * layer.k * (layer.n + layer.m)
-        tfs = flops * done / el / 1e12
-        kt = kernel_times([L], pf, 20)
-        kf = prefill_kernel_flops(layer, bt)
-        dom = max(kf, key=lambda kname: kt.get(kname, {"avg_us": 0})["avg_us"])
-        ach = kf[dom] / (kt[dom]["avg_us"] * 1e-6) / 1e12
-        print(f"[bench] prefill: {tfs:.1f} TFLOP/s-eq; kernels {kt}", file=sys.stderr, flush=True)
-        result["prefill"] = {
-            "value": tfs, "unit": "TFLOP/s-eq", "ms_per_forward": el * 1e3 / done,
-            "frac_of_mfma_peak": tfs / MFMA_F16_PEAK_TFLOPS, "kernels": kt,
-            "roofline": {"bound": "mfma", "achieved": ach, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": ach / MFMA_F16_PEAK_TFLOPS, "traffic": recorded_traffic(dom), "kernel": dom,
-                         "algorithmic_flops_per_launch": kf[dom]},
-            "workload": "4096x4096 projection, k=4096 (~2 bits/weight), batch 2048",
-        }
-        L.close()
-
-    # ---------------------------------------------------------------- gradients, batch 2048 (secondary)
+        result["prefill"] = prefill_leg(args)
     if args.only in (None, "backward") and not args.no_backward:
         result["backward"] = backward_leg()
-
-    # ---------------------------------------------------------------- decoder block, batch 1 (secondary)
-    if args.only in (None, "block") and not args.no_block:
-        result["block"] = block_leg(args)
-
-    # ---------------------------------------------------------------- BQQ-form layer (secondary)
     if args.only in (None, "bqq") and not args.no_bqq:
         result["bqq"] = bqq_leg(args)
-
-    # ---------------------------------------------------------------- fp16 matvec and copy context
-    if args.only in (None, "context") and not args.no_context:
-        result["context"] = fp16_context_leg(args)
-
-    # ---------------------------------------------------------------- factorization (secondary)
     if args.only in (None, "factorize") and not args.no_factorize:
         result["factorize"] = factorize_leg(args)
-
+    if args.only in (None, "context") and not args.no_context:
+        result["context"] = context_leg()
     if args.only is not None:
-        print(json.dumps({k: {kk: vv for kk, vv in v.items() if kk not in ("layer", "copies")}
-                          for k, v in result.items()}, default=str))
+        print(json.dumps(result, default=str))
         return
-
-    d = result["decode"]
+    d = result["block"]
     cpu = None
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(d["layer"], args.cpu_seconds)
+        cpu = cpu_baseline(args.cpu_seconds)
     line = {
         "metric": "DBF linear packed-weight GB/s (% HBM peak) at batch 1; TFLOP/s-eq at batch 2048",
         "value": round(d["value"], 3),
@@ -707,23 +714,24 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": "i8",
         "data": "synthetic",
-        "config": {"workload": "DBF linear 4096x4096, k=2048 (~1 bit/weight), batch 1, fp16 I/O, "
-                               f"{d['layer'].n}x{d['layer'].m}; weights rotated over >=512 MB; {args.mode}",
-                   "n": d["layer"].n, "m": d["layer"].m, "k": d["layer"].k, "batch": 1,
-                   "mode": args.mode},
+        "config": {"workload": "Llama-3-8B-shaped decoder block of 7 DBF linears (q 4096x4096, k/v 1024x4096, "
+                               "o 4096x4096, gate/up 14336x4096, down 4096x14336), k per layer for 1.0-2.3 "
+                               "bits/weight, batch 1, fp16 in and out; q/k/v and gate/up grouped, groups in "
+                               "dependency order; weights rotated over >= 512 MB",
+                   "batch": 1, "layers": 7, "block_bytes": d["block_bytes"], "copies": d["copies"]},
         "frac_of_hbm_peak": d["value"] / HBM_PEAK_GBS,
         "roofline": d["roofline"],
         "cpu_baseline": cpu,
-        "decode_kernels_us": d["kernels"],
-        "eager_gbs": d["eager_gbs"],
-        "cold_call_us_median": d["cold_call_us_median"],
+        "parity_worst_row_rel_err": d["parity_worst_row_rel_err"],
+        "decode_block_steady_state": d["steady_state"],
+        "decode_kernels": d["kernels"],
     }
     if "prefill" in result:
         line["prefill_batch2048"] = result["prefill"]
-    if "block" in result:
-        line["decode_block_b1"] = result["block"]
+    if "layer" in result:
+        line["decode_layer_4096x4096_k2048_b1"] = result["layer"]
     if "backward" in result:
         line["backward_batch2048"] = result["backward"]
     if "bqq" in result:
