@@ -55,13 +55,18 @@ struct I8Layer {
     int rows = 0, K = 0;
     int SC = 0, wlast = 0;             // superchunks; words per lane of the last one (1..4)
     int ntiles = 0;                    // 16-row tiles
-    int wg0 = 0, nwg = 0;              // set by launch_decode_i8
+    // set by launch_decode_i8: tiles per workgroup, waves (parts of the
+    // reduction) per tile, workgroups of the layer, and each wave's job as
+    // 16 bits (tile of the workgroup: 3, first superchunk: 6, superchunks: 7)
+    int tpw = 0, parts = 0, nwg = 0;
+    uint32_t job[4] = {0, 0, 0, 0};
 };
 struct I8Args {
     I8Layer L[8];
     int count = 0;
     // stage 1 of a 0/1 layer: one more workgroup forms the row sums of x
     // (stats[0] = Σ x, stats[1] = Σ gamma x); stat_wg >= 0 asks for it
+    // (the workgroup at blockIdx = (0, count); count < 8 then)
     const __half *stat_x = nullptr;
     int stat_m = 0;
     const float *gamma = nullptr;
