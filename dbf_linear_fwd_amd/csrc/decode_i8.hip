@@ -64,13 +64,25 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kW = 8;                 // waves per workgroup
 constexpr int kT = kW * 64;           // threads per workgroup
 constexpr int kCUs = 256;             // MI355X
-constexpr int kActSC = 2048;          // LDS bytes of digits per superchunk: [8 j][4 g][4 c][16]
-constexpr int kPartBytes = kW * 16 * 4 * 4;  // [wave][row][c] int32
-constexpr int kMiscBytes = kW * 4 + kW * 8;  // wave maxima, wave sums of q
+constexpr int kMaxTPWc = 8;           // tiles per workgroup, at most
+constexpr int kActSC = 2048;          // LDS bytes of digits per superchunk: [8 j][16 slots][16]
+constexpr int kPartBytes = kMaxTPWc * 16 * 8;  // [tile][row] int64: Z of the workgroup's rows
+constexpr int kMiscBytes = kW * 4 + kW * 8 + (2 * kMaxTPWc * 16 + 2) * 4;  // wave maxima and sums, row scales
 constexpr int kRing = 4;              // superchunks of signs in flight per wave
 
 __host__ __device__ constexpr size_t lds_bytes_for(int SC) {
     return static_cast<size_t>(SC) * kActSC + kPartBytes + kMiscBytes;
+}
+
+// Digits in LDS.  Block (s, j, g) -- the 16 vector entries 512 s + 128 i +
+// 16 j + 4 g + b (i, b < 4) -- holds one 16-byte row per digit plane c
+// (byte 4 i + b), the B operand of lane (c, g) in the product for bit j of
+// superchunk s.  Superchunk s, bit j is a 256-byte chunk of 16 slots; plane
+// c of block g sits in slot digit_slot(g, c, j), a permutation under which
+// the prologue's writes (lanes over (j, g), one plane) and the operand reads
+// (lanes over (c, g), one j) each reach every bank once.
+__device__ __forceinline__ int digit_slot(int g, int c, int j) {
+    return 8 * (g >> 1) + 4 * (g & 1) + ((c + 2 * (g >> 1) + j) & 3);
 }
 
 // Buffer resources: loads through them at offsets past num_records return 0
@@ -82,58 +94,64 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, uint32_t b
 }
 constexpr uint32_t kOff = 0x7FFFFFF0u;  // an offset past every range
 
-// Raw loads of four consecutive entries base .. base + 3 (base a multiple of
-// 4) of the stage's vector: stage 1, x and b (fp16); stage 2, v (fp32).
-// Entries at or past K read as 0 (runs past K lie outside the resources'
-// ranges).  When K is not a multiple of 4 (stage 1 only) the entries are
-// loaded one by one.
-struct Run {
-    uint32_t r[4];
+// Raw loads of eight consecutive entries base .. base + 7 (base a multiple
+// of 8) of the stage's vector: stage 1, x and b (fp16, 16 bytes each);
+// stage 2, v (fp32, two 16-byte loads).  Entries at or past K read as 0
+// (they lie outside the resources' ranges).  When K is not a multiple of 8
+// (stage 1 only) the entries are loaded one by one.
+struct Octet {
+    uint32_t r[8];
 };
-template <int STAGE, bool K4>
-__device__ __forceinline__ Run load_run(__amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rb, int base) {
-    Run o;
+template <int STAGE, bool K8>
+__device__ __forceinline__ Octet load_octet(__amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rb, int base) {
+    Octet o;
     if constexpr (STAGE == 1) {
-        if constexpr (K4) {
-            const uint2 xv = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rx, 2 * base, 0, 0));
-            const uint2 bv = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rb, 2 * base, 0, 0));
-            o.r[0] = xv.x;
-            o.r[1] = xv.y;
-            o.r[2] = bv.x;
-            o.r[3] = bv.y;
-        } else {
-            uint32_t xe[4], be[4];
+        if constexpr (K8) {
+            const u32x4 xv = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, 2 * base, 0, 0));
+            const u32x4 bv = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, 2 * base, 0, 0));
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
+                o.r[e] = xv[e];
+                o.r[4 + e] = bv[e];
+            }
+        } else {
+            uint32_t xe[8], be[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
                 xe[e] = __builtin_amdgcn_raw_buffer_load_b16(rx, 2 * (base + e), 0, 0);
                 be[e] = __builtin_amdgcn_raw_buffer_load_b16(rb, 2 * (base + e), 0, 0);
             }
-            o.r[0] = xe[0] | (xe[1] << 16);
-            o.r[1] = xe[2] | (xe[3] << 16);
-            o.r[2] = be[0] | (be[1] << 16);
-            o.r[3] = be[2] | (be[3] << 16);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                o.r[e] = xe[2 * e] | (xe[2 * e + 1] << 16);
+                o.r[4 + e] = be[2 * e] | (be[2 * e + 1] << 16);
+            }
         }
     } else {
-        const u32x4 t = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, 4 * base, 0, 0));
+        const u32x4 t0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, 4 * base, 0, 0));
+        const u32x4 t1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, 4 * base + 16, 0, 0));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o.r[e] = t[e];
+        for (int e = 0; e < 4; ++e) {
+            o.r[e] = t0[e];
+            o.r[4 + e] = t1[e];
+        }
     }
     return o;
 }
 
-// The four fp32 entries of a run: stage 1, x ⊙ b (exact); stage 2, v.
+// The eight fp32 entries of an octet: stage 1, x ⊙ b (exact); stage 2, v.
 template <int STAGE>
-__device__ __forceinline__ void run_values(const Run &o, float (&u)[4]) {
+__device__ __forceinline__ void octet_values(const Octet &o, float (&u)[8]) {
     if constexpr (STAGE == 1) {
-        const __half2 x01 = __builtin_bit_cast(__half2, o.r[0]), x23 = __builtin_bit_cast(__half2, o.r[1]);
-        const __half2 b01 = __builtin_bit_cast(__half2, o.r[2]), b23 = __builtin_bit_cast(__half2, o.r[3]);
-        u[0] = __low2float(x01) * __low2float(b01);
-        u[1] = __high2float(x01) * __high2float(b01);
-        u[2] = __low2float(x23) * __low2float(b23);
-        u[3] = __high2float(x23) * __high2float(b23);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const __half2 xh = __builtin_bit_cast(__half2, o.r[e]), bh = __builtin_bit_cast(__half2, o.r[4 + e]);
+            u[2 * e] = __low2float(xh) * __low2float(bh);
+            u[2 * e + 1] = __high2float(xh) * __high2float(bh);
+        }
     } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) u[e] = __uint_as_float(o.r[e]);
+        for (int e = 0; e < 8; ++e) u[e] = __uint_as_float(o.r[e]);
     }
 }
 
@@ -177,10 +195,13 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
     return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
 }
 
-// NR: runs of four vector entries per thread (the vector, padded to SC
-// superchunks, has SC * 128 runs; NR * kT >= that).
-template <int STAGE, bool BIN, bool K4, int NR>
-__global__ __launch_bounds__(kT, 2) void dec_i8_kernel(const I8Args args) {
+// NO: octets of the vector per thread in the prologue.  Octet o holds the
+// entries 512 s + 128 i + 16 j + 8 gp + (0..7) -- run i of blocks g = 2 gp
+// and 2 gp + 1 of (s, j) -- with (s, j, i, gp) = (o >> 6, (o >> 3) & 7,
+// (o >> 1) & 3, o & 1); the vector, padded to SC superchunks, has SC * 64
+// octets, NO * kT >= that.
+template <int STAGE, bool BIN, bool K8, int NO>
+__global__ __launch_bounds__(kT, NO <= 4 ? 2 : 1) void dec_i8_kernel(const I8Args args) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     // Every field of the layer, read at once (one round of scalar loads: the
     // empty asm takes them all as inputs, so none of the loads is sunk into
@@ -197,14 +218,13 @@ __global__ __launch_bounds__(kT, 2) void dec_i8_kernel(const I8Args args) {
         return;
     }
     const int wg = blockIdx.x;
+    if (wg >= L.nwg) return;  // padding of the grid's shorter rows
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int SC = L.SC, wl = L.wlast, P = L.parts;
+    const int SC = L.SC, wl = L.wlast;
     const int t0 = wg * L.tpw;
-    // tiles of this workgroup (none in the padding of the grid's shorter rows:
-    // such a workgroup issues only loads that read nothing, then leaves)
-    const int nt = wg < L.nwg ? min(L.tpw, L.ntiles - t0) : 0;
+    const int nt = min(L.tpw, L.ntiles - t0);  // tiles of this workgroup
     const int tile_words = 256 * (SC - 1) + 64 * wl;
     // this wave's job: tile lt of the workgroup, superchunks [s0, s0 + nu)
     const uint32_t jpair = w < 4 ? (w < 2 ? L.job[0] : L.job[1]) : (w < 6 ? L.job[2] : L.job[3]);
@@ -213,22 +233,24 @@ __global__ __launch_bounds__(kT, 2) void dec_i8_kernel(const I8Args args) {
     const int nu = lt < nt ? static_cast<int>(job >> 9) : 0;
 
     char *act = lds;                                                     // digits [SC][8 j][4 g][4 c][16]
-    int *part = reinterpret_cast<int *>(lds + static_cast<size_t>(SC) * kActSC);  // [wave][row][c]
-    float *wmax = reinterpret_cast<float *>(part + kPartBytes / 4);      // [kW]
+    long long *zrow = reinterpret_cast<long long *>(lds + static_cast<size_t>(SC) * kActSC);  // [tile][row]
+    float *wmax = reinterpret_cast<float *>(zrow + kPartBytes / 8);      // [kW]
     long long *wU = reinterpret_cast<long long *>(wmax + kW);            // [kW]
+    float *scl = reinterpret_cast<float *>(wU + kW);  // [2][kMaxTPWc * 16] row scales (a or mid; E), then 2 stats
 
     // ---- loads, in the order their data is used (a wave waits for its
     // loads in issue order): the vector, the row scales, then the first
     // kRing superchunks of signs
-    const int nruns = SC * 128;
-    const uint32_t kb = nt > 0 ? static_cast<uint32_t>(L.K) : 0u;
+    const int noct = SC * 64;
+    const uint32_t kb = static_cast<uint32_t>(L.K);
     const __amdgpu_buffer_rsrc_t rx = rsrc(L.vec, kb * (STAGE == 1 ? 2u : 4u));
     const __amdgpu_buffer_rsrc_t rb = rsrc(L.bsc, STAGE == 1 ? 2u * kb : 0u);
-    Run raw[NR];
+    Octet raw[NO];
 #pragma unroll
-    for (int k = 0; k < NR; ++k) {
-        const int r = tid + kT * k;
-        raw[k] = load_run<STAGE, K4>(rx, rb, r < nruns ? 4 * r : (1 << 28));
+    for (int k = 0; k < NO; ++k) {
+        const int o = tid + kT * k;
+        const int base = 512 * (o >> 6) + 16 * ((o >> 3) & 7) + 128 * ((o >> 1) & 3) + 8 * (o & 1);
+        raw[k] = load_octet<STAGE, K8>(rx, rb, o < noct ? base : (1 << 27));
     }
     // thread tid < nt * 16 finishes row t0 * 16 + tid
     const int my_row = min(t0 * 16 + tid, L.rows - 1);
@@ -259,16 +281,15 @@ __global__ __launch_bounds__(kT, 2) void dec_i8_kernel(const I8Args args) {
 #pragma unroll
     for (int q = 0; q < kRing; ++q)
         ring[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, unit_off(q), 0, 0));
-    if (nt <= 0) return;
 
     // ---- the vector as fixed-point digits, one exponent for the workgroup
     float mx = 0.0f;
 #pragma unroll
-    for (int k = 0; k < NR; ++k) {
-        float u[4];
-        run_values<STAGE>(raw[k], u);
+    for (int k = 0; k < NO; ++k) {
+        float u[8];
+        octet_values<STAGE>(raw[k], u);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fabsf(u[e]));
+        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(u[e]));
     }
     mx = wave_max_nonneg(mx);
     if (lane == 0) wmax[w] = mx;
@@ -281,42 +302,62 @@ __global__ __launch_bounds__(kT, 2) void dec_i8_kernel(const I8Args args) {
         (void)frexpf(mx, &E);  // mx = f 2^E, f in [0.5, 1)
         S = 30 - E;            // mx 2^S in [2^29, 2^30)
     }
-    long long usum = 0;
+    // the row scales, kept in LDS for the finishing threads (their loads
+    // are waited for here, not behind the last sign loads)
+    if (tid < nt * 16) {
+        zrow[tid] = 0;
+        scl[tid] = osc_v;
+        if constexpr (STAGE == 2 && BIN) scl[kMaxTPWc * 16 + tid] = affe_v;
+    }
+    if constexpr (STAGE == 2 && BIN) {
+        if (tid == 0) {
+            scl[2 * kMaxTPWc * 16] = aff_s0;
+            scl[2 * kMaxTPWc * 16 + 1] = aff_s1;
+        }
+    }
+    int dsum[4] = {0, 0, 0, 0};  // Σ of each digit plane over this thread's octets
 #pragma unroll
-    for (int k = 0; k < NR; ++k) {
-        const int r = tid + kT * k;
-        if (r < nruns) {
-            float u[4];
-            run_values<STAGE>(raw[k], u);
-            uint32_t E[4];
+    for (int k = 0; k < NO; ++k) {
+        const int o = tid + kT * k;
+        if (o < noct) {
+            float u[8];
+            octet_values<STAGE>(raw[k], u);
+            const int sj = o >> 3, j = sj & 7, i = (o >> 1) & 3, gp = o & 1;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int q = __float2int_rn(ldexpf(u[e], S));
-                usum += q;
-                // balanced base-256 digits: the bytes of (q + 0x808080) ^ 0x808080
-                E[e] = (static_cast<uint32_t>(q) + 0x808080u) ^ 0x808080u;
+            for (int h = 0; h < 2; ++h) {  // block g = 2 gp + h: entries 4 h .. 4 h + 3
+                uint32_t E[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int q = __float2int_rn(ldexpf(u[4 * h + e], S));
+                    // balanced base-256 digits: the bytes of (q + 0x808080) ^ 0x808080
+                    E[e] = (static_cast<uint32_t>(q) + 0x808080u) ^ 0x808080u;
+                }
+                // 4x4 byte transpose: plane c = (E[0].c, E[1].c, E[2].c, E[3].c)
+                const uint32_t lo01 = __builtin_amdgcn_perm(E[1], E[0], 0x05010400u);
+                const uint32_t hi01 = __builtin_amdgcn_perm(E[1], E[0], 0x07030602u);
+                const uint32_t lo23 = __builtin_amdgcn_perm(E[3], E[2], 0x05010400u);
+                const uint32_t hi23 = __builtin_amdgcn_perm(E[3], E[2], 0x07030602u);
+                const uint32_t Pc[4] = {__builtin_amdgcn_perm(lo23, lo01, 0x05040100u),
+                                        __builtin_amdgcn_perm(lo23, lo01, 0x07060302u),
+                                        __builtin_amdgcn_perm(hi23, hi01, 0x05040100u),
+                                        __builtin_amdgcn_perm(hi23, hi01, 0x07060302u)};
+                const int g = 2 * gp + h;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    dsum[c] = __builtin_amdgcn_sdot4(static_cast<int>(Pc[c]), 0x01010101, dsum[c], false);
+                    // bytes 4 i .. 4 i + 3 of plane c of block (s, j, g)
+                    *reinterpret_cast<uint32_t *>(act + 256 * sj + 16 * digit_slot(g, c, j) + 4 * i) = Pc[c];
+                }
             }
-            // 4x4 byte transpose: plane c = (E[0].c, E[1].c, E[2].c, E[3].c)
-            const uint32_t lo01 = __builtin_amdgcn_perm(E[1], E[0], 0x05010400u);
-            const uint32_t hi01 = __builtin_amdgcn_perm(E[1], E[0], 0x07030602u);
-            const uint32_t lo23 = __builtin_amdgcn_perm(E[3], E[2], 0x05010400u);
-            const uint32_t hi23 = __builtin_amdgcn_perm(E[3], E[2], 0x07030602u);
-            // entries 4r .. 4r + 3 = columns 512 s + 128 i + 16 j + 4 g + (0..3):
-            // bytes 4 i .. 4 i + 3 of block (s, j, g), plane c
-            uint32_t *d = reinterpret_cast<uint32_t *>(act + (r >> 7) * kActSC + ((r >> 2) & 7) * 256 +
-                                                       (r & 3) * 64 + ((r >> 5) & 3) * 4);
-            d[0] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
-            d[4] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
-            d[8] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
-            d[12] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
         }
     }
     if constexpr (!BIN) {
-        // usum = hi 2^16 + lo (|usum| < 2^33 per thread): both halves' wave
-        // sums stay inside 32 bits
-        const uint32_t lo = wave_sum_u32(static_cast<uint32_t>(usum) & 0xFFFFu);
-        const int hi = static_cast<int>(wave_sum_u32(static_cast<uint32_t>(static_cast<int>(usum >> 16))));
-        if (lane == 0) wU[w] = static_cast<long long>(hi) * 65536 + static_cast<long long>(lo);
+        // U = Σ q = Σ_c 256^c (Σ of plane c); each plane's wave sum fits 32 bits
+        long long U = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            U += static_cast<long long>(static_cast<int>(wave_sum_u32(static_cast<uint32_t>(dsum[c])))) * (1LL << (8 * c));
+        if (lane == 0) wU[w] = U;
     }
     __syncthreads();
 
@@ -326,8 +367,11 @@ __global__ __launch_bounds__(kT, 2) void dec_i8_kernel(const I8Args args) {
     for (int j = 0; j < 8; ++j) acc[j] = i32x4{0, 0, 0, 0};
     const int c = lane & 15, gq = lane >> 4;
     // B operand of lane (c, g): 16 bytes of digit plane c; lanes of the
-    // unused columns c >= 4 read nothing (their columns of D are not used)
-    const char *act_lane = act + 64 * gq + 16 * c;
+    // unused columns c >= 4 read nothing (their columns of D are not used).
+    // The slot depends on j mod 4.
+    int slot_off[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) slot_off[k] = 16 * digit_slot(gq, c & 3, k);
     if (nu > 0) {
         int i0 = 0;
         // one exit, at the bottom; every step issues its load (kRing units
@@ -340,9 +384,10 @@ __global__ __launch_bounds__(kT, 2) void dec_i8_kernel(const I8Args args) {
                     const int s = s0 + i;
                     i32x4 B[8];
                     if (c < 4) {
+                        const char *as = act + kActSC * s;
 #pragma unroll
                         for (int j = 0; j < 8; ++j)
-                            B[j] = *reinterpret_cast<const i32x4 *>(act_lane + kActSC * s + 256 * j);
+                            B[j] = *reinterpret_cast<const i32x4 *>(as + slot_off[j & 3] + 256 * j);
                     }
                     u32x4 wd = ring[q];
                     if (s == SC - 1) {  // words past wlast: not this superchunk's
@@ -360,7 +405,9 @@ __global__ __launch_bounds__(kT, 2) void dec_i8_kernel(const I8Args args) {
             }
             i0 += kRing;
         } while (i0 < nu);
-        // Z of the job's 16 rows, per digit column: Σ_j ±acc_j >> j
+        // Z of the job's 16 rows, per digit column: Σ_j ±acc_j >> j, added
+        // with its weight 256^c to the row's sum in LDS (exact integers, so
+        // the order of the additions does not matter)
         if (c < 4) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
@@ -368,7 +415,8 @@ __global__ __launch_bounds__(kT, 2) void dec_i8_kernel(const I8Args args) {
 #pragma unroll
                 for (int j = 0; j < 7; ++j) f += acc[j][v] >> j;
                 f -= acc[7][v] >> 7;
-                part[(w * 16 + 4 * gq + v) * 4 + c] = f;
+                __hip_atomic_fetch_add(&zrow[lt * 16 + 4 * gq + v], static_cast<long long>(f) * (1LL << (8 * c)),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             }
         }
     }
@@ -376,21 +424,14 @@ __global__ __launch_bounds__(kT, 2) void dec_i8_kernel(const I8Args args) {
 
     // ---- one thread per row: the parts' exact sums, then the scales
     if (tid < nt * 16) {
-        const int le = tid >> 4, r = tid & 15;
-        long long Z = 0;
-        for (int pp = 0; pp < P; ++pp) {
-            const int *pz = part + ((le * P + pp) * 16 + r) * 4;
-            Z += static_cast<long long>(pz[0]) + static_cast<long long>(pz[1]) * 256 +
-                 static_cast<long long>(pz[2]) * 65536 + static_cast<long long>(pz[3]) * 16777216;
-        }
-        long long sf = 2 * Z;
+        long long sf = 2 * zrow[tid];
         if constexpr (!BIN) {
             long long U = 0;
 #pragma unroll
             for (int ww = 0; ww < kW; ++ww) U += wU[ww];
             sf = U - sf;
         }
-        const double res = ldexp(static_cast<double>(sf), -S) * static_cast<double>(osc_v);
+        const double res = ldexp(static_cast<double>(sf), -S) * static_cast<double>(scl[tid]);
         const int row = t0 * 16 + tid;
         if (row < L.rows) {
             if constexpr (STAGE == 1) {
@@ -398,7 +439,8 @@ __global__ __launch_bounds__(kT, 2) void dec_i8_kernel(const I8Args args) {
             } else {
                 double val = res;
                 if constexpr (BIN)
-                    val += static_cast<double>(affe_v) * static_cast<double>(aff_s0) + static_cast<double>(aff_s1);
+                    val += static_cast<double>(scl[kMaxTPWc * 16 + tid]) * static_cast<double>(scl[2 * kMaxTPWc * 16]) +
+                           static_cast<double>(scl[2 * kMaxTPWc * 16 + 1]);
                 static_cast<__half *>(L.out)[row] = rne16_of(val);
             }
         }
@@ -424,19 +466,27 @@ int launch_decode_i8(I8Args &a, int stage, bool bin, void *stream) {
             L.rows > 16 * L.ntiles)
             return static_cast<int>(hipErrorInvalidValue);
     }
-    // tiles per workgroup: the largest of 8, 4, 2 that still gives 7/8 of a
-    // workgroup per CU or more (else 1); the waves of a workgroup are shared
-    // out among its tiles as parts of their reductions
-    int tpw = 1;
-    for (int cand = 8; cand >= 2; cand /= 2) {
-        long long wgs = 0;
-        for (int i = 0; i < a.count; ++i) wgs += (a.L[i].ntiles + cand - 1) / cand;
-        if (wgs >= kCUs * 7 / 8) {
+    int maxSC = 1;
+    for (int i = 0; i < a.count; ++i) maxSC = std::max(maxSC, a.L[i].SC);
+    // vector octets per thread NO = 1, 2, 4, 8 for up to 8, 16, 32, 64
+    // superchunks; two workgroups per CU where LDS and registers allow (NO <= 4)
+    const int ni = maxSC <= 8 ? 0 : maxSC <= 16 ? 1 : maxSC <= 32 ? 2 : 3;
+    const int slots = kCUs * ((ni <= 2 && 2 * lds_bytes_for(maxSC) <= 160 * 1024) ? 2 : 1);
+    // tiles per workgroup: the fewest (1, 2, 4, 8) with which every
+    // workgroup of the launch is resident at once; the waves of a workgroup
+    // are shared out among its tiles as parts of their reductions
+    // (the grid is rectangular: its shorter rows' padding workgroups hold a
+    // slot while they start and leave)
+    int tpw = kMaxTPWc;
+    for (int cand = 1; cand < kMaxTPWc; cand *= 2) {
+        long long wmax = 0;
+        for (int i = 0; i < a.count; ++i) wmax = std::max<long long>(wmax, (a.L[i].ntiles + cand - 1) / cand);
+        if (wmax * a.count <= slots) {
             tpw = cand;
             break;
         }
     }
-    int maxwg = 1, maxSC = 1;
+    int maxwg = 1;
     for (int i = 0; i < a.count; ++i) {
         I8Layer &L = a.L[i];
         const int P = std::min(kW / tpw, L.SC);
@@ -452,29 +502,27 @@ int launch_decode_i8(I8Args &a, int stage, bool bin, void *stream) {
             L.job[w >> 1] |= static_cast<uint32_t>(lt | (s0 << 3) | (nu << 9)) << (16 * (w & 1));
         }
         maxwg = std::max(maxwg, L.nwg);
-        maxSC = std::max(maxSC, L.SC);
     }
     const bool stat = bin && a.stat_wg >= 0;
     if (stat && a.count >= kMaxGroup) return static_cast<int>(hipErrorInvalidValue);
+    if (tpw > kMaxTPWc) return static_cast<int>(hipErrorInvalidValue);
     a.stat_wg = stat ? 0 : -1;
     if (stat) a.L[a.count] = I8Layer{};  // the row of the row-sum workgroup
     const dim3 grid(maxwg, a.count + (stat ? 1 : 0));
     const size_t lds = lds_bytes_for(maxSC);
-    // stage 1 reads x in runs of four entries when every layer's m allows
-    bool k4 = true;
-    for (int i = 0; i < a.count; ++i) k4 = k4 && (a.L[i].K % 4 == 0);
-    // (stage 2 reads v, k_pad entries: always whole runs); runs per thread
-    // NR = 2, 4, 8, 16 for up to 8, 16, 32, 64 superchunks
+    // stage 1 reads x in 16-byte octets when every layer's m allows
+    bool k8 = true;
+    for (int i = 0; i < a.count; ++i) k8 = k8 && (a.L[i].K % 8 == 0);
+    // (stage 2 reads v, k_pad entries: a multiple of 64)
     static void (*const kernels[4][6])(I8Args) = {
-#define DBF_I8_ROW(NR)                                                                                        \
-    {dec_i8_kernel<1, false, true, NR>, dec_i8_kernel<1, false, false, NR>, dec_i8_kernel<1, true, true, NR>, \
-     dec_i8_kernel<1, true, false, NR>, dec_i8_kernel<2, false, true, NR>, dec_i8_kernel<2, true, true, NR>}
-        DBF_I8_ROW(2), DBF_I8_ROW(4), DBF_I8_ROW(8), DBF_I8_ROW(16)
+#define DBF_I8_ROW(NO)                                                                                        \
+    {dec_i8_kernel<1, false, true, NO>, dec_i8_kernel<1, false, false, NO>, dec_i8_kernel<1, true, true, NO>, \
+     dec_i8_kernel<1, true, false, NO>, dec_i8_kernel<2, false, true, NO>, dec_i8_kernel<2, true, true, NO>}
+        DBF_I8_ROW(1), DBF_I8_ROW(2), DBF_I8_ROW(4), DBF_I8_ROW(8)
 #undef DBF_I8_ROW
     };
     static bool lds_set[4][6] = {};
-    const int ni = maxSC <= 8 ? 0 : maxSC <= 16 ? 1 : maxSC <= 32 ? 2 : 3;
-    const int ki = stage == 1 ? (bin ? 2 : 0) + (k4 ? 0 : 1) : 4 + (bin ? 1 : 0);
+    const int ki = stage == 1 ? (bin ? 2 : 0) + (k8 ? 0 : 1) : 4 + (bin ? 1 : 0);
     if (!lds_set[ni][ki]) {
         allow_lds(kernels[ni][ki], lds_bytes_for(kI8MaxSC));
         lds_set[ni][ki] = true;
