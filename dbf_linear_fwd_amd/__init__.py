@@ -30,7 +30,7 @@ __all__ = [
     "dbf_layout_words_dec",
     "dbf_timing_enable", "dbf_timing_read", "Layer", "dbf_linear_forward_group", "forward_group",
     "dbf_pack_ex", "dbf_linear_backward_data", "dbf_linear_backward", "DBF_PACK_BACKWARD", "dbf_bqq_pack",
-    "dbf_factorize", "factorize",
+    "dbf_factorize", "factorize", "dbf_linear_forward_noalloc",
 ]
 
 DBF_OK = 0
@@ -53,7 +53,7 @@ EXPORTED_SYMBOLS = (
     "dbf_pack", "dbf_pack_ex", "dbf_linear_forward", "dbf_linear_forward_ex", "dbf_linear_forward_group",
     "dbf_linear_backward_data", "dbf_linear_backward", "dbf_free", "dbf_get_info", "dbf_status_string",
     "dbf_pack_signs", "dbf_layout_signs", "dbf_layout_words", "dbf_layout_signs_dec", "dbf_layout_words_dec",
-    "dbf_timing_enable", "dbf_timing_read", "dbf_bqq_pack", "dbf_factorize",
+    "dbf_timing_enable", "dbf_timing_read", "dbf_bqq_pack", "dbf_factorize", "dbf_linear_forward_noalloc",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -102,6 +102,8 @@ def lib() -> ctypes.CDLL:
     L.dbf_linear_forward.restype = ctypes.c_int
     L.dbf_linear_forward_ex.argtypes = [vp, vp, vp, i32, i32, vp]
     L.dbf_linear_forward_ex.restype = ctypes.c_int
+    L.dbf_linear_forward_noalloc.argtypes = [vp, vp, vp, i32, vp]
+    L.dbf_linear_forward_noalloc.restype = ctypes.c_int
     L.dbf_pack_ex.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, i32, i32, ctypes.POINTER(vp)]
     L.dbf_pack_ex.restype = ctypes.c_int
     L.dbf_bqq_pack.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, ctypes.c_uint16, i32, ctypes.POINTER(vp)]
@@ -247,6 +249,11 @@ def dbf_linear_forward(h: int, x_ptr: int, y_ptr: int, batch: int, stream: int =
 
 def dbf_linear_forward_ex(h: int, x_ptr: int, y_ptr: int, batch: int, path: int, stream: int = 0) -> None:
     _check(lib().dbf_linear_forward_ex(h, x_ptr, y_ptr, batch, path, stream), "dbf_linear_forward_ex")
+
+
+def dbf_linear_forward_noalloc(h: int, x_ptr: int, y_ptr: int, batch: int, stream: int = 0) -> None:
+    """dbf_linear_forward with the kernels' scratch in the library's static device array."""
+    _check(lib().dbf_linear_forward_noalloc(h, x_ptr, y_ptr, batch, stream), "dbf_linear_forward_noalloc")
 
 
 def dbf_linear_forward_group(hs, x_ptr: int, y_ptrs, batch: int, stream: int = 0) -> None:

@@ -15,6 +15,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -885,5 +886,141 @@ extern "C" dbf_status_t dbf_timing_read(dbf_handle_t h, dbf_kernel_time_t *out, 
     }
     *count = i;
     h->totals.clear();
+    return st;
+}
+
+// ---------------------------------------------------------------------------
+// Forward without allocation: the kernels' scratch (the intermediate v or T,
+// split-K and stage-1 partials, tickets, row sums of 0/1 layers) comes from
+// one static device array instead of the handle's workspace.  Each device
+// that runs it holds its own copy of the array until the process ends.
+
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+__device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};  // the array's device address on each device
+
+// The address of this device's copy of the scratch array (resolved once per
+// device, with that device current; the array's name is not a device
+// address in host code).
+dbf_status_t scratch_on_device(int dev, char **out) {
+    if (dev < 0 || dev >= kMaxDevices) return DBF_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DBF_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = static_cast<char *>(g_scratch_ptr[dev]);
+    return DBF_OK;
+}
+
+__global__ void zero_u32_kernel(unsigned *p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+// Scratch of one forward at this batch on the default path: the pieces the
+// chosen kernels use, each 256-byte aligned, with the sizes the handle's own
+// workspace would give them for this batch.
+struct ScratchPlan {
+    size_t v32 = 0, v16 = 0, tpart = 0, tickets = 0, T = 0, split = 0, stats = 0, total = 0;
+    size_t tpart_cap = 0, split_cap = 0;
+    bool i8 = false, decode = false, parts = false;
+};
+
+ScratchPlan plan_scratch(const dbf_layer *h, int32_t batch) {
+    ScratchPlan p;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += (bytes + 255) & ~size_t(255);
+        return at;
+    };
+    p.decode = batch <= dbf::kDecodeMaxBatch;
+    if (p.decode && batch == 1 && h->i8_ok) {
+        p.i8 = true;
+        p.v32 = take(sizeof(float) * size_t(h->k_pad));
+    } else if (p.decode) {
+        p.v16 = take(sizeof(uint16_t) * 2 * size_t(dbf::kDecodeMaxBatch) * h->k_pad);
+        const int parts = dbf::mfma_stage1_parts(h->m_pad, h->k_pad, dbf::kDecodeMaxBatch);
+        if (!h->binary && parts > 1) {
+            p.parts = true;
+            p.tpart_cap = size_t(parts) * dbf::kDecodeMaxBatch * h->k_pad;
+            p.tpart = take(sizeof(float) * p.tpart_cap);
+            p.tickets = take(sizeof(unsigned) * size_t(h->ntickets));
+        }
+    } else {
+        p.T = take(sizeof(uint16_t) * size_t(batch) * h->k_pad);
+        p.split_cap = std::max<size_t>(64, std::max(dbf::sign_gemm_split_elems(batch, h->m, h->Wm, h->k_pad),
+                                                    dbf::sign_gemm_split_elems(batch, h->k_pad, h->Wk, h->n)));
+        p.split = take(sizeof(float) * p.split_cap);
+    }
+    if (h->binary) p.stats = take(sizeof(float) * 2 * size_t(batch));
+    p.total = off;
+    return p;
+}
+
+}  // namespace
+
+extern "C" dbf_status_t dbf_linear_forward_noalloc(dbf_handle_t h, const void *x, void *y, int32_t batch,
+                                                   hipStream_t stream) {
+    if (!h) return DBF_ERR_INVALID_ARG;
+    if (batch < 0 || batch > h->max_batch) return DBF_ERR_INVALID_ARG;
+    if (batch == 0) return DBF_OK;
+    if (!x || !y || !aligned16(x) || !aligned16(y)) return DBF_ERR_INVALID_ARG;
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return DBF_ERR_HIP;
+    if (cur != h->device) return DBF_ERR_INVALID_ARG;
+    const ScratchPlan p = plan_scratch(h, batch);
+    if (p.total > kNoAllocScratchBytes) return DBF_ERR_SHAPE;  // more scratch than the static array holds
+    char *base = nullptr;
+    dbf_status_t st = scratch_on_device(cur, &base);
+    if (st != DBF_OK) return st;
+    // tickets start at zero (the kernels leave them at zero; the array may
+    // hold anything from an earlier call)
+    if (p.parts) {
+        const int n = h->ntickets;
+        hipLaunchKernelGGL(zero_u32_kernel, dim3((n + 255) / 256), dim3(256), 0, stream,
+                           reinterpret_cast<unsigned *>(base + p.tickets), n);
+        if (hipGetLastError() != hipSuccess) return DBF_ERR_HIP;
+    }
+    // the handle's workspace pointers, pointed at the scratch for this call
+    // (calls on one handle are ordered, so nothing else sees the swap); no
+    // timing events either, which would be created on first use
+    float *const o_v32 = h->v32, *const o_tpart = h->tpart, *const o_split = h->split, *const o_stats = h->bqq_stats;
+    uint16_t *const o_v16 = h->v16, *const o_T = h->T;
+    unsigned *const o_tickets = h->tickets;
+    const size_t o_tpart_cap = h->tpart_cap, o_split_cap = h->split_cap;
+    const bool o_timing = h->timing;
+    if (p.i8) h->v32 = reinterpret_cast<float *>(base + p.v32);
+    if (p.decode && !p.i8) h->v16 = reinterpret_cast<uint16_t *>(base + p.v16);
+    if (p.parts) {
+        h->tpart = reinterpret_cast<float *>(base + p.tpart);
+        h->tpart_cap = p.tpart_cap;
+        h->tickets = reinterpret_cast<unsigned *>(base + p.tickets);
+    }
+    if (!p.decode) {
+        h->T = reinterpret_cast<uint16_t *>(base + p.T);
+        h->split = reinterpret_cast<float *>(base + p.split);
+        h->split_cap = p.split_cap;
+    }
+    if (h->binary) h->bqq_stats = reinterpret_cast<float *>(base + p.stats);
+    h->timing = false;
+    st = dbf_linear_forward_ex(h, x, y, batch, DBF_PATH_AUTO, stream);
+    h->v32 = o_v32;
+    h->tpart = o_tpart;
+    h->split = o_split;
+    h->bqq_stats = o_stats;
+    h->v16 = o_v16;
+    h->T = o_T;
+    h->tickets = o_tickets;
+    h->tpart_cap = o_tpart_cap;
+    h->split_cap = o_split_cap;
+    h->timing = o_timing;
     return st;
 }

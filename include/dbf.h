@@ -158,6 +158,31 @@ dbf_status_t dbf_linear_forward_group(const dbf_handle_t *hs, int32_t count, con
                                       int32_t batch, hipStream_t stream);
 
 /*
+ * dbf_linear_forward_noalloc -- dbf_linear_forward for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same kernels and the same results,
+ * bit for bit, but their scratch (the intermediate, split-K and stage-1
+ * partials, tickets, the row sums of 0/1 layers) lives in a static device
+ * array of 64 MiB compiled into the library instead of the handle's
+ * workspace.  Each device that runs it holds its own copy of the array until
+ * the process ends; the copy's address is resolved on the first call on that
+ * device.  No allocation at all: no hipMalloc or hipFree, no library routine
+ * that allocates, no timing events (kernel timing of the handle is paused
+ * for the call).
+ *   Arguments and their ownership are those of dbf_linear_forward.
+ *   Every call on a device shares that device's array, which keeps the last
+ *   call's contents: calls that overlap on one device (other streams, other
+ *   threads) race and must be ordered by the caller.  What must start at
+ *   zero is cleared by the call itself (a kernel, not a memset).
+ * Errors: as dbf_linear_forward, plus DBF_ERR_SHAPE when this batch needs
+ * more scratch than the array holds (decode batches always fit; the
+ * batch-2048 products fit for k_pad up to about 16000), and
+ * DBF_ERR_UNSUPPORTED for a device index of 64 or more.
+ */
+dbf_status_t dbf_linear_forward_noalloc(dbf_handle_t h, const void *x, void *y, int32_t batch,
+                                        hipStream_t stream);
+
+/*
  * dbf_pack_ex -- dbf_pack with flags.  DBF_PACK_BACKWARD also packs the
  * transposed factors (Aᵀ along n, Bᵀ along k; the transpose of a DBF matrix
  * is the DBF matrix diag(b) Bᵀ diag(mid) Aᵀ diag(a)) and allocates the fp32
