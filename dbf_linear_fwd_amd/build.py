@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdbf.so")
 
-HIP_SOURCES = ["runtime.hip", "decode.hip", "decode_mfma.hip", "decode_i8.hip", "prefill.hip", "grad.hip", "bqq.hip", "factor.hip"]
+HIP_SOURCES = ["runtime.hip", "decode_mfma.hip", "decode_i8.hip", "prefill.hip", "grad.hip", "bqq.hip", "factor.hip"]
 CXX_SOURCES = ["pack.cpp"]
 
 ARCH = "gfx950"
@@ -34,7 +34,11 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # denormals are ordinary values in this library: never flush them
     "-fno-gpu-flush-denormals-to-zero",
-    "-ffp-contract=fast",
+    # no implicit contraction: every product and sum rounds where the source
+    # writes it (no fused multiply-add); the epilogues keep a product that
+    # feeds an fp16 conversion in fp32 themselves (fp32_value), which the
+    # backend would otherwise fuse into the conversion in some kernel forms
+    "-ffp-contract=off",
     "-I", INCLUDE,
     "-I", CSRC,
 ]

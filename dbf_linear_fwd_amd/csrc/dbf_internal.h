@@ -21,8 +21,6 @@ namespace dbf {
 
 // Largest batch served by the decode (signed-sum) kernels.
 constexpr int kDecodeMaxBatch = 16;
-// Decode chunking: words of 32 signs handled by one workgroup along a
-// reduction dimension (1024 elements); bounds the LDS copy of the activations.
 
 uint32_t reorder_word(uint32_t canonical);
 
@@ -75,24 +73,6 @@ struct I8Args {
 };
 // stage = 1 or 2; bin: 0/1 matrices (Z instead of U - 2 Z, times 2).
 int launch_decode_i8(I8Args &a, int stage, bool bin, void *stream);
-
-// Largest batch served by the lookup-table decode kernels.
-constexpr int kLutMaxBatch = 4;
-// Upper bound on the words of one lookup-table chunk (register budget).
-constexpr int kMaxLutChunkWords = 124;
-
-// Arguments of the decode kernels for one forward.
-struct DecodeArgs {
-    const uint32_t *A_dev, *B_dev;
-    const void *a_dev, *mid_dev, *b_dev;
-    const void *x;
-    void *y;
-    float *tpart, *ypart;
-    unsigned *tickets;   // one per 64-row tile of A, zero between calls
-    int batch, n, m, n_pad, m_pad, k_pad;
-    int cw_m, nchunk_m;  // stage-1 chunk (words of B per workgroup) and chunk count
-    int cw_k, nchunk_k;  // stage-2 chunk (words of A per workgroup) and chunk count
-};
 
 // Arguments of the matrix-core decode kernels (batch 1..16).
 struct MfmaDecodeArgs {
@@ -147,13 +127,6 @@ struct MfmaGroupArgs {
     int batch, m, m_pad;
 };
 int launch_mfma_decode_group(const MfmaGroupArgs &g, void *stream, int which);
-
-// Words per lookup-table chunk allowed by the LDS budget for `nb` batch rows.
-int lut_max_chunk_words(int nb);
-// Lookup-table decode (batch 1..4): stage 1 writes chunk partials of t;
-// stage 2 builds the table of mid * t, sums along k and finishes y.
-int launch_lut_stage1(const DecodeArgs &d, void *stream);
-int launch_lut_stage2(const DecodeArgs &d, void *stream);
 
 // ---- kernel launchers (return hipError_t as int to keep HIP types out of here)
 

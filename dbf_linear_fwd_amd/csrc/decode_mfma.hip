@@ -140,12 +140,13 @@ __device__ __forceinline__ ExpandConsts expand_consts() {
     return c;
 }
 
-// x as an fp32 value the compiler must materialize: a product rounded to
-// fp32 here is not fused into a following fp16 conversion (one mixed-
-// precision instruction rounding the exact product once), which the compiler
-// would otherwise do in some instantiations and not others -- every kernel
-// form then rounds alike.
-__device__ __forceinline__ float rounded(float x) {
+// x as an fp32 value the compiler must materialize.  An epilogue's product
+// is rounded to fp32 here and then converted to fp16 (two roundings, in every
+// kernel form alike); without this the backend may fuse the product and the
+// conversion into one mixed-precision instruction that rounds the exact
+// product once -- in some kernel forms and not others, whatever the
+// contraction setting.
+__device__ __forceinline__ float fp32_value(float x) {
     asm volatile("" : "+v"(x));
     return x;
 }
@@ -615,6 +616,16 @@ __device__ __forceinline__ void stage1_body(int blk, char *base, const uint32_t 
                      static_cast<unsigned>(sp.parts - 1);
         __syncthreads();
         if (!s_last) return;
+        // The last part reads the others' sums.  Ordering: each part's stores
+        // are agent-scope atomics, performed at the device's coherence point
+        // (not in an XCD's L2), and its ticket is taken only after they have
+        // completed (the vmcnt wait above, then the barrier); the ticket
+        // itself is an agent-scope atomic at the same point.  So a part that
+        // draws the last ticket does so after every part's stores are in
+        // memory; this acquire fence then keeps its loads from being served
+        // by lines its own XCD's caches held from before (it invalidates
+        // them), and the loads themselves are agent-scope atomics.
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         if (wave == 0 && li < NB) {
 #pragma unroll
             for (int t = 0; t < RT; ++t) {
@@ -639,7 +650,7 @@ __device__ __forceinline__ void stage1_body(int blk, char *base, const uint32_t 
             f16x4 hi, lo;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const float val = rounded(d[v] * mid_pre[t][v]);
+                const float val = fp32_value(d[v] * mid_pre[t][v]);
                 hi[v] = static_cast<_Float16>(val);
                 lo[v] = static_cast<_Float16>(val - static_cast<float>(hi[v]));
             }
@@ -792,8 +803,8 @@ __device__ __forceinline__ void stage2_body(int blk, char *base, const uint32_t 
             for (int v = 0; v < 4; ++v) {
                 const int row = row0 + v;
                 if (row < n) {
-                    float val = rounded(d[v] * a_pre[t][v]);
-                    if (aff_E) val = rounded(val + (e_pre[t][v] * st.x + st.y));
+                    float val = fp32_value(d[v] * a_pre[t][v]);
+                    if (aff_E) val = fp32_value(val + (e_pre[t][v] * st.x + st.y));
                     y[static_cast<size_t>(li) * n + row] = __float2half_rn(val);
                 }
             }

@@ -103,11 +103,13 @@ __device__ __forceinline__ f16x8 expand(uint32_t word, int g, const u32x4 &sc, E
     return __builtin_bit_cast(f16x8, r);
 }
 
-// x as an fp32 value the compiler must materialize: the product rounded to
-// fp32 is then converted to fp16, in every kernel form alike (the compiler
-// may otherwise fuse product and conversion into one mixed-precision
-// instruction that rounds the exact product once, in some forms only).
-__device__ __forceinline__ float rounded(float x) {
+// x as an fp32 value the compiler must materialize.  An epilogue's product
+// is rounded to fp32 here and then converted to fp16 (two roundings, in every
+// kernel form alike); without this the backend may fuse the product and the
+// conversion into one mixed-precision instruction that rounds the exact
+// product once -- in some kernel forms and not others, whatever the
+// contraction setting.
+__device__ __forceinline__ float fp32_value(float x) {
     asm volatile("" : "+v"(x));
     return x;
 }
@@ -148,8 +150,8 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[MF_][NF_], const fl
                 const int row = row0 + i * 32 + 8 * (v >> 2) + 4 * kg + (v & 3);
                 if (row < M) {
                     if (out) {
-                        float val = rounded(acc[i][f][v] * snv[f]);
-                        if (aff.E) val = rounded(val + (aff.E[col] * aff.stats[2 * row] + aff.stats[2 * row + 1]));
+                        float val = fp32_value(acc[i][f][v] * snv[f]);
+                        if (aff.E) val = fp32_value(val + (aff.E[col] * aff.stats[2 * row] + aff.stats[2 * row + 1]));
                         out[static_cast<size_t>(row) * ldo + col] = __float2half_rn(val);
                     }
                     if (out32) out32[static_cast<size_t>(row) * ldo32 + col] = acc[i][f][v];
@@ -232,8 +234,8 @@ __global__ __launch_bounds__(256) void split_finish_kernel(const float *__restri
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int col = min(c0 + e, n_out - 1);
-        float val = rounded(sv[e] * __half2float(sn[col]));
-        if (aff.E) val = rounded(val + (aff.E[col] * aff.stats[2 * row] + aff.stats[2 * row + 1]));
+        float val = fp32_value(sv[e] * __half2float(sn[col]));
+        if (aff.E) val = fp32_value(val + (aff.E[col] * aff.stats[2 * row] + aff.stats[2 * row + 1]));
         o[e] = __float2half_rn(val);
     }
     __half *dst = out + static_cast<size_t>(row) * ldo + c0;

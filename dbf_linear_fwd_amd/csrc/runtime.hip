@@ -33,10 +33,9 @@ struct dbf_layer {
     uint32_t *B_dev = nullptr;
     uint16_t *a_dev = nullptr, *mid_dev = nullptr, *b_dev = nullptr;
     // workspace
-    float *tpart = nullptr;   // decode stage-1 partials [nchunk_m][16][k_pad] (or [parts][16][k_pad])
+    float *tpart = nullptr;   // matrix-core decode stage-1 partials [parts][16][k_pad]
     size_t tpart_cap = 0;     // floats
     int ntickets = 0;
-    float *ypart = nullptr;   // decode stage-2 partials [nchunk_k][16][n_pad]
     uint16_t *T = nullptr;    // prefill intermediate    [max_batch][k_pad] fp16
     unsigned *tickets = nullptr;  // per 64-row tile of A or 16-row block of B; zero between calls
     uint16_t *v16 = nullptr;      // matrix-core decode intermediate [2][16][k_pad] fp16
@@ -60,9 +59,6 @@ struct dbf_layer {
     dbf_layer *bwd = nullptr;
     float *t32 = nullptr;     // (X ⊙ b) Bᵀ in fp32          [max_batch][k_pad]
     float *red = nullptr;     // batch-sum partials [ceil(max_batch / 64)][max(n, k_pad, m)]
-    struct LutPlan {
-        int cw_m, nchunk_m, cw_k, nchunk_k;
-    } lut[dbf::kLutMaxBatch + 1]{};
     // kernel timing
     bool timing = false;
     struct Pending {
@@ -108,7 +104,6 @@ void release(dbf_layer *h) {
     (void)hipFree(h->mid_dev);
     (void)hipFree(h->b_dev);
     (void)hipFree(h->tpart);
-    (void)hipFree(h->ypart);
     (void)hipFree(h->T);
     (void)hipFree(h->tickets);
     (void)hipFree(h->v16);
@@ -131,22 +126,6 @@ void release(dbf_layer *h) {
 }
 
 int32_t round_up(int32_t v, int32_t q) { return (v + q - 1) / q * q; }
-
-// Workgroups a decode stage aims for: one per CU of the 256-CU MI355X.
-constexpr int kDecodeTargetGroups = 256;
-
-// Split `words` (even) words of each row among chunks so that tiles x chunks
-// is near the target, each chunk an even number of words <= max_cw.
-void choose_chunks(int tiles, int words, int max_cw, int &cw, int &nchunk) {
-    int nc = (kDecodeTargetGroups + tiles / 2) / tiles;
-    if (nc < 1) nc = 1;
-    if (nc > words / 2) nc = words / 2;
-    const int need = (words + max_cw - 1) / max_cw;
-    if (nc < need) nc = need;
-    cw = (((words + nc - 1) / nc) + 1) & ~1;
-    if (cw > max_cw) cw = max_cw;
-    nchunk = (words + cw - 1) / cw;
-}
 
 // Pack a +/-1 matrix (rows x cols) along cols and tile it for the device:
 // `tiled` in the dbf_layout_signs layout and, when dec_rows > 0, `dec` in the
@@ -321,27 +300,17 @@ static dbf_status_t pack_layer(int32_t n, int32_t m, int32_t k, const int8_t *A_
     if (st == DBF_OK) h->scale_bytes = 2 * size_t(n_pad + k_pad + m_pad);
 
     const int32_t dec_b = max_batch < dbf::kDecodeMaxBatch ? max_batch : dbf::kDecodeMaxBatch;
-    size_t tpart_elems = 64, ypart_elems = 64;
-    for (int nb = 1; nb <= dbf::kLutMaxBatch && nb <= max_batch; ++nb) {
-        auto &lp = h->lut[nb];
-        const int maxcw = dbf::lut_max_chunk_words(nb);
-        choose_chunks(k_pad / 64, h->Wm, maxcw, lp.cw_m, lp.nchunk_m);
-        choose_chunks(n_pad / 64, h->Wk, maxcw, lp.cw_k, lp.nchunk_k);
-        tpart_elems = std::max(tpart_elems, size_t(lp.nchunk_m) * nb * k_pad);
-        ypart_elems = std::max(ypart_elems, size_t(lp.nchunk_k) * nb * n_pad);
-    }
+    size_t tpart_elems = 64;
     // stage-1 reduction parts of the matrix-core decode (wide m, batch >= 2)
     const int s1_parts = dbf::mfma_stage1_parts(m_pad, k_pad, dbf::kDecodeMaxBatch);
     if (s1_parts > 1) tpart_elems = std::max(tpart_elems, size_t(s1_parts) * dbf::kDecodeMaxBatch * k_pad);
     const size_t tpart_bytes = sizeof(float) * tpart_elems;
-    const size_t ypart_bytes = sizeof(float) * ypart_elems;
     const int ntickets = std::max(n_pad / 64, k_pad / 16);
     const size_t ticket_bytes = sizeof(unsigned) * size_t(ntickets);
     const size_t T_bytes = sizeof(uint16_t) * size_t(max_batch) * k_pad;
     if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->tpart), tpart_bytes);
     if (st == DBF_OK) h->tpart_cap = tpart_elems;
     h->ntickets = ntickets;
-    if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->ypart), ypart_bytes);
     if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->T), T_bytes);
     if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->tickets), ticket_bytes);
     if (st == DBF_OK && hipMemset(h->tickets, 0, ticket_bytes) != hipSuccess) st = DBF_ERR_HIP;
@@ -364,7 +333,7 @@ static dbf_status_t pack_layer(int32_t n, int32_t m, int32_t k, const int8_t *A_
     if (st == DBF_OK) h->split_cap = split_elems;
     if (st == DBF_OK)
         h->workspace_bytes =
-            tpart_bytes + ypart_bytes + T_bytes + ticket_bytes + v16_bytes + v32_bytes + sizeof(float) * split_elems;
+            tpart_bytes + T_bytes + ticket_bytes + v16_bytes + v32_bytes + sizeof(float) * split_elems;
 
     if (st != DBF_OK) {
         release(h);
@@ -609,42 +578,6 @@ static dbf_status_t forward_decode_mfma(dbf_layer *h, const void *x, void *y, in
     return timed_launch(h, "decode_stage2", stream, [&] { return dbf::launch_mfma_decode(d, stream, 2); });
 }
 
-static dbf_status_t forward_decode(dbf_layer *h, const void *x, void *y, int32_t batch, hipStream_t stream) {
-    // Lookup-table decode, up to kLutMaxBatch rows per pair of launches;
-    // larger batches run as groups of rows (each row's result is the same
-    // in any group).
-    for (int32_t r0 = 0; r0 < batch; r0 += dbf::kLutMaxBatch) {
-        const int32_t nb = std::min<int32_t>(dbf::kLutMaxBatch, batch - r0);
-        const auto &lp = h->lut[nb];
-        dbf::DecodeArgs d{};
-        d.A_dev = h->A_dev;
-        d.B_dev = h->B_dev;
-        d.a_dev = h->a_dev;
-        d.mid_dev = h->mid_dev;
-        d.b_dev = h->b_dev;
-        d.x = static_cast<const uint16_t *>(x) + static_cast<size_t>(r0) * h->m;
-        d.y = static_cast<uint16_t *>(y) + static_cast<size_t>(r0) * h->n;
-        d.tpart = h->tpart;
-        d.ypart = h->ypart;
-        d.tickets = h->tickets;
-        d.batch = nb;
-        d.n = h->n;
-        d.m = h->m;
-        d.n_pad = h->n_pad;
-        d.m_pad = h->m_pad;
-        d.k_pad = h->k_pad;
-        d.cw_m = lp.cw_m;
-        d.nchunk_m = lp.nchunk_m;
-        d.cw_k = lp.cw_k;
-        d.nchunk_k = lp.nchunk_k;
-        dbf_status_t st = timed_launch(h, "table_stage1", stream, [&] { return dbf::launch_lut_stage1(d, stream); });
-        if (st != DBF_OK) return st;
-        st = timed_launch(h, "table_stage2", stream, [&] { return dbf::launch_lut_stage2(d, stream); });
-        if (st != DBF_OK) return st;
-    }
-    return DBF_OK;
-}
-
 static dbf_status_t forward_prefill(dbf_layer *h, const void *x, void *y, int32_t batch, hipStream_t stream) {
     // T = rne16(mid ⊙ (X (B ⊙ b)ᵀ)), all k_pad columns (padded ones are 0).
     // (BQQ-form layers: 0/1 matrices, b = 1 so no per-K scale, and the
@@ -686,16 +619,12 @@ extern "C" dbf_status_t dbf_linear_forward_ex(dbf_handle_t h, const void *x, voi
         path != DBF_PATH_DECODE_TABLE)
         return DBF_ERR_INVALID_ARG;
     if (path == DBF_PATH_DECODE && batch > dbf::kDecodeMaxBatch) return DBF_ERR_INVALID_ARG;
-    if (path == DBF_PATH_DECODE_TABLE && batch > dbf::kDecodeMaxBatch) return DBF_ERR_INVALID_ARG;
     if (batch == 0) return DBF_OK;
     if (!x || !y || !aligned16(x) || !aligned16(y)) return DBF_ERR_INVALID_ARG;
     int cur = -1;
     if (hipGetDevice(&cur) != hipSuccess) return DBF_ERR_HIP;
     if (cur != h->device) return DBF_ERR_INVALID_ARG;
-    if (path == DBF_PATH_DECODE_TABLE) {
-        if (h->binary) return DBF_ERR_UNSUPPORTED;
-        return forward_decode(h, x, y, batch, stream);
-    }
+    if (path == DBF_PATH_DECODE_TABLE) return DBF_ERR_UNSUPPORTED;  // (removed: slower than the matrix cores)
     const bool decode = path == DBF_PATH_DECODE || (path == DBF_PATH_AUTO && batch <= dbf::kDecodeMaxBatch);
     if (h->binary && !decode) {
         // (on the decode path the stage-1 launch forms the row sums itself)
