@@ -615,7 +615,7 @@ def prefill_leg(args):
             "workload": "MLP up 14336x4096 and down 4096x14336 projections, k=4800 (~1.5 bits/weight), batch 2048",
             "layers": out,
             "roofline": {"bound": "mfma", "achieved": ach, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": ach / MFMA_F16_PEAK_TFLOPS, "traffic": recorded_traffic(dom.split("_", 1)[1]),
+                         "frac": ach / MFMA_F16_PEAK_TFLOPS, "traffic": recorded_traffic(dom),
                          "kernel": dom, "algorithmic_flops_per_launch": kall[dom][0]}}
 
 
