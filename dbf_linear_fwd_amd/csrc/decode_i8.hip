@@ -33,11 +33,11 @@
 // Work split.  A workgroup (8 waves) owns tpw consecutive tiles of 16 rows;
 // each tile's reduction is cut into `parts` ranges of superchunks (512
 // columns, 1 KiB of signs per tile), one per wave, so a wave's job is one
-// (tile, range) pair.  The host picks tpw in {8, 4, 2, 1} so that the launch
-// has enough workgroups to fill the GPU, and parts = min(8 / tpw, SC).  A
-// wave streams its sign words from global memory into a ring of four
-// register sets (the first four issued before the vector prologue); the
-// digits of the whole vector sit in LDS.  The waves' partial Z meet in LDS
+// (tile, range) pair.  The host picks the fewest tiles per workgroup, tpw in
+// {1, 2, 4, 8}, with which the grid has at most one workgroup per CU, and
+// parts = min(8 / tpw, SC).  A wave streams its sign words from global
+// memory into a ring of three register sets (the first three issued before
+// the vector prologue); the digits of the whole vector sit in LDS.  The waves' partial Z meet in LDS
 // and one thread per row finishes it.
 //
 // Every wave issues at most one instruction per four cycles, so what a wave
@@ -68,7 +68,7 @@ constexpr int kMaxTPWc = 8;           // tiles per workgroup, at most
 constexpr int kActSC = 2048;          // LDS bytes of digits per superchunk: [8 j][16 slots][16]
 constexpr int kPartBytes = kMaxTPWc * 16 * 8;  // [tile][row] int64: Z of the workgroup's rows
 constexpr int kMiscBytes = kW * 4 + kW * 8 + (2 * kMaxTPWc * 16 + 2) * 4;  // wave maxima and sums, row scales
-constexpr int kRing = 4;              // superchunks of signs in flight per wave
+constexpr int kRing = 3;              // superchunks of signs in flight per wave
 
 __host__ __device__ constexpr size_t lds_bytes_for(int SC) {
     return static_cast<size_t>(SC) * kActSC + kPartBytes + kMiscBytes;
@@ -469,12 +469,15 @@ int launch_decode_i8(I8Args &a, int stage, bool bin, void *stream) {
     int maxSC = 1;
     for (int i = 0; i < a.count; ++i) maxSC = std::max(maxSC, a.L[i].SC);
     // vector octets per thread NO = 1, 2, 4, 8 for up to 8, 16, 32, 64
-    // superchunks; two workgroups per CU where LDS and registers allow (NO <= 4)
+    // superchunks
     const int ni = maxSC <= 8 ? 0 : maxSC <= 16 ? 1 : maxSC <= 32 ? 2 : 3;
-    const int slots = kCUs * ((ni <= 2 && 2 * lds_bytes_for(maxSC) <= 160 * 1024) ? 2 : 1);
-    // tiles per workgroup: the fewest (1, 2, 4, 8) with which every
-    // workgroup of the launch is resident at once; the waves of a workgroup
-    // are shared out among its tiles as parts of their reductions
+    // tiles per workgroup: the fewest (1, 2, 4, 8) with which the grid has
+    // one workgroup per CU at most; the waves of a workgroup are shared out
+    // among its tiles as parts of their reductions.  (Every workgroup brings
+    // the whole vector to fixed point, so more, smaller workgroups repeat
+    // that work: measured on the decoder block, one workgroup per CU beats
+    // two, and both beat fewer than one.)
+    const int slots = kCUs;
     // (the grid is rectangular: its shorter rows' padding workgroups hold a
     // slot while they start and leave)
     int tpw = kMaxTPWc;
