@@ -20,13 +20,17 @@
  * sums along k with A, scale by a.  The products with A and B are additions
  * and sign flips; no dense W is formed.
  *
- * Numerics: fp16 in and out, fp32 accumulation, one round-to-nearest-even
- * to fp16 at the end; no flush-to-zero.  The intermediate v = t * mid
- * (batch x k) is an operand of 16-bit matrix-core products: on the decode
- * path at batch 1 it is kept as the sum of two fp16 numbers (about 22
- * significant bits); at decode batch 2..16 and on the prefill path it is
- * rounded once to fp16.  On both it must stay inside the fp16 range
- * (|v| < 65520); the table path keeps it in fp32.
+ * Numerics: fp16 in and out, one round-to-nearest-even to fp16 at the end;
+ * no flush-to-zero.  At batch 1 (layers with m and k_pad up to 32768) each
+ * signed sum is exact: the vector (u = x * b, then v) is brought to 32-bit
+ * fixed point with one power-of-two exponent per workgroup, summed as
+ * integers on the int8 matrix cores, and v = t * mid is kept in fp32; u may
+ * exceed the fp16 range there.  At decode batch 2..16 and on the prefill
+ * path the sums accumulate in fp32 and v is rounded once to fp16, the
+ * operand of 16-bit matrix-core products, so it must stay inside the fp16
+ * range (|v| < 65520); batch 1 on wider layers keeps v as the sum of two
+ * fp16 numbers (about 22 significant bits), and u = x * b as well, so there
+ * |x * b| must stay below 65520 too.
  *
  * Packed sign format (the pages fix none; this is the library's own)
  * ----------------------------------------------------------------------
@@ -71,12 +75,12 @@ typedef enum {
 /* Kernel-path selection for dbf_linear_forward_ex(). */
 typedef enum {
     DBF_PATH_AUTO = 0,         /* batch <= 16: DBF_PATH_DECODE; batch > 16: DBF_PATH_PREFILL */
-    DBF_PATH_DECODE = 1,       /* small-batch kernels: batch as the MFMA N dimension, intermediate
-                                  kept as an fp16 hi+lo pair (batch 1) or rounded once to fp16
-                                  (batch 2..16); batch must be <= 16 */
+    DBF_PATH_DECODE = 1,       /* small-batch kernels: exact int8 matrix-core sums with v in fp32
+                                  (batch 1), batch as the MFMA N dimension with v rounded once to
+                                  fp16 (batch 2..16); batch must be <= 16 */
     DBF_PATH_PREFILL = 2,      /* tiled MFMA products, intermediate rounded once to fp16; any batch */
-    DBF_PATH_DECODE_TABLE = 3  /* vector-ALU signed sums (4-sign lookup tables for batch <= 4, one
-                                  add per sign above), intermediate in fp32; batch must be <= 16 */
+    DBF_PATH_DECODE_TABLE = 3  /* no longer built (it was slower than the matrix cores at every
+                                  measured shape): always DBF_ERR_UNSUPPORTED */
 } dbf_path_t;
 
 typedef struct {
@@ -214,11 +218,11 @@ dbf_status_t dbf_pack_ex(int32_t n, int32_t m, int32_t k,
  * γ[l] = Σ_i t_i (column l of Z_i summed), formed at pack time in double
  * precision and kept in fp32; the per-row sums Σx and γ·x (fp32, one small
  * kernel per forward) enter the output epilogue before its rounding.  The
- * intermediate (batch x p d) follows the DBF path rules (hi+lo pair at
- * decode batch 1, else one fp16 rounding) and must stay in fp16 range.
+ * intermediate (batch x p d) follows the DBF path rules (fp32 from exact
+ * sums at decode batch 1, else one fp16 rounding, in fp16 range).
  * Errors: DBF_ERR_INVALID_ARG (null pointers, sizes < 1, entries not 0/1),
- * DBF_ERR_SHAPE, DBF_ERR_OOM, DBF_ERR_HIP.  The table path, grouped
- * forwards and gradients return DBF_ERR_UNSUPPORTED for such a handle.
+ * DBF_ERR_SHAPE, DBF_ERR_OOM, DBF_ERR_HIP.  Grouped forwards and gradients
+ * return DBF_ERR_UNSUPPORTED for such a handle.
  */
 dbf_status_t dbf_bqq_pack(int32_t n, int32_t m, int32_t d, int32_t p,
                           const uint8_t *Y, const uint8_t *Z,

@@ -39,15 +39,13 @@ def test_library_exports_every_declared_symbol():
     assert set(declared_functions()) <= exported
 
 
-def test_header_compiles_as_c():
+def test_header_compiles_as_c(tmp_path):
     """The header is plain C: it compiles in a C translation unit without HIP headers."""
     src = '#include "dbf.h"\nint main(void){ dbf_info_t i; (void)i; return (int)DBF_OK; }\n'
-    tmp = os.path.join(ROOT, "_work", "hdr_check")
-    os.makedirs(tmp, exist_ok=True)
-    c = os.path.join(tmp, "t.c")
+    c = os.path.join(str(tmp_path), "t.c")
     open(c, "w").write(src)
     res = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
-                          "-c", c, "-o", os.path.join(tmp, "t.o")], capture_output=True, text=True)
+                          "-c", c, "-o", os.path.join(str(tmp_path), "t.o")], capture_output=True, text=True)
     assert res.returncode == 0, res.stderr
 
 
