@@ -622,10 +622,11 @@ __device__ __forceinline__ void stage1_body(int blk, char *base, const uint32_t 
         // completed (the vmcnt wait above, then the barrier); the ticket
         // itself is an agent-scope atomic at the same point.  So a part that
         // draws the last ticket does so after every part's stores are in
-        // memory; this acquire fence then keeps its loads from being served
-        // by lines its own XCD's caches held from before (it invalidates
-        // them), and the loads themselves are agent-scope atomics.
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        // memory, and its reads below are agent-scope atomic loads, served at
+        // that point too -- no line of its own XCD's caches can stand in for
+        // them.  (An acquire fence here would invalidate that XCD's L2 as
+        // well, where this launch has read stage 2's sign words ahead: it
+        // measured 4-8 us slower on the 14336-wide layers at batch 8-16.)
         if (wave == 0 && li < NB) {
 #pragma unroll
             for (int t = 0; t < RT; ++t) {
