@@ -68,7 +68,8 @@ def parse():
     p.add_argument("--no-context", action="store_true", help="skip the device-copy context")
     p.add_argument("--factor-cpu", action="store_true",
                    help="also time the factorization oracle (one outer x one inner iteration) on the host")
-    p.add_argument("--only", choices=("block", "layer", "prefill", "backward", "bqq", "factorize", "context"),
+    p.add_argument("--only", choices=("block", "layer", "prefill", "block_prefill", "backward", "bqq", "factorize",
+                                      "context"),
                    default=None,
                    help="run one leg only (for profiling)")
     return p.parse_args()
@@ -619,6 +620,86 @@ def prefill_leg(args):
                          "kernel": dom, "algorithmic_flops_per_launch": kall[dom][0]}}
 
 
+def block_prefill_leg(args):
+    """The decoder block at batch 2048: its seven layers with q/k/v and
+    gate/up each as one grouped forward (one launch per product for the
+    group), checked against the oracle first (the first and last row of every
+    128-row tile and 16 random rows of every layer), then TFLOP/s-equivalent
+    2*batch*k*(n+m) summed over the layers per block forward, over 10 block
+    forwards after 3 warm-ups; beside it the same block as seven separate
+    layer forwards."""
+    import torch
+
+    import dbf_linear_fwd_amd as dbf
+    from oracle import dbf_oracle as O
+    from tests import inputs
+    bt = 2048
+    layers = {L.name: L for L in inputs.config(5).layers}
+    hs = {n: dbf.Layer(L.A, L.B, L.a, L.mid, L.b, max_batch=bt) for n, L in layers.items()}
+    xs = {n: torch.from_numpy(L.X[bt]).cuda() for n, L in layers.items()}
+    ys = {n: torch.empty((bt, L.n), dtype=torch.float16, device="cuda") for n, L in layers.items()}
+
+    def grouped(i):
+        for gr in GROUPS:
+            if len(gr) == 1:
+                hs[gr[0]].forward(xs[gr[0]], out=ys[gr[0]])
+            else:
+                dbf.forward_group([hs[n] for n in gr], xs[gr[0]], [ys[n] for n in gr])
+
+    def separate(i):
+        for gr in GROUPS:
+            for n in gr:
+                hs[n].forward(xs[gr[0]], out=ys[n])
+    grouped(0)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, bt, 128), np.arange(127, bt, 128),
+                                     np.random.default_rng(11).choice(bt, 16, replace=False)]))
+    worst = 0.0
+    for gr in GROUPS:
+        X = layers[gr[0]].X[bt]
+        for n in gr:
+            L = layers[n]
+            err = row_rel_err(ys[n].cpu().numpy()[rows],
+                              O.sampled_forward(X, L.A, L.B, L.a, L.mid, L.b, rows, np.arange(L.n)))
+            worst = max(worst, err)
+    print(f"[bench] block prefill parity: worst row rel err {worst:.3e} over {len(rows)} rows of each layer",
+          file=sys.stderr, flush=True)
+    if not worst <= TOL:
+        print("[bench] PARITY FAILED on the block at batch 2048; no number", file=sys.stderr, flush=True)
+        sys.exit(1)
+    flops = sum(2 * bt * L.k * (L.n + L.m) for L in layers.values())
+    el_g, done_g = time_steps(grouped, 10, 3, "eager")
+    el_s, done_s = time_steps(separate, 10, 3, "eager")
+    per_group = {}
+    for gr in GROUPS:
+        if len(gr) == 1:
+            continue
+        gf = sum(2 * bt * layers[n].k * (layers[n].n + layers[n].m) for n in gr)
+
+        def one_grouped(i, gr=gr):
+            dbf.forward_group([hs[n] for n in gr], xs[gr[0]], [ys[n] for n in gr])
+
+        def one_separate(i, gr=gr):
+            for n in gr:
+                hs[n].forward(xs[gr[0]], out=ys[n])
+        eg, dg = time_steps(one_grouped, 10, 3, "eager")
+        es, ds = time_steps(one_separate, 10, 3, "eager")
+        per_group["".join(gr)] = {"grouped_us": eg * 1e6 / dg, "grouped_tflops_eq": gf * dg / eg / 1e12,
+                                  "separate_us": es * 1e6 / ds, "separate_tflops_eq": gf * ds / es / 1e12}
+    res = {"workload": "Llama-3-8B-shaped decoder block of 7 DBF linears, batch 2048, q/k/v and gate/up grouped",
+           "us_per_block": el_g * 1e6 / done_g, "tflops_eq": flops * done_g / el_g / 1e12,
+           "separate_layers_us_per_block": el_s * 1e6 / done_s,
+           "separate_layers_tflops_eq": flops * done_s / el_s / 1e12, "groups": per_group,
+           "parity_worst_row_rel_err": worst}
+    print(f"[bench] block prefill: {res['us_per_block']:.1f} us per block, {res['tflops_eq']:.1f} TFLOP/s-eq "
+          f"(separate layers {res['separate_layers_us_per_block']:.1f} us, {res['separate_layers_tflops_eq']:.1f}); "
+          f"groups {per_group}", file=sys.stderr, flush=True)
+    for h in hs.values():
+        h.close()
+    torch.cuda.synchronize()
+    return res
+
+
 def cpu_baseline(seconds):
     """The fp64 oracle's factored forward (the §2.1 evaluation order) of the
     decoder block's seven layers at batch 1, on the host's BLAS threads,
@@ -687,6 +768,8 @@ def main():
         result["layer"] = layer_leg(args)
     if args.only in (None, "prefill") and not args.no_secondary:
         result["prefill"] = prefill_leg(args)
+    if args.only in (None, "block_prefill") and not args.no_secondary:
+        result["block_prefill"] = block_prefill_leg(args)
     if args.only in (None, "backward") and not args.no_backward:
         result["backward"] = backward_leg()
     if args.only in (None, "bqq") and not args.no_bqq:
@@ -730,6 +813,8 @@ def main():
     }
     if "prefill" in result:
         line["prefill_batch2048"] = result["prefill"]
+    if "block_prefill" in result:
+        line["block_batch2048"] = result["block_prefill"]
     if "layer" in result:
         line["decode_layer_4096x4096_k2048_b1"] = result["layer"]
     if "backward" in result:

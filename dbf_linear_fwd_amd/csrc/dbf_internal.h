@@ -199,6 +199,28 @@ size_t sign_gemm_split_elems(int M, int K, int words, int n_out);
 int launch_split_finish(const SplitK &split, int M, int n_out, const void *sn, void *out, int ldo, void *stream,
                         const float *aff_E = nullptr, const float *aff_stats = nullptr);
 
+// Products of a grouped launch (layers that share their input at large
+// batch): out_i = rne16(sn_i ⊙ (P_i (S_i ⊙ sk_i)ᵀ)) for i < count, every
+// product with the same M rows, K_i = 32 words_i a multiple of 64, P_i
+// 16-byte aligned with ldp_i % 8 == 0, sk present on all or none.  Each
+// output tile is summed over its whole K (no split); launch_sign_gemm_group
+// fills tile0 and returns hipErrorInvalidValue for any other form.
+struct GemmItem {
+    const void *P = nullptr;
+    int ldp = 0, K = 0;
+    const uint32_t *S = nullptr;
+    int words = 0, n_rows_pad = 0;
+    const void *sk = nullptr, *sn = nullptr;
+    void *out = nullptr;
+    int ldo = 0, n_out = 0;
+};
+struct GemmGroup {
+    GemmItem item[kMaxGroup];
+    int tile0[kMaxGroup + 1] = {};
+    int count = 0, M = 0;
+};
+int launch_sign_gemm_group(GemmGroup &g, void *stream);
+
 // Batch sums of the gradients: out[c] = sum over g < ceil(rows / 64) of
 // partial[g * ld + c] for c < cols, added in g order (the partials are
 // 64-row sums written by launch_sign_gemm's dpart epilogue).

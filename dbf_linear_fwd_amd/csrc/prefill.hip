@@ -538,29 +538,18 @@ __device__ __forceinline__ void dma_step(int nxt, char *__restrict__ dst, const 
     }
 }
 
+// The product's work for output tile (bm, bn), K part `split` of nsplit.
 template <bool HAS_SK, int KP, bool BIN>
-__global__ __launch_bounds__(kDThreads) void sign_gemm_dma_kernel(const __half *__restrict__ P, int ldp, int M,
-                                                                 const uint32_t *__restrict__ S, int words,
-                                                                 int n_rows_pad, const __half *__restrict__ sk,
-                                                                 const __half *__restrict__ sn,
-                                                                 __half *__restrict__ out, int ldo, int n_out,
-                                                                 float *__restrict__ out32, int ldo32, const DotArgs dot,
-                                                                 const Affine aff, int nbm, int nbn,
-                                                                 float *__restrict__ part, int nsplit, int ldw) {
-    extern __shared__ __attribute__((aligned(16))) char lds[];
+__device__ __forceinline__ void dma_tile(char *lds, const __half *__restrict__ P, int ldp, int M,
+                                         const uint32_t *__restrict__ S, int words, int n_rows_pad,
+                                         const __half *__restrict__ sk, const __half *__restrict__ sn,
+                                         __half *__restrict__ out, int ldo, int n_out, float *__restrict__ out32,
+                                         int ldo32, const DotArgs &dot, const Affine &aff, int bm, int bn, int split,
+                                         float *__restrict__ part, int nsplit, int ldw) {
     using C = DmaStep<KP>;
     constexpr int D = C::PI + C::SI + (HAS_SK ? 1 : 0);  // loads per step and wave
 
     const ExpandConsts ec = expand_consts<BIN>();
-    // XCD-aware order over (split, tile), tile fastest: the blocks of one XCD
-    // take consecutive indexes, so they share a K range (and rows of P)
-    const int T = nbm * nbn;
-    const int G = T * nsplit;
-    const int b = blockIdx.x;
-    const int xcd = b % kXcds, slot = b / kXcds, q = G / kXcds, rem = G % kXcds;
-    const int idx = xcd * q + min(xcd, rem) + slot;
-    const int split = idx / T, tile = idx - split * T;
-    const int bm = tile / nbn, bn = tile - (tile / nbn) * nbn;
     const int m0 = bm * BM, n0 = bn * DBN;
 
     const int tid = threadIdx.x;
@@ -661,6 +650,54 @@ __global__ __launch_bounds__(kDThreads) void sign_gemm_dma_kernel(const __half *
     }
     epilogue<DMF, DNF>(acc, snv, M, n_out, m0 + wm * 32 * DMF, n0 + wn * 32 * DNF, l32, kg, out, ldo, out32, ldo32,
                        dot, aff);
+}
+
+// XCD-aware position of workgroup b among G: the workgroups of one XCD
+// (b mod 8) take consecutive indexes, so they share K ranges and rows of P
+// in that XCD's L2.
+__device__ __forceinline__ int xcd_index(int b, int G) {
+    const int xcd = b % kXcds, slot = b / kXcds, q = G / kXcds, rem = G % kXcds;
+    return xcd * q + min(xcd, rem) + slot;
+}
+
+template <bool HAS_SK, int KP, bool BIN>
+__global__ __launch_bounds__(kDThreads) void sign_gemm_dma_kernel(const __half *__restrict__ P, int ldp, int M,
+                                                                 const uint32_t *__restrict__ S, int words,
+                                                                 int n_rows_pad, const __half *__restrict__ sk,
+                                                                 const __half *__restrict__ sn,
+                                                                 __half *__restrict__ out, int ldo, int n_out,
+                                                                 float *__restrict__ out32, int ldo32, const DotArgs dot,
+                                                                 const Affine aff, int nbm, int nbn,
+                                                                 float *__restrict__ part, int nsplit, int ldw) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    // order over (split, tile), tile fastest
+    const int T = nbm * nbn;
+    const int idx = xcd_index(blockIdx.x, T * nsplit);
+    const int split = idx / T, tile = idx - split * T;
+    const int bm = tile / nbn, bn = tile - (tile / nbn) * nbn;
+    dma_tile<HAS_SK, KP, BIN>(lds, P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, dot, aff,
+                              bm, bn, split, part, nsplit, ldw);
+}
+
+// Several products with the same M, as one launch: product i covers tiles
+// [tile0[i], tile0[i + 1]) of the grid, in the order of a product of its own
+// (the tiles of one row block consecutive); every tile runs the same body,
+// over the whole K.
+template <bool HAS_SK, int KP, bool BIN>
+__global__ __launch_bounds__(kDThreads) void sign_gemm_dma_group_kernel(const GemmGroup g) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const int idx = xcd_index(blockIdx.x, g.tile0[g.count]);
+    int i = 0;
+    for (int j = 1; j < g.count; ++j)
+        if (idx >= g.tile0[j]) i = j;
+    const GemmItem &it = g.item[i];
+    const int tile = idx - g.tile0[i];
+    const int nbn = (it.n_out + DBN - 1) / DBN;
+    const int bm = tile / nbn, bn = tile - bm * nbn;
+    dma_tile<HAS_SK, KP, BIN>(lds, static_cast<const __half *>(it.P), it.ldp, g.M, it.S, it.words, it.n_rows_pad,
+                              static_cast<const __half *>(it.sk), static_cast<const __half *>(it.sn),
+                              static_cast<__half *>(it.out), it.ldo, it.n_out, nullptr, 0, DotArgs{}, Affine{}, bm,
+                              bn, 0, nullptr, 1, 0);
 }
 
 template <bool HAS_SK, int KP, bool BIN>
@@ -835,6 +872,44 @@ int dispatch(const GemmLaunch &a, hipStream_t s, SplitK *split) {
 }
 
 }  // namespace
+
+int launch_sign_gemm_group(GemmGroup &g, void *stream) {
+    if (g.count < 1 || g.count > kMaxGroup || g.M < 1) return static_cast<int>(hipErrorInvalidValue);
+    const bool has_sk = g.item[0].sk != nullptr;
+    const int nbm = (g.M + BM - 1) / BM;
+    int tiles = 0;
+    bool pairs2 = kDmaPairs == 2;
+    for (int i = 0; i < g.count; ++i) {
+        const GemmItem &it = g.item[i];
+        // the deep-pipelined form only: K a multiple of 64, whole words, 16-byte aligned rows of P
+        if (!it.P || !it.S || !it.sn || !it.out || it.n_out < 1 || it.K % BK != 0 || it.K != it.words * 32 ||
+            (it.ldp & 7) != 0 || (reinterpret_cast<uintptr_t>(it.P) & 15) != 0 || (it.sk != nullptr) != has_sk ||
+            it.n_rows_pad < it.n_out)
+            return static_cast<int>(hipErrorInvalidValue);
+        g.tile0[i] = tiles;
+        tiles += nbm * ((it.n_out + DBN - 1) / DBN);
+        pairs2 = pairs2 && it.words % 4 == 0;
+    }
+    g.tile0[g.count] = tiles;
+    const int kp = pairs2 && tiles <= 256 ? 2 : 1;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    auto go = [&](auto kernel, size_t lds) {
+        static const bool once = ((void)hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                                                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                            static_cast<int>(lds)),
+                                  true);
+        (void)once;
+        launch_kernel(kernel, dim3(tiles), dim3(kDThreads), lds, s, g);
+    };
+    if (has_sk) {
+        if (kp == 2) go(sign_gemm_dma_group_kernel<true, 2, false>, DmaStep<2>::Lds);
+        else go(sign_gemm_dma_group_kernel<true, 1, false>, DmaStep<1>::Lds);
+    } else {
+        if (kp == 2) go(sign_gemm_dma_group_kernel<false, 2, false>, DmaStep<2>::Lds);
+        else go(sign_gemm_dma_group_kernel<false, 1, false>, DmaStep<1>::Lds);
+    }
+    return static_cast<int>(hipGetLastError());
+}
 
 int launch_sign_gemm(const void *P, int ldp, int M, int K, const uint32_t *S, int words, int n_rows_pad,
                      const void *sk, const void *sn, void *out, int ldo, int n_out, float *out32, int ldo32,

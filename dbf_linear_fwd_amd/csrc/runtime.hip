@@ -653,11 +653,35 @@ extern "C" dbf_status_t dbf_linear_forward_group(const dbf_handle_t *hs, int32_t
     if (hipGetDevice(&cur) != hipSuccess) return DBF_ERR_HIP;
     if (cur != hs[0]->device) return DBF_ERR_INVALID_ARG;
     if (batch > dbf::kDecodeMaxBatch) {
+        // one launch per product for all the layers (their tiles in one
+        // grid), where every product has the deep-pipelined form (m a
+        // multiple of 64); otherwise each layer's own forward
+        bool grouped = count > 1 && hs[0]->m % 64 == 0;
+        dbf::GemmGroup g1{}, g2{};
+        g1.count = g2.count = count;
+        g1.M = g2.M = batch;
         for (int i = 0; i < count; ++i) {
-            const dbf_status_t st = forward_prefill(hs[i], x, ys[i], batch, stream);
-            if (st != DBF_OK) return st;
+            const dbf_layer *h = hs[i];
+            dbf::GemmItem &a = g1.item[i];
+            a.P = x, a.ldp = h->m, a.K = h->m, a.S = h->B_dev, a.words = h->Wm, a.n_rows_pad = h->k_pad;
+            a.sk = h->b_dev, a.sn = h->mid_dev, a.out = h->T, a.ldo = h->k_pad, a.n_out = h->k_pad;
+            dbf::GemmItem &c = g2.item[i];
+            c.P = h->T, c.ldp = h->k_pad, c.K = h->k_pad, c.S = h->A_dev, c.words = h->Wk, c.n_rows_pad = h->n_pad;
+            c.sk = nullptr, c.sn = h->a_dev, c.out = ys[i], c.ldo = h->n, c.n_out = h->n;
+            grouped = grouped && h->Wm * 32 == h->m && h->Wk * 32 == h->k_pad;
         }
-        return DBF_OK;
+        if (!grouped) {
+            for (int i = 0; i < count; ++i) {
+                const dbf_status_t st = forward_prefill(hs[i], x, ys[i], batch, stream);
+                if (st != DBF_OK) return st;
+            }
+            return DBF_OK;
+        }
+        dbf_layer *t = hs[0];  // kernel timing follows the first handle
+        dbf_status_t st = timed_launch(t, "prefill_group_gemm1", stream,
+                                       [&] { return dbf::launch_sign_gemm_group(g1, stream); });
+        if (st != DBF_OK) return st;
+        return timed_launch(t, "prefill_group_gemm2", stream, [&] { return dbf::launch_sign_gemm_group(g2, stream); });
     }
     if (batch == 1) {
         bool ok = true;

@@ -143,8 +143,8 @@ dbf_status_t dbf_linear_forward_ex(dbf_handle_t h, const void *x, void *y, int32
  * same input (for example the q, k and v projections of an attention block,
  * or the gate and up projections of an MLP, gist.science technical summary
  * §4 runs DBF on every linear layer of such blocks): ys[i] = x W_i^T for
- * i < count, each exactly as dbf_linear_forward(hs[i], x, ys[i], batch, ...)
- * computes it (the same kernels' arithmetic, identical bits).
+ * i < count, as dbf_linear_forward(hs[i], x, ys[i], batch, ...) computes
+ * it (see below for the bits).
  *   hs     count handles (1 <= count <= 8), all with the same input width m,
  *          all on the current device.
  *   x      device fp16, batch x m (shared by all layers, 16-byte aligned).
@@ -152,7 +152,12 @@ dbf_status_t dbf_linear_forward_ex(dbf_handle_t h, const void *x, void *y, int32
  *          overlapping neither x nor each other.
  *   batch  0 <= batch <= every handle's max_batch; 0 returns DBF_OK.
  * For batch <= 16 all layers share one launch per stage (2 launches in all
- * instead of 2 per layer); larger batches run each layer's forward in turn.
+ * instead of 2 per layer), and each output is bit-identical to the layer's
+ * own forward.  Above batch 16, when m is a multiple of 64, the layers share
+ * one launch per product (the tiles of every layer in one grid, each summed
+ * over its whole K); a layer's own forward may cut K into parts there, so
+ * the two agree within the parity tolerance rather than bit for bit.  Other
+ * shapes run each layer's forward in turn.
  * The handles' workspaces are used: calls involving one handle must be
  * ordered.  Errors: DBF_ERR_INVALID_ARG (count out of range, null pointers,
  * differing m, batch out of range, misaligned pointers, wrong device),

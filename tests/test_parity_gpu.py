@@ -645,14 +645,18 @@ GROUPS = [
     (1100, [(257, 100), (64, 1500)]),
     (96, [(64, 64)]),
     (4096, [(4096, 2688), (1024, 1216), (1024, 1536)]),   # attention q/k/v shapes
+    (640, [(130, 190), (64, 64), (300, 1000)]),          # m % 64 == 0: grouped products above batch 16
 ]
 
 
 @pytest.mark.parametrize("gi", range(len(GROUPS)))
-@pytest.mark.parametrize("batch", [1, 3, 9, 16, 40])
+@pytest.mark.parametrize("batch", [1, 3, 9, 16, 40, 2048])
 def test_group_forward_equals_single_layers(gpu, gi, batch):
     """One launch per stage for layers sharing x gives each layer's own
-    forward bit for bit (same kernel arithmetic), and the oracle's values."""
+    forward bit for bit at decode batches (same kernel arithmetic) and the
+    oracle's values at every batch.  Above batch 16 the grouped products sum
+    each output over its whole K, where a layer's own product may cut K into
+    parts: equal within the parity tolerance there."""
     torch = _torch()
     m, dims = GROUPS[gi]
     _say(f"group m={m} layers={dims} batch={batch}")
@@ -676,12 +680,16 @@ def test_group_forward_equals_single_layers(gpu, gi, batch):
         for j, (H, y) in enumerate(zip(hs, ys)):
             single = H.forward(x).cpu().numpy()
             got = y.cpu().numpy()
-            assert np.array_equal(got.view(np.uint16), single.view(np.uint16)), f"layer {j}"
+            if batch <= 16:
+                assert np.array_equal(got.view(np.uint16), single.view(np.uint16)), f"layer {j}"
+            else:
+                d = np.abs(got.astype(np.float64) - single.astype(np.float64)).max(axis=1)
+                assert np.all(d <= TOL * np.abs(single.astype(np.float64)).max(axis=1)), f"layer {j} vs own forward"
             A, B, a, mid, b = layers[j]
-            if A.shape[0] * m * A.shape[1] <= 1 << 26:
+            if A.shape[0] * m * A.shape[1] * batch <= 1 << 30:
                 assert_tol(got, O.dense_forward(X, A, B, a, mid, b), f"group layer {j}")
             else:
-                rows = np.arange(min(batch, 3))
+                rows = np.arange(min(batch, 3)) if batch <= 16 else tile_rows(batch, 5 + j)
                 ref = O.sampled_forward(X, A, B, a, mid, b, rows, np.arange(A.shape[0]))
                 assert_tol(got[rows], ref, f"group layer {j} (sampled rows)")
     finally:
