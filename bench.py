@@ -112,6 +112,27 @@ def time_steps(fwd, steps, warmup, mode):
     return e0.elapsed_time(e1) / 1e3, steps
 
 
+def time_median(fwd, groups=5, per=10, warmup=20):
+    """Eager steady state: `warmup` untimed steps (the clocks ramp up after an
+    idle spell such as a CPU parity check), then `groups` timed groups of
+    `per` steps; returns (seconds of the median group, per)."""
+    import torch
+    for i in range(warmup):
+        fwd(i)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(groups):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(per):
+            fwd(i)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) / 1e3)
+    ts.sort()
+    return ts[len(ts) // 2], per
+
+
 def kernel_times(layers, fwd, steps):
     """Per-kernel average event time (ms) over `steps` eager steps."""
     import dbf_linear_fwd_amd as dbf
@@ -564,7 +585,8 @@ def prefill_leg(args):
     (4096x14336) projections, k = 4800: outputs checked against the oracle
     first (the first and last row of every 128-row tile and 16 random rows,
     every output of each), then TFLOP/s-equivalent 2*batch*k*(n+m) per
-    forward over 20 forwards after 5 warm-ups, and the kernels' launch times."""
+    forward (the median of 5 groups of 10 forwards after 20 warm-ups), and
+    the kernels' launch times."""
     import torch
 
     import dbf_linear_fwd_amd as dbf
@@ -594,7 +616,7 @@ def prefill_leg(args):
 
         def pf(i):
             L.forward(x, out=y)
-        el, done = time_steps(pf, 20, 5, "eager")
+        el, done = time_median(pf)
         flops = 2 * bt * layer.k * (layer.n + layer.m)
         kt = kernel_times([L], pf, 10)
         kf = prefill_kernel_flops(layer, bt)
@@ -625,9 +647,9 @@ def block_prefill_leg(args):
     gate/up each as one grouped forward (one launch per product for the
     group), checked against the oracle first (the first and last row of every
     128-row tile and 16 random rows of every layer), then TFLOP/s-equivalent
-    2*batch*k*(n+m) summed over the layers per block forward, over 10 block
-    forwards after 3 warm-ups; beside it the same block as seven separate
-    layer forwards."""
+    2*batch*k*(n+m) summed over the layers per block forward (the median of 5
+    groups of 4 block forwards after 6 warm-ups); beside it the same block as
+    seven separate layer forwards, and each group alone both ways."""
     import torch
 
     import dbf_linear_fwd_amd as dbf
@@ -668,8 +690,8 @@ def block_prefill_leg(args):
         print("[bench] PARITY FAILED on the block at batch 2048; no number", file=sys.stderr, flush=True)
         sys.exit(1)
     flops = sum(2 * bt * L.k * (L.n + L.m) for L in layers.values())
-    el_g, done_g = time_steps(grouped, 10, 3, "eager")
-    el_s, done_s = time_steps(separate, 10, 3, "eager")
+    el_g, done_g = time_median(grouped, per=4, warmup=6)
+    el_s, done_s = time_median(separate, per=4, warmup=6)
     per_group = {}
     for gr in GROUPS:
         if len(gr) == 1:
@@ -682,8 +704,8 @@ def block_prefill_leg(args):
         def one_separate(i, gr=gr):
             for n in gr:
                 hs[n].forward(xs[gr[0]], out=ys[n])
-        eg, dg = time_steps(one_grouped, 10, 3, "eager")
-        es, ds = time_steps(one_separate, 10, 3, "eager")
+        eg, dg = time_median(one_grouped, warmup=10)
+        es, ds = time_median(one_separate, warmup=10)
         per_group["".join(gr)] = {"grouped_us": eg * 1e6 / dg, "grouped_tflops_eq": gf * dg / eg / 1e12,
                                   "separate_us": es * 1e6 / ds, "separate_tflops_eq": gf * ds / es / 1e12}
     res = {"workload": "Llama-3-8B-shaped decoder block of 7 DBF linears, batch 2048, q/k/v and gate/up grouped",
