@@ -259,3 +259,65 @@ def bqq_layer(name: str, n: int, m: int, d: int, p: int, seed, batches: Sequence
         u = np.float16(d * rho.sum() * (1.0 + e_u))
         X = {bt: random_x(rng, bt, m) for bt in batches}
     return BqqLayer(name, n, m, d, p, Y, Z, r, s, t, u, X)
+
+
+@dataclasses.dataclass
+class BqqGroupedLayer:
+    name: str
+    n: int                      # output features
+    m: int                      # input features
+    d: int                      # inner dimension of each binary product
+    p: int                      # number of binary products
+    group: int                  # input columns per scaling group (the last may be shorter)
+    Y: np.ndarray               # uint8 (p, n, d), entries 0/1
+    Z: np.ndarray               # uint8 (p, d, m), entries 0/1
+    r: np.ndarray               # float16 (p, ngroups)
+    s: np.ndarray               # float16 (p, ngroups)
+    t: np.ndarray               # float16 (p, ngroups)
+    u: np.ndarray               # float16 (ngroups,)
+    X: Dict[int, np.ndarray]    # batch -> float16 (batch, m)
+
+    @property
+    def ngroups(self) -> int:
+        return -(-self.m // self.group)
+
+    @property
+    def bit_bytes(self) -> int:
+        return self.p * self.d * (self.n + self.m) // 8
+
+
+def bqq_grouped_layer(name: str, n: int, m: int, d: int, p: int, group: int, seed, batches: Sequence[int],
+                      sigma: float = 0.02, jitter: float = 0.05, integer: bool = False) -> BqqGroupedLayer:
+    """A seeded BQQ-form layer with group-wise scalars (ngroups = ceil(m /
+    group) groups of input columns).
+
+    Draw order with one ``Generator(PCG64(seed))``: Y bits (p, n, d), Z bits
+    (p, d, m), then rho ~ U[0.5, 1.5] * sigma / sqrt(d) of shape (p,
+    ngroups), the jitters e_s, e_t (p, ngroups) and e_u (ngroups,) ~
+    U[-jitter, jitter], then X per batch.  Per group the scalars follow
+    ``bqq_layer``: r = 4 rho, s = -2 rho (1 + e_s), t = -2 rho (1 + e_t),
+    u = d * sum_i rho (1 + e_u), rounded to fp16, so each group's columns are
+    centred with entries of size sigma.  ``integer=True`` draws r, s, t from
+    {-2, -1, 1, 2}, u from {-4, ..., 4} and X from {-1, 0, 1}.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ng = -(-m // group)
+    Y = rng.integers(0, 2, size=(p, n, d), dtype=np.uint8)
+    Z = rng.integers(0, 2, size=(p, d, m), dtype=np.uint8)
+    if integer:
+        r = rng.choice([-2.0, -1.0, 1.0, 2.0], size=(p, ng)).astype(np.float16)
+        s = rng.choice([-2.0, -1.0, 1.0, 2.0], size=(p, ng)).astype(np.float16)
+        t = rng.choice([-2.0, -1.0, 1.0, 2.0], size=(p, ng)).astype(np.float16)
+        u = rng.integers(-4, 5, size=ng).astype(np.float16)
+        X = {bt: integer_x(rng, bt, m) for bt in batches}
+    else:
+        rho = rng.uniform(0.5, 1.5, size=(p, ng)) * sigma / math.sqrt(d)
+        e_s = rng.uniform(-jitter, jitter, size=(p, ng))
+        e_t = rng.uniform(-jitter, jitter, size=(p, ng))
+        e_u = rng.uniform(-jitter, jitter, size=ng)
+        r = (4.0 * rho).astype(np.float16)
+        s = (-2.0 * rho * (1.0 + e_s)).astype(np.float16)
+        t = (-2.0 * rho * (1.0 + e_t)).astype(np.float16)
+        u = (d * rho.sum(axis=0) * (1.0 + e_u)).astype(np.float16)
+        X = {bt: random_x(rng, bt, m) for bt in batches}
+    return BqqGroupedLayer(name, n, m, d, p, group, Y, Z, r, s, t, u, X)

@@ -173,3 +173,129 @@ def test_synthetic_layer_is_centred():
     W = Q.bqq_weight(L.Y, L.Z, L.r, L.s, L.t, L.u)
     assert abs(W.mean()) < 0.1 * W.std()
     assert 0.005 < W.std() < 0.08
+
+
+# --------------------------------------------------------------------------- group-wise scaling
+
+def _random_grouped(seed, p, n, d, m, group, batch):
+    rng = np.random.default_rng(seed)
+    ng = -(-m // group)
+    Y = rng.integers(0, 2, size=(p, n, d), dtype=np.uint8)
+    Z = rng.integers(0, 2, size=(p, d, m), dtype=np.uint8)
+    r, s, t = (_f16(rng.uniform(-2, 2, size=(p, ng))) for _ in range(3))
+    u = _f16(rng.uniform(-2, 2, size=ng))
+    X = _f16(rng.uniform(-3, 3, size=(batch, m)))
+    return X, Y, Z, r, s, t, u
+
+
+def _grouped_pin_failures(weight_fn):
+    """Run every pin of the group-wise form with `weight_fn(Y, Z, r, s, t, u,
+    group)` as the weight builder; return the names of the pins that fail."""
+    bad = []
+
+    def fwd(X, Y, Z, r, s, t, u, g):
+        return np.asarray(X, dtype=np.float64) @ weight_fn(Y, Z, r, s, t, u, g).T
+
+    # exact rational brute force; ragged last groups (m not a multiple of group)
+    for seed, (p, n, d, m, g) in enumerate([(1, 3, 3, 4, 2), (2, 4, 3, 5, 2), (2, 3, 4, 7, 3), (3, 2, 2, 5, 4)]):
+        X, Y, Z, r, s, t, u = _random_grouped(100 + seed, p, n, d, m, g, 2)
+        want = np.array([[float(v) for v in row] for row in Q.brute_force_grouped(X, Y, Z, r, s, t, u, g)])
+        if not np.allclose(fwd(X, Y, Z, r, s, t, u, g), want, rtol=1e-12, atol=1e-12):
+            bad.append(f"grouped brute force {seed}")
+
+    # hand-worked, two groups of two columns, p = 1:
+    #   Y = [[1,0],[1,1]], Z = [[0,1,1,0],[1,1,0,1]]
+    #   Y Z = [[0,1,1,0],[1,2,1,1]], rows of Y summed [1, 2], columns of Z summed [1, 2, 1, 1]
+    #   group 0 (columns 0, 1): r = 2, s = 1, t = -1, u = 0.5
+    #   group 1 (columns 2, 3): r = -1, s = 0.5, t = 2, u = -1
+    #   W = [[0.5, 1.5, 0.5, 1.5], [3.5, 4.5, 1.0, 1.0]];  x = [1, -2, 2, 1] -> y = [0, -2.5]
+    Y = np.array([[[1, 0], [1, 1]]], dtype=np.uint8)
+    Z = np.array([[[0, 1, 1, 0], [1, 1, 0, 1]]], dtype=np.uint8)
+    r, s, t = _f16([[2.0, -1.0]]), _f16([[1.0, 0.5]]), _f16([[-1.0, 2.0]])
+    u = _f16([0.5, -1.0])
+    if not np.array_equal(weight_fn(Y, Z, r, s, t, u, 2), np.array([[0.5, 1.5, 0.5, 1.5], [3.5, 4.5, 1.0, 1.0]])):
+        bad.append("grouped hand-worked W")
+    if not np.array_equal(fwd(_f16([[1.0, -2.0, 2.0, 1.0]]), Y, Z, r, s, t, u, 2), np.array([[0.0, -2.5]])):
+        bad.append("grouped hand-worked y")
+
+    # the layer is the sum over column blocks of single-group layers, each
+    # on its block of the input (single-group form: pinned above)
+    p, n, d, m, g = 2, 5, 6, 11, 4
+    X, Y, Z, r, s, t, u = _random_grouped(7, p, n, d, m, g, 3)
+    want = np.zeros((3, n))
+    for h, c0 in enumerate(range(0, m, g)):
+        c1 = min(m, c0 + g)
+        want += Q.bqq_forward(X[:, c0:c1], Y, Z[:, :, c0:c1], r[:, h], s[:, h], t[:, h], u[h])
+    if not np.allclose(fwd(X, Y, Z, r, s, t, u, g), want, rtol=1e-12, atol=1e-12):
+        bad.append("sum of column blocks")
+
+    # the same scalars in every group: the single-group form
+    X, Y, Z, r, s, t, u = _random_case(8, 2, 4, 5, 9, 2)
+    rg, sg, tg = (np.repeat(v[:, None], 3, axis=1) for v in (r, s, t))
+    if not np.allclose(fwd(X, Y, Z, rg, sg, tg, np.repeat(u, 3), 4), Q.bqq_forward(X, Y, Z, r, s, t, u),
+                       rtol=1e-12, atol=1e-12):
+        bad.append("equal groups")
+    return bad
+
+
+def test_grouped_oracle_meets_every_pin():
+    assert _grouped_pin_failures(Q.bqq_weight_grouped) == []
+
+
+def test_group_columns():
+    assert Q.group_columns(10, 4) == [(0, 4), (4, 8), (8, 10)]
+    assert Q.group_columns(8, 8) == [(0, 8)]
+    assert Q.group_columns(3, 5) == [(0, 3)]
+
+
+def _grouped_mutant(kind):
+    def weight(Y, Z, r, s, t, u, group):
+        Y = np.asarray(Y, dtype=np.float64)
+        Z = np.asarray(Z, dtype=np.float64)
+        p, n, d = Y.shape
+        m = Z.shape[2]
+        W = np.zeros((n, m))
+        for l in range(m):
+            h = l // group
+            if kind == "group_off_by_one":
+                h = min((l + 1) // group, r.shape[1] - 1)
+            hs = 0 if kind == "s_first_group" else h
+            W[:, l] = float(u[h])
+            for i in range(p):
+                ri = float(r[i, h])
+                if kind == "r_by_row":
+                    ri = float(r[i, min(i, r.shape[1] - 1)])
+                W[:, l] += ri * (Y[i] @ Z[i][:, l]) + float(s[i, hs]) * Y[i].sum(axis=1) + float(t[i, h]) * Z[i][:, l].sum()
+        return W
+    return weight
+
+
+@pytest.mark.parametrize("kind", ["group_off_by_one", "s_first_group", "r_by_row"])
+def test_grouped_pins_catch_plausible_mistakes(kind):
+    assert _grouped_pin_failures(_grouped_mutant(kind)) != [], f"mutant {kind} passed every pin"
+
+
+def test_grouped_mutant_control():
+    """The mutant builder with no mutation meets every pin (so the pins test
+    the mutations, not the builder)."""
+    assert _grouped_pin_failures(_grouped_mutant("none")) == []
+
+
+def test_grouped_synthetic_layer_is_centred_per_group():
+    """With zero jitter every group's columns are ±1 products scaled by that
+    group's rho: zero-mean entries of size about sigma in each group."""
+    L = inputs.bqq_grouped_layer("g", 64, 96, 128, 2, 32, 5, (1,), sigma=0.02, jitter=0.0)
+    W = Q.bqq_weight_grouped(L.Y, L.Z, L.r, L.s, L.t, L.u, L.group)
+    for c0, c1 in Q.group_columns(L.m, L.group):
+        Wg = W[:, c0:c1]
+        assert abs(Wg.mean()) < 0.15 * Wg.std()
+        assert 0.005 < Wg.std() < 0.08
+
+
+def test_grouped_integer_layer_values_are_exact_in_fp64():
+    L = inputs.bqq_grouped_layer("gi", 5, 11, 4, 2, 4, 9, (2,), integer=True)
+    X = L.X[2]
+    got = Q.bqq_forward_grouped(X, L.Y, L.Z, L.r, L.s, L.t, L.u, L.group)
+    want = np.array([[float(v) for v in row] for row in Q.brute_force_grouped(X, L.Y, L.Z, L.r, L.s, L.t, L.u,
+                                                                              L.group)])
+    assert np.array_equal(got, want)
