@@ -30,7 +30,7 @@ __all__ = [
     "dbf_layout_words_dec",
     "dbf_timing_enable", "dbf_timing_read", "Layer", "dbf_linear_forward_group", "forward_group",
     "dbf_pack_ex", "dbf_linear_backward_data", "dbf_linear_backward", "DBF_PACK_BACKWARD", "dbf_bqq_pack",
-    "dbf_factorize", "factorize", "dbf_linear_forward_noalloc",
+    "dbf_factorize", "factorize", "dbf_linear_forward_noalloc", "dbf_bqq_pack_grouped",
 ]
 
 DBF_OK = 0
@@ -54,6 +54,7 @@ EXPORTED_SYMBOLS = (
     "dbf_linear_backward_data", "dbf_linear_backward", "dbf_free", "dbf_get_info", "dbf_status_string",
     "dbf_pack_signs", "dbf_layout_signs", "dbf_layout_words", "dbf_layout_signs_dec", "dbf_layout_words_dec",
     "dbf_timing_enable", "dbf_timing_read", "dbf_bqq_pack", "dbf_factorize", "dbf_linear_forward_noalloc",
+    "dbf_bqq_pack_grouped",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -108,6 +109,8 @@ def lib() -> ctypes.CDLL:
     L.dbf_pack_ex.restype = ctypes.c_int
     L.dbf_bqq_pack.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, ctypes.c_uint16, i32, ctypes.POINTER(vp)]
     L.dbf_bqq_pack.restype = ctypes.c_int
+    L.dbf_bqq_pack_grouped.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32, ctypes.POINTER(vp)]
+    L.dbf_bqq_pack_grouped.restype = ctypes.c_int
     L.dbf_factorize.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, ctypes.c_float, i32, i32, i32,
                                 vp, vp, vp, vp, vp, vp, vp]
     L.dbf_factorize.restype = ctypes.c_int
@@ -199,6 +202,26 @@ def dbf_bqq_pack(n: int, m: int, d: int, p: int, Y, Z, r, s, t, u, max_batch: in
     h = ctypes.c_void_p()
     _check(lib().dbf_bqq_pack(n, m, d, p, _ptr(Y8), _ptr(Z8), _ptr(r16), _ptr(s16), _ptr(t16), u16, max_batch,
                               ctypes.byref(h)), "dbf_bqq_pack")
+    return h.value
+
+
+def dbf_bqq_pack_grouped(n: int, m: int, d: int, p: int, group: int, Y, Z, r, s, t, u, max_batch: int) -> int:
+    """Handle of a BQQ-form layer with group-wise scalars (see dbf_bqq_pack_grouped in
+    include/dbf.h): Y (p, n, d) and Z (p, d, m) of 0/1, fp16 r, s, t (p, ngroups) and u
+    (ngroups,), ngroups = ceil(m / group)."""
+    Y8 = np.ascontiguousarray(np.asarray(Y), dtype=np.uint8)
+    Z8 = np.ascontiguousarray(np.asarray(Z), dtype=np.uint8)
+    if Y8.size != p * n * d or Z8.size != p * d * m:
+        raise ValueError("Y must hold p*n*d and Z p*d*m entries")
+    if group < 1:
+        raise ValueError("group must be positive")
+    ng = -(-m // group)
+    r16, s16, t16, u16 = _as_half_bits(r), _as_half_bits(s), _as_half_bits(t), _as_half_bits(u)
+    if r16.size != p * ng or s16.size != p * ng or t16.size != p * ng or u16.size != ng:
+        raise ValueError(f"r, s, t must have p * ngroups = {p * ng} entries and u ngroups = {ng}")
+    h = ctypes.c_void_p()
+    _check(lib().dbf_bqq_pack_grouped(n, m, d, p, group, _ptr(Y8), _ptr(Z8), _ptr(r16), _ptr(s16), _ptr(t16),
+                                      _ptr(u16), max_batch, ctypes.byref(h)), "dbf_bqq_pack_grouped")
     return h.value
 
 
@@ -391,6 +414,22 @@ class Layer:
         self.k = p * d
         self.max_batch = int(max_batch)
         self.handle = dbf_bqq_pack(self.n, self.m, d, p, Y, Z, r, s, t, u, self.max_batch)
+        return self
+
+    @classmethod
+    def bqq_grouped(cls, Y, Z, r, s, t, u, group: int, max_batch: int = 2048) -> "Layer":
+        """A BQQ-form layer whose scalars r, s, t (p, ngroups) and u (ngroups,) change from one
+        group of `group` input columns to the next; forward only."""
+        Y = np.asarray(Y)
+        Z = np.asarray(Z)
+        if Y.ndim != 3 or Z.ndim != 3 or Y.shape[0] != Z.shape[0] or Y.shape[2] != Z.shape[1]:
+            raise ValueError("Y must be (p, n, d) and Z (p, d, m)")
+        self = cls.__new__(cls)
+        p, self.n, d = Y.shape
+        self.m = Z.shape[2]
+        self.k = p * d
+        self.max_batch = int(max_batch)
+        self.handle = dbf_bqq_pack_grouped(self.n, self.m, d, p, int(group), Y, Z, r, s, t, u, self.max_batch)
         return self
 
     def info(self) -> Dict[str, int]:

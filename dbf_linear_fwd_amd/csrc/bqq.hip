@@ -9,7 +9,9 @@
 // reduce, for an input row x, to E[o] * Σ_l x_l + Σ_l γ_l x_l with
 // E[o] = Σ_i s_i (row o of Y_i summed) + u and γ_l = Σ_i t_i (column l of
 // Z_i summed), both fixed at pack time.  This kernel forms the two sums per
-// row; the products' epilogue adds the term before the one rounding.
+// row; the products' epilogue adds the term before the one rounding.  With
+// group-wise scalars the term has rank p + 1 (Σ_i R_i[o] σ_i + κ, runtime.hip)
+// and the second kernel forms its p + 1 weighted sums per row.
 
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
@@ -32,7 +34,29 @@ __global__ __launch_bounds__(kStatThreads) void bqq_rowstats_kernel(const __half
     bqq_rowstats_row<kStatThreads>(x + static_cast<size_t>(r) * m, m, gamma, stats + 2 * r, sh);
 }
 
+// Group-wise form, one workgroup per row of x: stats[r * Q + q] = Σ_l
+// w[q * m + l] x[r][l], two statistics per pass over the row.
+__global__ __launch_bounds__(kStatThreads) void bqq_rowstats_q_kernel(const __half *__restrict__ x, int m,
+                                                                      const float *__restrict__ w, int Q,
+                                                                      float *__restrict__ stats) {
+    __shared__ float sh[2 * kStatThreads];
+    const int r = blockIdx.x;
+    const __half *xr = x + static_cast<size_t>(r) * m;
+    for (int q = 0; q < Q; q += 2)
+        bqq_rowstats_dot2<kStatThreads>(xr, m, w + static_cast<size_t>(q) * m,
+                                        q + 1 < Q ? w + static_cast<size_t>(q + 1) * m : nullptr,
+                                        stats + static_cast<size_t>(r) * Q + q, sh);
+}
+
 }  // namespace
+
+int launch_bqq_rowstats_q(const void *x, int batch, int m, const float *w, int Q, float *stats, void *stream) {
+    if (Q < 1 || Q > kMaxStatQ) return static_cast<int>(hipErrorInvalidValue);
+    if (batch <= 0) return 0;
+    launch_kernel(bqq_rowstats_q_kernel, dim3(batch), dim3(kStatThreads), 0, static_cast<hipStream_t>(stream),
+                  static_cast<const __half *>(x), m, w, Q, stats);
+    return static_cast<int>(hipGetLastError());
+}
 
 int launch_bqq_rowstats(const void *x, int batch, int m, const float *gamma, float *stats, void *stream) {
     if (batch <= 0) return 0;

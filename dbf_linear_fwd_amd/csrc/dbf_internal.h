@@ -48,7 +48,7 @@ struct I8Layer {
     const __half *bsc = nullptr;
     const __half *osc = nullptr;
     void *out = nullptr;
-    const float *aff_E = nullptr;      // stage 2 of a 0/1 layer: y += E[row] * stats[0] + stats[1]
+    const float *aff_E = nullptr;      // stage 2 of a 0/1 layer: y += E[row] * stats[0] + stats[1] (I8Args::aff_Q)
     const float *aff_stats = nullptr;
     int rows = 0, K = 0;
     int SC = 0, wlast = 0;             // superchunks; words per lane of the last one (1..4)
@@ -70,7 +70,12 @@ struct I8Args {
     const float *gamma = nullptr;
     float *stats = nullptr;
     int stat_wg = -1;
+    // stage 2 of a 0/1 layer: the affine term's rank, y += Σ_{q < aff_Q - 1}
+    // aff_E[q * rows + row] * aff_stats[q] + aff_stats[aff_Q - 1]
+    // (2 <= aff_Q <= kI8MaxQ; the same for every layer of the launch)
+    int aff_Q = 2;
 };
+constexpr int kI8MaxQ = 9;
 // stage = 1 or 2; bin: 0/1 matrices (Z instead of U - 2 Z, times 2).
 int launch_decode_i8(I8Args &a, int stage, bool bin, void *stream);
 
@@ -180,12 +185,14 @@ struct SplitK {
 };
 //   flavor (may be null): binary = S holds a 0/1 matrix (bit 1 = 1), the
 //   operand is then {0, 2} (callers fold the 2 into sn) and sk must be null;
-//   aff_E / aff_stats: out[i][c] = rne16(sn[c] * sum + aff_E[c] *
-//   aff_stats[2i] + aff_stats[2i + 1]).
+//   aff_E / aff_stats: out[i][c] = rne16(sn[c] * sum + term(i, c)) with
+//   term(i, c) = Σ_{q < Q-1} aff_E[q * aff_ldE + c] * aff_stats[i * Q + q]
+//   + aff_stats[i * Q + Q - 1] (fp32, q in order; Q = aff_Q).
 struct GemmFlavor {
     int binary = 0;
     const float *aff_E = nullptr;
     const float *aff_stats = nullptr;
+    int aff_Q = 2, aff_ldE = 0;
 };
 int launch_sign_gemm(const void *P, int ldp, int M, int K, const uint32_t *S, int words, int n_rows_pad,
                      const void *sk, const void *sn, void *out, int ldo, int n_out, float *out32, int ldo32,
@@ -195,9 +202,10 @@ int launch_sign_gemm(const void *P, int ldp, int M, int K, const uint32_t *S, in
 // product (0: it would not split), assuming 16-byte aligned rows of P.
 size_t sign_gemm_split_elems(int M, int K, int words, int n_out);
 // out[i][c] = rne16(sn[c] * (ws[0][i][c - col0] + ws[1][i][c - col0] + ...)
-//                  [+ aff_E[c] * aff_stats[2i] + aff_stats[2i + 1]]), i < M, split.col0 <= c < n_out.
+//                  [+ term(i, c) of GemmFlavor's affine form]), i < M, split.col0 <= c < n_out.
 int launch_split_finish(const SplitK &split, int M, int n_out, const void *sn, void *out, int ldo, void *stream,
-                        const float *aff_E = nullptr, const float *aff_stats = nullptr);
+                        const float *aff_E = nullptr, const float *aff_stats = nullptr, int aff_Q = 2,
+                        int aff_ldE = 0);
 
 // Products of a grouped launch (layers that share their input at large
 // batch): out_i = rne16(sn_i ⊙ (P_i (S_i ⊙ sk_i)ᵀ)) for i < count, every
@@ -230,6 +238,10 @@ int launch_colsum_finish(const float *partial, int ld, int rows, int cols, float
 // BQQ-form layers: stats[2r] = sum of row r of x (fp16, batch x m), stats[2r + 1]
 // = Σ_l gamma[l] x[r][l]; fp32, fixed summation order.
 int launch_bqq_rowstats(const void *x, int batch, int m, const float *gamma, float *stats, void *stream);
+// Group-wise BQQ form: stats[r * Q + q] = Σ_l w[q * m + l] x[r][l] for q < Q
+// (Q <= kMaxStatQ); fp32, fixed summation order.
+constexpr int kMaxStatQ = 9;
+int launch_bqq_rowstats_q(const void *x, int batch, int m, const float *w, int Q, float *stats, void *stream);
 
 }  // namespace dbf
 

@@ -67,7 +67,8 @@ constexpr int kCUs = 256;             // MI355X
 constexpr int kMaxTPWc = 8;           // tiles per workgroup, at most
 constexpr int kActSC = 2048;          // LDS bytes of digits per superchunk: [8 j][16 slots][16]
 constexpr int kPartBytes = kMaxTPWc * 16 * 8;  // [tile][row] int64: Z of the workgroup's rows
-constexpr int kMiscBytes = kW * 4 + kW * 8 + (2 * kMaxTPWc * 16 + 2) * 4;  // wave maxima and sums, row scales
+// wave maxima and sums, row scales (fp32), affine terms of 0/1 layers (fp64)
+constexpr int kMiscBytes = kW * 4 + kW * 8 + kMaxTPWc * 16 * 4 + kMaxTPWc * 16 * 8;
 constexpr int kRing = 3;              // superchunks of signs in flight per wave
 
 __host__ __device__ constexpr size_t lds_bytes_for(int SC) {
@@ -236,7 +237,8 @@ __global__ __launch_bounds__(kT, NO <= 4 ? 2 : 1) void dec_i8_kernel(const I8Arg
     long long *zrow = reinterpret_cast<long long *>(lds + static_cast<size_t>(SC) * kActSC);  // [tile][row]
     float *wmax = reinterpret_cast<float *>(zrow + kPartBytes / 8);      // [kW]
     long long *wU = reinterpret_cast<long long *>(wmax + kW);            // [kW]
-    float *scl = reinterpret_cast<float *>(wU + kW);  // [2][kMaxTPWc * 16] row scales (a or mid; E), then 2 stats
+    float *scl = reinterpret_cast<float *>(wU + kW);  // [kMaxTPWc * 16] row scales (a or mid)
+    double *saff = reinterpret_cast<double *>(scl + kMaxTPWc * 16);  // [kMaxTPWc * 16] affine terms (0/1 layers)
 
     // ---- loads, in the order their data is used (a wave waits for its
     // loads in issue order): the vector, the row scales, then the first
@@ -255,14 +257,20 @@ __global__ __launch_bounds__(kT, NO <= 4 ? 2 : 1) void dec_i8_kernel(const I8Arg
     // thread tid < nt * 16 finishes row t0 * 16 + tid
     const int my_row = min(t0 * 16 + tid, L.rows - 1);
     const float osc_v = __half2float(L.osc[my_row]);
-    float affe_v = 0.0f, aff_s0 = 0.0f, aff_s1 = 0.0f;
+    // 0/1 layers: the affine term's E of this row (Q - 1 rows of E) and the
+    // Q statistics; loads past them read nothing (zero)
+    float aff_e[kI8MaxQ - 1], aff_s[kI8MaxQ];
     if constexpr (STAGE == 2 && BIN) {
         const bool aff = L.aff_E != nullptr;
-        const __amdgpu_buffer_rsrc_t re = rsrc(L.aff_E, aff ? 4u * static_cast<uint32_t>(L.rows) : 0u);
-        const __amdgpu_buffer_rsrc_t rt = rsrc(L.aff_stats, aff ? 8u : 0u);
-        affe_v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(re, 4 * my_row, 0, 0));
-        aff_s0 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rt, 0, 0, 0));
-        aff_s1 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rt, 4, 0, 0));
+        const uint32_t Q = static_cast<uint32_t>(args.aff_Q);
+        const __amdgpu_buffer_rsrc_t re = rsrc(L.aff_E, aff ? 4u * static_cast<uint32_t>(L.rows) * (Q - 1) : 0u);
+        const __amdgpu_buffer_rsrc_t rt = rsrc(L.aff_stats, aff ? 4u * Q : 0u);
+#pragma unroll
+        for (int q = 0; q < kI8MaxQ - 1; ++q)
+            aff_e[q] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(re, 4 * (q * L.rows + my_row), 0, 0));
+#pragma unroll
+        for (int q = 0; q < kI8MaxQ; ++q)
+            aff_s[q] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rt, 4 * q, 0, 0));
     }
     // One superchunk of the wave's tile: 4 words per lane (16-byte aligned),
     // or wlast words in a short last superchunk, read as one 16-byte access
@@ -307,12 +315,18 @@ __global__ __launch_bounds__(kT, NO <= 4 ? 2 : 1) void dec_i8_kernel(const I8Arg
     if (tid < nt * 16) {
         zrow[tid] = 0;
         scl[tid] = osc_v;
-        if constexpr (STAGE == 2 && BIN) scl[kMaxTPWc * 16 + tid] = affe_v;
-    }
-    if constexpr (STAGE == 2 && BIN) {
-        if (tid == 0) {
-            scl[2 * kMaxTPWc * 16] = aff_s0;
-            scl[2 * kMaxTPWc * 16 + 1] = aff_s1;
+        if constexpr (STAGE == 2 && BIN) {
+            // Σ_{q < Q-1} E_q[row] s_q + s_{Q-1} in fp64 (exact products of fp32 values)
+            const int Q = args.aff_Q;
+            double t = static_cast<double>(aff_e[0]) * static_cast<double>(aff_s[0]);
+            double last = static_cast<double>(aff_s[1]);
+#pragma unroll
+            for (int q = 1; q < kI8MaxQ - 1; ++q) {
+                if (q < Q - 1) t += static_cast<double>(aff_e[q]) * static_cast<double>(aff_s[q]);
+                if (q == Q - 1) last = static_cast<double>(aff_s[q]);
+            }
+            if (Q == kI8MaxQ) last = static_cast<double>(aff_s[kI8MaxQ - 1]);
+            saff[tid] = t + last;
         }
     }
     int dsum[4] = {0, 0, 0, 0};  // Σ of each digit plane over this thread's octets
@@ -438,9 +452,7 @@ __global__ __launch_bounds__(kT, NO <= 4 ? 2 : 1) void dec_i8_kernel(const I8Arg
                 static_cast<float *>(L.out)[row] = static_cast<float>(res);
             } else {
                 double val = res;
-                if constexpr (BIN)
-                    val += static_cast<double>(scl[kMaxTPWc * 16 + tid]) * static_cast<double>(scl[2 * kMaxTPWc * 16]) +
-                           static_cast<double>(scl[2 * kMaxTPWc * 16 + 1]);
+                if constexpr (BIN) val += saff[tid];
                 static_cast<__half *>(L.out)[row] = rne16_of(val);
             }
         }
@@ -460,6 +472,7 @@ int i8_superchunks(int K) { return (round_up_int(K, 128) + 511) / 512; }
 int launch_decode_i8(I8Args &a, int stage, bool bin, void *stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (a.count < 1 || a.count > kMaxGroup) return static_cast<int>(hipErrorInvalidValue);
+    if (stage == 2 && bin && (a.aff_Q < 2 || a.aff_Q > kI8MaxQ)) return static_cast<int>(hipErrorInvalidValue);
     for (int i = 0; i < a.count; ++i) {
         const I8Layer &L = a.L[i];
         if (L.SC < 1 || L.SC > kI8MaxSC || L.wlast < 1 || L.wlast > 4 || L.ntiles < 1 || L.rows < 1 ||

@@ -114,12 +114,23 @@ __device__ __forceinline__ float fp32_value(float x) {
     return x;
 }
 
-// Optional affine output term: out[r][c] = rne16(sn[c] * C[r][c] + E[c] *
-// stats[r].x + stats[r].y) (E null: none).
+// Optional affine output term: out[r][c] = rne16(sn[c] * C[r][c] +
+// term(r, c)) with
+//   term(r, c) = Σ_{q < Q-1} E[q * ldE + c] * stats[r * Q + q] + stats[r * Q + Q - 1]
+// (E null: none).  Q = 2 is one row of E and two statistics per row.
 struct Affine {
-    const float *E;
-    const float *stats;  // [M][2]
+    const float *E = nullptr;
+    const float *stats = nullptr;  // [M][Q]
+    int Q = 2, ldE = 0;
 };
+
+// term(r, c) above in fp32, the products added in q order.
+__device__ __forceinline__ float affine_term(const Affine &aff, int row, int col) {
+    const float *st = aff.stats + static_cast<size_t>(row) * aff.Q;
+    float t = aff.E[col] * st[0];
+    for (int q = 1; q < aff.Q - 1; ++q) t = t + aff.E[static_cast<size_t>(q) * aff.ldE + col] * st[q];
+    return t + st[aff.Q - 1];
+}
 
 // Batch-sum epilogue (gradients): for every output column c, the sum over
 // the wave's 64 rows of C[r][c] * Q[r][c], written to part[(r0 / 64) * n_out
@@ -151,7 +162,7 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[MF_][NF_], const fl
                 if (row < M) {
                     if (out) {
                         float val = fp32_value(acc[i][f][v] * snv[f]);
-                        if (aff.E) val = fp32_value(val + (aff.E[col] * aff.stats[2 * row] + aff.stats[2 * row + 1]));
+                        if (aff.E) val = fp32_value(val + affine_term(aff, row, col));
                         out[static_cast<size_t>(row) * ldo + col] = __float2half_rn(val);
                     }
                     if (out32) out32[static_cast<size_t>(row) * ldo32 + col] = acc[i][f][v];
@@ -235,7 +246,7 @@ __global__ __launch_bounds__(256) void split_finish_kernel(const float *__restri
     for (int e = 0; e < 4; ++e) {
         const int col = min(c0 + e, n_out - 1);
         float val = fp32_value(sv[e] * __half2float(sn[col]));
-        if (aff.E) val = fp32_value(val + (aff.E[col] * aff.stats[2 * row] + aff.stats[2 * row + 1]));
+        if (aff.E) val = fp32_value(val + affine_term(aff, row, col));
         o[e] = __float2half_rn(val);
     }
     __half *dst = out + static_cast<size_t>(row) * ldo + c0;
@@ -796,14 +807,14 @@ size_t sign_gemm_split_elems(int M, int K, int words, int n_out) {
 }
 
 int launch_split_finish(const SplitK &split, int M, int n_out, const void *sn, void *out, int ldo, void *stream,
-                        const float *aff_E, const float *aff_stats) {
+                        const float *aff_E, const float *aff_stats, int aff_Q, int aff_ldE) {
     const int items = M * (split.ldw >> 2);
     if (items == 0) return 0;
     const int c0 = split.col0;
     launch_kernel(split_finish_kernel, dim3((items + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream),
                   static_cast<const float *>(split.ws), split.nsplit, M, n_out - c0, split.ldw,
                   static_cast<const __half *>(sn) + c0, static_cast<__half *>(out) + c0, ldo,
-                  Affine{aff_E ? aff_E + c0 : nullptr, aff_stats});
+                  Affine{aff_E ? aff_E + c0 : nullptr, aff_stats, aff_Q, aff_ldE});
     return static_cast<int>(hipGetLastError());
 }
 
@@ -917,7 +928,8 @@ int launch_sign_gemm(const void *P, int ldp, int M, int K, const uint32_t *S, in
                      const GemmFlavor *flavor) {
     const GemmLaunch a{P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32,
                        DotArgs{dq, dq_f32, lddq, dpart},
-                       Affine{flavor ? flavor->aff_E : nullptr, flavor ? flavor->aff_stats : nullptr}};
+                       flavor ? Affine{flavor->aff_E, flavor->aff_stats, flavor->aff_Q, flavor->aff_ldE}
+                              : Affine{}};
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (split) {
         split->nsplit = 1;

@@ -52,6 +52,13 @@ struct dbf_layer {
     // gains E[o] * Σx + γ·x (per-row sums in bqq_stats [max_batch][2])
     bool binary = false;
     float *bqq_E = nullptr, *bqq_gamma = nullptr, *bqq_stats = nullptr;
+    // group-wise scalars (dbf_bqq_pack_grouped, more than one group): the
+    // p products' first stage runs as p signed DBF products with per-term
+    // input scales bqq_b [p][m_pad] (fp16); bqq_E holds [p][n] row sums of
+    // the Y_i, bqq_gamma the [p + 1][m] weights of the row statistics and
+    // bqq_stats [max_batch][p + 1] (bqq_Q = p + 1)
+    int32_t bqq_groups = 0, bqq_p = 0, bqq_d = 0, bqq_Q = 2;
+    uint16_t *bqq_b = nullptr;
     size_t packed_bytes = 0, scale_bytes = 0, workspace_bytes = 0;
     // backward (dbf_pack_ex with DBF_PACK_BACKWARD): the transposed layer
     // Wᵀ = diag(b) Bᵀ diag(mid) Aᵀ diag(a), and fp32 intermediates of the
@@ -114,6 +121,7 @@ void release(dbf_layer *h) {
     (void)hipFree(h->bqq_E);
     (void)hipFree(h->bqq_gamma);
     (void)hipFree(h->bqq_stats);
+    (void)hipFree(h->bqq_b);
     (void)hipFree(h->t32);
     (void)hipFree(h->red);
     release(h->bwd);
@@ -469,6 +477,129 @@ extern "C" dbf_status_t dbf_bqq_pack(int32_t n, int32_t m, int32_t d, int32_t p,
     return DBF_OK;
 }
 
+// Group-wise scalars: on the columns l of group h = l / group,
+//   W[:, l] = Σ_i ( r_i[h] Y_i Z_i + s_i[h] Y_i 1 + t_i[h] 1 Z_i )[:, l] + u[h].
+// With S_i = 1 - 2 Z_i (entries ±1) and b_i[l] = r_i[h(l)],
+//   Σ_l (Y_i Z_i)[o, l] r_i[h(l)] x_l = ½ R_i[o] β_i - ½ (Y_i t_i)[o],
+// t_i = S_i (b_i ⊙ x) the signed DBF first stage of term i, β_i = b_i·x and
+// R_i[o] = Σ_j Y_i[o, j].  So the first stage is p signed products (the DBF
+// kernels, per-term b, mid = 1), the second is the 0/1 product of the Y_i
+// ({0, 2} operand, a = -1/4), and the rest is the rank-(p + 1) term
+//   Σ_i R_i[o] σ_i + κ,  σ_i = Σ_l (s_i[h(l)] + ½ r_i[h(l)]) x_l,
+//   κ = Σ_l ( Σ_i t_i[h(l)] C_i[l] + u[h(l)] ) x_l,  C_i[l] = Σ_j Z_i[j, l],
+// with the weights formed in double precision and kept in fp32.
+extern "C" dbf_status_t dbf_bqq_pack_grouped(int32_t n, int32_t m, int32_t d, int32_t p, int32_t group,
+                                             const uint8_t *Y, const uint8_t *Z, const uint16_t *r,
+                                             const uint16_t *s, const uint16_t *t, const uint16_t *u,
+                                             int32_t max_batch, dbf_handle_t *out) {
+    if (out) *out = nullptr;
+    if (!out || !Y || !Z || !r || !s || !t || !u) return DBF_ERR_INVALID_ARG;
+    if (n < 1 || m < 1 || d < 1 || p < 1 || group < 1 || max_batch < 1) return DBF_ERR_INVALID_ARG;
+    const int32_t ng = static_cast<int32_t>((int64_t(m) + group - 1) / group);
+    if (ng == 1) return dbf_bqq_pack(n, m, d, p, Y, Z, r, s, t, u[0], max_batch, out);
+    // term boundaries on 64-row tiles of the sign layouts; p + 1 statistics per row
+    if (d % 64 != 0 || p + 1 > dbf::kMaxStatQ || p > dbf::kMaxGroup) return DBF_ERR_SHAPE;
+    const int64_t k = int64_t(p) * d;
+    if (k > (int64_t(1) << 30)) return DBF_ERR_SHAPE;
+    for (int64_t i = 0; i < int64_t(p) * n * d; ++i)
+        if (Y[i] > 1) return DBF_ERR_INVALID_ARG;
+    for (int64_t i = 0; i < int64_t(p) * d * m; ++i)
+        if (Z[i] > 1) return DBF_ERR_INVALID_ARG;
+    g_alloc_calls = 0;
+    const int32_t Q = p + 1;
+    const int32_t m_pad = round_up(m, 64);
+    std::vector<int8_t> As, Bs;
+    std::vector<uint16_t> a16, mid16, b16, bt16;
+    std::vector<float> E32, w32;
+    try {
+        As.resize(static_cast<size_t>(n) * k);
+        Bs.resize(static_cast<size_t>(k) * m);
+        a16.assign(static_cast<size_t>(n), 0xB400);  // fp16 -0.25
+        mid16.assign(static_cast<size_t>(k), 0x3C00);
+        b16.assign(static_cast<size_t>(m), 0x3C00);  // (the per-term scales below serve instead)
+        bt16.assign(static_cast<size_t>(p) * m_pad, 0);
+        E32.assign(static_cast<size_t>(p) * n, 0.0f);
+        w32.assign(static_cast<size_t>(Q) * m, 0.0f);
+    } catch (const std::bad_alloc &) {
+        return DBF_ERR_OOM;
+    }
+    std::vector<double> kappa(static_cast<size_t>(m), 0.0);
+    for (int64_t l = 0; l < m; ++l) kappa[l] = half_bits_value(u[l / group]);
+    for (int64_t i = 0; i < p; ++i) {
+        for (int64_t o = 0; o < n; ++o) {
+            const uint8_t *yrow = Y + (i * n + o) * d;
+            int64_t deg = 0;
+            for (int64_t j = 0; j < d; ++j) {
+                As[o * k + i * d + j] = yrow[j] ? -1 : 1;
+                deg += yrow[j];
+            }
+            E32[i * n + o] = static_cast<float>(deg);
+        }
+        std::vector<int64_t> colsum(static_cast<size_t>(m), 0);
+        for (int64_t j = 0; j < d; ++j) {
+            const uint8_t *zrow = Z + (i * d + j) * m;
+            int8_t *brow = Bs.data() + (i * d + j) * m;
+            for (int64_t l = 0; l < m; ++l) {
+                brow[l] = zrow[l] ? -1 : 1;
+                colsum[l] += zrow[l];
+            }
+        }
+        for (int64_t l = 0; l < m; ++l) {
+            const int64_t hg = l / group;
+            const double ri = half_bits_value(r[i * ng + hg]), si = half_bits_value(s[i * ng + hg]),
+                         ti = half_bits_value(t[i * ng + hg]);
+            bt16[i * m_pad + l] = r[i * ng + hg];
+            w32[i * m + l] = static_cast<float>(si + 0.5 * ri);
+            kappa[l] += ti * double(colsum[l]);
+        }
+    }
+    for (int64_t l = 0; l < m; ++l) w32[int64_t(p) * m + l] = static_cast<float>(kappa[l]);
+    dbf_layer *h = nullptr;
+    dbf_status_t st = pack_layer(n, m, static_cast<int32_t>(k), As.data(), Bs.data(), a16.data(), mid16.data(),
+                                 b16.data(), max_batch, &h);
+    if (st != DBF_OK) return st;
+    std::vector<int8_t>().swap(As);
+    std::vector<int8_t>().swap(Bs);
+    h->binary = true;
+    h->bqq_groups = ng;
+    h->bqq_p = p;
+    h->bqq_d = d;
+    h->bqq_Q = Q;
+    // split-K workspace for the per-term first products (n_out = d)
+    size_t split_elems = h->split_cap;
+    for (int32_t mb = 1;; mb += 128) {
+        const int32_t M = std::min(max_batch, mb + 127);
+        split_elems = std::max(split_elems, dbf::sign_gemm_split_elems(M, m, h->Wm, d));
+        if (M >= max_batch) break;
+    }
+    if (split_elems > h->split_cap) {
+        (void)hipFree(h->split);
+        h->split = nullptr;
+        st = dev_alloc(reinterpret_cast<void **>(&h->split), sizeof(float) * split_elems);
+        if (st == DBF_OK) {
+            h->workspace_bytes += sizeof(float) * (split_elems - h->split_cap);
+            h->split_cap = split_elems;
+        }
+    }
+    if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->bqq_E), sizeof(float) * E32.size());
+    if (st == DBF_OK) st = upload(h->bqq_E, E32.data(), sizeof(float) * E32.size());
+    if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->bqq_gamma), sizeof(float) * w32.size());
+    if (st == DBF_OK) st = upload(h->bqq_gamma, w32.data(), sizeof(float) * w32.size());
+    if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->bqq_b), sizeof(uint16_t) * bt16.size());
+    if (st == DBF_OK) st = upload(h->bqq_b, bt16.data(), sizeof(uint16_t) * bt16.size());
+    if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->bqq_stats), sizeof(float) * Q * size_t(max_batch));
+    if (st == DBF_OK) {
+        h->scale_bytes += sizeof(float) * (E32.size() + w32.size()) + sizeof(uint16_t) * bt16.size();
+        h->workspace_bytes += sizeof(float) * Q * size_t(max_batch);
+    }
+    if (st != DBF_OK) {
+        release(h);
+        return st;
+    }
+    *out = h;
+    return DBF_OK;
+}
+
 extern "C" void dbf_free(dbf_handle_t h) {
     if (!h) return;
     int cur = 0;
@@ -611,6 +742,80 @@ static dbf_status_t forward_prefill(dbf_layer *h, const void *x, void *y, int32_
     return st;
 }
 
+// Forward of a layer with group-wise BQQ scalars (see dbf_bqq_pack_grouped):
+// the row statistics, then the p signed first products (per-term input
+// scales) into v / T, then the 0/1 second product with the rank-(p + 1)
+// affine term.  Batch 1 runs the int8 decode kernels (the p first products
+// as one launch of p layers); other batches run the prefill products.
+static dbf_status_t forward_bqq_grouped(dbf_layer *h, const void *x, void *y, int32_t batch, int32_t path,
+                                        hipStream_t stream) {
+    const int p = h->bqq_p, d = h->bqq_d;
+    const bool i8 = path != DBF_PATH_PREFILL && batch == 1 && h->i8_ok;
+    if (path == DBF_PATH_DECODE && !i8) return DBF_ERR_UNSUPPORTED;
+    dbf_status_t st = timed_launch(h, "bqq_rowstats", stream, [&] {
+        return dbf::launch_bqq_rowstats_q(x, batch, h->m, h->bqq_gamma, h->bqq_Q, h->bqq_stats, stream);
+    });
+    if (st != DBF_OK) return st;
+    if (i8) {
+        dbf::I8Args a1{}, a2{};
+        dbf::I8Layer s1, s2;
+        i8_stages(h, x, y, s1, s2);
+        const size_t tile_words = static_cast<size_t>(256 * (s1.SC - 1) + 64 * s1.wlast);
+        a1.count = p;
+        for (int i = 0; i < p; ++i) {
+            dbf::I8Layer L = s1;
+            L.S = h->B_i8 + static_cast<size_t>(i) * (d / 16) * tile_words;
+            L.bsc = reinterpret_cast<const __half *>(h->bqq_b + static_cast<size_t>(i) * h->m_pad);
+            L.osc = reinterpret_cast<const __half *>(h->mid_dev + static_cast<size_t>(i) * d);
+            L.out = h->v32 + static_cast<size_t>(i) * d;
+            L.rows = d;
+            L.ntiles = d / 16;
+            a1.L[i] = L;
+        }
+        a2.count = 1;
+        a2.L[0] = s2;
+        a2.aff_Q = h->bqq_Q;
+        st = timed_launch(h, "decode_stage1", stream, [&] { return dbf::launch_decode_i8(a1, 1, false, stream); });
+        if (st != DBF_OK) return st;
+        return timed_launch(h, "decode_stage2", stream, [&] { return dbf::launch_decode_i8(a2, 2, true, stream); });
+    }
+    dbf::SplitK sp;
+    sp.ws = h->split;
+    sp.cap = h->split_cap;
+    for (int i = 0; i < p && st == DBF_OK; ++i) {
+        // T[:, i d : (i + 1) d] = rne16(S_i (b_i ⊙ x)) (mid = 1); B's rows of term i from its 64-row tile i d / 64
+        const uint32_t *S = h->B_dev + static_cast<size_t>(i) * (d / 64) * (h->Wm >> 1) * 128;
+        const uint16_t *bi = h->bqq_b + static_cast<size_t>(i) * h->m_pad;
+        const uint16_t *midi = h->mid_dev + static_cast<size_t>(i) * d;
+        uint16_t *Ti = h->T + static_cast<size_t>(i) * d;
+        st = timed_launch(h, "prefill_gemm1", stream, [&] {
+            return dbf::launch_sign_gemm(x, h->m, batch, h->m, S, h->Wm, d, bi, midi, Ti, h->k_pad, d, nullptr, 0,
+                                         nullptr, 0, 0, nullptr, stream, &sp, nullptr);
+        });
+        if (st == DBF_OK && sp.nsplit > 1)
+            st = timed_launch(h, "prefill_split1", stream, [&] {
+                return dbf::launch_split_finish(sp, batch, d, midi, Ti, h->k_pad, stream);
+            });
+    }
+    if (st != DBF_OK) return st;
+    dbf::GemmFlavor f2;
+    f2.binary = 1;
+    f2.aff_E = h->bqq_E;
+    f2.aff_stats = h->bqq_stats;
+    f2.aff_Q = h->bqq_Q;
+    f2.aff_ldE = h->n;
+    st = timed_launch(h, "prefill_gemm2", stream, [&] {
+        return dbf::launch_sign_gemm(h->T, h->k_pad, batch, h->k_pad, h->A_dev, h->Wk, h->n_pad, nullptr, h->a_dev,
+                                     y, h->n, h->n, nullptr, 0, nullptr, 0, 0, nullptr, stream, &sp, &f2);
+    });
+    if (st == DBF_OK && sp.nsplit > 1)
+        st = timed_launch(h, "prefill_split2", stream, [&] {
+            return dbf::launch_split_finish(sp, batch, h->n, h->a_dev, y, h->n, stream, h->bqq_E, h->bqq_stats,
+                                            h->bqq_Q, h->n);
+        });
+    return st;
+}
+
 extern "C" dbf_status_t dbf_linear_forward_ex(dbf_handle_t h, const void *x, void *y, int32_t batch, int32_t path,
                                               hipStream_t stream) {
     if (!h) return DBF_ERR_INVALID_ARG;
@@ -625,6 +830,8 @@ extern "C" dbf_status_t dbf_linear_forward_ex(dbf_handle_t h, const void *x, voi
     if (hipGetDevice(&cur) != hipSuccess) return DBF_ERR_HIP;
     if (cur != h->device) return DBF_ERR_INVALID_ARG;
     if (path == DBF_PATH_DECODE_TABLE) return DBF_ERR_UNSUPPORTED;  // (removed: slower than the matrix cores)
+    if (h->bqq_groups > 0)
+        return forward_bqq_grouped(h, x, y, batch, path, stream);
     const bool decode = path == DBF_PATH_DECODE || (path == DBF_PATH_AUTO && batch <= dbf::kDecodeMaxBatch);
     if (h->binary && !decode) {
         // (on the decode path the stage-1 launch forms the row sums itself)
@@ -929,6 +1136,7 @@ extern "C" dbf_status_t dbf_linear_forward_noalloc(dbf_handle_t h, const void *x
     int cur = -1;
     if (hipGetDevice(&cur) != hipSuccess) return DBF_ERR_HIP;
     if (cur != h->device) return DBF_ERR_INVALID_ARG;
+    if (h->bqq_groups > 0) return DBF_ERR_UNSUPPORTED;  // (group-wise BQQ scalars: the allocating forward only)
     const ScratchPlan p = plan_scratch(h, batch);
     if (p.total > kNoAllocScratchBytes) return DBF_ERR_SHAPE;  // more scratch than the static array holds
     char *base = nullptr;

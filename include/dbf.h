@@ -235,6 +235,38 @@ dbf_status_t dbf_bqq_pack(int32_t n, int32_t m, int32_t d, int32_t p,
                           int32_t max_batch, dbf_handle_t *out);
 
 /*
+ * dbf_bqq_pack_grouped -- the binary-quadratic form with group-wise scalars.
+ * The same TL;DR names group-wise scaling as the way the form keeps its
+ * parameter overhead low (and the page's Figure 2 is on weight scaling) but
+ * gives no formula; the reading here: the m input columns fall into groups
+ * of `group` consecutive columns (the last may be shorter), each with its
+ * own scalars, the 0/1 matrices shared.  On the columns l of group h,
+ *   W[:, l] = Σ_{i<p} ( r_i[h] Y_i Z_i + s_i[h] Y_i 1 + t_i[h] 1 Z_i )[:, l] + u[h].
+ *   Y, Z   as for dbf_bqq_pack.
+ *   r,s,t  host fp16 bit patterns, p x ngroups (term-major), ngroups =
+ *          ceil(m / group); u host fp16 bit patterns, ngroups.
+ * One group (group >= m) is dbf_bqq_pack exactly.  With more groups the
+ * layer runs as: p signed first products on the DBF kernels (Z_i as ±1 signs,
+ * per-term input scale b_i[l] = r_i[h(l)], mid = 1), the 0/1 product of the
+ * Y_i with a = -1/4, and a rank-(p + 1) affine term Σ_i R_i[o] σ_i + κ
+ * (R_i[o] the row sums of Y_i; σ_i, κ per input row: fp32 sums of x with
+ * weights s_i[h] + r_i[h] / 2 and Σ_i t_i[h] (column sums of Z_i) + u[h],
+ * formed at pack time in double precision and kept in fp32) added before
+ * the one rounding.  Paths: AUTO runs the int8 decode kernels at batch 1
+ * and the prefill products at every other batch; DECODE serves batch 1
+ * only (DBF_ERR_UNSUPPORTED otherwise); PREFILL any batch.  The
+ * intermediate follows the DBF path rules.
+ * Limits: d a multiple of 64 and p <= 8 when there is more than one group
+ * (DBF_ERR_SHAPE otherwise).
+ * Errors: as dbf_bqq_pack.  Grouped forwards, gradients and
+ * dbf_linear_forward_noalloc return DBF_ERR_UNSUPPORTED for such a handle.
+ */
+dbf_status_t dbf_bqq_pack_grouped(int32_t n, int32_t m, int32_t d, int32_t p, int32_t group,
+                                  const uint8_t *Y, const uint8_t *Z,
+                                  const uint16_t *r, const uint16_t *s, const uint16_t *t, const uint16_t *u,
+                                  int32_t max_batch, dbf_handle_t *out);
+
+/*
  * dbf_factorize -- the DBF factors of a weight matrix W (n x m), the step
  * before packing.  Technical summary (gist.science) of "Addition is almost
  * all you need", §2.2: alternating minimization of the two factors, ADMM

@@ -192,6 +192,45 @@ def test_bqq_pack_validates_before_any_device_call():
         assert h.value is None
 
 
+def test_bqq_pack_grouped_validates_before_any_device_call():
+    """dbf_bqq_pack_grouped reports argument and shape errors (null
+    pointers, sizes, entries other than 0/1, d not a multiple of 64 or more
+    than 8 terms with several groups) without touching a GPU."""
+    L = dbf.lib()
+    p, n, d, m, g = 2, 4, 64, 10, 4  # three groups
+    ng = 3
+    Y = np.ones((p, n, d), np.uint8)
+    Z = np.zeros((p, d, m), np.uint8)
+    r = np.ones(p * ng, np.float16).view(np.uint16)
+    u = np.ones(ng, np.float16).view(np.uint16)
+    h = ctypes.c_void_p()
+    P = lambda arr: arr.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
+    E = dbf.DBF_ERR_INVALID_ARG
+    assert L.dbf_bqq_pack_grouped(n, m, d, p, g, P(Y), P(Z), P(r), P(r), P(r), P(u), 4, None) == E
+    assert L.dbf_bqq_pack_grouped(n, m, d, p, g, P(Y), P(Z), P(r), P(r), P(r), None, 4, ctypes.byref(h)) == E
+    assert L.dbf_bqq_pack_grouped(n, m, d, p, 0, P(Y), P(Z), P(r), P(r), P(r), P(u), 4, ctypes.byref(h)) == E
+    for bad in ((0, m, d, p), (n, 0, d, p), (n, m, 0, p), (n, m, d, 0)):
+        assert L.dbf_bqq_pack_grouped(*bad, g, P(Y), P(Z), P(r), P(r), P(r), P(u), 4, ctypes.byref(h)) == E
+    Y2 = Y.copy()
+    Y2[1, 2, 0] = 2
+    assert L.dbf_bqq_pack_grouped(n, m, d, p, g, P(Y2), P(Z), P(r), P(r), P(r), P(u), 4, ctypes.byref(h)) == E
+    # several groups: the term boundaries must fall on 64-row tiles, at most 8 terms
+    Yb = np.ones((p, n, 96), np.uint8)
+    Zb = np.zeros((p, 96, m), np.uint8)
+    assert L.dbf_bqq_pack_grouped(n, m, 96, p, g, P(Yb), P(Zb), P(r), P(r), P(r), P(u),
+                                  4, ctypes.byref(h)) == dbf.DBF_ERR_SHAPE
+    Y9 = np.ones((9, n, d), np.uint8)
+    Z9 = np.zeros((9, d, m), np.uint8)
+    r9 = np.ones(9 * ng, np.float16).view(np.uint16)
+    assert L.dbf_bqq_pack_grouped(n, m, d, 9, g, P(Y9), P(Z9), P(r9), P(r9), P(r9), P(u),
+                                  4, ctypes.byref(h)) == dbf.DBF_ERR_SHAPE
+    assert h.value is None
+    if not _have_gpu():
+        assert L.dbf_bqq_pack_grouped(n, m, d, p, g, P(Y), P(Z), P(r), P(r), P(r), P(u), 4,
+                                      ctypes.byref(h)) == dbf.DBF_ERR_HIP
+        assert h.value is None
+
+
 def test_factorize_validates_before_any_device_call():
     L = dbf.lib()
     E = dbf.DBF_ERR_INVALID_ARG
