@@ -317,6 +317,61 @@ def bqq_leg(args):
           file=sys.stderr, flush=True)
     H.close()
     torch.cuda.synchronize()
+    res["grouped_g128"] = bqq_grouped_leg(args)
+    return res
+
+
+def bqq_grouped_leg(args):
+    """The same 4096x4096, p = 2, d = 1024 layer with group-wise scalars
+    (one set per 128 input columns: 32 groups): batch-1 decode over rotated
+    copies (GB/s of bits + per-forward scale and weight bytes) and
+    batch-2048 prefill (TFLOP/s-equivalent 2 * batch * p d (n + m))."""
+    import torch
+
+    import dbf_linear_fwd_amd as dbf
+    from tests import inputs
+
+    n, m, d, p, g = 4096, 4096, 1024, 2, 128
+    L = inputs.bqq_grouped_layer("bqqg", n, m, d, p, g, 8300, (1, 2048))
+    # bits; per-term input scales, mid and a (fp16); row sums of the Y_i and the p + 1 statistic weights (fp32)
+    bytes_step = L.bit_bytes + 2 * (p * m + p * d + n) + 4 * (p * n + (p + 1) * m)
+    R = max(1, -(-args.rotate_mb * (1 << 20) // bytes_step))
+    print(f"[bench] bqq grouped: {n}x{m} d={d} p={p} group={g}, {R} copies", file=sys.stderr, flush=True)
+    copies = [dbf.Layer.bqq_grouped(L.Y, L.Z, L.r, L.s, L.t, L.u, g, max_batch=1) for _ in range(R)]
+    x = torch.from_numpy(L.X[1]).cuda()
+    y = torch.empty((1, n), dtype=torch.float16, device="cuda")
+
+    def fwd(i):
+        copies[i % R].forward(x, out=y)
+    fwd.period = R
+    el, done = time_steps(fwd, max(R, min(args.steps, 10 * R)), min(args.warmup, R), args.mode)
+    kt = kernel_times(copies, fwd, min(args.steps, 2 * R))
+    res = {"workload": "BQQ-form layer 4096x4096, p=2 products of d=1024, scalars per group of 128 input columns",
+           "decode_b1": {"us_per_forward": el * 1e6 / done, "gbs": bytes_step * done / el / 1e9,
+                         "frac_of_hbm_peak": bytes_step * done / el / 1e9 / HBM_PEAK_GBS, "kernels": kt,
+                         "bytes_per_forward": bytes_step, "copies": R}}
+    print(f"[bench] bqq grouped decode: {res['decode_b1']['us_per_forward']:.2f} us, "
+          f"{res['decode_b1']['gbs']:.1f} GB/s; kernels {kt}", file=sys.stderr, flush=True)
+    for c in copies:
+        c.close()
+    del copies
+    torch.cuda.synchronize()
+    bt = 2048
+    H = dbf.Layer.bqq_grouped(L.Y, L.Z, L.r, L.s, L.t, L.u, g, max_batch=bt)
+    x = torch.from_numpy(L.X[bt]).cuda()
+    y = torch.empty((bt, n), dtype=torch.float16, device="cuda")
+
+    def pf(i):
+        H.forward(x, out=y)
+    el, done = time_steps(pf, 30, 5, "eager")
+    kt = kernel_times([H], pf, 10)
+    flops = 2 * bt * p * d * (n + m)
+    res["prefill_b2048"] = {"us_per_forward": el * 1e6 / done, "tflops_eq": flops * done / el / 1e12,
+                            "frac_of_mfma_peak": flops * done / el / 1e12 / MFMA_F16_PEAK_TFLOPS, "kernels": kt}
+    print(f"[bench] bqq grouped prefill: {res['prefill_b2048']['tflops_eq']:.1f} TFLOP/s-eq; kernels {kt}",
+          file=sys.stderr, flush=True)
+    H.close()
+    torch.cuda.synchronize()
     return res
 
 

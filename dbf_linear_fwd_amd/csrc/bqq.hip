@@ -35,17 +35,14 @@ __global__ __launch_bounds__(kStatThreads) void bqq_rowstats_kernel(const __half
 }
 
 // Group-wise form, one workgroup per row of x: stats[r * Q + q] = Σ_l
-// w[q * m + l] x[r][l], two statistics per pass over the row.
+// w[q * m + l] x[r][l], all Q statistics in one pass over the row.
+template <int Q>
 __global__ __launch_bounds__(kStatThreads) void bqq_rowstats_q_kernel(const __half *__restrict__ x, int m,
-                                                                      const float *__restrict__ w, int Q,
+                                                                      const float *__restrict__ w,
                                                                       float *__restrict__ stats) {
-    __shared__ float sh[2 * kStatThreads];
+    __shared__ float sh[Q * kStatThreads];
     const int r = blockIdx.x;
-    const __half *xr = x + static_cast<size_t>(r) * m;
-    for (int q = 0; q < Q; q += 2)
-        bqq_rowstats_dot2<kStatThreads>(xr, m, w + static_cast<size_t>(q) * m,
-                                        q + 1 < Q ? w + static_cast<size_t>(q + 1) * m : nullptr,
-                                        stats + static_cast<size_t>(r) * Q + q, sh);
+    bqq_rowstats_dotq<kStatThreads, Q>(x + static_cast<size_t>(r) * m, m, w, stats + static_cast<size_t>(r) * Q, sh);
 }
 
 }  // namespace
@@ -53,8 +50,13 @@ __global__ __launch_bounds__(kStatThreads) void bqq_rowstats_q_kernel(const __ha
 int launch_bqq_rowstats_q(const void *x, int batch, int m, const float *w, int Q, float *stats, void *stream) {
     if (Q < 1 || Q > kMaxStatQ) return static_cast<int>(hipErrorInvalidValue);
     if (batch <= 0) return 0;
-    launch_kernel(bqq_rowstats_q_kernel, dim3(batch), dim3(kStatThreads), 0, static_cast<hipStream_t>(stream),
-                  static_cast<const __half *>(x), m, w, Q, stats);
+    static void (*const kernels[kMaxStatQ])(const __half *, int, const float *, float *) = {
+        bqq_rowstats_q_kernel<1>, bqq_rowstats_q_kernel<2>, bqq_rowstats_q_kernel<3>,
+        bqq_rowstats_q_kernel<4>, bqq_rowstats_q_kernel<5>, bqq_rowstats_q_kernel<6>,
+        bqq_rowstats_q_kernel<7>, bqq_rowstats_q_kernel<8>, bqq_rowstats_q_kernel<9>};
+    static_assert(kMaxStatQ == 9, "one kernel per statistic count");
+    launch_kernel(kernels[Q - 1], dim3(batch), dim3(kStatThreads), 0, static_cast<hipStream_t>(stream),
+                  static_cast<const __half *>(x), m, w, stats);
     return static_cast<int>(hipGetLastError());
 }
 

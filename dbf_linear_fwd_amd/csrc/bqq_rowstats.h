@@ -70,46 +70,45 @@ __device__ __forceinline__ void bqq_rowstats_row(const __half *__restrict__ xr, 
     }
 }
 
-// For one row x of the input (m fp16 values): out[0] = Σ_l wa[l] x_l and,
-// if wb is not null, out[1] = Σ_l wb[l] x_l, in fp32 (one product and one
-// add per term), with the chunking and the fixed-order tree of
-// bqq_rowstats_row.
-template <int THREADS>
-__device__ __forceinline__ void bqq_rowstats_dot2(const __half *__restrict__ xr, int m, const float *__restrict__ wa,
-                                                  const float *__restrict__ wb, float *__restrict__ out,
-                                                  float *sh /* LDS, 2 * THREADS floats */) {
+// For one row x of the input (m fp16 values): out[q] = Σ_l w[q * m + l] x_l
+// for q < Q, in fp32 (one product and one add per term), all Q sums in one
+// pass over the row: every load of a round (x and the Q weight rows) is
+// issued before the first add, so the pass waits on memory once per round.
+// The chunking and the fixed-order tree are those of bqq_rowstats_row (one
+// tree per statistic).
+template <int THREADS, int Q>
+__device__ __forceinline__ void bqq_rowstats_dotq(const __half *__restrict__ xr, int m, const float *__restrict__ w,
+                                                  float *__restrict__ out, float *sh /* LDS, Q * THREADS floats */) {
     typedef _Float16 h8 __attribute__((ext_vector_type(8)));
     const int tid = threadIdx.x;
-    const bool two = wb != nullptr;
-    float s = 0.0f, k = 0.0f;
+    float acc[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) acc[q] = 0.0f;
     if ((m & 7) == 0 && (reinterpret_cast<uintptr_t>(xr) & 15) == 0) {
         const int nch = m >> 3;
-        for (int c0 = 0; c0 < nch; c0 += 4 * THREADS) {
-            h8 xv[4];
-            float4 a0[4], a1[4], b0[4], b1[4];
+        for (int c0 = 0; c0 < nch; c0 += 2 * THREADS) {
+            h8 xv[2];
+            float4 a[Q][2][2];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int c = min(c0 + tid + THREADS * q, nch - 1);  // past the end: a valid chunk, not added
-                xv[q] = *reinterpret_cast<const h8 *>(xr + 8 * c);
-                a0[q] = *reinterpret_cast<const float4 *>(wa + 8 * c);
-                a1[q] = *reinterpret_cast<const float4 *>(wa + 8 * c + 4);
-                if (two) {
-                    b0[q] = *reinterpret_cast<const float4 *>(wb + 8 * c);
-                    b1[q] = *reinterpret_cast<const float4 *>(wb + 8 * c + 4);
-                } else {
-                    b0[q] = b1[q] = float4{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int u = 0; u < 2; ++u) {
+                const int c = min(c0 + tid + THREADS * u, nch - 1);  // past the end: a valid chunk, not added
+                xv[u] = *reinterpret_cast<const h8 *>(xr + 8 * c);
+#pragma unroll
+                for (int q = 0; q < Q; ++q) {
+                    const float *wr = w + static_cast<size_t>(q) * m + 8 * c;
+                    a[q][u][0] = *reinterpret_cast<const float4 *>(wr);
+                    a[q][u][1] = *reinterpret_cast<const float4 *>(wr + 4);
                 }
             }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if (c0 + tid + THREADS * q < nch) {
-                    const float av[8] = {a0[q].x, a0[q].y, a0[q].z, a0[q].w, a1[q].x, a1[q].y, a1[q].z, a1[q].w};
-                    const float bv[8] = {b0[q].x, b0[q].y, b0[q].z, b0[q].w, b1[q].x, b1[q].y, b1[q].z, b1[q].w};
+            for (int u = 0; u < 2; ++u) {
+                if (c0 + tid + THREADS * u < nch) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float v = static_cast<float>(xv[q][e]);
-                        s += av[e] * v;
-                        k += bv[e] * v;
+                    for (int q = 0; q < Q; ++q) {
+                        const float wv[8] = {a[q][u][0].x, a[q][u][0].y, a[q][u][0].z, a[q][u][0].w,
+                                             a[q][u][1].x, a[q][u][1].y, a[q][u][1].z, a[q][u][1].w};
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) acc[q] += wv[e] * static_cast<float>(xv[u][e]);
                     }
                 }
             }
@@ -117,25 +116,21 @@ __device__ __forceinline__ void bqq_rowstats_dot2(const __half *__restrict__ xr,
     } else {
         for (int l = tid; l < m; l += THREADS) {
             const float v = __half2float(xr[l]);
-            s += wa[l] * v;
-            if (two) k += wb[l] * v;
+#pragma unroll
+            for (int q = 0; q < Q; ++q) acc[q] += w[static_cast<size_t>(q) * m + l] * v;
         }
     }
-    sh[tid] = s;
-    sh[THREADS + tid] = k;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) sh[q * THREADS + tid] = acc[q];
     __syncthreads();
-    for (int w = THREADS / 2; w > 0; w >>= 1) {
-        if (tid < w) {
-            sh[tid] += sh[tid + w];
-            sh[THREADS + tid] += sh[THREADS + tid + w];
+    for (int s = THREADS / 2; s > 0; s >>= 1) {
+        if (tid < s) {
+#pragma unroll
+            for (int q = 0; q < Q; ++q) sh[q * THREADS + tid] += sh[q * THREADS + tid + s];
         }
         __syncthreads();
     }
-    if (tid == 0) {
-        out[0] = sh[0];
-        if (two) out[1] = sh[THREADS];
-    }
-    __syncthreads();  // sh is reused by the next call
+    if (tid < Q) out[tid] = sh[tid * THREADS];
 }
 
 }  // namespace dbf
