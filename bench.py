@@ -198,7 +198,7 @@ def backward_leg():
 
     def step(i):
         H.backward(x, dy)
-    el, done = time_steps(step, 30, 5, "eager")
+    el, done = time_median(step)
     flops = 4 * bt * layer.k * (layer.n + layer.m)
     kt = kernel_times([H], step, 10)
     print(f"[bench] backward: {flops * done / el / 1e12:.1f} TFLOP/s-eq; kernels {kt}", file=sys.stderr, flush=True)
@@ -211,7 +211,8 @@ def backward_leg():
 def all_configs(args):
     """Every layer of the five workloads: decode (batch 1 and 16, weights
     rotated over >= rotate-mb of copies, graph replay) and prefill (batch
-    2048).  One JSON line each."""
+    2048, steady state: the median of 5 groups of 10 forwards after 20
+    untimed ones).  One JSON line each."""
     import torch
 
     import dbf_linear_fwd_amd as dbf
@@ -255,7 +256,7 @@ def all_configs(args):
 
                 def pf(i):
                     L.forward(x, out=y)
-                el, done = time_steps(pf, 30, 5, "eager")
+                el, done = time_median(pf)
                 flops = 2 * bt * layer.k * (layer.n + layer.m)
                 print(json.dumps({"config": cid, "layer": layer.name, "n": layer.n, "m": layer.m, "k": layer.k,
                                   "batch": bt, "path": "prefill", "us_per_forward": el * 1e6 / done,
@@ -308,7 +309,7 @@ def bqq_leg(args):
 
     def pf(i):
         H.forward(x, out=y)
-    el, done = time_steps(pf, 30, 5, "eager")
+    el, done = time_median(pf)
     kt = kernel_times([H], pf, 10)
     flops = 2 * bt * p * d * (n + m)
     res["prefill_b2048"] = {"us_per_forward": el * 1e6 / done, "tflops_eq": flops * done / el / 1e12,
@@ -363,7 +364,7 @@ def bqq_grouped_leg(args):
 
     def pf(i):
         H.forward(x, out=y)
-    el, done = time_steps(pf, 30, 5, "eager")
+    el, done = time_median(pf)
     kt = kernel_times([H], pf, 10)
     flops = 2 * bt * p * d * (n + m)
     res["prefill_b2048"] = {"us_per_forward": el * 1e6 / done, "tflops_eq": flops * done / el / 1e12,
