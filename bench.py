@@ -538,32 +538,47 @@ def time_exact(step, steps, warmup, start=0):
     return e0.elapsed_time(e1) / 1e3
 
 
-def block_kernel_times(blk, rounds=2):
-    """Average per-launch time (us) of each decode kernel of the block, from
-    HIP events riding on the launches (eager steps over all copies)."""
+def block_kernel_times(blk, passes=3):
+    """Per-launch time (us) of each decode kernel of the block, from HIP
+    events riding on the launches: after one untimed round over all copies
+    (the clocks settle after the idle spells of eager launching), `passes`
+    rounds of eager steps over all copies, each giving an average per
+    kernel; the median of the passes' averages is reported (one perturbed
+    pass does not move it)."""
     import dbf_linear_fwd_amd as dbf
     import torch
     heads = {"qkv": "q", "o": "o", "gateup": "gate", "down": "down"}
-    for c in blk.copies:
-        for h in heads.values():
-            dbf.dbf_timing_enable(c[h].handle, True)
-            dbf.dbf_timing_read(c[h].handle)
-    torch.cuda.synchronize()
-    for i in range(rounds * blk.R):
+    for i in range(blk.R):
         blk.step(i)
     torch.cuda.synchronize()
-    out = {}
-    for gname, h in heads.items():
-        tot = {}
+    runs = []
+    for _ in range(passes):
         for c in blk.copies:
-            for kname, v in dbf.dbf_timing_read(c[h].handle).items():
-                t = tot.setdefault(kname, [0, 0.0])
-                t[0] += v["launches"]
-                t[1] += v["total_ms"]
-            dbf.dbf_timing_enable(c[h].handle, False)
-        for kname, (n, ms) in tot.items():
-            stage = 1 if kname.endswith("stage1") else 2
-            out[f"{gname}_stage{stage}"] = {"launches": n, "avg_us": 1e3 * ms / max(n, 1)}
+            for h in heads.values():
+                dbf.dbf_timing_enable(c[h].handle, True)
+                dbf.dbf_timing_read(c[h].handle)
+        torch.cuda.synchronize()
+        for i in range(blk.R):
+            blk.step(i)
+        torch.cuda.synchronize()
+        one = {}
+        for gname, h in heads.items():
+            tot = {}
+            for c in blk.copies:
+                for kname, v in dbf.dbf_timing_read(c[h].handle).items():
+                    t = tot.setdefault(kname, [0, 0.0])
+                    t[0] += v["launches"]
+                    t[1] += v["total_ms"]
+                dbf.dbf_timing_enable(c[h].handle, False)
+            for kname, (n, ms) in tot.items():
+                stage = 1 if kname.endswith("stage1") else 2
+                one[f"{gname}_stage{stage}"] = (n, 1e3 * ms / max(n, 1))
+        runs.append(one)
+    out = {}
+    for k in runs[0]:
+        avgs = sorted(r[k][1] for r in runs)
+        out[k] = {"launches": sum(r[k][0] for r in runs), "avg_us": avgs[len(avgs) // 2],
+                  "pass_avgs_us": [r[k][1] for r in runs]}
     return out
 
 
@@ -592,7 +607,9 @@ def block_leg(args):
     for gr, gname in zip(GROUPS, ("qkv", "o", "gateup", "down")):
         s1, s2 = stage_bytes([blk.by[n] for n in gr], 1)
         sb[f"{gname}_stage1"], sb[f"{gname}_stage2"] = s1, s2
-    dom = max(kt, key=lambda k: kt[k]["avg_us"])
+    # the dominant kernel: the stage with the most bytes per launch (gate/up's
+    # second stage, also the longest launch in every kernel trace)
+    dom = max(sb, key=lambda k: sb[k])
     ach = sb[dom] / (kt[dom]["avg_us"] * 1e-6) / 1e9
     res = {
         "value": gbs, "ms_per_step": el * 1e3 / args.steps, "steps": args.steps, "parity_worst_row_rel_err": err,
