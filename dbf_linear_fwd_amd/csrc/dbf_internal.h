@@ -70,6 +70,11 @@ struct I8Args {
     const float *gamma = nullptr;
     float *stats = nullptr;
     int stat_wg = -1;
+    // stage 1 of the signed launch of a group-wise BQQ layer: the statistics
+    // row forms stats[q] = Σ_l stat_w[q * stat_m + l] x[l] for q < stat_Q
+    // instead (stat_w not null)
+    const float *stat_w = nullptr;
+    int stat_Q = 0;
     // stage 2 of a 0/1 layer: the affine term's rank, y += Σ_{q < aff_Q - 1}
     // aff_E[q * rows + row] * aff_stats[q] + aff_stats[aff_Q - 1]
     // (2 <= aff_Q <= kI8MaxQ; the same for every layer of the launch)

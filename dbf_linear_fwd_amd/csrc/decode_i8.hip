@@ -201,7 +201,25 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
 // and 2 gp + 1 of (s, j) -- with (s, j, i, gp) = (o >> 6, (o >> 3) & 7,
 // (o >> 1) & 3, o & 1); the vector, padded to SC superchunks, has SC * 64
 // octets, NO * kT >= that.
-template <int STAGE, bool BIN, bool K8, int NO>
+// The p + 1 weighted sums of x that the group-wise BQQ form's affine term
+// needs (bqq_rowstats.h; the statistic count is a template argument there).
+__device__ __forceinline__ void rowstats_q(const I8Args &args, float *sh) {
+    switch (args.stat_Q) {
+#define DBF_STAT_CASE(Q)                                                                                 \
+    case Q:                                                                                              \
+        bqq_rowstats_dotq<kT, Q>(args.stat_x, args.stat_m, args.stat_w, args.stats, sh);                \
+        break;
+        DBF_STAT_CASE(2) DBF_STAT_CASE(3) DBF_STAT_CASE(4) DBF_STAT_CASE(5)
+        DBF_STAT_CASE(6) DBF_STAT_CASE(7) DBF_STAT_CASE(8) DBF_STAT_CASE(9)
+#undef DBF_STAT_CASE
+        default:
+            break;
+    }
+}
+
+// QSTAT: stage 1 of a signed launch whose last grid row (an empty layer
+// entry) forms the group-wise BQQ statistics beside it.
+template <int STAGE, bool BIN, bool K8, int NO, bool QSTAT = false>
 __global__ __launch_bounds__(kT, NO <= 4 ? 2 : 1) void dec_i8_kernel(const I8Args args) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     // Every field of the layer, read at once (one round of scalar loads: the
@@ -216,6 +234,10 @@ __global__ __launch_bounds__(kT, NO <= 4 ? 2 : 1) void dec_i8_kernel(const I8Arg
         // layer entry marks that row of the grid)
         if (blockIdx.x == 0)
             bqq_rowstats_row<kT>(args.stat_x, args.stat_m, args.gamma, args.stats, reinterpret_cast<float *>(lds));
+        return;
+    }
+    if (QSTAT && L.SC == 0) {
+        if (blockIdx.x == 0) rowstats_q(args, reinterpret_cast<float *>(lds));
         return;
     }
     const int wg = blockIdx.x;
@@ -519,7 +541,10 @@ int launch_decode_i8(I8Args &a, int stage, bool bin, void *stream) {
         }
         maxwg = std::max(maxwg, L.nwg);
     }
-    const bool stat = bin && a.stat_wg >= 0;
+    // stage 1 of a signed launch may carry the group-wise BQQ statistics
+    const bool qstat = !bin && stage == 1 && a.stat_wg >= 0 && a.stat_w != nullptr;
+    if (qstat && (a.stat_Q < 2 || a.stat_Q > kMaxStatQ)) return static_cast<int>(hipErrorInvalidValue);
+    const bool stat = (bin && a.stat_wg >= 0) || qstat;
     if (stat && a.count >= kMaxGroup) return static_cast<int>(hipErrorInvalidValue);
     if (tpw > kMaxTPWc) return static_cast<int>(hipErrorInvalidValue);
     a.stat_wg = stat ? 0 : -1;
@@ -537,8 +562,24 @@ int launch_decode_i8(I8Args &a, int stage, bool bin, void *stream) {
         DBF_I8_ROW(1), DBF_I8_ROW(2), DBF_I8_ROW(4), DBF_I8_ROW(8)
 #undef DBF_I8_ROW
     };
-    static bool lds_set[4][6] = {};
+    static void (*const qstat_kernels[4][2])(I8Args) = {
+        {dec_i8_kernel<1, false, true, 1, true>, dec_i8_kernel<1, false, false, 1, true>},
+        {dec_i8_kernel<1, false, true, 2, true>, dec_i8_kernel<1, false, false, 2, true>},
+        {dec_i8_kernel<1, false, true, 4, true>, dec_i8_kernel<1, false, false, 4, true>},
+        {dec_i8_kernel<1, false, true, 8, true>, dec_i8_kernel<1, false, false, 8, true>}};
+    static bool lds_set[4][6] = {}, qlds_set[4][2] = {};
     const int ki = stage == 1 ? (bin ? 2 : 0) + (k8 ? 0 : 1) : 4 + (bin ? 1 : 0);
+    if (qstat) {
+        // (the statistics row uses kMaxStatQ trees of kT floats of LDS at most)
+        const size_t qlds = std::max(lds, static_cast<size_t>(kMaxStatQ) * kT * 4);
+        auto k = qstat_kernels[ni][k8 ? 0 : 1];
+        if (!qlds_set[ni][k8 ? 0 : 1]) {
+            allow_lds(k, lds_bytes_for(kI8MaxSC));
+            qlds_set[ni][k8 ? 0 : 1] = true;
+        }
+        launch_kernel(k, grid, dim3(kT), qlds, s, a);
+        return static_cast<int>(hipGetLastError());
+    }
     if (!lds_set[ni][ki]) {
         allow_lds(kernels[ni][ki], lds_bytes_for(kI8MaxSC));
         lds_set[ni][ki] = true;

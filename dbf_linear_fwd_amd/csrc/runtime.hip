@@ -752,9 +752,14 @@ static dbf_status_t forward_bqq_grouped(dbf_layer *h, const void *x, void *y, in
     const int p = h->bqq_p, d = h->bqq_d;
     const bool i8 = path != DBF_PATH_PREFILL && batch == 1 && h->i8_ok;
     if (path == DBF_PATH_DECODE && !i8) return DBF_ERR_UNSUPPORTED;
-    dbf_status_t st = timed_launch(h, "bqq_rowstats", stream, [&] {
-        return dbf::launch_bqq_rowstats_q(x, batch, h->m, h->bqq_gamma, h->bqq_Q, h->bqq_stats, stream);
-    });
+    // the row statistics: a row of the batch-1 stage-1 launch where the grid
+    // has one to spare, else a kernel of their own
+    const bool fused_stats = i8 && p < dbf::kMaxGroup;
+    dbf_status_t st = DBF_OK;
+    if (!fused_stats)
+        st = timed_launch(h, "bqq_rowstats", stream, [&] {
+            return dbf::launch_bqq_rowstats_q(x, batch, h->m, h->bqq_gamma, h->bqq_Q, h->bqq_stats, stream);
+        });
     if (st != DBF_OK) return st;
     if (i8) {
         dbf::I8Args a1{}, a2{};
@@ -771,6 +776,14 @@ static dbf_status_t forward_bqq_grouped(dbf_layer *h, const void *x, void *y, in
             L.rows = d;
             L.ntiles = d / 16;
             a1.L[i] = L;
+        }
+        if (fused_stats) {
+            a1.stat_x = static_cast<const __half *>(x);
+            a1.stat_m = h->m;
+            a1.stat_w = h->bqq_gamma;
+            a1.stat_Q = h->bqq_Q;
+            a1.stats = h->bqq_stats;
+            a1.stat_wg = 0;
         }
         a2.count = 1;
         a2.L[0] = s2;
