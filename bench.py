@@ -24,8 +24,10 @@ Secondary measurements in the same line: the batch-2048 half of the metric
 (TFLOP/s-equivalent = 2*batch*k*(n+m) per forward) on the MLP up and down
 projections (14336x4096 and 4096x14336, k = 4800), also parity-checked
 first; the roofline of the dominant decode kernel (per-launch HIP events on
-the launch stream); the CPU oracle timed on the host on a bounded sample of
-the same workload; gradients, the BQQ-form layer and the factorization.
+the launch stream); one cold forward of each layer after a 512 MiB scrub;
+the CPU oracle timed on the host on a bounded sample of the same workload
+(all BLAS threads and one); gradients, the BQQ-form layer, the factorization,
+and the GPU's attainable copy and streaming-read rates.
 """
 
 from __future__ import annotations
@@ -603,6 +605,8 @@ def block_leg(args):
     el_long = time_exact(blk.step, long_steps, blk.R, start=args.steps)
     kt = block_kernel_times(blk)
     print(f"[bench] block kernels: {kt}", file=sys.stderr, flush=True)
+    cold = cold_latency(blk)
+    print(f"[bench] cold single-layer forwards after a 512 MiB scrub (us): {cold}", file=sys.stderr, flush=True)
     sb = {}
     for gr, gname in zip(GROUPS, ("qkv", "o", "gateup", "down")):
         s1, s2 = stage_bytes([blk.by[n] for n in gr], 1)
@@ -619,10 +623,35 @@ def block_leg(args):
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBS, "traffic": recorded_traffic(dom), "kernel": dom,
                      "algorithmic_bytes_per_launch": sb[dom]},
-        "block_bytes": blk.bytes, "copies": blk.R,
+        "block_bytes": blk.bytes, "copies": blk.R, "cold_us": cold,
     }
     blk.close()
     return res
+
+
+def cold_latency(blk, reps=5, scrub_mb=512):
+    """One batch-1 forward of each layer of the block, alone, after a
+    512 MiB scrub write (nothing of the layer left in the caches): the median
+    over `reps` tries of its wall time between events on the launch stream
+    (launch gaps included), in us."""
+    import torch
+    scrub = torch.empty(scrub_mb << 18, dtype=torch.float32, device="cuda")
+    c = blk.copies[0]
+    out = {}
+    for L in blk.layers:
+        ts = []
+        for _ in range(reps):
+            scrub.fill_(1.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            c[L.name].forward(blk.xs[L.name], out=blk.ys[L.name])
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        out[L.name] = sorted(ts)[reps // 2]
+    del scrub
+    torch.cuda.empty_cache()
+    return out
 
 
 def layer_leg(args):
@@ -798,48 +827,82 @@ def block_prefill_leg(args):
 def cpu_baseline(seconds):
     """The fp64 oracle's factored forward (the §2.1 evaluation order) of the
     decoder block's seven layers at batch 1, on the host's BLAS threads,
-    repeated for about `seconds`; GB/s of packed weights, the headline's unit."""
+    repeated for about `seconds`; GB/s of packed weights, the headline's unit.
+    Beside it: the same on one BLAS thread (about a quarter of `seconds`), and
+    the oracle's dense form on the block's q projection -- forming W once
+    (2nmk fp64 flops) and one batch-1 X Wᵀ (the median of 5)."""
     from oracle import dbf_oracle as O
     from tests import inputs
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     except Exception:
+        threadpool_limits = None
         threads = os.cpu_count() or 1
     layers = inputs.config(5).layers
     nbytes = block_bytes_of(layers)
-    blocks = 0
+
+    def run(limit_s):
+        blocks = 0
+        t0 = time.perf_counter()
+        while True:
+            for L in layers:
+                O.factored_forward(L.X[1], L.A, L.B, L.a, L.mid, L.b)
+            blocks += 1
+            el = time.perf_counter() - t0
+            if el >= limit_s:
+                return blocks, el
+    blocks, el = run(seconds)
+    res = {"value": nbytes * blocks / el / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"{blocks} batch-1 forwards of the decoder block's 7 layers through the fp64 oracle "
+                     f"(factored evaluation order) in {el:.1f} s",
+           "host_cpu_count": os.cpu_count()}
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            b1, e1 = run(seconds / 4)
+        res["one_core"] = {"value": nbytes * b1 / e1 / 1e9, "unit": "GB/s", "cores": 1,
+                           "sample": f"{b1} block forwards in {e1:.1f} s"}
+    q = layers[0]
     t0 = time.perf_counter()
-    while True:
-        for L in layers:
-            O.factored_forward(L.X[1], L.A, L.B, L.a, L.mid, L.b)
-        blocks += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": nbytes * blocks / el / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{blocks} batch-1 forwards of the decoder block's 7 layers through the fp64 oracle "
-                      f"(factored evaluation order) in {el:.1f} s",
-            "host_cpu_count": os.cpu_count()}
+    W = O.dense_weight(q.A, q.B, q.a, q.mid, q.b)
+    w_s = time.perf_counter() - t0
+    ts = []
+    x = O.widen(q.X[1])
+    for _ in range(5):
+        t0 = time.perf_counter()
+        _ = x @ W.T
+        ts.append(time.perf_counter() - t0)
+    res["dense_q_layer"] = {"layer": f"{q.n}x{q.m}, k={q.k}", "weight_s": w_s,
+                            "weight_gflop": 2 * q.n * q.m * q.k / 1e9, "forward_ms": 1e3 * sorted(ts)[2],
+                            "cores": int(threads)}
+    return res
 
 
 def context_leg():
-    """The attainable HBM rate on this GPU: a plain 1 GiB device copy."""
+    """The attainable HBM rates on this GPU: a plain 1 GiB device copy (read
+    and write), and a streaming read of 1 GiB (torch's sum: one read of the
+    buffer, a few bytes written)."""
     import torch
-    buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(buf)
     dst.copy_(buf)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(10):
-        dst.copy_(buf)
-    e1.record()
-    torch.cuda.synchronize()
-    gbs = 10 * 2 * buf.numel() * 4 / (e0.elapsed_time(e1) / 1e3) / 1e9
+
+    def rate(fn, bytes_per_call, reps=10):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return reps * bytes_per_call / (e0.elapsed_time(e1) / 1e3) / 1e9
+    copy_gbs = rate(lambda: dst.copy_(buf), 2 * buf.numel() * 4)
+    acc = torch.empty((), dtype=torch.float32, device="cuda")
+    torch.sum(buf, dim=0, out=acc)
+    read_gbs = rate(lambda: torch.sum(buf, dim=0, out=acc), buf.numel() * 4)
     del buf, dst
     torch.cuda.empty_cache()
-    return {"device_copy_1GiB_gbs": gbs}
+    return {"device_copy_1GiB_gbs": copy_gbs, "streaming_read_1GiB_gbs": read_gbs}
 
 
 def main():
@@ -905,6 +968,7 @@ def main():
         "parity_worst_row_rel_err": d["parity_worst_row_rel_err"],
         "decode_block_steady_state": d["steady_state"],
         "decode_kernels": d["kernels"],
+        "decode_cold_layer_us": d["cold_us"],
     }
     if "prefill" in result:
         line["prefill_batch2048"] = result["prefill"]
