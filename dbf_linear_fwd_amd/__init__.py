@@ -298,9 +298,12 @@ def forward_group(layers, x, outs=None):
         raise ValueError("x must be a contiguous 2-D float16 CUDA tensor")
     if outs is None:
         outs = [torch.empty((x.shape[0], L.n), dtype=torch.float16, device=x.device) for L in layers]
+    if len(outs) != len(layers):
+        raise ValueError("one output per layer")
     for L, y in zip(layers, outs):
-        if y.dtype != torch.float16 or not y.is_cuda or tuple(y.shape) != (x.shape[0], L.n) or not y.is_contiguous():
-            raise ValueError("outs[i] must be a contiguous float16 CUDA tensor of shape (batch, n_i)")
+        if (y.dtype != torch.float16 or not y.is_cuda or tuple(y.shape) != (x.shape[0], L.n) or not y.is_contiguous()
+                or y.device != x.device):
+            raise ValueError("outs[i] must be a contiguous float16 tensor of shape (batch, n_i) on x's device")
     stream = torch.cuda.current_stream(x.device).cuda_stream
     dbf_linear_forward_group([L.handle for L in layers], x.data_ptr(), [y.data_ptr() for y in outs], x.shape[0],
                              stream)
@@ -439,6 +442,11 @@ class Layer:
         import torch
         if x.dtype != torch.float16 or not x.is_cuda or x.dim() != 2 or x.shape[1] != self.m:
             raise ValueError(f"x must be a CUDA float16 tensor of shape (batch, {self.m})")
+        dev = getattr(self, "_device", None)
+        if dev is None:
+            dev = self._device = self.info()["device"]
+        if x.device.index is not None and x.device.index != dev:
+            raise ValueError("x must be on the layer's device")
         if not x.is_contiguous():
             raise ValueError("x must be contiguous")
         batch = x.shape[0]
@@ -466,6 +474,8 @@ class Layer:
         if out is None:
             out = torch.empty((dy.shape[0], self.m), dtype=torch.float16, device=dy.device)
         self._check_act(out, self.m, "out")
+        if out.shape[0] != dy.shape[0] or out.device != dy.device:
+            raise ValueError("out must have dy's batch and device")
         stream = torch.cuda.current_stream(dy.device).cuda_stream
         dbf_linear_backward_data(self.handle, dy.data_ptr(), out.data_ptr(), dy.shape[0], stream)
         return out
@@ -475,8 +485,8 @@ class Layer:
         import torch
         self._check_act(x, self.m, "x")
         self._check_act(dy, self.n, "dy")
-        if x.shape[0] != dy.shape[0]:
-            raise ValueError("x and dy must have the same batch")
+        if x.shape[0] != dy.shape[0] or x.device != dy.device:
+            raise ValueError("x and dy must have the same batch and device")
         dev = x.device
         dx = torch.empty((x.shape[0], self.m), dtype=torch.float16, device=dev)
         da = torch.empty(self.n, dtype=torch.float32, device=dev)

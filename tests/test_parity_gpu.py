@@ -424,16 +424,28 @@ def test_large_input_products_bit_exact(gpu, batch):
 
 
 def test_forward_rejects_host_output(gpu):
-    """An out= tensor in host memory (or on another device) is refused before
-    anything is launched."""
+    """An out= tensor in host memory (or on another device), a missing
+    grouped output or a dX output of another batch is refused before anything
+    is launched."""
     torch = _torch()
     _say("host out tensor")
     L = inputs.random_layer("h", 64, 96, 32, 3, 0.05, 1.0, 0.05, (2,))
-    H = dbf.Layer(L.A, L.B, L.a, L.mid, L.b, max_batch=2)
+    H = dbf.Layer(L.A, L.B, L.a, L.mid, L.b, max_batch=4, backward=True)
     try:
         x = torch.from_numpy(L.X[2]).cuda()
         with pytest.raises(ValueError):
             H.forward(x, out=torch.empty((2, 64), dtype=torch.float16))
+        # grouped outputs: in host memory, or fewer than the layers
+        with pytest.raises(ValueError):
+            dbf.forward_group([H, H], x, [torch.empty((2, 64), dtype=torch.float16, device="cuda"),
+                                          torch.empty((2, 64), dtype=torch.float16)])
+        with pytest.raises(ValueError):
+            dbf.forward_group([H, H], x, [torch.empty((2, 64), dtype=torch.float16, device="cuda")])
+        # dX output with another batch than dy (the kernel would write dy's rows)
+        dy = torch.zeros((2, 64), dtype=torch.float16, device="cuda")
+        with pytest.raises(ValueError):
+            H.backward_data(dy, out=torch.empty((1, 96), dtype=torch.float16, device="cuda"))
+        torch.cuda.synchronize()
     finally:
         H.close()
 
