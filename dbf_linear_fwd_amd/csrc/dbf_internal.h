@@ -79,7 +79,13 @@ struct I8Args {
     // aff_E[q * rows + row] * aff_stats[q] + aff_stats[aff_Q - 1]
     // (2 <= aff_Q <= kI8MaxQ; the same for every layer of the launch)
     int aff_Q = 2;
+    // batch rows (1..kI8MaxRows): vector r is at vec + r * K entries and its
+    // result at out + r * rows; more than one row: signed layers, no
+    // statistics row, at most kI8RowsMaxSC superchunks
+    int nrows = 1;
 };
+constexpr int kI8MaxRows = 4;
+constexpr int kI8RowsMaxSC = 16;
 constexpr int kI8MaxQ = 9;
 // stage = 1 or 2; bin: 0/1 matrices (Z instead of U - 2 Z, times 2).
 int launch_decode_i8(I8Args &a, int stage, bool bin, void *stream);

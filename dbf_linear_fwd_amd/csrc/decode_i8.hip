@@ -66,13 +66,14 @@ constexpr int kT = kW * 64;           // threads per workgroup
 constexpr int kCUs = 256;             // MI355X
 constexpr int kMaxTPWc = 8;           // tiles per workgroup, at most
 constexpr int kActSC = 2048;          // LDS bytes of digits per superchunk: [8 j][16 slots][16]
-constexpr int kPartBytes = kMaxTPWc * 16 * 8;  // [tile][row] int64: Z of the workgroup's rows
-// wave maxima and sums, row scales (fp32), affine terms of 0/1 layers (fp64)
-constexpr int kMiscBytes = kW * 4 + kW * 8 + kMaxTPWc * 16 * 4 + kMaxTPWc * 16 * 8;
+constexpr int kPartBytes = kMaxTPWc * 16 * 8;  // [tile][row] int64: Z of the workgroup's rows, per vector
+// wave maxima and sums (per vector), row scales (fp32), affine terms of 0/1 layers (fp64)
+constexpr int kMiscBytes = kMaxTPWc * 16 * 4 + kMaxTPWc * 16 * 8;
+constexpr int kWaveBytes = kW * 4 + kW * 8;
 constexpr int kRing = 3;              // superchunks of signs in flight per wave
 
-__host__ __device__ constexpr size_t lds_bytes_for(int SC) {
-    return static_cast<size_t>(SC) * kActSC + kPartBytes + kMiscBytes;
+__host__ __device__ constexpr size_t lds_bytes_for(int SC, int NB = 1) {
+    return static_cast<size_t>(NB) * (static_cast<size_t>(SC) * kActSC + kPartBytes + kWaveBytes) + kMiscBytes;
 }
 
 // Digits in LDS.  Block (s, j, g) -- the 16 vector entries 512 s + 128 i +
@@ -219,8 +220,12 @@ __device__ __forceinline__ void rowstats_q(const I8Args &args, float *sh) {
 
 // QSTAT: stage 1 of a signed launch whose last grid row (an empty layer
 // entry) forms the group-wise BQQ statistics beside it.
-template <int STAGE, bool BIN, bool K8, int NO, bool QSTAT = false>
+// NB: the workgroup takes NB input vectors (batch rows) at once, each with
+// its own exponent and its own digits (columns 4 r .. 4 r + 3 of the product
+// for row r); rows from args.nrows on read as zero and are not stored.
+template <int STAGE, bool BIN, bool K8, int NO, bool QSTAT = false, int NB = 1>
 __global__ __launch_bounds__(kT, NO <= 4 ? 2 : 1) void dec_i8_kernel(const I8Args args) {
+    static_assert(NB == 1 || (!BIN && !QSTAT && NB * 4 <= 16), "batch rows: signed layers, 16 product columns");
     extern __shared__ __attribute__((aligned(16))) char lds[];
     // Every field of the layer, read at once (one round of scalar loads: the
     // empty asm takes them all as inputs, so none of the loads is sunk into
@@ -255,11 +260,11 @@ __global__ __launch_bounds__(kT, NO <= 4 ? 2 : 1) void dec_i8_kernel(const I8Arg
     const int lt = job & 7, s0 = (job >> 3) & 63;
     const int nu = lt < nt ? static_cast<int>(job >> 9) : 0;
 
-    char *act = lds;                                                     // digits [SC][8 j][4 g][4 c][16]
-    long long *zrow = reinterpret_cast<long long *>(lds + static_cast<size_t>(SC) * kActSC);  // [tile][row]
-    float *wmax = reinterpret_cast<float *>(zrow + kPartBytes / 8);      // [kW]
-    long long *wU = reinterpret_cast<long long *>(wmax + kW);            // [kW]
-    float *scl = reinterpret_cast<float *>(wU + kW);  // [kMaxTPWc * 16] row scales (a or mid)
+    char *act = lds;  // digits [NB][SC][8 j][4 g][4 c][16]
+    long long *zrow = reinterpret_cast<long long *>(lds + static_cast<size_t>(NB) * SC * kActSC);  // [NB][tile][row]
+    float *wmax = reinterpret_cast<float *>(zrow + NB * (kPartBytes / 8));  // [NB][kW]
+    long long *wU = reinterpret_cast<long long *>(wmax + NB * kW);          // [NB][kW]
+    float *scl = reinterpret_cast<float *>(wU + NB * kW);  // [kMaxTPWc * 16] row scales (a or mid)
     double *saff = reinterpret_cast<double *>(scl + kMaxTPWc * 16);  // [kMaxTPWc * 16] affine terms (0/1 layers)
 
     // ---- loads, in the order their data is used (a wave waits for its
@@ -267,14 +272,21 @@ __global__ __launch_bounds__(kT, NO <= 4 ? 2 : 1) void dec_i8_kernel(const I8Arg
     // kRing superchunks of signs
     const int noct = SC * 64;
     const uint32_t kb = static_cast<uint32_t>(L.K);
-    const __amdgpu_buffer_rsrc_t rx = rsrc(L.vec, kb * (STAGE == 1 ? 2u : 4u));
     const __amdgpu_buffer_rsrc_t rb = rsrc(L.bsc, STAGE == 1 ? 2u * kb : 0u);
-    Octet raw[NO];
+    const int nrows = NB == 1 ? 1 : args.nrows;
+    Octet raw[NB][NO];
 #pragma unroll
-    for (int k = 0; k < NO; ++k) {
-        const int o = tid + kT * k;
-        const int base = 512 * (o >> 6) + 16 * ((o >> 3) & 7) + 128 * ((o >> 1) & 3) + 8 * (o & 1);
-        raw[k] = load_octet<STAGE, K8>(rx, rb, o < noct ? base : (1 << 27));
+    for (int r = 0; r < NB; ++r) {
+        // vector r: row r of the batch (K entries apart); rows past nrows read as zero
+        const __amdgpu_buffer_rsrc_t rx =
+            rsrc(static_cast<const char *>(L.vec) + static_cast<size_t>(r) * kb * (STAGE == 1 ? 2u : 4u),
+                 r < nrows ? kb * (STAGE == 1 ? 2u : 4u) : 0u);
+#pragma unroll
+        for (int k = 0; k < NO; ++k) {
+            const int o = tid + kT * k;
+            const int base = 512 * (o >> 6) + 16 * ((o >> 3) & 7) + 128 * ((o >> 1) & 3) + 8 * (o & 1);
+            raw[r][k] = load_octet<STAGE, K8>(rx, rb, o < noct ? base : (1 << 27));
+        }
     }
     // thread tid < nt * 16 finishes row t0 * 16 + tid
     const int my_row = min(t0 * 16 + tid, L.rows - 1);
@@ -312,30 +324,39 @@ __global__ __launch_bounds__(kT, NO <= 4 ? 2 : 1) void dec_i8_kernel(const I8Arg
     for (int q = 0; q < kRing; ++q)
         ring[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, unit_off(q), 0, 0));
 
-    // ---- the vector as fixed-point digits, one exponent for the workgroup
-    float mx = 0.0f;
+    // ---- each vector as fixed-point digits, one exponent per vector for the workgroup
 #pragma unroll
-    for (int k = 0; k < NO; ++k) {
-        float u[8];
-        octet_values<STAGE>(raw[k], u);
+    for (int r = 0; r < NB; ++r) {
+        float mx = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(u[e]));
+        for (int k = 0; k < NO; ++k) {
+            float u[8];
+            octet_values<STAGE>(raw[r][k], u);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(u[e]));
+        }
+        mx = wave_max_nonneg(mx);
+        if (lane == 0) wmax[r * kW + w] = mx;
     }
-    mx = wave_max_nonneg(mx);
-    if (lane == 0) wmax[w] = mx;
     __syncthreads();
+    int S[NB];
 #pragma unroll
-    for (int ww = 0; ww < kW; ++ww) mx = fmaxf(mx, wmax[ww]);
-    int S = 0;
-    if (mx > 0.0f) {
-        int E;
-        (void)frexpf(mx, &E);  // mx = f 2^E, f in [0.5, 1)
-        S = 30 - E;            // mx 2^S in [2^29, 2^30)
+    for (int r = 0; r < NB; ++r) {
+        float mx = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < kW; ++ww) mx = fmaxf(mx, wmax[r * kW + ww]);
+        S[r] = 0;
+        if (mx > 0.0f) {
+            int E;
+            (void)frexpf(mx, &E);  // mx = f 2^E, f in [0.5, 1)
+            S[r] = 30 - E;         // mx 2^S in [2^29, 2^30)
+        }
     }
     // the row scales, kept in LDS for the finishing threads (their loads
     // are waited for here, not behind the last sign loads)
     if (tid < nt * 16) {
-        zrow[tid] = 0;
+#pragma unroll
+        for (int r = 0; r < NB; ++r) zrow[r * (kPartBytes / 8) + tid] = 0;
         scl[tid] = osc_v;
         if constexpr (STAGE == 2 && BIN) {
             // Σ_{q < Q-1} E_q[row] s_q + s_{Q-1} in fp64 (exact products of fp32 values)
@@ -351,20 +372,23 @@ __global__ __launch_bounds__(kT, NO <= 4 ? 2 : 1) void dec_i8_kernel(const I8Arg
             saff[tid] = t + last;
         }
     }
+#pragma unroll
+    for (int r = 0; r < NB; ++r) {
+    char *actr = act + static_cast<size_t>(r) * SC * kActSC;
     int dsum[4] = {0, 0, 0, 0};  // Σ of each digit plane over this thread's octets
 #pragma unroll
     for (int k = 0; k < NO; ++k) {
         const int o = tid + kT * k;
         if (o < noct) {
             float u[8];
-            octet_values<STAGE>(raw[k], u);
+            octet_values<STAGE>(raw[r][k], u);
             const int sj = o >> 3, j = sj & 7, i = (o >> 1) & 3, gp = o & 1;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {  // block g = 2 gp + h: entries 4 h .. 4 h + 3
                 uint32_t E[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int q = __float2int_rn(ldexpf(u[4 * h + e], S));
+                    const int q = __float2int_rn(ldexpf(u[4 * h + e], S[r]));
                     // balanced base-256 digits: the bytes of (q + 0x808080) ^ 0x808080
                     E[e] = (static_cast<uint32_t>(q) + 0x808080u) ^ 0x808080u;
                 }
@@ -382,7 +406,7 @@ __global__ __launch_bounds__(kT, NO <= 4 ? 2 : 1) void dec_i8_kernel(const I8Arg
                 for (int c = 0; c < 4; ++c) {
                     dsum[c] = __builtin_amdgcn_sdot4(static_cast<int>(Pc[c]), 0x01010101, dsum[c], false);
                     // bytes 4 i .. 4 i + 3 of plane c of block (s, j, g)
-                    *reinterpret_cast<uint32_t *>(act + 256 * sj + 16 * digit_slot(g, c, j) + 4 * i) = Pc[c];
+                    *reinterpret_cast<uint32_t *>(actr + 256 * sj + 16 * digit_slot(g, c, j) + 4 * i) = Pc[c];
                 }
             }
         }
@@ -393,7 +417,8 @@ __global__ __launch_bounds__(kT, NO <= 4 ? 2 : 1) void dec_i8_kernel(const I8Arg
 #pragma unroll
         for (int c = 0; c < 4; ++c)
             U += static_cast<long long>(static_cast<int>(wave_sum_u32(static_cast<uint32_t>(dsum[c])))) * (1LL << (8 * c));
-        if (lane == 0) wU[w] = U;
+        if (lane == 0) wU[r * kW + w] = U;
+    }
     }
     __syncthreads();
 
@@ -402,9 +427,9 @@ __global__ __launch_bounds__(kT, NO <= 4 ? 2 : 1) void dec_i8_kernel(const I8Arg
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = i32x4{0, 0, 0, 0};
     const int c = lane & 15, gq = lane >> 4;
-    // B operand of lane (c, g): 16 bytes of digit plane c; lanes of the
-    // unused columns c >= 4 read nothing (their columns of D are not used).
-    // The slot depends on j mod 4.
+    // B operand of lane (c, g): 16 bytes of digit plane c mod 4 of vector
+    // c / 4; lanes of the unused columns c >= 4 NB read nothing (their
+    // columns of D are not used).  The slot depends on j mod 4.
     int slot_off[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) slot_off[k] = 16 * digit_slot(gq, c & 3, k);
@@ -419,8 +444,8 @@ __global__ __launch_bounds__(kT, NO <= 4 ? 2 : 1) void dec_i8_kernel(const I8Arg
                 if (i < nu) {
                     const int s = s0 + i;
                     i32x4 B[8];
-                    if (c < 4) {
-                        const char *as = act + kActSC * s;
+                    if (c < 4 * NB) {
+                        const char *as = act + kActSC * (static_cast<size_t>(c >> 2) * SC + s);
 #pragma unroll
                         for (int j = 0; j < 8; ++j)
                             B[j] = *reinterpret_cast<const i32x4 *>(as + slot_off[j & 3] + 256 * j);
@@ -444,38 +469,46 @@ __global__ __launch_bounds__(kT, NO <= 4 ? 2 : 1) void dec_i8_kernel(const I8Arg
         // Z of the job's 16 rows, per digit column: Σ_j ±acc_j >> j, added
         // with its weight 256^c to the row's sum in LDS (exact integers, so
         // the order of the additions does not matter)
-        if (c < 4) {
+        if (c < 4 * NB) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 int f = 0;
 #pragma unroll
                 for (int j = 0; j < 7; ++j) f += acc[j][v] >> j;
                 f -= acc[7][v] >> 7;
-                __hip_atomic_fetch_add(&zrow[lt * 16 + 4 * gq + v], static_cast<long long>(f) * (1LL << (8 * c)),
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                __hip_atomic_fetch_add(&zrow[(c >> 2) * (kPartBytes / 8) + lt * 16 + 4 * gq + v],
+                                       static_cast<long long>(f) * (1LL << (8 * (c & 3))), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
             }
         }
     }
     __syncthreads();
 
-    // ---- one thread per row: the parts' exact sums, then the scales
-    if (tid < nt * 16) {
-        long long sf = 2 * zrow[tid];
+    // ---- one thread per (vector, row): the parts' exact sums, then the scales
+    // vector and row of the workgroup (kMaxTPWc * 16 = 128 rows per vector)
+    const int fr = NB == 1 ? 0 : tid >> 7, fi = NB == 1 ? tid : tid & 127;
+    if ((NB == 1 || fr < nrows) && fi < nt * 16) {
+        int Sr = S[0];
+#pragma unroll
+        for (int r = 1; r < NB; ++r) Sr = fr == r ? S[r] : Sr;
+        long long sf = 2 * zrow[fr * (kPartBytes / 8) + fi];
         if constexpr (!BIN) {
             long long U = 0;
 #pragma unroll
-            for (int ww = 0; ww < kW; ++ww) U += wU[ww];
+            for (int ww = 0; ww < kW; ++ww) U += wU[fr * kW + ww];
             sf = U - sf;
         }
-        const double res = ldexp(static_cast<double>(sf), -S) * static_cast<double>(scl[tid]);
-        const int row = t0 * 16 + tid;
+        const double res = ldexp(static_cast<double>(sf), -Sr) * static_cast<double>(scl[fi]);
+        const int row = t0 * 16 + fi;
         if (row < L.rows) {
+            // output rows are L.rows apart
+            const size_t at = NB == 1 ? static_cast<size_t>(row) : static_cast<size_t>(fr) * L.rows + row;
             if constexpr (STAGE == 1) {
-                static_cast<float *>(L.out)[row] = static_cast<float>(res);
+                static_cast<float *>(L.out)[at] = static_cast<float>(res);
             } else {
                 double val = res;
-                if constexpr (BIN) val += saff[tid];
-                static_cast<__half *>(L.out)[row] = rne16_of(val);
+                if constexpr (BIN) val += saff[fi];
+                static_cast<__half *>(L.out)[at] = rne16_of(val);
             }
         }
     }
@@ -494,6 +527,7 @@ int i8_superchunks(int K) { return (round_up_int(K, 128) + 511) / 512; }
 int launch_decode_i8(I8Args &a, int stage, bool bin, void *stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (a.count < 1 || a.count > kMaxGroup) return static_cast<int>(hipErrorInvalidValue);
+    if (a.nrows < 1 || a.nrows > kI8MaxRows || (a.nrows > 1 && bin)) return static_cast<int>(hipErrorInvalidValue);
     if (stage == 2 && bin && (a.aff_Q < 2 || a.aff_Q > kI8MaxQ)) return static_cast<int>(hipErrorInvalidValue);
     for (int i = 0; i < a.count; ++i) {
         const I8Layer &L = a.L[i];
@@ -503,6 +537,7 @@ int launch_decode_i8(I8Args &a, int stage, bool bin, void *stream) {
     }
     int maxSC = 1;
     for (int i = 0; i < a.count; ++i) maxSC = std::max(maxSC, a.L[i].SC);
+    if (a.nrows > 1 && maxSC > kI8RowsMaxSC) return static_cast<int>(hipErrorInvalidValue);
     // vector octets per thread NO = 1, 2, 4, 8 for up to 8, 16, 32, 64
     // superchunks
     const int ni = maxSC <= 8 ? 0 : maxSC <= 16 ? 1 : maxSC <= 32 ? 2 : 3;
@@ -545,12 +580,15 @@ int launch_decode_i8(I8Args &a, int stage, bool bin, void *stream) {
     const bool qstat = !bin && stage == 1 && a.stat_wg >= 0 && a.stat_w != nullptr;
     if (qstat && (a.stat_Q < 2 || a.stat_Q > kMaxStatQ)) return static_cast<int>(hipErrorInvalidValue);
     const bool stat = (bin && a.stat_wg >= 0) || qstat;
+    if (a.nrows > 1 && stat) return static_cast<int>(hipErrorInvalidValue);
     if (stat && a.count >= kMaxGroup) return static_cast<int>(hipErrorInvalidValue);
     if (tpw > kMaxTPWc) return static_cast<int>(hipErrorInvalidValue);
     a.stat_wg = stat ? 0 : -1;
     if (stat) a.L[a.count] = I8Layer{};  // the row of the row-sum workgroup
     const dim3 grid(maxwg, a.count + (stat ? 1 : 0));
-    const size_t lds = lds_bytes_for(maxSC);
+    // batch rows: one kernel form for 2, one for 3 and 4 (rows past nrows read as zero)
+    const int NB = a.nrows == 1 ? 1 : a.nrows == 2 ? 2 : 4;
+    const size_t lds = lds_bytes_for(maxSC, NB);
     // stage 1 reads x in 16-byte octets when every layer's m allows
     bool k8 = true;
     for (int i = 0; i < a.count; ++i) k8 = k8 && (a.L[i].K % 8 == 0);
@@ -569,6 +607,27 @@ int launch_decode_i8(I8Args &a, int stage, bool bin, void *stream) {
         {dec_i8_kernel<1, false, true, 8, true>, dec_i8_kernel<1, false, false, 8, true>}};
     static bool lds_set[4][6] = {}, qlds_set[4][2] = {};
     const int ki = stage == 1 ? (bin ? 2 : 0) + (k8 ? 0 : 1) : 4 + (bin ? 1 : 0);
+    if (NB > 1) {
+        // signed layers only; reductions of at most kI8RowsMaxSC superchunks (NO = 1 or 2)
+        static void (*const rkernels[2][2][3])(I8Args) = {
+#define DBF_I8_NB_ROW(NB_, NO)                                                                              \
+    {dec_i8_kernel<1, false, true, NO, false, NB_>, dec_i8_kernel<1, false, false, NO, false, NB_>,           \
+     dec_i8_kernel<2, false, true, NO, false, NB_>}
+            {DBF_I8_NB_ROW(2, 1), DBF_I8_NB_ROW(2, 2)},
+            {DBF_I8_NB_ROW(4, 1), DBF_I8_NB_ROW(4, 2)}
+#undef DBF_I8_NB_ROW
+        };
+        static bool rlds_set[2][2][3] = {};
+        const int bi = NB == 2 ? 0 : 1, ri = stage == 1 ? (k8 ? 0 : 1) : 2;
+        if (ni > 1) return static_cast<int>(hipErrorInvalidValue);
+        auto k = rkernels[bi][ni][ri];
+        if (!rlds_set[bi][ni][ri]) {
+            allow_lds(k, lds_bytes_for(kI8RowsMaxSC, NB));
+            rlds_set[bi][ni][ri] = true;
+        }
+        launch_kernel(k, grid, dim3(kT), lds, s, a);
+        return static_cast<int>(hipGetLastError());
+    }
     if (qstat) {
         // (the statistics row uses kMaxStatQ trees of kT floats of LDS at most)
         const size_t qlds = std::max(lds, static_cast<size_t>(kMaxStatQ) * kT * 4);

@@ -325,7 +325,8 @@ static dbf_status_t pack_layer(int32_t n, int32_t m, int32_t k, const int8_t *A_
     if (st == DBF_OK && hipDeviceSynchronize() != hipSuccess) st = DBF_ERR_HIP;
     const size_t v16_bytes = sizeof(uint16_t) * 2 * size_t(dec_b) * k_pad;
     if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->v16), v16_bytes);
-    const size_t v32_bytes = sizeof(float) * size_t(k_pad);
+    // v of the batch-1..4 int8 decode, one row of k_pad per batch row
+    const size_t v32_bytes = sizeof(float) * size_t(std::min(max_batch, dbf::kI8MaxRows)) * k_pad;
     if (st == DBF_OK) st = dev_alloc(reinterpret_cast<void **>(&h->v32), v32_bytes);
     // split-K parts: the most that either prefill product takes at any batch
     // <= max_batch (the part count depends on the batch through its 128-row
@@ -659,10 +660,25 @@ static void i8_stages(const dbf_layer *h, const void *x, void *y, dbf::I8Layer &
     }
 }
 
-// Batch 1: two launches of the int8 matrix-core kernels (decode_i8.hip).
-static dbf_status_t forward_decode_i8(dbf_layer *h, const void *x, void *y, hipStream_t stream) {
+// Whether the int8 matrix-core kernels can run a forward at this batch:
+// batch 1 wherever the layouts exist (m and k_pad within the kernels'
+// reduction limit; the default path there); batch 2..4 for signed layers
+// whose reductions have at most kI8RowsMaxSC superchunks (m and k_pad up to
+// 8192), so that the batch's digit planes fit LDS (DBF_PATH_DECODE_EXACT).
+// Each batch row is summed exactly with its own exponent, so its result is
+// bit-identical to its batch-1 forward.
+static bool i8_rows_ok(const dbf_layer *h, int32_t batch) {
+    if (!h->i8_ok || batch < 1 || batch > dbf::kI8MaxRows) return false;
+    if (batch == 1) return true;
+    return !h->binary && h->bqq_groups == 0 && dbf::i8_superchunks(h->m) <= dbf::kI8RowsMaxSC &&
+           dbf::i8_superchunks(h->k_pad) <= dbf::kI8RowsMaxSC;
+}
+
+// Batch 1..4: two launches of the int8 matrix-core kernels (decode_i8.hip).
+static dbf_status_t forward_decode_i8(dbf_layer *h, const void *x, void *y, int32_t batch, hipStream_t stream) {
     dbf::I8Args a1{}, a2{};
     a1.count = a2.count = 1;
+    a1.nrows = a2.nrows = batch;
     i8_stages(h, x, y, a1.L[0], a2.L[0]);
     if (h->binary) {
         a1.stat_x = static_cast<const __half *>(x);
@@ -679,7 +695,7 @@ static dbf_status_t forward_decode_i8(dbf_layer *h, const void *x, void *y, hipS
 
 static dbf_status_t forward_decode_mfma(dbf_layer *h, const void *x, void *y, int32_t batch,
                                         hipStream_t stream) {
-    if (batch == 1 && h->i8_ok) return forward_decode_i8(h, x, y, stream);
+    if (batch == 1 && h->i8_ok) return forward_decode_i8(h, x, y, 1, stream);
     dbf::MfmaDecodeArgs d{};
     d.A_dev = h->A_dev;
     d.B_dev = h->B_dev;
@@ -834,15 +850,21 @@ extern "C" dbf_status_t dbf_linear_forward_ex(dbf_handle_t h, const void *x, voi
     if (!h) return DBF_ERR_INVALID_ARG;
     if (batch < 0 || batch > h->max_batch) return DBF_ERR_INVALID_ARG;
     if (path != DBF_PATH_AUTO && path != DBF_PATH_DECODE && path != DBF_PATH_PREFILL &&
-        path != DBF_PATH_DECODE_TABLE)
+        path != DBF_PATH_DECODE_TABLE && path != DBF_PATH_DECODE_EXACT)
         return DBF_ERR_INVALID_ARG;
     if (path == DBF_PATH_DECODE && batch > dbf::kDecodeMaxBatch) return DBF_ERR_INVALID_ARG;
+    if (path == DBF_PATH_DECODE_EXACT && batch > dbf::kI8MaxRows) return DBF_ERR_INVALID_ARG;
     if (batch == 0) return DBF_OK;
     if (!x || !y || !aligned16(x) || !aligned16(y)) return DBF_ERR_INVALID_ARG;
     int cur = -1;
     if (hipGetDevice(&cur) != hipSuccess) return DBF_ERR_HIP;
     if (cur != h->device) return DBF_ERR_INVALID_ARG;
     if (path == DBF_PATH_DECODE_TABLE) return DBF_ERR_UNSUPPORTED;  // (removed: slower than the matrix cores)
+    if (path == DBF_PATH_DECODE_EXACT) {
+        // the exact int8 sums at batch 1..4, every row the bits of its batch-1 forward
+        if (!i8_rows_ok(h, batch) || h->binary || h->bqq_groups > 0) return DBF_ERR_UNSUPPORTED;
+        return forward_decode_i8(h, x, y, batch, stream);
+    }
     if (h->bqq_groups > 0)
         return forward_bqq_grouped(h, x, y, batch, path, stream);
     const bool decode = path == DBF_PATH_DECODE || (path == DBF_PATH_AUTO && batch <= dbf::kDecodeMaxBatch);
@@ -904,11 +926,21 @@ extern "C" dbf_status_t dbf_linear_forward_group(const dbf_handle_t *hs, int32_t
         return timed_launch(t, "prefill_group_gemm2", stream, [&] { return dbf::launch_sign_gemm_group(g2, stream); });
     }
     if (batch == 1) {
-        bool ok = true;
-        for (int i = 0; i < count; ++i) ok = ok && hs[i]->i8_ok;
-        if (ok) {
+        int nok = 0;
+        for (int i = 0; i < count; ++i) nok += hs[i]->i8_ok ? 1 : 0;
+        if (nok > 0 && nok < count) {
+            // some layers on the int8 kernels, some not: each layer's own
+            // forward, so every output keeps the bits of that forward
+            for (int i = 0; i < count; ++i) {
+                const dbf_status_t st = forward_decode_mfma(hs[i], x, ys[i], batch, stream);
+                if (st != DBF_OK) return st;
+            }
+            return DBF_OK;
+        }
+        if (nok == count) {
             dbf::I8Args a1{}, a2{};
             a1.count = a2.count = count;
+            a1.nrows = a2.nrows = batch;
             for (int i = 0; i < count; ++i) i8_stages(hs[i], x, ys[i], a1.L[i], a2.L[i]);
             dbf_layer *t = hs[0];  // kernel timing follows the first handle
             dbf_status_t st = timed_launch(t, "decode_group_stage1", stream,

@@ -23,13 +23,16 @@
  * Numerics: fp16 in and out, one round-to-nearest-even to fp16 at the end;
  * no flush-to-zero.  At batch 1 (layers with m and k_pad up to 32768) each
  * signed sum is exact: the vector (u = x * b, then v) is brought to 32-bit
- * fixed point with one power-of-two exponent per workgroup, summed as
- * integers on the int8 matrix cores, and v = t * mid is kept in fp32; u may
- * exceed the fp16 range there.  At decode batch 2..16 and on the prefill
- * path the sums accumulate in fp32 and v is rounded once to fp16, the
- * operand of 16-bit matrix-core products, so it must stay inside the fp16
- * range (|v| < 65520); batch 1 on wider layers keeps v as the sum of two
- * fp16 numbers (about 22 significant bits), and u = x * b as well, so there
+ * fixed point with one power-of-two exponent, summed as integers on the
+ * int8 matrix cores, and v = t * mid is kept in fp32; u may exceed the fp16
+ * range there.  DBF_PATH_DECODE_EXACT runs the same exact sums at batch 2..4
+ * (+/-1 layers with m and k_pad up to 8192), each batch row with its own
+ * exponent, so a row's result is the same bits whatever batch it runs in.
+ * At decode batch 2..16 otherwise and on the prefill path the sums
+ * accumulate in fp32 and v is rounded once to fp16, the operand of 16-bit
+ * matrix-core products, so it must stay inside the fp16 range
+ * (|v| < 65520); batch 1 on wider layers keeps v as the sum of two fp16
+ * numbers (about 22 significant bits), and u = x * b as well, so there
  * |x * b| must stay below 65520 too.
  *
  * Packed sign format (the pages fix none; this is the library's own)
@@ -79,8 +82,15 @@ typedef enum {
                                   (batch 1), batch as the MFMA N dimension with v rounded once to
                                   fp16 (batch 2..16); batch must be <= 16 */
     DBF_PATH_PREFILL = 2,      /* tiled MFMA products, intermediate rounded once to fp16; any batch */
-    DBF_PATH_DECODE_TABLE = 3  /* no longer built (it was slower than the matrix cores at every
+    DBF_PATH_DECODE_TABLE = 3, /* no longer built (it was slower than the matrix cores at every
                                   measured shape): always DBF_ERR_UNSUPPORTED */
+    DBF_PATH_DECODE_EXACT = 4  /* batch 1..4: the exact int8 sums of batch 1, one fixed-point
+                                  exponent per batch row, so every output row has the bits of its
+                                  own batch-1 forward (batch-invariant results, for callers that
+                                  must reproduce a request's output whatever it was batched with);
+                                  slower than DBF_PATH_DECODE at batch 3..4.  batch > 4 is
+                                  DBF_ERR_INVALID_ARG; 0/1 (BQQ-form) layers and layers with m or
+                                  k_pad above 8192 (at batch > 1) are DBF_ERR_UNSUPPORTED */
 } dbf_path_t;
 
 typedef struct {
@@ -132,8 +142,8 @@ dbf_status_t dbf_linear_forward(dbf_handle_t h, const void *x, void *y, int32_t 
 /*
  * dbf_linear_forward_ex -- dbf_linear_forward with an explicit kernel path
  * (dbf_path_t).  DBF_PATH_DECODE with batch > 16 is DBF_ERR_INVALID_ARG.
- * Both paths compute the same function; they differ in the fp16 rounding of
- * the intermediate (see "Numerics" above).
+ * The paths compute the same function; they differ in the fp16 rounding of
+ * the intermediate and in the summation (see "Numerics" above).
  */
 dbf_status_t dbf_linear_forward_ex(dbf_handle_t h, const void *x, void *y, int32_t batch,
                                    int32_t path, hipStream_t stream);

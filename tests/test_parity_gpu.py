@@ -504,11 +504,83 @@ def test_determinism_and_batch_independence(gpu):
                 else:
                     # batch 1 keeps v in fp32 (exact sums of a 32-bit fixed
                     # point vector), batch 16 rounds it to fp16 once: equal
-                    # within the parity tolerance
+                    # within the parity tolerance (the exact path gives batch
+                    # 1's bits at batch 2..4: test_decode_exact_rows_match_batch1)
                     d = np.abs(yr[0].astype(np.float64) - y1[r].astype(np.float64)).max()
                     assert d <= TOL * np.abs(y1[r].astype(np.float64)).max(), f"row {r}"
         finally:
             H.close()
+
+
+# Layers on which the exact path runs batch 2..4 (m and k_pad up to 8192):
+# ragged sizes, m not a multiple of 8 (element-wise vector loads), the
+# 4096x4096 projection at about 1 bit per weight, and the largest reduction
+# that qualifies (m = 8192: 16 superchunks, two octets per thread).
+ROWS_SHAPES = [
+    # n, m, k
+    (130, 200, 190),
+    (77, 1001, 333),
+    (4096, 4096, 2048),
+    (300, 8192, 8192),
+]
+
+
+@pytest.mark.parametrize("n,m,k", ROWS_SHAPES)
+def test_decode_exact_rows_match_batch1(gpu, n, m, k):
+    """DBF_PATH_DECODE_EXACT runs batch 1..4 on the batch-1 int8 kernels with
+    one fixed-point exponent per batch row: every row of the batch gives the
+    bits of that row's own batch-1 forward (on either path), and the oracle's
+    values."""
+    torch = _torch()
+    _say(f"int8 batch rows n={n} m={m} k={k}")
+    L = inputs.random_layer("r", n, m, k, 9100 + n + m, 0.02, 1.0, 0.02, (4,))
+    X = L.X[4]
+    H = dbf.Layer(L.A, L.B, L.a, L.mid, L.b, max_batch=4)
+    try:
+        x = torch.from_numpy(X).cuda()
+        one = [H.forward(x[r:r + 1].clone()).cpu().numpy() for r in range(4)]
+        exact = dbf.DBF_PATH_DECODE_EXACT
+        for r in range(4):
+            y1 = H.forward(x[r:r + 1].clone(), path=exact).cpu().numpy()
+            assert np.array_equal(y1.view(np.uint16), one[r].view(np.uint16)), f"batch 1 row {r}"
+        for bt in (2, 3, 4):
+            y = H.forward(x[:bt].clone(), path=exact).cpu().numpy()
+            for r in range(bt):
+                assert np.array_equal(y[r].view(np.uint16), one[r][0].view(np.uint16)), f"batch {bt} row {r}"
+            again = H.forward(x[:bt].clone(), path=exact).cpu().numpy()
+            assert np.array_equal(again.view(np.uint16), y.view(np.uint16)), f"batch {bt} repeated"
+        ref = O.sampled_forward(X, L.A, L.B, L.a, L.mid, L.b, np.arange(4), np.arange(n))
+        assert_tol(y, ref, f"int8 batch 4 {n}x{m}x{k}")
+    finally:
+        H.close()
+
+
+def test_decode_exact_unsupported_layers(gpu):
+    """The exact path refuses batch 2..4 on a layer wider than 8192 and any
+    batch on a 0/1 (BQQ-form) layer, and leaves the output untouched."""
+    torch = _torch()
+    _say("exact path: unsupported layers")
+    L = inputs.random_layer("w", 64, 8320, 64, 11, 0.02, 1.0, 0.02, (2,))
+    H = dbf.Layer(L.A, L.B, L.a, L.mid, L.b, max_batch=2)
+    Q = inputs.bqq_layer("q", 64, 96, 64, 2, 12, (2,))
+    HQ = dbf.Layer.bqq(Q.Y, Q.Z, Q.r, Q.s, Q.t, Q.u, max_batch=2)
+    try:
+        x = torch.from_numpy(L.X[2]).cuda()
+        y = torch.full((2, 64), 7.0, dtype=torch.float16, device="cuda")
+        with pytest.raises(dbf.DbfError) as e:
+            dbf.dbf_linear_forward_ex(H.handle, x.data_ptr(), y.data_ptr(), 2, dbf.DBF_PATH_DECODE_EXACT, 0)
+        assert e.value.status == dbf.DBF_ERR_UNSUPPORTED
+        y1 = H.forward(x[:1].clone(), path=dbf.DBF_PATH_DECODE_EXACT).cpu().numpy()   # batch 1: served
+        assert np.array_equal(y1.view(np.uint16), H.forward(x[:1].clone()).cpu().numpy().view(np.uint16))
+        xq = torch.from_numpy(Q.X[2]).cuda()
+        with pytest.raises(dbf.DbfError) as e:
+            dbf.dbf_linear_forward_ex(HQ.handle, xq.data_ptr(), y.data_ptr(), 1, dbf.DBF_PATH_DECODE_EXACT, 0)
+        assert e.value.status == dbf.DBF_ERR_UNSUPPORTED
+        torch.cuda.synchronize()
+        assert np.all(y.cpu().numpy() == 7.0)
+    finally:
+        H.close()
+        HQ.close()
 
 
 def test_output_guard_regions(gpu):
@@ -584,6 +656,9 @@ def test_error_paths_on_gpu(gpu):
         assert e.value.status == dbf.DBF_ERR_UNSUPPORTED
         with pytest.raises(dbf.DbfError):
             dbf.dbf_linear_forward_ex(H.handle, x.data_ptr(), y.data_ptr(), 4, 7, 0)
+        with pytest.raises(dbf.DbfError) as e:   # the exact path serves batch 1..4
+            dbf.dbf_linear_forward_ex(H.handle, x.data_ptr(), y.data_ptr(), 5, dbf.DBF_PATH_DECODE_EXACT, 0)
+        assert e.value.status == dbf.DBF_ERR_INVALID_ARG
         with pytest.raises(dbf.DbfError):   # misaligned output pointer
             dbf.dbf_linear_forward(H.handle, x.data_ptr(), y.data_ptr() + 2, 4, 0)
         info = H.info()
