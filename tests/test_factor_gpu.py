@@ -10,7 +10,8 @@ is compared is what the method fixes:
   recovered exactly, with and without importance weights, at small and full
   size;
 * from the same start on a noisy DBF matrix, the per-iteration errors agree
-  with the oracle's and the signs agree almost everywhere;
+  with the oracle's and the signs agree almost everywhere (256 x 192 up to
+  2048 x 2048 with k = 1024, with and without importance weights);
 * repeated calls give identical bits;
 * the factors pack into a layer whose forward matches the oracle's DBF
   forward of the same factors.
@@ -88,6 +89,35 @@ def test_matches_the_oracle_on_a_noisy_dbf_matrix(gpu):
     Wo = F.dbf_from_factors(Ao, Bo, ao, mido, bo)
     assert np.linalg.norm(Wg - Wo) <= 5e-3 * np.linalg.norm(Wo)
     assert err[-1] < 0.05
+
+
+# Larger iterate comparisons: ragged sizes with importance weights, and a
+# 2048 x 2048 matrix at k = 1024 (a quarter of the full-size layer per side).
+LARGE_CASES = [
+    # n, m, k, importance, outer, inner
+    (1024, 768, 384, True, 3, 4),
+    (2048, 2048, 1024, False, 2, 3),
+]
+
+
+@pytest.mark.parametrize("n,m,k,importance,outer,inner", LARGE_CASES)
+def test_matches_the_oracle_at_larger_sizes(gpu, n, m, k, importance, outer, inner):
+    _say(f"factorize vs oracle {n}x{m} k={k} importance={importance}")
+    SA, SB, W, U0, V0 = _dbf_case(17 + n, n, m, k, noise=0.02, start_noise=0.3)
+    d_o = d_i = None
+    if importance:
+        rng = np.random.default_rng(18)
+        d_o = rng.uniform(0.5, 2.0, n)
+        d_i = rng.uniform(0.5, 2.0, m)
+    kw = dict(rho_rel=1.0, outer=outer, inner=inner, power_iters=8)
+    A, B, a, mid, b, err = _gpu(W, k, U0, V0, d_o, d_i, **kw)
+    Ao, Bo, ao, mido, bo, erro = F.factorize(W, k, U0, V0, d_out=d_o, d_in=d_i, **kw)
+    _say(f"  gpu err {err.tolist()} oracle err {erro.tolist()}")
+    assert np.allclose(err, erro, rtol=2e-3, atol=1e-5)
+    assert (A == Ao).mean() > 0.995 and (B == Bo).mean() > 0.995
+    Wg = F.dbf_from_factors(A, B, a, mid, b)
+    Wo = F.dbf_from_factors(Ao, Bo, ao, mido, bo)
+    assert np.linalg.norm(Wg - Wo) <= 5e-3 * np.linalg.norm(Wo)
 
 
 def test_repeated_calls_are_identical(gpu):
