@@ -89,8 +89,9 @@ typedef enum {
                                   own batch-1 forward (batch-invariant results, for callers that
                                   must reproduce a request's output whatever it was batched with);
                                   slower than DBF_PATH_DECODE at batch 3..4.  batch > 4 is
-                                  DBF_ERR_INVALID_ARG; 0/1 (BQQ-form) layers and layers with m or
-                                  k_pad above 8192 (at batch > 1) are DBF_ERR_UNSUPPORTED */
+                                  DBF_ERR_INVALID_ARG; 0/1 (BQQ-form) layers, and layers with m
+                                  or k_pad above 32768 (batch 1) or above 8192 (batch 2..4), are
+                                  DBF_ERR_UNSUPPORTED */
 } dbf_path_t;
 
 typedef struct {
