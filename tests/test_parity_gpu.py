@@ -154,7 +154,8 @@ ROW_TILE_SHAPES = [
 
 
 @pytest.mark.parametrize("n,m,k", ROW_TILE_SHAPES)
-# 1: hi/lo planes in one MFMA; 6, 9: the single-plane form
+# 1: the int8 kernels (every k here is within their reduction limit); 6, 9: the
+# single-plane f16 form
 @pytest.mark.parametrize("batch", [1, 6, 9])
 def test_decode_row_tile_variants(gpu, n, m, k, batch):
     _say(f"decode row tiles n={n} m={m} k={k} batch={batch}")
@@ -510,6 +511,49 @@ def test_determinism_and_batch_independence(gpu):
                     assert d <= TOL * np.abs(y1[r].astype(np.float64)).max(), f"row {r}"
         finally:
             H.close()
+
+
+# The batch-1 int8 kernels take reductions up to 32768 (64 superchunks of 512;
+# the largest vector per thread and the largest digit buffer in LDS); one
+# 128-column step past it, the layer runs batch 1 on the f16 kernels with v
+# (and u) as hi/lo fp16 planes.  Both reductions: m (stage 1) and k (stage 2).
+LIMIT_SHAPES = [
+    # n, m, k, int8 at batch 1
+    (64, 32768, 64, True),
+    (64, 32896, 64, False),
+    (80, 96, 32768, True),
+    (80, 96, 32832, False),
+]
+
+
+@pytest.mark.parametrize("n,m,k,i8", LIMIT_SHAPES)
+def test_batch1_reduction_limits(gpu, n, m, k, i8):
+    """At and just past the int8 kernels' reduction limit: the oracle's values
+    at batch 1 on the default path, and the same bits on the explicit decode
+    path; the exact path serves the layer at batch 1 only where the int8
+    kernels do."""
+    torch = _torch()
+    _say(f"batch-1 reduction limit n={n} m={m} k={k} int8={i8}")
+    L = inputs.random_layer("lim", n, m, k, 9500 + m + k, 0.02, 1.0, 0.02, (1,))
+    X = L.X[1]
+    H = dbf.Layer(L.A, L.B, L.a, L.mid, L.b, max_batch=1)
+    try:
+        x = torch.from_numpy(X).cuda()
+        y = H.forward(x).cpu().numpy()
+        assert_tol(y, O.dense_forward(X, L.A, L.B, L.a, L.mid, L.b), f"limit {n}x{m}x{k}")
+        yd = H.forward(x, path=dbf.DBF_PATH_DECODE).cpu().numpy()
+        assert np.array_equal(yd.view(np.uint16), y.view(np.uint16))
+        if i8:
+            ye = H.forward(x, path=dbf.DBF_PATH_DECODE_EXACT).cpu().numpy()
+            assert np.array_equal(ye.view(np.uint16), y.view(np.uint16))
+        else:
+            out = torch.empty((1, n), dtype=torch.float16, device="cuda")
+            with pytest.raises(dbf.DbfError) as e:
+                dbf.dbf_linear_forward_ex(H.handle, x.data_ptr(), out.data_ptr(), 1, dbf.DBF_PATH_DECODE_EXACT, 0)
+            assert e.value.status == dbf.DBF_ERR_UNSUPPORTED
+        torch.cuda.synchronize()
+    finally:
+        H.close()
 
 
 # Layers on which the exact path runs batch 2..4 (m and k_pad up to 8192):
