@@ -1064,6 +1064,65 @@ def test_graph_replay_of_prefill_and_backward(gpu):
         H.close()
 
 
+def test_graph_replay_of_decode_paths(gpu):
+    """Decode forwards captured in one HIP graph and replayed several times,
+    with eager work between the replays, give the eager bits every time: the
+    batch-1 int8 kernels (single layer and a group sharing x), the exact path
+    at batch 3, the f16 decode at batch 9 on a wide layer whose stage 1 is cut
+    into ticketed reduction parts, and the no-allocation forward."""
+    torch = _torch()
+    _say("graph replay of the decode paths")
+    m = 640
+    L1 = inputs.random_layer("g1", 300, m, 190, 31, 0.02, 1.0, 0.02, (3,))
+    L2 = inputs.random_layer("g2", 130, m, 260, 32, 0.02, 1.0, 0.02, ())
+    LW = inputs.random_layer("gw", 200, 10300, 600, 33, 0.02, 1.0, 0.02, (9,))
+    H1 = dbf.Layer(L1.A, L1.B, L1.a, L1.mid, L1.b, max_batch=3)
+    H2 = dbf.Layer(L2.A, L2.B, L2.a, L2.mid, L2.b, max_batch=3)
+    HW = dbf.Layer(LW.A, LW.B, LW.a, LW.mid, LW.b, max_batch=9)
+    try:
+        x3 = torch.from_numpy(L1.X[3]).cuda()
+        x1 = x3[:1].clone()
+        xw = torch.from_numpy(LW.X[9]).cuda()
+        outs = {"single": torch.empty((1, 300), dtype=torch.float16, device="cuda"),
+                "g1": torch.empty((1, 300), dtype=torch.float16, device="cuda"),
+                "g2": torch.empty((1, 130), dtype=torch.float16, device="cuda"),
+                "exact": torch.empty((3, 300), dtype=torch.float16, device="cuda"),
+                "wide": torch.empty((9, 200), dtype=torch.float16, device="cuda"),
+                "noalloc": torch.empty((1, 300), dtype=torch.float16, device="cuda")}
+
+        def work(stream):
+            H1.forward(x1, out=outs["single"])
+            dbf.forward_group([H1, H2], x1, [outs["g1"], outs["g2"]])
+            H1.forward(x3, out=outs["exact"], path=dbf.DBF_PATH_DECODE_EXACT)
+            HW.forward(xw, out=outs["wide"])
+            dbf.dbf_linear_forward_noalloc(H1.handle, x1.data_ptr(), outs["noalloc"].data_ptr(), 1, stream)
+        work(torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        want = {k: v.cpu().numpy().copy() for k, v in outs.items()}
+        assert np.array_equal(want["noalloc"].view(np.uint16), want["single"].view(np.uint16))
+        assert np.array_equal(want["exact"][0].view(np.uint16), want["single"][0].view(np.uint16))
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                work(s.cuda_stream)
+        torch.cuda.current_stream().wait_stream(s)
+        for rep in range(4):
+            for t in outs.values():
+                t.fill_(3.0)
+            g.replay()
+            torch.cuda.synchronize()
+            for k, t in outs.items():
+                assert np.array_equal(t.cpu().numpy().view(np.uint16), want[k].view(np.uint16)), (rep, k)
+            HW.forward(xw)   # eager work between replays (the same tickets and partials)
+            torch.cuda.synchronize()
+    finally:
+        H1.close()
+        H2.close()
+        HW.close()
+
+
 def test_non_default_stream(gpu):
     """Forwards enqueued on a side stream give the default-stream results."""
     torch = _torch()
