@@ -711,6 +711,56 @@ __global__ __launch_bounds__(kDThreads) void sign_gemm_dma_group_kernel(const Ge
                               bn, 0, nullptr, 1, 0);
 }
 
+// One product's arguments of dma_tile, with its grid of tiles and its K parts.
+struct DmaPart {
+    const __half *P;
+    int ldp, M;
+    const uint32_t *S;
+    int words, n_rows_pad;
+    const __half *sk, *sn;
+    __half *out;
+    int ldo, n_out;
+    float *out32;
+    int ldo32;
+    DotArgs dot;
+    Affine aff;
+    int nbm, nbn;
+    float *part;
+    int nsplit, ldw;
+};
+
+// A head-and-tail product as one launch: workgroup b first runs head tile b
+// (its columns [0, c0) over the whole K, as the head grid would place it),
+// then, after a barrier that frees the LDS ring, tail piece b (a K part of a
+// column tile from c0 on, as the tail grid would place it) into the split-K
+// workspace.  The pieces, their K ranges and their XCDs are those of the two
+// separate launches, so the results are the same bits; a tail piece starts
+// as soon as its own workgroup's head tile is done, instead of after the
+// slowest head tile and a launch.
+template <bool HAS_SK, bool BIN>
+__global__ __launch_bounds__(kDThreads) void sign_gemm_dma_headtail_kernel(const DmaPart head, const DmaPart tail) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const int b = blockIdx.x;
+    const int TH = head.nbm * head.nbn;
+    if (b < TH) {
+        const int idx = xcd_index(b, TH);
+        const int bm = idx / head.nbn, bn = idx - (idx / head.nbn) * head.nbn;
+        dma_tile<HAS_SK, 2, BIN>(lds, head.P, head.ldp, head.M, head.S, head.words, head.n_rows_pad, head.sk,
+                                 head.sn, head.out, head.ldo, head.n_out, head.out32, head.ldo32, head.dot, head.aff,
+                                 bm, bn, 0, nullptr, 1, 0);
+    }
+    const int TT = tail.nbm * tail.nbn, GT = TT * tail.nsplit;
+    if (b < GT) {
+        __syncthreads();  // every wave is done with the head's LDS stages
+        const int idx = xcd_index(b, GT);
+        const int split = idx / TT, tile = idx - split * TT;
+        const int bm = tile / tail.nbn, bn = tile - (tile / tail.nbn) * tail.nbn;
+        dma_tile<HAS_SK, 2, BIN>(lds, tail.P, tail.ldp, tail.M, tail.S, tail.words, tail.n_rows_pad, tail.sk,
+                                 tail.sn, tail.out, tail.ldo, tail.n_out, tail.out32, tail.ldo32, tail.dot, tail.aff,
+                                 bm, bn, split, tail.part, tail.nsplit, tail.ldw);
+    }
+}
+
 template <bool HAS_SK, int KP, bool BIN>
 void launch_dma(const GemmLaunch &a, hipStream_t s, float *part = nullptr, int nsplit = 1, int ldw = 0) {
     using C = DmaStep<KP>;
@@ -725,6 +775,27 @@ void launch_dma(const GemmLaunch &a, hipStream_t s, float *part = nullptr, int n
                   static_cast<const __half *>(a.P), a.ldp, a.M, a.S, a.words, a.n_rows_pad,
                   static_cast<const __half *>(a.sk), static_cast<const __half *>(a.sn), static_cast<__half *>(a.out),
                   a.ldo, a.n_out, a.out32, a.ldo32, a.dot, a.aff, nbm, nbn, part, nsplit, ldw);
+}
+
+DmaPart dma_part(const GemmLaunch &a, float *part, int nsplit, int ldw) {
+    return DmaPart{static_cast<const __half *>(a.P), a.ldp, a.M, a.S, a.words, a.n_rows_pad,
+                   static_cast<const __half *>(a.sk), static_cast<const __half *>(a.sn), static_cast<__half *>(a.out),
+                   a.ldo, a.n_out, a.out32, a.ldo32, a.dot, a.aff, (a.M + BM - 1) / BM, (a.n_out + DBN - 1) / DBN,
+                   part, nsplit, ldw};
+}
+
+template <bool HAS_SK, bool BIN>
+void launch_headtail(const GemmLaunch &head, const GemmLaunch &tail, hipStream_t s, float *part, int nsplit,
+                     int ldw) {
+    using C = DmaStep<2>;
+    static const bool once =
+        ((void)hipFuncSetAttribute(reinterpret_cast<const void *>(sign_gemm_dma_headtail_kernel<HAS_SK, BIN>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(C::Lds)),
+         true);
+    (void)once;
+    const DmaPart h = dma_part(head, nullptr, 1, 0), t = dma_part(tail, part, nsplit, ldw);
+    const int grid = std::max(h.nbm * h.nbn, t.nbm * t.nbn * nsplit);
+    launch_kernel((sign_gemm_dma_headtail_kernel<HAS_SK, BIN>), dim3(grid), dim3(kDThreads), C::Lds, s, h, t);
 }
 
 #ifndef DBF_SPLIT_BELOW
@@ -759,6 +830,9 @@ int split_parts(int M, int words, int n_out) {
 
 #ifndef DBF_PREFILL_TAIL
 #define DBF_PREFILL_TAIL 1
+#endif
+#ifndef DBF_PREFILL_FUSED_TAIL
+#define DBF_PREFILL_FUSED_TAIL 1
 #endif
 #ifndef DBF_TAIL_BELOW
 #define DBF_TAIL_BELOW 512
@@ -846,13 +920,8 @@ int dispatch(const GemmLaunch &a, hipStream_t s, SplitK *split) {
             const int c0 = tail_split(a.M, a.words, a.n_out, &tparts);
             const int ldt = (a.n_out - c0 + 3) & ~3;
             if (c0 > 0 && static_cast<size_t>(tparts) * a.M * ldt <= split->cap) {
-                // timed as one product: the start event on the head, the stop event on the tail
-                const LaunchEvents ev = launch_events();
-                launch_events() = {ev.start, nullptr};
                 GemmLaunch head = a;  // columns [0, c0), whole K
                 head.n_out = c0;
-                dispatch_dma<HAS_SK, BIN>(head, s, 2);
-                launch_events() = {nullptr, ev.stop};
                 GemmLaunch tail = a;  // columns [c0, n_out): sign rows from 64-row tile c0 / 64 on
                 tail.S = a.S + static_cast<size_t>(c0 / 64) * (a.words >> 1) * 128;
                 tail.n_rows_pad = a.n_rows_pad - c0;
@@ -860,8 +929,17 @@ int dispatch(const GemmLaunch &a, hipStream_t s, SplitK *split) {
                 tail.out = static_cast<__half *>(a.out) + c0;
                 tail.n_out = a.n_out - c0;
                 tail.aff.E = a.aff.E ? a.aff.E + c0 : nullptr;
+#if DBF_PREFILL_FUSED_TAIL
+                launch_headtail<HAS_SK, BIN>(head, tail, s, split->ws, tparts, ldt);
+#else
+                // timed as one product: the start event on the head, the stop event on the tail
+                const LaunchEvents ev = launch_events();
+                launch_events() = {ev.start, nullptr};
+                dispatch_dma<HAS_SK, BIN>(head, s, 2);
+                launch_events() = {nullptr, ev.stop};
                 dispatch_dma<HAS_SK, BIN>(tail, s, 2, split->ws, tparts, ldt);
                 launch_events() = ev;
+#endif
                 split->nsplit = tparts;
                 split->ldw = ldt;
                 split->col0 = c0;
