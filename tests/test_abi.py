@@ -49,6 +49,26 @@ def test_header_compiles_as_c(tmp_path):
     assert res.returncode == 0, res.stderr
 
 
+def test_binding_constants_match_the_header(tmp_path):
+    """Every status, path and flag value the binding uses is the header's:
+    a C program built against dbf.h prints them."""
+    names = ["DBF_OK", "DBF_ERR_INVALID_ARG", "DBF_ERR_SHAPE", "DBF_ERR_OOM", "DBF_ERR_HIP", "DBF_ERR_UNSUPPORTED",
+             "DBF_PATH_AUTO", "DBF_PATH_DECODE", "DBF_PATH_PREFILL", "DBF_PATH_DECODE_TABLE", "DBF_PATH_DECODE_EXACT",
+             "DBF_PACK_BACKWARD"]
+    body = "".join(f'    printf("{n} %d\\n", (int){n});\n' for n in names)
+    src = f'#include <stdio.h>\n#include "dbf.h"\nint main(void) {{\n{body}    return 0;\n}}\n'
+    c = os.path.join(str(tmp_path), "consts.c")
+    exe = os.path.join(str(tmp_path), "consts")
+    open(c, "w").write(src)
+    res = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), c, "-o", exe],
+                         capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+    out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split("\n")
+    values = dict(line.split() for line in out if line)
+    for n in names:
+        assert int(values[n]) == getattr(dbf, n), n
+
+
 def test_status_strings():
     for code in range(6):
         assert dbf.dbf_status_string(code)
