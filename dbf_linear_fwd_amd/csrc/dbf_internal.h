@@ -199,11 +199,17 @@ struct SplitK {
 //   aff_E / aff_stats: out[i][c] = rne16(sn[c] * sum + term(i, c)) with
 //   term(i, c) = Σ_{q < Q-1} aff_E[q * aff_ldE + c] * aff_stats[i * Q + q]
 //   + aff_stats[i * Q + Q - 1] (fp32, q in order; Q = aff_Q).
+//   sk_cols > 0: output columns [j sk_cols, (j + 1) sk_cols) take the per-K
+//   scale sk + j sk_stride (several products that share P, stacked along
+//   the columns, each with its own scale); sk_cols a multiple of 256 (one
+//   scale per output tile), the deep-pipelined product form only (K a
+//   multiple of 64, 16-byte aligned rows of P), no split head and tail.
 struct GemmFlavor {
     int binary = 0;
     const float *aff_E = nullptr;
     const float *aff_stats = nullptr;
     int aff_Q = 2, aff_ldE = 0;
+    int sk_cols = 0, sk_stride = 0;
 };
 int launch_sign_gemm(const void *P, int ldp, int M, int K, const uint32_t *S, int words, int n_rows_pad,
                      const void *sk, const void *sn, void *out, int ldo, int n_out, float *out32, int ldo32,

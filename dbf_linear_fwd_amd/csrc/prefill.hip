@@ -406,6 +406,7 @@ struct GemmLaunch {
     int ldo32;
     DotArgs dot;
     Affine aff;
+    int sk_cols = 0, sk_stride = 0;  // per-column-block scales (GemmFlavor)
 };
 
 template <bool HAS_SK, bool PVEC, bool KFULL, bool BIN>
@@ -679,14 +680,17 @@ __global__ __launch_bounds__(kDThreads) void sign_gemm_dma_kernel(const __half *
                                                                  __half *__restrict__ out, int ldo, int n_out,
                                                                  float *__restrict__ out32, int ldo32, const DotArgs dot,
                                                                  const Affine aff, int nbm, int nbn,
-                                                                 float *__restrict__ part, int nsplit, int ldw) {
+                                                                 float *__restrict__ part, int nsplit, int ldw,
+                                                                 int sk_cols, int sk_stride) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     // order over (split, tile), tile fastest
     const int T = nbm * nbn;
     const int idx = xcd_index(blockIdx.x, T * nsplit);
     const int split = idx / T, tile = idx - split * T;
     const int bm = tile / nbn, bn = tile - (tile / nbn) * nbn;
-    dma_tile<HAS_SK, KP, BIN>(lds, P, ldp, M, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32, dot, aff,
+    // stacked products: this tile's columns take the scale of their block
+    const __half *skt = sk && sk_cols > 0 ? sk + static_cast<size_t>(bn * DBN / sk_cols) * sk_stride : sk;
+    dma_tile<HAS_SK, KP, BIN>(lds, P, ldp, M, S, words, n_rows_pad, skt, sn, out, ldo, n_out, out32, ldo32, dot, aff,
                               bm, bn, split, part, nsplit, ldw);
 }
 
@@ -774,7 +778,8 @@ void launch_dma(const GemmLaunch &a, hipStream_t s, float *part = nullptr, int n
     launch_kernel((sign_gemm_dma_kernel<HAS_SK, KP, BIN>), dim3(nbm * nbn * nsplit), dim3(kDThreads), C::Lds, s,
                   static_cast<const __half *>(a.P), a.ldp, a.M, a.S, a.words, a.n_rows_pad,
                   static_cast<const __half *>(a.sk), static_cast<const __half *>(a.sn), static_cast<__half *>(a.out),
-                  a.ldo, a.n_out, a.out32, a.ldo32, a.dot, a.aff, nbm, nbn, part, nsplit, ldw);
+                  a.ldo, a.n_out, a.out32, a.ldo32, a.dot, a.aff, nbm, nbn, part, nsplit, ldw, a.sk_cols,
+                  a.sk_stride);
 }
 
 DmaPart dma_part(const GemmLaunch &a, float *part, int nsplit, int ldw) {
@@ -917,7 +922,7 @@ int dispatch(const GemmLaunch &a, hipStream_t s, SplitK *split) {
                 return static_cast<int>(hipGetLastError());
             }
             int tparts = 1;
-            const int c0 = tail_split(a.M, a.words, a.n_out, &tparts);
+            const int c0 = a.sk_cols > 0 ? 0 : tail_split(a.M, a.words, a.n_out, &tparts);
             const int ldt = (a.n_out - c0 + 3) & ~3;
             if (c0 > 0 && static_cast<size_t>(tparts) * a.M * ldt <= split->cap) {
                 GemmLaunch head = a;  // columns [0, c0), whole K
@@ -954,6 +959,7 @@ int dispatch(const GemmLaunch &a, hipStream_t s, SplitK *split) {
         return static_cast<int>(hipGetLastError());
     }
 #endif
+    if (a.sk_cols > 0) return static_cast<int>(hipErrorInvalidValue);  // stacked scales: the DMA form only
     if (kfull) launch<HAS_SK, true, true, BIN>(a, s);
     else if (pvec) launch<HAS_SK, true, false, BIN>(a, s);
     else launch<HAS_SK, false, false, BIN>(a, s);
@@ -1004,10 +1010,14 @@ int launch_sign_gemm(const void *P, int ldp, int M, int K, const uint32_t *S, in
                      const void *sk, const void *sn, void *out, int ldo, int n_out, float *out32, int ldo32,
                      const void *dq, int dq_f32, int lddq, float *dpart, void *stream, SplitK *split,
                      const GemmFlavor *flavor) {
-    const GemmLaunch a{P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32,
-                       DotArgs{dq, dq_f32, lddq, dpart},
-                       flavor ? Affine{flavor->aff_E, flavor->aff_stats, flavor->aff_Q, flavor->aff_ldE}
-                              : Affine{}};
+    GemmLaunch a{P, ldp, M, K, S, words, n_rows_pad, sk, sn, out, ldo, n_out, out32, ldo32,
+                 DotArgs{dq, dq_f32, lddq, dpart},
+                 flavor ? Affine{flavor->aff_E, flavor->aff_stats, flavor->aff_Q, flavor->aff_ldE} : Affine{}};
+    if (flavor && flavor->sk_cols > 0) {
+        if (!sk || flavor->sk_cols % DBN != 0 || flavor->sk_stride < K) return static_cast<int>(hipErrorInvalidValue);
+        a.sk_cols = flavor->sk_cols;
+        a.sk_stride = flavor->sk_stride;
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (split) {
         split->nsplit = 1;

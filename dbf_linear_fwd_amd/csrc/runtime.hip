@@ -811,7 +811,23 @@ static dbf_status_t forward_bqq_grouped(dbf_layer *h, const void *x, void *y, in
     dbf::SplitK sp;
     sp.ws = h->split;
     sp.cap = h->split_cap;
-    for (int i = 0; i < p && st == DBF_OK; ++i) {
+    if (d % 256 == 0 && h->m % 64 == 0) {
+        // the p products share x: one product over all p d rows of B (the
+        // terms' rows are consecutive), each 256-column output tile taking
+        // its term's input scale b_i; T = rne16(S (b_term ⊙ x)) (mid = 1)
+        dbf::GemmFlavor f1;
+        f1.sk_cols = d;
+        f1.sk_stride = h->m_pad;
+        st = timed_launch(h, "prefill_gemm1", stream, [&] {
+            return dbf::launch_sign_gemm(x, h->m, batch, h->m, h->B_dev, h->Wm, p * d, h->bqq_b, h->mid_dev, h->T,
+                                         h->k_pad, p * d, nullptr, 0, nullptr, 0, 0, nullptr, stream, &sp, &f1);
+        });
+        if (st == DBF_OK && sp.nsplit > 1)
+            st = timed_launch(h, "prefill_split1", stream, [&] {
+                return dbf::launch_split_finish(sp, batch, p * d, h->mid_dev, h->T, h->k_pad, stream);
+            });
+    }
+    for (int i = 0; i < p && st == DBF_OK && !(d % 256 == 0 && h->m % 64 == 0); ++i) {
         // T[:, i d : (i + 1) d] = rne16(S_i (b_i ⊙ x)) (mid = 1); B's rows of term i from its 64-row tile i d / 64
         const uint32_t *S = h->B_dev + static_cast<size_t>(i) * (d / 64) * (h->Wm >> 1) * 128;
         const uint16_t *bi = h->bqq_b + static_cast<size_t>(i) * h->m_pad;

@@ -113,6 +113,23 @@ def test_grouped_split_k(gpu, batch):
     _assert_tol(_run(L, X), _ref(L, X), f"grouped split-K b{batch}")
 
 
+# Above the decode batches, the p first products run as one product over all
+# p d rows of B when d is a multiple of 256 and m of 64 (each 256-column
+# output tile takes its own term's input scale); otherwise one product per
+# term.  Both forms, ragged groups, split-K and whole-K grids, and integer
+# data bit-exact.
+@pytest.mark.parametrize("n,m,d,p,group", [(200, 640, 256, 3, 64), (70, 300, 256, 2, 100), (130, 512, 256, 2, 48)])
+@pytest.mark.parametrize("batch", [17, 300])
+def test_grouped_stacked_first_products(gpu, n, m, d, p, group, batch):
+    _say(f"bqq grouped stacked n={n} m={m} d={d} p={p} group={group} batch={batch}")
+    L = inputs.bqq_grouped_layer("gs", n, m, d, p, group, 8400 + n + m + batch, (batch,))
+    X = L.X[batch]
+    _assert_tol(_run(L, X), _ref(L, X), f"grouped stacked {n}x{m} d{d} p{p} g{group} b{batch}")
+    Li = inputs.bqq_grouped_layer("gsi", n, m, d, p, group, 8500 + n + m + batch, (batch,), integer=True)
+    Xi = Li.X[batch]
+    _assert_bits(_run(Li, Xi), _integer_preconditions(Li, Xi, True), f"grouped stacked integer b{batch}")
+
+
 def _integer_preconditions(L, X, fp16_intermediate):
     """Integer data: the first stage's signed sums t_i = (1 - 2 Z_i)(b_i ⊙ x)
     (b_i[l] = r_i[l // group]) are integers, exact in fp16 where the path
