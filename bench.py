@@ -540,13 +540,21 @@ def time_exact(step, steps, warmup, start=0):
     return e0.elapsed_time(e1) / 1e3
 
 
+# device-side spin ahead of each timed round of eager forwards (about 10 ms
+# at 2 GHz: longer than the host takes to enqueue a round)
+SPIN_CYCLES = 20_000_000
+
+
 def block_kernel_times(blk, passes=3):
     """Per-launch time (us) of each decode kernel of the block, from HIP
     events riding on the launches: after one untimed round over all copies
     (the clocks settle after the idle spells of eager launching), `passes`
     rounds of eager steps over all copies, each giving an average per
     kernel; the median of the passes' averages is reported (one perturbed
-    pass does not move it)."""
+    pass does not move it).  Each round is queued behind a short device-side
+    spin, so that the host has enqueued the whole round before it starts and
+    its kernels run back to back, as in the graph replay, rather than one
+    at a time with the GPU idle between host calls."""
     import dbf_linear_fwd_amd as dbf
     import torch
     heads = {"qkv": "q", "o": "o", "gateup": "gate", "down": "down"}
@@ -560,6 +568,7 @@ def block_kernel_times(blk, passes=3):
                 dbf.dbf_timing_enable(c[h].handle, True)
                 dbf.dbf_timing_read(c[h].handle)
         torch.cuda.synchronize()
+        torch.cuda._sleep(SPIN_CYCLES)
         for i in range(blk.R):
             blk.step(i)
         torch.cuda.synchronize()
